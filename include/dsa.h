@@ -1,0 +1,210 @@
+/*
+ * dsa.h -- C ABI of a gfx950 (MI355X) implementation of the DeepSeek-style
+ * sparse attention (DSA) step over a block-packed paged cache.
+ *
+ * Pages cited (title, then section):
+ *   [ZH]     "vLLM 为 Kimi K3.1 Pro 提供 Day-0 支持"
+ *   [EN]     "vLLM Adds Day-0 Support for Moonshot AI's Kimi K3.1 Pro"
+ *   [RECIPE] "moonshotai/Kimi-K3.1-Pro"
+ *
+ * The step, per DSA layer ([ZH] "K3.1 Pro 中的稀疏注意力", figure 1):
+ *   1. dsa_resolve_pages      block table -> kernel page addresses
+ *   2. dsa_indexer_score      every earlier token scored by a 32-head indexer
+ *   3. dsa_topk               the 2048 best tokens kept per query row
+ *   4. dsa_sparse_mla_decode / dsa_sparse_mla_prefill
+ *                             exact MLA attention over only those tokens
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Memory: every buffer is allocated by the caller.  Pointers documented
+ *    as "device" must be device (HBM) memory; "host" means host memory.  The
+ *    library allocates no device memory; scratch space is a caller buffer
+ *    sized by the matching *_workspace_size call.
+ *  - Streams: device calls enqueue asynchronously on `stream` (a hipStream_t
+ *    passed as an opaque pointer; NULL = the null stream) and never block
+ *    the host.  Calls hold no state between them and may be made from any
+ *    thread; calls that share a workspace must not overlap.
+ *  - Errors: arguments are checked on the host before anything is
+ *    enqueued; a bad argument returns a non-zero dsa_status and enqueues
+ *    nothing.  DSA_ERR_HIP means a launch failed (hipGetLastError).  Errors
+ *    in device data (a block id outside the pool, an index past a request's
+ *    context, ...) cannot be seen on the host: kernels OR a DSA_DEVERR_* bit
+ *    into the optional device int32 `err_flag` (NULL = do not report), skip
+ *    the offending element, and never trap.
+ *  - Layouts are row-major; `*_ld` arguments are leading dimensions in
+ *    elements.  bf16 values are passed as uint16_t bit patterns.
+ *  - Floating-point data must be finite; NaN/Inf inputs give unspecified
+ *    (but memory-safe) results.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *dsa_stream_t; /* hipStream_t */
+typedef int32_t dsa_status;
+
+#define DSA_OK 0
+#define DSA_ERR_NULL_ARG 1            /* a required pointer is NULL */
+#define DSA_ERR_BAD_SHAPE 2           /* a size, count or leading dimension is invalid */
+#define DSA_ERR_MISALIGNED 3          /* a pointer lacks the alignment stated for it */
+#define DSA_ERR_UNSUPPORTED 4         /* a format, head count or size this build does not run */
+#define DSA_ERR_WORKSPACE_TOO_SMALL 5 /* workspace_bytes < the *_workspace_size answer */
+#define DSA_ERR_HIP 6                 /* a HIP launch failed */
+
+/* Bits kernels OR into *err_flag. */
+#define DSA_DEVERR_BLOCK_RANGE 1u  /* block id outside [0, pool_rows) */
+#define DSA_DEVERR_PAGE_COUNT 2u   /* n_pages outside [0, max_pages] */
+#define DSA_DEVERR_PAGE_OFFSET 4u  /* page offset negative or page outside the pool */
+#define DSA_DEVERR_ROW_LEN 8u      /* row_len outside [0, ld] or past the page table */
+#define DSA_DEVERR_INDEX 16u       /* selected index outside [0, ctx_len) */
+#define DSA_DEVERR_REQUEST 32u     /* q_req outside [0, n_req) */
+
+/* Index-key row formats ([ZH] "K3.1 Pro 中的稀疏注意力" and "量化：原生 MXFP4 索引器"). */
+#define DSA_KEY_FP8_E4M3_SCALED 0 /* 132 B: 128 OCP e4m3 codes, then a little-endian fp32 scale */
+#define DSA_KEY_MXFP4 1           /* 68 B: 64 B of e2m1 pairs (element 2i in the low nibble),
+                                     then 4 E8M0 scales (dims 0-31, 32-63, 64-95, 96-127) */
+/* Latent row formats ([EN] "Sparse attention targets long-context costs"; [RECIPE] "NVFP4 KV cache"). */
+#define DSA_LAT_FP8_E4M3 0 /* 576 B: 576 e4m3 codes; value = code * kv_scale */
+#define DSA_LAT_NVFP4 1    /* 352 B: 256 B e2m1 pairs for dims 0-511, 32 e4m3 block scales
+                              (one per 16 dims), 64 e4m3 rope dims 512-575;
+                              value = code * block_scale * kv_scale (rope: code * kv_scale) */
+/* Query formats. */
+#define DSA_Q_BF16 0     /* bf16 values */
+#define DSA_Q_FP8_E4M3 1 /* e4m3 codes plus one fp32 scale per (row, head): value = code * scale */
+
+/* Block-packed cache layout ([ZH] "面向三种状态的 KV 缓存", figure 3): one
+ * contiguous row per cache block holds, for each DSA layer in turn, the
+ * layer's latent page (page_size latents) then its key page (page_size keys);
+ * each layer slot is rounded up to 256 B and opaque per-block extra state
+ * (e.g. recurrent state) follows the last layer:
+ *   lat_page(row, layer) = row*row_stride + layer*layer_stride
+ *   key_page(row, layer) = lat_page(row, layer) + lat_page_bytes
+ *   token slot s of a page: + s*lat_bytes (latent) / + s*key_bytes (key)   */
+typedef struct dsa_layout {
+  int32_t page_size; /* tokens per page (64 on this build) */
+  int32_t n_layers;
+  int32_t key_fmt; /* DSA_KEY_* */
+  int32_t lat_fmt; /* DSA_LAT_* */
+  int32_t key_bytes;
+  int32_t lat_bytes;
+  int64_t lat_page_bytes;
+  int64_t key_page_bytes;
+  int64_t layer_stride;
+  int64_t extra_row_bytes;
+  int64_t row_stride;
+} dsa_layout;
+
+/* Static, NUL-terminated text for a status code / the library version. */
+const char *dsa_status_str(dsa_status s);
+const char *dsa_version(void);
+
+/* Fill *out (host) for the given page size, layer count, formats and extra
+ * per-row bytes.  Host only.  DSA_ERR_BAD_SHAPE for a non-positive page size
+ * or layer count or negative extra bytes; DSA_ERR_UNSUPPORTED for an unknown
+ * format. */
+dsa_status dsa_layout_make(int32_t page_size, int32_t n_layers, int32_t key_fmt, int32_t lat_fmt,
+                           int64_t extra_row_bytes, dsa_layout *out);
+
+/* Page resolve ([ZH] "面向三种状态的 KV 缓存": before each step, block tables
+ * and cache slots become the kernels' page addresses, so the kernels read the
+ * packed cache unmodified).  Integer only.
+ *   block_table  device int32 [n_req][bt_ld]   pool row of each logical page
+ *   n_pages      device int32 [n_req]          pages in use per request
+ *   lat_off, key_off  device int64 [n_req][off_ld]  (out) byte offsets from the
+ *                pool base of layer `layer`'s latent / key page; for pages
+ *                p < max_pages: p >= n_pages[b] or a bad block id gives -1
+ *                (the latter also sets DSA_DEVERR_BLOCK_RANGE); columns
+ *                >= max_pages are not written.
+ * Requires max_pages <= bt_ld and max_pages <= off_ld, 0 <= layer < n_layers. */
+dsa_status dsa_resolve_pages(const dsa_layout *layout, int32_t layer, const int32_t *block_table, int64_t bt_ld,
+                             const int32_t *n_pages, int32_t n_req, int32_t max_pages, int64_t pool_rows,
+                             int64_t *lat_off, int64_t *key_off, int64_t off_ld, int32_t *err_flag,
+                             dsa_stream_t stream);
+
+/* Indexer score ([ZH] "K3.1 Pro 中的稀疏注意力": one 132-byte FP8 key per token,
+ * 32 light heads score every earlier token for each query; MXFP4 keys per
+ * "量化：原生 MXFP4 索引器").  For query row r, request b = q_req[r], and every
+ * token t < row_len[r] of request b:
+ *     score[r][t] = sum_{j<32} w[r][j] * max(0, (q[r][j] . k_t) * scale_t)
+ * with k_t the decoded key (MXFP4: E8M0 block scales included, scale_t = 1);
+ * fp32 result, fp32 accumulation.  Decode: one row per request, row_len =
+ * context length.  Prefill: row_len = position + 1 (causal).
+ *   pool       device uint8, pool_bytes long, 16-B aligned
+ *   key_off    device int64 [n_req][off_ld] from dsa_resolve_pages
+ *   q          device [n_q][32][128]: bf16 (q_fmt DSA_Q_BF16) or e4m3 codes
+ *              (DSA_Q_FP8_E4M3, with q_scale device fp32 [n_q][32]; else NULL)
+ *   w          device fp32 [n_q][32]
+ *   q_req, row_len  device int32 [n_q]
+ *   scores     device fp32 [n_q][ld] (out): entries t < row_len[r] written,
+ *              the rest untouched.
+ * The BF16 path streams each row's keys (decode); the FP8 path is an MFMA
+ * GEMM over tiles of consecutive rows and is fastest when consecutive rows
+ * share a request (a prefill chunk).  Both accept any q_req. */
+dsa_status dsa_indexer_score(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                             const int64_t *key_off, int64_t off_ld, int32_t n_req, const void *q, int32_t q_fmt,
+                             const float *q_scale, const float *w, const int32_t *q_req, const int32_t *row_len,
+                             int32_t n_q, float *scores, int64_t ld, int32_t *err_flag, dsa_stream_t stream);
+
+/* Top-k ([ZH] "K3.1 Pro 中的稀疏注意力": the top 2048 are kept; an exact top-k
+ * per "低延迟解码：融合的 DSA 解码路径").  For each row r, the min(k, row_len[r])
+ * tokens with the largest scores[r][t]; a tie goes to the lower token index
+ * (one consistent tie-break, cf. "通信：高效的跨 GPU 通信"), -0 equals +0.
+ * Output idx[r][0..k): the kept token indices in ascending order, then -1.
+ * The result depends only on the row's own scores (batch-invariant, cf.
+ * "day 0 零失配 RL") and is bitwise deterministic.
+ *   scores  device fp32 [n_rows][ld]; row_len device int32 [n_rows]
+ *   idx     device int32 [n_rows][idx_ld] (out), idx_ld >= k
+ *   workspace  device, >= dsa_topk_workspace_size(n_rows, ld, k) bytes, 16-B aligned
+ * 1 <= k <= 4096. */
+dsa_status dsa_topk_workspace_size(int32_t n_rows, int64_t ld, int32_t k, size_t *bytes);
+dsa_status dsa_topk(const float *scores, int64_t ld, const int32_t *row_len, int32_t n_rows, int32_t k, int32_t *idx,
+                    int64_t idx_ld, void *workspace, size_t workspace_bytes, int32_t *err_flag, dsa_stream_t stream);
+
+/* Sparse MLA decode ([ZH] "K3.1 Pro 中的稀疏注意力": every query head attends
+ * exactly to the kept tokens' latents; partial results merged by
+ * log-sum-exp as in "长上下文：带稀疏 indexer 的 decode 上下文并行").
+ * For request b, head h and the non-negative entries t of idx[b] (each
+ * entry one term; -1 entries are skipped):
+ *     z_t = sm_scale * (q[b][h] . kv_t)                 kv_t includes kv_scale
+ *     lse[b][h] = ln sum_t exp(z_t)
+ *     out[b][h][c] = sum_t exp(z_t - lse) * kv_t[c]     c < 512 (values = first 512 dims)
+ * An empty set writes out = 0, lse = -inf.  Entries >= ctx_len[b] are
+ * skipped and flag DSA_DEVERR_INDEX.
+ *   pool, lat_off (device, from dsa_resolve_pages), ctx_len device int32 [n_req]
+ *   idx   device int32 [n_req][idx_ld] (logical token ids)
+ *   q     device bf16 [n_req][n_heads][576]
+ *   out   device bf16 [n_req][n_heads][512] (out); lse device fp32 [n_req][n_heads] (out)
+ *   workspace  device, >= dsa_sparse_mla_decode_workspace_size(...) bytes
+ * 1 <= n_heads <= 128. */
+dsa_status dsa_sparse_mla_decode_workspace_size(int32_t n_req, int32_t n_heads, int32_t k, size_t *bytes);
+dsa_status dsa_sparse_mla_decode(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                                 const int64_t *lat_off, int64_t off_ld, const int32_t *ctx_len, const int32_t *idx,
+                                 int64_t idx_ld, int32_t k, const uint16_t *q, int32_t n_req, int32_t n_heads,
+                                 float sm_scale, float kv_scale, uint16_t *out, float *lse, void *workspace,
+                                 size_t workspace_bytes, int32_t *err_flag, dsa_stream_t stream);
+
+/* Sparse MLA prefill ([ZH] "预填充：上下文并行稀疏注意力": each query row of a
+ * prefill chunk attends over its own selected tokens, all local heads at
+ * once).  Same definition as the decode call, per query row r with request
+ * b = q_req[r] and set idx[r]; q is bf16 or e4m3 codes with q_scale device
+ * fp32 [n_q][n_heads] (value = code * scale).
+ *   q    device [n_q][n_heads][576];  q_req device int32 [n_q]
+ *   out  device bf16 [n_q][n_heads][512] (out); lse device fp32 [n_q][n_heads] (out) */
+dsa_status dsa_sparse_mla_prefill_workspace_size(int32_t n_q, int32_t n_heads, int32_t k, size_t *bytes);
+dsa_status dsa_sparse_mla_prefill(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                                  const int64_t *lat_off, int64_t off_ld, int32_t n_req, const int32_t *ctx_len,
+                                  const int32_t *idx, int64_t idx_ld, int32_t k, const void *q, int32_t q_fmt,
+                                  const float *q_scale, const int32_t *q_req, int32_t n_q, int32_t n_heads,
+                                  float sm_scale, float kv_scale, uint16_t *out, float *lse, void *workspace,
+                                  size_t workspace_bytes, int32_t *err_flag, dsa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

@@ -1,0 +1,209 @@
+"""Python binding of libdsa (gfx950 HIP kernels for the DSA step), via ctypes.
+
+Argument marshalling only: each ``dsa_*`` function below checks tensor
+devices/dtypes, passes raw pointers and sizes to the C entry point of the same
+name (``include/dsa.h``), and raises ``DsaError`` on a non-zero status.  All
+computation runs in the library's kernels.  There is no fallback: if the
+library is not built, importing this package raises.
+
+Tensors are torch tensors on the GPU; the stream defaults to torch's current
+stream.  bf16 tensors are passed as their bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from pathlib import Path
+
+import torch
+
+from .build import LIB as _LIB_PATH
+
+DSA_OK, DSA_ERR_NULL_ARG, DSA_ERR_BAD_SHAPE, DSA_ERR_MISALIGNED = 0, 1, 2, 3
+DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE_TOO_SMALL, DSA_ERR_HIP = 4, 5, 6
+DSA_DEVERR_BLOCK_RANGE, DSA_DEVERR_PAGE_COUNT, DSA_DEVERR_PAGE_OFFSET = 1, 2, 4
+DSA_DEVERR_ROW_LEN, DSA_DEVERR_INDEX, DSA_DEVERR_REQUEST = 8, 16, 32
+DSA_KEY_FP8_E4M3_SCALED, DSA_KEY_MXFP4 = 0, 1
+DSA_LAT_FP8_E4M3, DSA_LAT_NVFP4 = 0, 1
+DSA_Q_BF16, DSA_Q_FP8_E4M3 = 0, 1
+
+__all__ = [
+    "DsaError", "dsa_layout", "lib", "dsa_status_str", "dsa_version", "dsa_layout_make", "dsa_resolve_pages",
+    "dsa_indexer_score", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_decode_workspace_size",
+    "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill_workspace_size", "dsa_sparse_mla_prefill",
+]
+
+
+class DsaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: status {status} ({dsa_status_str(status)})")
+        self.status = status
+
+
+class dsa_layout(C.Structure):
+    _fields_ = [("page_size", C.c_int32), ("n_layers", C.c_int32), ("key_fmt", C.c_int32), ("lat_fmt", C.c_int32),
+                ("key_bytes", C.c_int32), ("lat_bytes", C.c_int32), ("lat_page_bytes", C.c_int64),
+                ("key_page_bytes", C.c_int64), ("layer_stride", C.c_int64), ("extra_row_bytes", C.c_int64),
+                ("row_stride", C.c_int64)]
+
+    def as_dict(self) -> dict:
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+def _load():
+    if not _LIB_PATH.exists():
+        raise ImportError(f"{_LIB_PATH} is not built; run `python -m long_context_sparse_paged_amd.build` "
+                          "(the DSA kernels have no CPU fallback)")
+    L = C.CDLL(str(_LIB_PATH))
+    P, I32, I64, SZ, F = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_float
+    LP = C.POINTER(dsa_layout)
+    sig = {
+        "dsa_status_str": ([I32], C.c_char_p),
+        "dsa_version": ([], C.c_char_p),
+        "dsa_layout_make": ([I32, I32, I32, I32, I64, LP], I32),
+        "dsa_resolve_pages": ([LP, I32, P, I64, P, I32, I32, I64, P, P, I64, P, P], I32),
+        "dsa_indexer_score": ([LP, P, I64, P, I64, I32, P, I32, P, P, P, P, I32, P, I64, P, P], I32),
+        "dsa_topk_workspace_size": ([I32, I64, I32, C.POINTER(SZ)], I32),
+        "dsa_topk": ([P, I64, P, I32, I32, P, I64, P, SZ, P, P], I32),
+        "dsa_sparse_mla_decode_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
+        "dsa_sparse_mla_decode": ([LP, P, I64, P, I64, P, P, I64, I32, P, I32, I32, F, F, P, P, P, SZ, P, P], I32),
+        "dsa_sparse_mla_prefill_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
+        "dsa_sparse_mla_prefill": ([LP, P, I64, P, I64, I32, P, P, I64, I32, P, I32, P, P, I32, I32, F, F, P, P, P,
+                                    SZ, P, P], I32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    return L
+
+
+lib = _load()
+
+
+def dsa_status_str(s: int) -> str:
+    return lib.dsa_status_str(s).decode()
+
+
+def dsa_version() -> str:
+    return lib.dsa_version().decode()
+
+
+def _check(fn: str, st: int):
+    if st != DSA_OK:
+        raise DsaError(fn, st)
+
+
+def _ptr(t, dtypes=None, name="tensor"):
+    """Device pointer of a contiguous GPU tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise TypeError(f"{name}: must be a GPU tensor (no CPU path exists)")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise TypeError(f"{name}: must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+I32, I64, U8, F32 = (torch.int32,), (torch.int64,), (torch.uint8,), (torch.float32,)
+BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def dsa_layout_make(page_size: int, n_layers: int, key_fmt: int, lat_fmt: int, extra_row_bytes: int = 0) -> dsa_layout:
+    out = dsa_layout()
+    _check("dsa_layout_make", lib.dsa_layout_make(page_size, n_layers, key_fmt, lat_fmt, extra_row_bytes, C.byref(out)))
+    return out
+
+
+def dsa_resolve_pages(layout: dsa_layout, layer: int, block_table, n_pages, pool_rows: int, lat_off, key_off,
+                      err_flag=None, stream=None):
+    n_req, max_pages = block_table.shape
+    st = lib.dsa_resolve_pages(C.byref(layout), layer, _ptr(block_table, I32, "block_table"), block_table.stride(0),
+                               _ptr(n_pages, I32, "n_pages"), n_req, max_pages, pool_rows,
+                               _ptr(lat_off, I64, "lat_off"), _ptr(key_off, I64, "key_off"), lat_off.shape[1],
+                               _ptr(err_flag, I32, "err_flag"), _stream(stream))
+    _check("dsa_resolve_pages", st)
+
+
+def dsa_indexer_score(layout: dsa_layout, pool, key_off, n_req: int, q, q_fmt: int, q_scale, w, q_req, row_len,
+                      scores, err_flag=None, stream=None):
+    qd = BF16 if q_fmt == DSA_Q_BF16 else U8
+    st = lib.dsa_indexer_score(C.byref(layout), _ptr(pool, U8, "pool"), pool.numel(), _ptr(key_off, I64, "key_off"),
+                               key_off.shape[1], n_req, _ptr(q, qd, "q"), q_fmt, _ptr(q_scale, F32, "q_scale"),
+                               _ptr(w, F32, "w"), _ptr(q_req, I32, "q_req"), _ptr(row_len, I32, "row_len"),
+                               row_len.shape[0], _ptr(scores, F32, "scores"), scores.shape[1],
+                               _ptr(err_flag, I32, "err_flag"), _stream(stream))
+    _check("dsa_indexer_score", st)
+
+
+def dsa_topk_workspace_size(n_rows: int, ld: int, k: int) -> int:
+    out = C.c_size_t()
+    _check("dsa_topk_workspace_size", lib.dsa_topk_workspace_size(n_rows, ld, k, C.byref(out)))
+    return out.value
+
+
+def dsa_topk(scores, row_len, k: int, idx, workspace, err_flag=None, stream=None):
+    st = lib.dsa_topk(_ptr(scores, F32, "scores"), scores.shape[1], _ptr(row_len, I32, "row_len"), scores.shape[0], k,
+                      _ptr(idx, I32, "idx"), idx.shape[1], _ptr(workspace, None, "workspace"),
+                      workspace.numel() * workspace.element_size(), _ptr(err_flag, I32, "err_flag"), _stream(stream))
+    _check("dsa_topk", st)
+
+
+def dsa_sparse_mla_decode_workspace_size(n_req: int, n_heads: int, k: int) -> int:
+    out = C.c_size_t()
+    _check("dsa_sparse_mla_decode_workspace_size",
+           lib.dsa_sparse_mla_decode_workspace_size(n_req, n_heads, k, C.byref(out)))
+    return out.value
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size()
+
+
+def dsa_sparse_mla_decode(layout: dsa_layout, pool, lat_off, ctx_len, idx, k: int, q, sm_scale: float,
+                          kv_scale: float, out, lse, workspace=None, err_flag=None, stream=None):
+    n_req, n_heads = q.shape[0], q.shape[1]
+    wp, wb = _ws(workspace)
+    st = lib.dsa_sparse_mla_decode(C.byref(layout), _ptr(pool, U8, "pool"), pool.numel(),
+                                   _ptr(lat_off, I64, "lat_off"), lat_off.shape[1], _ptr(ctx_len, I32, "ctx_len"),
+                                   _ptr(idx, I32, "idx"), idx.shape[1], k, _ptr(q, BF16, "q"), n_req, n_heads,
+                                   float(sm_scale), float(kv_scale), _ptr(out, BF16, "out"), _ptr(lse, F32, "lse"),
+                                   wp, wb, _ptr(err_flag, I32, "err_flag"), _stream(stream))
+    _check("dsa_sparse_mla_decode", st)
+
+
+def dsa_sparse_mla_prefill_workspace_size(n_q: int, n_heads: int, k: int) -> int:
+    out = C.c_size_t()
+    _check("dsa_sparse_mla_prefill_workspace_size",
+           lib.dsa_sparse_mla_prefill_workspace_size(n_q, n_heads, k, C.byref(out)))
+    return out.value
+
+
+def dsa_sparse_mla_prefill(layout: dsa_layout, pool, lat_off, n_req: int, ctx_len, idx, k: int, q, q_fmt: int,
+                           q_scale, q_req, sm_scale: float, kv_scale: float, out, lse, workspace=None,
+                           err_flag=None, stream=None):
+    n_q, n_heads = q.shape[0], q.shape[1]
+    qd = BF16 if q_fmt == DSA_Q_BF16 else U8
+    wp, wb = _ws(workspace)
+    st = lib.dsa_sparse_mla_prefill(C.byref(layout), _ptr(pool, U8, "pool"), pool.numel(),
+                                    _ptr(lat_off, I64, "lat_off"), lat_off.shape[1], n_req,
+                                    _ptr(ctx_len, I32, "ctx_len"), _ptr(idx, I32, "idx"), idx.shape[1], k,
+                                    _ptr(q, qd, "q"), q_fmt, _ptr(q_scale, F32, "q_scale"), _ptr(q_req, I32, "q_req"),
+                                    n_q, n_heads, float(sm_scale), float(kv_scale), _ptr(out, BF16, "out"),
+                                    _ptr(lse, F32, "lse"), wp, wb, _ptr(err_flag, I32, "err_flag"), _stream(stream))
+    _check("dsa_sparse_mla_prefill", st)
+
+
+from .step import DecodeStep, PrefillStep  # noqa: E402,F401

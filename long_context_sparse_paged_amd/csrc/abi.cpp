@@ -1,0 +1,274 @@
+// abi.cpp -- the C entry points declared in include/dsa.h.
+// Every argument is checked here, on the host, before anything is enqueued.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "dsa_device.hpp"
+#include "dsa_kernels.hpp"
+
+using namespace dsa;
+
+namespace {
+
+// Token splits of the decode attention: fixed, so a request's result does not
+// depend on the batch it is in.
+constexpr int32_t kDecodeTokensPerSplit = 128;
+constexpr int32_t kMaxHeads = 128;
+constexpr int32_t kMaxGridY = 65535;
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+
+int64_t round_up_256(int64_t x) { return (x + 255) / 256 * 256; }
+
+dsa_status check_layout(const dsa_layout *L) {
+  if (!L) return DSA_ERR_NULL_ARG;
+  dsa_layout ref;
+  const dsa_status s = dsa_layout_make(L->page_size, L->n_layers, L->key_fmt, L->lat_fmt, L->extra_row_bytes, &ref);
+  if (s != DSA_OK) return s;
+  if (ref.key_bytes != L->key_bytes || ref.lat_bytes != L->lat_bytes || ref.lat_page_bytes != L->lat_page_bytes ||
+      ref.key_page_bytes != L->key_page_bytes || ref.layer_stride != L->layer_stride || ref.row_stride != L->row_stride)
+    return DSA_ERR_BAD_SHAPE;
+  if (L->page_size != kPage) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
+dsa_status launched(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+hipStream_t stream_of(dsa_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char *dsa_status_str(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_NULL_ARG: return "a required pointer is NULL";
+    case DSA_ERR_BAD_SHAPE: return "invalid size, count or leading dimension";
+    case DSA_ERR_MISALIGNED: return "pointer lacks the required alignment";
+    case DSA_ERR_UNSUPPORTED: return "format, head count or size not supported";
+    case DSA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the *_workspace_size answer";
+    case DSA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char *dsa_version(void) { return "dsa-gfx950 0.1"; }
+
+dsa_status dsa_layout_make(int32_t page_size, int32_t n_layers, int32_t key_fmt, int32_t lat_fmt,
+                           int64_t extra_row_bytes, dsa_layout *out) {
+  if (!out) return DSA_ERR_NULL_ARG;
+  if (page_size <= 0 || n_layers <= 0 || extra_row_bytes < 0) return DSA_ERR_BAD_SHAPE;
+  if ((key_fmt != DSA_KEY_FP8_E4M3_SCALED && key_fmt != DSA_KEY_MXFP4) ||
+      (lat_fmt != DSA_LAT_FP8_E4M3 && lat_fmt != DSA_LAT_NVFP4))
+    return DSA_ERR_UNSUPPORTED;
+  dsa_layout L;
+  memset(&L, 0, sizeof L);
+  L.page_size = page_size;
+  L.n_layers = n_layers;
+  L.key_fmt = key_fmt;
+  L.lat_fmt = lat_fmt;
+  L.key_bytes = key_fmt == DSA_KEY_FP8_E4M3_SCALED ? 132 : 68;
+  L.lat_bytes = lat_fmt == DSA_LAT_FP8_E4M3 ? 576 : 352;
+  L.lat_page_bytes = (int64_t)page_size * L.lat_bytes;
+  L.key_page_bytes = (int64_t)page_size * L.key_bytes;
+  L.layer_stride = round_up_256(L.lat_page_bytes + L.key_page_bytes);
+  L.extra_row_bytes = extra_row_bytes;
+  L.row_stride = round_up_256((int64_t)n_layers * L.layer_stride + extra_row_bytes);
+  *out = L;
+  return DSA_OK;
+}
+
+dsa_status dsa_resolve_pages(const dsa_layout *layout, int32_t layer, const int32_t *block_table, int64_t bt_ld,
+                             const int32_t *n_pages, int32_t n_req, int32_t max_pages, int64_t pool_rows,
+                             int64_t *lat_off, int64_t *key_off, int64_t off_ld, int32_t *err_flag,
+                             dsa_stream_t stream) {
+  dsa_status st = check_layout(layout);
+  if (st != DSA_OK) return st;
+  if (!block_table || !n_pages || !lat_off || !key_off) return DSA_ERR_NULL_ARG;
+  if (n_req < 0 || max_pages < 0 || pool_rows < 0 || bt_ld < max_pages || off_ld < max_pages || layer < 0 ||
+      layer >= layout->n_layers)
+    return DSA_ERR_BAD_SHAPE;
+  if (n_req > kMaxGridY) return DSA_ERR_UNSUPPORTED;
+  if (!aligned(block_table, 4) || !aligned(n_pages, 4) || !aligned(lat_off, 8) || !aligned(key_off, 8) ||
+      !aligned(err_flag, 4))
+    return DSA_ERR_MISALIGNED;
+  ResolveArgs a;
+  a.bt = block_table;
+  a.bt_ld = bt_ld;
+  a.n_pages = n_pages;
+  a.n_req = n_req;
+  a.max_pages = max_pages;
+  a.pool_rows = pool_rows;
+  a.row_stride = layout->row_stride;
+  a.layer_off = (int64_t)layer * layout->layer_stride;
+  a.lat_page_bytes = layout->lat_page_bytes;
+  a.lat_off = lat_off;
+  a.key_off = key_off;
+  a.off_ld = off_ld;
+  a.err = err_flag;
+  return launched(launch_resolve(a, stream_of(stream)));
+}
+
+dsa_status dsa_indexer_score(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                             const int64_t *key_off, int64_t off_ld, int32_t n_req, const void *q, int32_t q_fmt,
+                             const float *q_scale, const float *w, const int32_t *q_req, const int32_t *row_len,
+                             int32_t n_q, float *scores, int64_t ld, int32_t *err_flag, dsa_stream_t stream) {
+  dsa_status st = check_layout(layout);
+  if (st != DSA_OK) return st;
+  if (q_fmt != DSA_Q_BF16 && q_fmt != DSA_Q_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
+  if (n_q < 0 || n_req < 0 || ld < 0 || off_ld < 1 || pool_bytes < 0) return DSA_ERR_BAD_SHAPE;
+  if (n_q == 0) return DSA_OK;
+  if (!pool || !key_off || !q || !w || !q_req || !row_len || !scores) return DSA_ERR_NULL_ARG;
+  if (q_fmt == DSA_Q_FP8_E4M3 && !q_scale) return DSA_ERR_NULL_ARG;
+  if (!aligned(pool, 16) || !aligned(q, 16) || !aligned(key_off, 8) || !aligned(w, 4) || !aligned(q_req, 4) ||
+      !aligned(row_len, 4) || !aligned(scores, 4) || !aligned(q_scale, 4) || !aligned(err_flag, 4))
+    return DSA_ERR_MISALIGNED;
+  ScoreArgs a;
+  a.pool = pool;
+  a.pool_bytes = pool_bytes;
+  a.key_off = key_off;
+  a.off_ld = off_ld;
+  a.n_req = n_req;
+  a.q = q;
+  a.q_scale = q_scale;
+  a.w = w;
+  a.q_req = q_req;
+  a.row_len = row_len;
+  a.n_q = n_q;
+  a.scores = scores;
+  a.ld = ld;
+  a.err = err_flag;
+  a.key_fmt = layout->key_fmt;
+  if (q_fmt == DSA_Q_BF16) {
+    if (n_q > 4096) return DSA_ERR_UNSUPPORTED;
+    return launched(launch_indexer_scan(a, stream_of(stream)));
+  }
+  if (layout->key_fmt != DSA_KEY_FP8_E4M3_SCALED) return DSA_ERR_UNSUPPORTED;  // FP8 queries need FP8 keys
+  return launched(launch_indexer_gemm(a, stream_of(stream)));
+}
+
+dsa_status dsa_topk_workspace_size(int32_t n_rows, int64_t ld, int32_t k, size_t *bytes) {
+  if (!bytes) return DSA_ERR_NULL_ARG;
+  if (n_rows < 0 || ld < 0 || k < 1) return DSA_ERR_BAD_SHAPE;
+  if (k > kMaxTopK || ld > (int64_t)1024 * kSlice) return DSA_ERR_UNSUPPORTED;
+  *bytes = topk_workspace_bytes(n_rows, ld);
+  return DSA_OK;
+}
+
+dsa_status dsa_topk(const float *scores, int64_t ld, const int32_t *row_len, int32_t n_rows, int32_t k, int32_t *idx,
+                    int64_t idx_ld, void *workspace, size_t workspace_bytes, int32_t *err_flag,
+                    dsa_stream_t stream) {
+  size_t need;
+  dsa_status st = dsa_topk_workspace_size(n_rows, ld, k, &need);
+  if (st != DSA_OK) return st;
+  if (idx_ld < k) return DSA_ERR_BAD_SHAPE;
+  if (n_rows == 0) return DSA_OK;
+  if (!scores || !row_len || !idx || !workspace) return DSA_ERR_NULL_ARG;
+  if (n_rows > kMaxGridY) return DSA_ERR_UNSUPPORTED;
+  if (!aligned(scores, 4) || !aligned(row_len, 4) || !aligned(idx, 4) || !aligned(workspace, 16) ||
+      !aligned(err_flag, 4))
+    return DSA_ERR_MISALIGNED;
+  if (workspace_bytes < need) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  TopkArgs a;
+  a.scores = scores;
+  a.ld = ld;
+  a.row_len = row_len;
+  a.n_rows = n_rows;
+  a.k = k;
+  a.idx = idx;
+  a.idx_ld = idx_ld;
+  a.ws = workspace;
+  a.err = err_flag;
+  return launched(launch_topk(a, stream_of(stream)));
+}
+
+static dsa_status mla_common(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                             const int64_t *lat_off, int64_t off_ld, int32_t n_req, const int32_t *ctx_len,
+                             const int32_t *idx, int64_t idx_ld, int32_t k, const void *q, int32_t q_fmt,
+                             const float *q_scale, const int32_t *q_req, int32_t n_q, int32_t n_heads,
+                             float sm_scale, float kv_scale, uint16_t *out, float *lse, void *workspace,
+                             size_t workspace_bytes, int32_t *err_flag, dsa_stream_t stream, int32_t tps) {
+  dsa_status st = check_layout(layout);
+  if (st != DSA_OK) return st;
+  if (q_fmt != DSA_Q_BF16 && q_fmt != DSA_Q_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
+  if (n_q < 0 || n_req < 0 || k < 0 || idx_ld < k || off_ld < 1 || pool_bytes < 0 || n_heads < 1)
+    return DSA_ERR_BAD_SHAPE;
+  if (n_heads > kMaxHeads || n_q > kMaxGridY) return DSA_ERR_UNSUPPORTED;
+  if (n_q == 0) return DSA_OK;
+  if (!pool || !lat_off || !ctx_len || !idx || !q || !out || !lse) return DSA_ERR_NULL_ARG;
+  if (q_fmt == DSA_Q_FP8_E4M3 && !q_scale) return DSA_ERR_NULL_ARG;
+  if (!aligned(pool, 16) || !aligned(q, 16) || !aligned(lat_off, 8) || !aligned(ctx_len, 4) || !aligned(idx, 4) ||
+      !aligned(out, 8) || !aligned(lse, 4) || !aligned(q_scale, 4) || !aligned(q_req, 4) || !aligned(err_flag, 4) ||
+      !aligned(workspace, 16))
+    return DSA_ERR_MISALIGNED;
+  const size_t need = mla_workspace_bytes(n_q, n_heads, k, tps);
+  if (need > 0 && !workspace) return DSA_ERR_NULL_ARG;
+  if (workspace_bytes < need) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  MlaArgs a;
+  a.pool = pool;
+  a.pool_bytes = pool_bytes;
+  a.lat_off = lat_off;
+  a.off_ld = off_ld;
+  a.n_req = n_req;
+  a.ctx_len = ctx_len;
+  a.idx = idx;
+  a.idx_ld = idx_ld;
+  a.k = k;
+  a.q = q;
+  a.q_scale = q_scale;
+  a.q_req = q_req;
+  a.n_q = n_q;
+  a.n_heads = n_heads;
+  a.sm_scale = sm_scale;
+  a.kv_scale = kv_scale;
+  a.out = out;
+  a.lse = lse;
+  a.err = err_flag;
+  a.lat_fmt = layout->lat_fmt;
+  a.q_fmt = q_fmt;
+  a.ws = workspace;
+  a.tokens_per_split = tps;
+  return launched(launch_mla(a, stream_of(stream)));
+}
+
+static int32_t prefill_tokens_per_split(int32_t k) { return k <= 32 ? 32 : (k + 31) / 32 * 32; }
+
+dsa_status dsa_sparse_mla_decode_workspace_size(int32_t n_req, int32_t n_heads, int32_t k, size_t *bytes) {
+  if (!bytes) return DSA_ERR_NULL_ARG;
+  if (n_req < 0 || n_heads < 1 || k < 0) return DSA_ERR_BAD_SHAPE;
+  *bytes = mla_workspace_bytes(n_req, n_heads, k, kDecodeTokensPerSplit);
+  return DSA_OK;
+}
+
+dsa_status dsa_sparse_mla_decode(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                                 const int64_t *lat_off, int64_t off_ld, const int32_t *ctx_len, const int32_t *idx,
+                                 int64_t idx_ld, int32_t k, const uint16_t *q, int32_t n_req, int32_t n_heads,
+                                 float sm_scale, float kv_scale, uint16_t *out, float *lse, void *workspace,
+                                 size_t workspace_bytes, int32_t *err_flag, dsa_stream_t stream) {
+  return mla_common(layout, pool, pool_bytes, lat_off, off_ld, n_req, ctx_len, idx, idx_ld, k, q, DSA_Q_BF16, nullptr,
+                    nullptr, n_req, n_heads, sm_scale, kv_scale, out, lse, workspace, workspace_bytes, err_flag,
+                    stream, kDecodeTokensPerSplit);
+}
+
+dsa_status dsa_sparse_mla_prefill_workspace_size(int32_t n_q, int32_t n_heads, int32_t k, size_t *bytes) {
+  if (!bytes) return DSA_ERR_NULL_ARG;
+  if (n_q < 0 || n_heads < 1 || k < 0) return DSA_ERR_BAD_SHAPE;
+  *bytes = mla_workspace_bytes(n_q, n_heads, k, prefill_tokens_per_split(k));
+  return DSA_OK;
+}
+
+dsa_status dsa_sparse_mla_prefill(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                                  const int64_t *lat_off, int64_t off_ld, int32_t n_req, const int32_t *ctx_len,
+                                  const int32_t *idx, int64_t idx_ld, int32_t k, const void *q, int32_t q_fmt,
+                                  const float *q_scale, const int32_t *q_req, int32_t n_q, int32_t n_heads,
+                                  float sm_scale, float kv_scale, uint16_t *out, float *lse, void *workspace,
+                                  size_t workspace_bytes, int32_t *err_flag, dsa_stream_t stream) {
+  if (n_q > 0 && !q_req) return DSA_ERR_NULL_ARG;
+  return mla_common(layout, pool, pool_bytes, lat_off, off_ld, n_req, ctx_len, idx, idx_ld, k, q, q_fmt, q_scale,
+                    q_req, n_q, n_heads, sm_scale, kv_scale, out, lse, workspace, workspace_bytes, err_flag, stream,
+                    prefill_tokens_per_split(k));
+}
+
+}  // extern "C"

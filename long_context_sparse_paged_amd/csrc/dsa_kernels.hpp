@@ -1,0 +1,88 @@
+// dsa_kernels.hpp -- internal launcher interface between the C ABI (abi.cpp) and the kernels.
+// Arguments arrive here already validated on the host.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/dsa.h"
+
+namespace dsa {
+
+struct ResolveArgs {
+  const int32_t *bt;
+  int64_t bt_ld;
+  const int32_t *n_pages;
+  int32_t n_req, max_pages;
+  int64_t pool_rows;
+  int64_t row_stride, layer_off, lat_page_bytes;  // layer_off = layer * layer_stride
+  int64_t *lat_off, *key_off;
+  int64_t off_ld;
+  int32_t *err;
+};
+hipError_t launch_resolve(const ResolveArgs &a, hipStream_t s);
+
+struct ScoreArgs {
+  const uint8_t *pool;
+  int64_t pool_bytes;
+  const int64_t *key_off;
+  int64_t off_ld;
+  int32_t n_req;
+  const void *q;         // [n_q][32][128] bf16 or e4m3
+  const float *q_scale;  // [n_q][32] (FP8 queries)
+  const float *w;        // [n_q][32]
+  const int32_t *q_req, *row_len;
+  int32_t n_q;
+  float *scores;
+  int64_t ld;
+  int32_t *err;
+  int32_t key_fmt;
+};
+hipError_t launch_indexer_scan(const ScoreArgs &a, hipStream_t s);  // bf16 queries
+hipError_t launch_indexer_gemm(const ScoreArgs &a, hipStream_t s);  // e4m3 queries
+
+// Top-k: slices of kSlice scores, candidates per slice <= kSliceCap, rows of up to
+// kShortRow scores are selected wholly in LDS.
+constexpr int kSlice = 8192;
+constexpr int kSliceCap = 4096;
+constexpr int kShortRow = 12288;
+constexpr int kMaxTopK = 4096;
+size_t topk_workspace_bytes(int32_t n_rows, int64_t ld);
+struct TopkArgs {
+  const float *scores;
+  int64_t ld;
+  const int32_t *row_len;
+  int32_t n_rows, k;
+  int32_t *idx;
+  int64_t idx_ld;
+  void *ws;
+  int32_t *err;
+};
+hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+
+struct MlaArgs {
+  const uint8_t *pool;
+  int64_t pool_bytes;
+  const int64_t *lat_off;
+  int64_t off_ld;
+  int32_t n_req;
+  const int32_t *ctx_len;
+  const int32_t *idx;
+  int64_t idx_ld;
+  int32_t k;
+  const void *q;  // [n_q][H][576] bf16 or e4m3
+  const float *q_scale;
+  const int32_t *q_req;  // NULL: row r is request r
+  int32_t n_q, n_heads;
+  float sm_scale, kv_scale;
+  uint16_t *out;
+  float *lse;
+  int32_t *err;
+  int32_t lat_fmt, q_fmt;
+  void *ws;
+  int32_t tokens_per_split;  // multiple of 32; nsplit = ceil(k / tokens_per_split)
+};
+size_t mla_workspace_bytes(int32_t n_q, int32_t n_heads, int32_t k, int32_t tokens_per_split);
+hipError_t launch_mla(const MlaArgs &a, hipStream_t s);
+
+}  // namespace dsa

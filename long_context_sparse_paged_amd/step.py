@@ -1,0 +1,118 @@
+"""One DSA layer-step, as a sequence of the four C entry points.
+
+``DecodeStep`` / ``PrefillStep`` own the device buffers a step needs (page
+offsets, scores, selected indices, outputs, workspaces) and call
+dsa_resolve_pages -> dsa_indexer_score -> dsa_topk -> dsa_sparse_mla_* on one
+stream.  No arithmetic happens here.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (DSA_Q_BF16, DSA_Q_FP8_E4M3, dsa_indexer_score, dsa_layout_make, dsa_resolve_pages, dsa_sparse_mla_decode,
+               dsa_sparse_mla_decode_workspace_size, dsa_sparse_mla_prefill, dsa_sparse_mla_prefill_workspace_size,
+               dsa_topk, dsa_topk_workspace_size)
+
+
+def _layout_of(cache):
+    lp = cache.layout
+    return dsa_layout_make(lp["page_size"], lp["n_layers"], lp["key_fmt"], lp["lat_fmt"], lp["extra_row_bytes"])
+
+
+class _Base:
+    def __init__(self, cache, k: int, n_rows: int, ld: int, device):
+        self.cache = cache
+        self.layout = _layout_of(cache)
+        self.k = k
+        self.device = device
+        n_req, max_pages = cache.block_table.shape
+        self.lat_off = torch.empty(n_req, max_pages, dtype=torch.int64, device=device)
+        self.key_off = torch.empty(n_req, max_pages, dtype=torch.int64, device=device)
+        self.scores = torch.empty(n_rows, max(ld, 1), dtype=torch.float32, device=device)
+        self.idx = torch.empty(n_rows, k, dtype=torch.int32, device=device)
+        self.ws_topk = torch.empty(max(dsa_topk_workspace_size(n_rows, max(ld, 1), k), 16), dtype=torch.uint8,
+                                   device=device)
+        self.err = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def resolve(self, stream=None):
+        c = self.cache
+        dsa_resolve_pages(self.layout, c.layer, c.block_table, c.n_pages, c.pool_rows, self.lat_off, self.key_off,
+                          self.err, stream)
+
+    def topk(self, stream=None):
+        dsa_topk(self.scores, self.row_len, self.k, self.idx, self.ws_topk, self.err, stream)
+
+
+class DecodeStep(_Base):
+    """Decode: one query row per request (row_len = context length)."""
+
+    def __init__(self, cache, q_idx, w, q_mla, sm_scale: float, k: int = 2048, device="cuda"):
+        n_req = cache.block_table.shape[0]
+        ld = int(cache.ctx_len.max().item()) if n_req else 1
+        super().__init__(cache, k, n_req, ld, device)
+        self.q_idx, self.w, self.q_mla = q_idx, w, q_mla
+        self.sm_scale = sm_scale
+        self.n_heads = q_mla.shape[1]
+        self.q_req = torch.arange(n_req, dtype=torch.int32, device=device)
+        self.row_len = cache.ctx_len
+        self.out = torch.empty(n_req, self.n_heads, 512, dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty(n_req, self.n_heads, dtype=torch.float32, device=device)
+        nb = dsa_sparse_mla_decode_workspace_size(n_req, self.n_heads, k)
+        self.ws_mla = torch.empty(nb, dtype=torch.uint8, device=device) if nb else None
+
+    def score(self, stream=None):
+        c = self.cache
+        dsa_indexer_score(self.layout, c.pool, self.key_off, c.n_req, self.q_idx, DSA_Q_BF16, None, self.w, self.q_req,
+                          self.row_len, self.scores, self.err, stream)
+
+    def attend(self, stream=None):
+        c = self.cache
+        dsa_sparse_mla_decode(self.layout, c.pool, self.lat_off, c.ctx_len, self.idx, self.k, self.q_mla,
+                              self.sm_scale, c.kv_scale, self.out, self.lse, self.ws_mla, self.err, stream)
+
+    def run(self, stream=None):
+        self.resolve(stream)
+        self.score(stream)
+        self.topk(stream)
+        self.attend(stream)
+
+
+class PrefillStep(_Base):
+    """Prefill chunk: rows at consecutive positions of one request (row_len = position + 1)."""
+
+    def __init__(self, cache, pq, k: int = 2048, q_fmt: int = DSA_Q_FP8_E4M3, device="cuda"):
+        ld = int(cache.ctx_len.max().item())
+        super().__init__(cache, k, pq.n_q, ld, device)
+        self.pq = pq
+        self.q_fmt = q_fmt
+        self.n_heads = pq.q_mla_bf16.shape[1]
+        self.row_len = pq.row_len
+        self.out = torch.empty(pq.n_q, self.n_heads, 512, dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty(pq.n_q, self.n_heads, dtype=torch.float32, device=device)
+        nb = dsa_sparse_mla_prefill_workspace_size(pq.n_q, self.n_heads, k)
+        self.ws_mla = torch.empty(nb, dtype=torch.uint8, device=device) if nb else None
+
+    def score(self, stream=None):
+        c, pq = self.cache, self.pq
+        if self.q_fmt == DSA_Q_FP8_E4M3:
+            q, qs = pq.q_idx_fp8, pq.q_idx_scale
+        else:
+            q, qs = pq.q_idx_bf16, None
+        dsa_indexer_score(self.layout, c.pool, self.key_off, c.n_req, q, self.q_fmt, qs, pq.w, pq.q_req, pq.row_len,
+                          self.scores, self.err, stream)
+
+    def attend(self, stream=None):
+        c, pq = self.cache, self.pq
+        if self.q_fmt == DSA_Q_FP8_E4M3:
+            q, qs = pq.q_mla_fp8, pq.q_mla_scale
+        else:
+            q, qs = pq.q_mla_bf16, None
+        dsa_sparse_mla_prefill(self.layout, c.pool, self.lat_off, c.n_req, c.ctx_len, self.idx, self.k, q, self.q_fmt,
+                               qs, pq.q_req, pq.sm_scale, c.kv_scale, self.out, self.lse, self.ws_mla, self.err,
+                               stream)
+
+    def run(self, stream=None):
+        self.resolve(stream)
+        self.score(stream)
+        self.topk(stream)
+        self.attend(stream)

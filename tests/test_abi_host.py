@@ -1,0 +1,162 @@
+"""Host-only checks of the C ABI: the library loads without a GPU, exports every
+function include/dsa.h declares, and rejects bad arguments with the documented
+status before enqueuing anything (no compute calls here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def d():
+    from long_context_sparse_paged_amd import build
+    build.ensure_built()
+    import long_context_sparse_paged_amd as d
+    return d
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(d):
+    names = declared_functions()
+    assert len(names) == 11
+    for n in names:
+        assert hasattr(d.lib, n), n
+
+
+def test_layout_make_matches_pages(d):
+    L = d.dsa_layout_make(64, 24, d.DSA_KEY_FP8_E4M3_SCALED, d.DSA_LAT_FP8_E4M3, 0)
+    assert (L.key_bytes, L.lat_bytes, L.layer_stride, L.row_stride) == (132, 576, 45312, 24 * 45312)
+    L = d.dsa_layout_make(64, 1, d.DSA_KEY_MXFP4, d.DSA_LAT_NVFP4, 300)
+    assert (L.key_bytes, L.lat_bytes, L.layer_stride, L.row_stride) == (68, 352, 26880, 27392)
+
+
+def test_layout_agrees_with_generator_and_oracle(d):
+    import oracle
+    from synth import workloads as W
+    for kf in (0, 1):
+        for lf in (0, 1):
+            for nl, ex in ((1, 0), (3, 17), (24, 4096)):
+                got = d.dsa_layout_make(64, nl, kf, lf, ex).as_dict()
+                gen = W.layout_params(kf, lf, nl, 64, ex)
+                orc = oracle.layout_make(64, nl, kf, lf, ex).as_dict()
+                for k in ("key_bytes", "lat_bytes", "layer_stride", "row_stride"):
+                    assert got[k] == gen[k] == orc[k], (kf, lf, nl, ex, k)
+
+
+def test_layout_make_errors(d):
+    out = d.dsa_layout()
+    assert d.lib.dsa_layout_make(64, 1, 0, 0, 0, None) == d.DSA_ERR_NULL_ARG
+    assert d.lib.dsa_layout_make(0, 1, 0, 0, 0, C.byref(out)) == d.DSA_ERR_BAD_SHAPE
+    assert d.lib.dsa_layout_make(64, 0, 0, 0, 0, C.byref(out)) == d.DSA_ERR_BAD_SHAPE
+    assert d.lib.dsa_layout_make(64, 1, 0, 0, -1, C.byref(out)) == d.DSA_ERR_BAD_SHAPE
+    assert d.lib.dsa_layout_make(64, 1, 2, 0, 0, C.byref(out)) == d.DSA_ERR_UNSUPPORTED
+    assert d.lib.dsa_layout_make(64, 1, 0, 5, 0, C.byref(out)) == d.DSA_ERR_UNSUPPORTED
+
+
+FAKE = C.c_void_p(1 << 20)      # aligned, never dereferenced: every call below fails validation first
+ODD = C.c_void_p((1 << 20) + 2)
+
+
+def test_resolve_errors(d):
+    L = d.dsa_layout_make(64, 2, 0, 0, 0)
+    f = d.lib.dsa_resolve_pages
+    assert f(None, 0, FAKE, 8, FAKE, 1, 8, 10, FAKE, FAKE, 8, None, None) == d.DSA_ERR_NULL_ARG
+    assert f(C.byref(L), 0, None, 8, FAKE, 1, 8, 10, FAKE, FAKE, 8, None, None) == d.DSA_ERR_NULL_ARG
+    assert f(C.byref(L), 2, FAKE, 8, FAKE, 1, 8, 10, FAKE, FAKE, 8, None, None) == d.DSA_ERR_BAD_SHAPE   # layer
+    assert f(C.byref(L), 0, FAKE, 4, FAKE, 1, 8, 10, FAKE, FAKE, 8, None, None) == d.DSA_ERR_BAD_SHAPE   # bt_ld
+    assert f(C.byref(L), 0, FAKE, 8, FAKE, 1, 8, 10, FAKE, FAKE, 7, None, None) == d.DSA_ERR_BAD_SHAPE   # off_ld
+    assert f(C.byref(L), 0, ODD, 8, FAKE, 1, 8, 10, FAKE, FAKE, 8, None, None) == d.DSA_ERR_MISALIGNED
+    bad = d.dsa_layout_make(64, 2, 0, 0, 0)
+    bad.row_stride += 256
+    assert f(C.byref(bad), 0, FAKE, 8, FAKE, 1, 8, 10, FAKE, FAKE, 8, None, None) == d.DSA_ERR_BAD_SHAPE
+    p32 = d.dsa_layout_make(32, 2, 0, 0, 0)
+    assert f(C.byref(p32), 0, FAKE, 8, FAKE, 1, 8, 10, FAKE, FAKE, 8, None, None) == d.DSA_ERR_UNSUPPORTED
+
+
+def test_score_errors(d):
+    L = d.dsa_layout_make(64, 1, 0, 0, 0)
+    f = d.lib.dsa_indexer_score
+    args = [C.byref(L), FAKE, 1 << 30, FAKE, 16, 1, FAKE, 0, None, FAKE, FAKE, FAKE, 4, FAKE, 1024, None, None]
+    a = list(args); a[1] = None
+    assert f(*a) == d.DSA_ERR_NULL_ARG
+    a = list(args); a[7] = 1        # FP8 queries without q_scale
+    assert f(*a) == d.DSA_ERR_NULL_ARG
+    a = list(args); a[7] = 3
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED
+    a = list(args); a[1] = ODD
+    assert f(*a) == d.DSA_ERR_MISALIGNED
+    a = list(args); a[12] = -1
+    assert f(*a) == d.DSA_ERR_BAD_SHAPE
+    a = list(args); a[12] = 5000    # the streaming (bf16) path takes <= 4096 rows
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED
+    Lm = d.dsa_layout_make(64, 1, 1, 1, 0)
+    a = list(args); a[0] = C.byref(Lm); a[7] = 1; a[8] = FAKE   # FP8 queries need FP8 keys
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED
+    a = list(args); a[12] = 0       # nothing to do
+    assert f(*a) == d.DSA_OK
+
+
+def test_topk_errors(d):
+    f = d.lib.dsa_topk
+    need = d.dsa_topk_workspace_size(4, 20000, 2048)
+    args = [FAKE, 20000, FAKE, 4, 2048, FAKE, 2048, FAKE, need, None, None]
+    a = list(args); a[4] = 0
+    assert f(*a) == d.DSA_ERR_BAD_SHAPE
+    a = list(args); a[4] = 5000
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED
+    a = list(args); a[6] = 100
+    assert f(*a) == d.DSA_ERR_BAD_SHAPE
+    a = list(args); a[8] = need - 1
+    assert f(*a) == d.DSA_ERR_WORKSPACE_TOO_SMALL
+    a = list(args); a[7] = None
+    assert f(*a) == d.DSA_ERR_NULL_ARG
+    a = list(args); a[7] = C.c_void_p((1 << 20) + 8)
+    assert f(*a) == d.DSA_ERR_MISALIGNED
+    with pytest.raises(d.DsaError):
+        d.dsa_topk_workspace_size(1, 1 << 30, 2048)
+
+
+def test_mla_errors(d):
+    L = d.dsa_layout_make(64, 1, 0, 0, 0)
+    f = d.lib.dsa_sparse_mla_decode
+    need = d.dsa_sparse_mla_decode_workspace_size(2, 12, 2048)
+    assert need > 0
+    args = [C.byref(L), FAKE, 1 << 30, FAKE, 16, FAKE, FAKE, 2048, 2048, FAKE, 2, 12, 0.04, 0.01, FAKE, FAKE, FAKE,
+            need, None, None]
+    a = list(args); a[11] = 0
+    assert f(*a) == d.DSA_ERR_BAD_SHAPE
+    a = list(args); a[11] = 129
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED
+    a = list(args); a[17] = need - 1
+    assert f(*a) == d.DSA_ERR_WORKSPACE_TOO_SMALL
+    a = list(args); a[7] = 100     # idx_ld < k
+    assert f(*a) == d.DSA_ERR_BAD_SHAPE
+    a = list(args); a[9] = None
+    assert f(*a) == d.DSA_ERR_NULL_ARG
+    g = d.lib.dsa_sparse_mla_prefill
+    pargs = [C.byref(L), FAKE, 1 << 30, FAKE, 16, 1, FAKE, FAKE, 2048, 2048, FAKE, 1, None, None, 4, 96, 0.04, 0.01,
+             FAKE, FAKE, None, 0, None, None]
+    assert g(*pargs) == d.DSA_ERR_NULL_ARG    # q_req and FP8 q_scale missing
+    assert d.dsa_sparse_mla_prefill_workspace_size(2048, 96, 2048) == 0   # one split per prefill row
+
+
+def test_status_strings(d):
+    for s in range(7):
+        assert d.dsa_status_str(s)
+    assert "unknown" in d.dsa_status_str(99)
+
+
+def test_binding_refuses_cpu_tensors(d):
+    import torch
+    L = d.dsa_layout_make(64, 1, 0, 0, 0)
+    with pytest.raises(TypeError):
+        d.dsa_resolve_pages(L, 0, torch.zeros(1, 4, dtype=torch.int32), torch.zeros(1, dtype=torch.int32), 4,
+                            torch.zeros(1, 4, dtype=torch.int64), torch.zeros(1, 4, dtype=torch.int64))

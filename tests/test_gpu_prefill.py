@@ -1,0 +1,101 @@
+"""GPU parity of the prefill path (FP8 indexer GEMM, per-row top-k, sparse MLA prefill)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import formats as F
+from synth import workloads as W
+from tests.helpers import topk_set_ok
+from tests.test_gpu_decode import check_attention, check_scores, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def d(gpu):
+    from long_context_sparse_paged_amd import build
+    build.ensure_built()
+    import long_context_sparse_paged_amd as d
+    return d
+
+
+def make_prefill(d, prefix, chunk, heads=96, seed=0, q_fmt=1, k=2048, spare_rows=3):
+    log(f"[case] prefill prefix={prefix} chunk={chunk} heads={heads} q_fmt={q_fmt} seed={seed}")
+    cache = W.build_cache([prefix + chunk], seed=seed, device="cuda", spare_rows=spare_rows)
+    pq = W.prefill_queries(prefix, chunk, heads, seed=seed, device="cuda")
+    return cache, pq, d.PrefillStep(cache, pq, k=k, q_fmt=q_fmt)
+
+
+def oracle_prefill_scores(cache, pq, q_fmt):
+    oc = oracle.OracleCache(cache)
+    if q_fmt == 1:
+        q, qs = pq.q_idx_fp8, pq.q_idx_scale
+    else:
+        q, qs = pq.q_idx_bf16, None
+    rl = pq.row_len.cpu().numpy()
+    return oc, oracle.indexer_score(oc, q, q_fmt, qs, pq.w, pq.q_req, rl, ld=int(cache.ctx_len.max()))
+
+
+@pytest.mark.parametrize("q_fmt", [1, 0])
+def test_prefill_scores_match_oracle(d, q_fmt):
+    cache, pq, step = make_prefill(d, 3000, 70, seed=1, q_fmt=q_fmt)
+    step.scores.fill_(float("nan"))
+    step.resolve()
+    step.score()
+    torch.cuda.synchronize()
+    assert int(step.err.item()) == 0
+    got = step.scores.cpu().numpy()
+    _, ref = oracle_prefill_scores(cache, pq, q_fmt)
+    rl = pq.row_len.cpu().numpy()
+    check_scores(got, ref, rl)
+    for r, L in enumerate(rl):     # causal: nothing written past the row's position
+        assert np.isnan(got[r, L:]).all()
+
+
+def test_prefill_gemm_rows_of_several_requests(d):
+    """Rows of one 32-row tile from different requests (interleaved) and negative query scales."""
+    ctx = [1500, 700, 2100]
+    cache = W.build_cache(ctx, seed=5, device="cuda", spare_rows=2)
+    rng = np.random.default_rng(5)
+    n_q = 45
+    q_req = rng.integers(0, 3, size=n_q).astype(np.int32)
+    row_len = np.array([rng.integers(1, ctx[b] + 1) for b in q_req], np.int32)
+    q = torch.randn(n_q, 32, 128, generator=torch.Generator().manual_seed(5))
+    codes, qs = F.fp8_rowhead_quant(q)
+    qs[::5, 3] *= -1.0                     # a negative query scale: ReLU sees the sign
+    w = torch.rand(n_q, 32, generator=torch.Generator().manual_seed(6)) / 32
+    layout = d.dsa_layout_make(64, 1, 0, 0, 0)
+    lat_off = torch.empty(3, cache.max_pages, dtype=torch.int64, device="cuda")
+    key_off = torch.empty_like(lat_off)
+    d.dsa_resolve_pages(layout, 0, cache.block_table, cache.n_pages, cache.pool_rows, lat_off, key_off)
+    scores = torch.full((n_q, max(ctx)), float("nan"), device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    d.dsa_indexer_score(layout, cache.pool, key_off, 3, codes.cuda(), d.DSA_Q_FP8_E4M3, qs.cuda(), w.cuda(),
+                        torch.from_numpy(q_req).cuda(), torch.from_numpy(row_len).cuda(), scores, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    oc = oracle.OracleCache(cache)
+    ref = oracle.indexer_score(oc, codes, 1, qs, w, q_req, row_len, ld=max(ctx))
+    check_scores(scores.cpu().numpy(), ref, row_len)
+
+
+@pytest.mark.parametrize("q_fmt", [1, 0])
+def test_prefill_chain(d, q_fmt):
+    cache, pq, step = make_prefill(d, 2500, 40, heads=96, seed=2 + q_fmt, q_fmt=q_fmt)
+    step.run()
+    torch.cuda.synchronize()
+    assert int(step.err.item()) == 0
+    rl = pq.row_len.cpu().numpy()
+    got_s = step.scores.cpu().numpy()
+    oc, ref_s = oracle_prefill_scores(cache, pq, q_fmt)
+    check_scores(got_s, ref_s, rl)
+    got_idx = step.idx.cpu().numpy()
+    assert np.array_equal(got_idx, oracle.topk(np.nan_to_num(got_s), rl, 2048))
+    topk_set_ok(ref_s, oracle.topk(np.nan_to_num(ref_s), rl, 2048), got_idx, rl, 2048)
+    if q_fmt == 1:
+        q, qs = pq.q_mla_fp8, pq.q_mla_scale
+    else:
+        q, qs = pq.q_mla_bf16, None
+    ref_o, ref_l = oracle.sparse_mla(oc, got_idx, q, q_fmt, qs, pq.q_req, 96, pq.sm_scale)
+    check_attention(step.out, step.lse, ref_o, ref_l)
