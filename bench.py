@@ -1,0 +1,259 @@
+"""Benchmark of the DSA hot path on one MI355X.
+
+Default workload: one decode layer-step (resolve -> indexer scan -> top-2048 ->
+sparse MLA) for 32 requests at 131,072 tokens of context each, FP8 index keys
+(132 B/token) and FP8 latents (576 B/token) in a block-packed pool of 65,536
+rows, 12 query heads (one TP8 GPU's share).  Inputs are seeded, synthetic and
+resident in HBM before timing starts.
+
+Timing: W untimed warmup steps, then K timed steps between device
+synchronisations.  A 1 GiB copy runs before every step (outside the per-step
+HIP events) so that no step finds the previous step's latents or scores in the
+256 MB Infinity Cache; ms_per_step is the mean of the per-step event times,
+wall_ms_per_step the bracketed wall time including the scrubs.
+
+Metric: algorithmic bytes of the layer-step (sum_b L_b*132 + min(2048, L_b)*576)
+divided by the step time, in GB/s, against the 8 TB/s HBM peak.  The roofline
+object is the indexer scan (the dominant kernel): its key bytes per launch over
+its own mean launch time.  cpu_baseline is the CPU oracle on a bounded sample of
+the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|mixed|long|prefill]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
+
+WORKLOADS = {"decode": 1, "long": 2, "mixed": 3, "prefill": 4}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "long_context_sparse_paged_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel_src, workload):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it still matches the source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha") != source_sha(*kernel_src):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from long_context_sparse_paged_amd import build as B
+    B.ensure_built()
+    import long_context_sparse_paged_amd as d
+    from synth import workloads as W
+
+    cfg_id = WORKLOADS[args.workload]
+    wl = W.WORKLOADS[cfg_id]
+    ctx = W.workload_ctx(cfg_id)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    k = wl["topk"]
+    t0 = time.time()
+    log(f"[bench] building workload {wl['name']} (seed {cfg_id}) on {torch.cuda.get_device_name(0)}")
+    cache = W.build_cache(ctx, key_fmt=wl["key_fmt"], lat_fmt=wl["lat_fmt"], seed=cfg_id, device=dev,
+                          spare_rows=wl["spare_rows"])
+    kb, lb = cache.layout["key_bytes"], cache.layout["lat_bytes"]
+    if wl["kind"] == "decode":
+        dq = W.decode_queries(len(ctx), wl["heads"], seed=cfg_id, device=dev)
+        step = d.DecodeStep(cache, dq.q_idx, dq.w, dq.q_mla, dq.sm_scale, k=k)
+    else:
+        pq = W.prefill_queries(wl["prefix"], wl["chunk"], wl["heads"], seed=cfg_id, device=dev)
+        step = d.PrefillStep(cache, pq, k=k, q_fmt=d.DSA_Q_FP8_E4M3)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s; pool {cache.pool.numel() / 1e9:.2f} GB")
+
+    scrub_src = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+    scrub_dst = torch.empty_like(scrub_src)
+    stages = [("resolve", step.resolve), ("score", step.score), ("topk", step.topk), ("attend", step.attend)]
+
+    def one_step(ev):
+        for i, (_, fn) in enumerate(stages):
+            ev[i].record()
+            fn()
+        ev[len(stages)].record()
+
+    for _ in range(args.warmup):
+        scrub_dst.copy_(scrub_src)
+        one_step([torch.cuda.Event(enable_timing=True) for _ in range(5)])
+    torch.cuda.synchronize()
+    assert int(step.err.item()) == 0, "device error flag set"
+
+    evs = []
+    torch.cuda.synchronize()
+    tw = time.time()
+    for _ in range(args.steps):
+        scrub_dst.copy_(scrub_src)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        one_step(ev)
+        evs.append(ev)
+    torch.cuda.synchronize()
+    wall = time.time() - tw
+    per_stage = {n: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in evs])) for i, (n, _) in enumerate(stages)}
+    step_ms = float(np.mean([ev[0].elapsed_time(ev[4]) for ev in evs]))
+
+    out = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "scaling": "weak", "vs_baseline": None,
+           "data": "synthetic (seeded; N(0,1) keys/latents/queries quantised to the cache formats)"}
+    if wl["kind"] == "decode":
+        alg = W.algorithmic_decode_bytes(ctx, kb, lb, k)
+        key_bytes = sum(ctx) * kb
+        gbs = alg / (step_ms * 1e-3) / 1e9
+        score_ms = per_stage["score"]
+        ach = key_bytes / (score_ms * 1e-3) / 1e9
+        traffic = counter_traffic(["indexer_scan.hip", "dsa_device.hpp"], args.workload)
+        out.update({
+            "metric": "us/layer-step & HBM GB/s (frac of peak), DSA decode 128K ctx batch 32, one MI355X"
+            if cfg_id == 1 else f"us/layer-step & HBM GB/s, DSA decode ({wl['name']}), one MI355X",
+            "value": round(gbs, 1), "unit": "GB/s", "higher_is_better": True,
+            "ms_per_step": round(step_ms, 4), "us_per_layer_step": round(step_ms * 1e3, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "wall_ms_per_step": round(wall / args.steps * 1e3, 3),
+            "algorithmic_bytes": alg, "dtype": "bf16",
+            "config": {"workload": wl["name"], "batch": len(ctx), "ctx_total": int(sum(ctx)),
+                       "ctx_max": int(max(ctx)), "heads": wl["heads"], "topk": k,
+                       "key_format": ["fp8_e4m3+fp32 scale (132 B)", "mxfp4 (68 B)"][wl["key_fmt"]],
+                       "latent_format": ["fp8_e4m3 (576 B)", "nvfp4 (352 B)"][wl["lat_fmt"]], "page_tokens": 64,
+                       "pool_rows": cache.pool_rows, "scrub_between_steps_bytes": scrub_src.numel()},
+            "kernels_us": {n: round(v * 1e3, 2) for n, v in per_stage.items()},
+            "roofline": {"kernel": "indexer_scan (dsa_indexer_score, bf16 queries)", "bound": "hbm",
+                         "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_launch": key_bytes,
+                         "traffic": traffic},
+        })
+    else:
+        rl = pq.row_len.cpu().numpy().astype(np.int64)
+        pairs = int(rl.sum())
+        flop_idx = pairs * 32 * 128 * 2
+        flop_mla = 2 * pq.n_q * wl["heads"] * k * (576 + 512)
+        score_ms = per_stage["score"]
+        tf = flop_idx / (score_ms * 1e-3) / 1e12
+        traffic = counter_traffic(["indexer_gemm.hip", "dsa_device.hpp"], args.workload)
+        out.update({
+            "metric": "us/layer-step & TFLOP/s (frac of MFMA peak), DSA prefill 2K chunk on 150K prefix, one MI355X",
+            "value": round((flop_idx + flop_mla) / (step_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "higher_is_better": True, "ms_per_step": round(step_ms, 4), "us_per_layer_step": round(step_ms * 1e3, 1),
+            "wall_ms_per_step": round(wall / args.steps * 1e3, 3), "dtype": "bf16",
+            "config": {"workload": wl["name"], "rows": pq.n_q, "prefix": wl["prefix"], "heads": wl["heads"],
+                       "topk": k, "scored_pairs": pairs, "query_format": "fp8_e4m3 + fp32 scale per (row, head)"},
+            "kernels_us": {n: round(v * 1e3, 2) for n, v in per_stage.items()},
+            "roofline": {"kernel": "indexer_gemm (dsa_indexer_score, fp8 queries, bf16 MFMA)", "bound": "mfma",
+                         "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / BF16_PEAK_TFLOPS, 4), "frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
+                         "flop_per_launch": flop_idx, "traffic": traffic},
+        })
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cache, step, wl, ctx, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cache, step, wl, ctx, budget_s):
+    """Time the CPU oracle (as it stands) on whole requests / rows of the same workload."""
+    import numpy as np
+
+    import oracle
+    t0 = time.time()
+    oc = oracle.OracleCache(cache)
+    log(f"[bench] host copy for the oracle: {time.time() - t0:.1f}s")
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    kb, lb = cache.layout["key_bytes"], cache.layout["lat_bytes"]
+    k = wl["topk"]
+    spent, done_bytes, done_units, t_score, t_topk, t_mla = 0.0, 0, 0, 0.0, 0.0, 0.0
+    if wl["kind"] == "decode":
+        q_idx = step.q_idx.cpu()
+        w = step.w.cpu()
+        q_mla = step.q_mla.cpu()
+        for b in range(len(ctx)):
+            L = ctx[b]
+            a = time.time()
+            s = oracle.indexer_score(oc, q_idx[b:b + 1], 0, None, w[b:b + 1], np.array([b], np.int32),
+                                     np.array([L], np.int32))
+            t1 = time.time()
+            idx = oracle.topk(s, np.array([L], np.int32), k)
+            t2 = time.time()
+            oracle.sparse_mla(oc, idx, q_mla[b:b + 1], 0, None, np.array([b], np.int32), q_mla.shape[1],
+                              step.sm_scale)
+            t3 = time.time()
+            t_score += t1 - a
+            t_topk += t2 - t1
+            t_mla += t3 - t2
+            spent += t3 - a
+            done_bytes += L * kb + min(k, L) * lb
+            done_units += 1
+            if spent >= budget_s:
+                break
+        return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+                "sample": f"{done_units} of {len(ctx)} requests (full score + sort + attention each), "
+                          f"{spent:.1f}s: score {t_score:.1f}s, top-k {t_topk:.1f}s, attention {t_mla:.1f}s"}
+    pq = step.pq
+    rows = pq.n_q
+    order = np.random.default_rng(0).permutation(rows)
+    qi, qis, wv = pq.q_idx_fp8.cpu(), pq.q_idx_scale.cpu(), pq.w.cpu()
+    qm, qms = pq.q_mla_fp8.cpu(), pq.q_mla_scale.cpu()
+    rl_all = pq.row_len.cpu().numpy()
+    flops = 0
+    for r in order:
+        a = time.time()
+        L = int(rl_all[r])
+        s = oracle.indexer_score(oc, qi[r:r + 1], 1, qis[r:r + 1], wv[r:r + 1], np.zeros(1, np.int32),
+                                 np.array([L], np.int32))
+        t1 = time.time()
+        idx = oracle.topk(s, np.array([L], np.int32), k)
+        t2 = time.time()
+        oracle.sparse_mla(oc, idx, qm[r:r + 1], 1, qms[r:r + 1], np.zeros(1, np.int32), qm.shape[1], pq.sm_scale)
+        t3 = time.time()
+        t_score += t1 - a
+        t_topk += t2 - t1
+        t_mla += t3 - t2
+        spent += t3 - a
+        flops += L * 32 * 128 * 2 + 2 * qm.shape[1] * min(k, L) * (576 + 512)
+        done_units += 1
+        if spent >= budget_s:
+            break
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done_units} of {rows} rows (seeded random order), {spent:.1f}s: score {t_score:.1f}s, "
+                      f"top-k {t_topk:.1f}s, attention {t_mla:.1f}s"}
+
+
+if __name__ == "__main__":
+    main()
