@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/dsa.h"
+#include "dsa.h"
 
 namespace dsa {
 

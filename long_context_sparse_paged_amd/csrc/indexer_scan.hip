@@ -26,6 +26,8 @@
 // The dot product's dims may be visited in any order as long as q and k agree: lane
 // (n, h) at K-step s takes dims [64h + 8s, 64h + 8s + 8), which makes both the
 // query fragment and the key fragment contiguous runs of bytes.
+#include <math.h>
+
 #include "dsa_device.hpp"
 #include "dsa_kernels.hpp"
 
@@ -42,6 +44,7 @@ struct KeyRow {
   static constexpr int kPageBytes = kPage * kBytes;               // 8448 / 4352
   static constexpr int kChunks = kPageBytes / 16;                 // 528 / 272
   static constexpr int kLoadsPerLane = (kChunks + 63) / 64;       // 9 / 5
+  static constexpr int kFullLoads = kChunks / 64;                 // 8 / 4 (then 16 lanes of a tail)
 };
 
 // Clamped length of row r (0 for an invalid request); flags bad rows once (block 0).
@@ -62,7 +65,7 @@ __device__ __forceinline__ int row_length(const ScoreArgs &a, int r, int64_t max
 }
 
 template <int KEY_FMT>
-__global__ __launch_bounds__(256) void indexer_scan_kernel(const ScoreArgs a) {
+__global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a) {
   using KR = KeyRow<KEY_FMT>;
   __shared__ __align__(16) uint8_t s_page[kScanWaves][KR::kPageBytes];
   __shared__ int s_tmp[4];
@@ -72,7 +75,6 @@ __global__ __launch_bounds__(256) void indexer_scan_kernel(const ScoreArgs a) {
   const int n_q = a.n_q;
   const int64_t max_tok = a.ld < a.off_ld * kPage ? a.ld : a.off_ld * kPage;
 
-  // 1) prefix of page counts over rows (each thread a contiguous run of rows)
   const int per = (n_q + 255) / 256;
   const int r0 = min(n_q, tid * per), r1 = min(n_q, r0 + per);
   int mine = 0;
@@ -86,126 +88,170 @@ __global__ __launch_bounds__(256) void indexer_scan_kernel(const ScoreArgs a) {
   if (tid == 0) s_start[n_q] = total;
   __syncthreads();
 
-  // 2) this workgroup's share of units; its waves take every kScanWaves-th unit in lockstep
-  const int u_beg = (int)((int64_t)total * blockIdx.x / gridDim.x);
-  const int u_end = (int)((int64_t)total * (blockIdx.x + 1) / gridDim.x);
-  const int n_iter = (u_end - u_beg + kScanWaves - 1) / kScanWaves;
-  if (n_iter == 0) return;  // uniform across the workgroup
-
-  int u = u_beg + wid;
+  // each wave: an equal contiguous share of all units; no block barriers from here on
+  const int64_t nw = (int64_t)gridDim.x * kScanWaves, gw = (int64_t)blockIdx.x * kScanWaves + wid;
+  // values below are wave-uniform; readfirstlane lets the compiler keep them (and the
+  // control flow that depends on them) in scalar registers
+  const int total_u = __builtin_amdgcn_readfirstlane(total);
+  const int u_beg = (int)((int64_t)total_u * gw / nw), u_end = (int)((int64_t)total_u * (gw + 1) / nw);
+  if (u_beg >= u_end) return;
   int r = 0;
-  if (u < u_end) {  // largest r < n_q with s_start[r] <= u
+  {
     int lo = 0, hi = n_q;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (s_start[mid] <= u) lo = mid; else hi = mid;
+      if (__builtin_amdgcn_readfirstlane(s_start[mid]) <= u_beg) lo = mid; else hi = mid;
     }
     r = lo;
   }
-
-  u32x4_t buf[KR::kLoadsPerLane];
-  auto page_of = [&](int uu, int rr, const uint8_t *&src) -> bool {
-    const int p = uu - s_start[rr];
-    const int64_t off = a.key_off[(int64_t)a.q_req[rr] * a.off_ld + p];
+  // Page offsets of the wave's units, 64 at a time: lane i looks up unit ob + i once, and the
+  // loop reads its unit's offset with v_readlane.  So the steady-state loop issues no
+  // dependent memory read that would make the compiler wait on vmcnt -- and with it on the
+  // page prefetches in flight.
+  int ob = -1;
+  int64_t lane_off = -1;
+  auto fill_offsets = [&](int first) {
+    ob = first;
+    const int uu = first + lane;
+    lane_off = -1;
+    if (uu < u_end) {
+      int lo = 0, hi = n_q;  // row of unit uu: largest row with s_start[row] <= uu
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_start[mid] <= uu) lo = mid; else hi = mid;
+      }
+      lane_off = a.key_off[(int64_t)a.q_req[lo] * a.off_ld + (uu - s_start[lo])];
+    }
+  };
+  auto src_of = [&](int uu) -> const uint8_t * {
+    if (uu - ob >= 64 || ob < 0) fill_offsets(uu);
+    const int li = __builtin_amdgcn_readfirstlane(uu - ob);
+    const uint32_t olo = __builtin_amdgcn_readlane((uint32_t)(uint64_t)lane_off, li);
+    const uint32_t ohi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)lane_off >> 32), li);
+    const int64_t off = (int64_t)(((uint64_t)ohi << 32) | olo);
     if (off < 0 || off + KR::kPageBytes > a.pool_bytes || (off & 15)) {
       if (lane == 0) flag_error(a.err, DSA_DEVERR_PAGE_OFFSET);
-      return false;
+      return nullptr;
     }
-    src = a.pool + off;
-    return true;
+    return a.pool + off;
   };
-  auto issue_loads = [&](const uint8_t *src) {
+  auto row_of = [&](int uu, int rr) {  // advance rr to unit uu's row (LDS reads only)
+    while (uu >= __builtin_amdgcn_readfirstlane(s_start[rr + 1])) ++rr;
+    return rr;
+  };
+  u32x4_t b0[KR::kLoadsPerLane], b1[KR::kLoadsPerLane];
+  // keys are read once per step: nontemporal loads keep them from displacing cached data
+  auto load = [&](u32x4_t (&buf)[KR::kLoadsPerLane], const uint8_t *src) {
+    const u32x4_t *p = reinterpret_cast<const u32x4_t *>(src) + lane;
 #pragma unroll
-    for (int i = 0; i < KR::kLoadsPerLane; ++i) {
-      const int c = lane + 64 * i;
-      if (c < KR::kChunks) buf[i] = *reinterpret_cast<const u32x4_t *>(src + 16 * c);
-    }
+    for (int i = 0; i < KR::kFullLoads; ++i) buf[i] = __builtin_nontemporal_load(p + 64 * i);
+    if constexpr (KR::kFullLoads < KR::kLoadsPerLane)
+      if (lane < KR::kChunks - 64 * KR::kFullLoads) buf[KR::kFullLoads] = __builtin_nontemporal_load(p + 64 * KR::kFullLoads);
   };
-
-  bool have = false;
-  if (u < u_end) {
-    const uint8_t *src;
-    have = page_of(u, r, src);
-    if (have) issue_loads(src);
-  }
+  uint8_t *slot = s_page[wid];
+  auto park = [&](const u32x4_t (&buf)[KR::kLoadsPerLane]) {
+    u32x4_t *q = reinterpret_cast<u32x4_t *>(slot) + lane;
+#pragma unroll
+    for (int i = 0; i < KR::kFullLoads; ++i) q[64 * i] = buf[i];
+    if constexpr (KR::kFullLoads < KR::kLoadsPerLane)
+      if (lane < KR::kChunks - 64 * KR::kFullLoads) q[64 * KR::kFullLoads] = buf[KR::kFullLoads];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
 
   int cur_row = -1, cur_len = 0;
   bf16x8_t qf[8];
   float wv[16];
   const int n = lane & 31, h = lane >> 5;
-  uint8_t *slot = s_page[wid];
-
-  for (int it = 0; it < n_iter; ++it) {
-    if (have) {
+  auto compute = [&](int uu, int rr) {
+    if (rr != cur_row) {
+      cur_row = rr;
+      cur_len = __builtin_amdgcn_readfirstlane(row_length(a, rr, max_tok, false));
+      const uint16_t *qr = reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)rr * kIdxHeads + n) * kIdxDim;
 #pragma unroll
-      for (int i = 0; i < KR::kLoadsPerLane; ++i) {
-        const int c = lane + 64 * i;
-        if (c < KR::kChunks) *reinterpret_cast<u32x4_t *>(slot + 16 * c) = buf[i];
-      }
+      for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8_t *>(qr + 64 * h + 8 * s);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) wv[i] = a.w[(int64_t)rr * kIdxHeads + 8 * (i >> 2) + 4 * h + (i & 3)];
     }
-    const int cu = u, cr = r;
-    const bool chave = have;
-    // prefetch the wave's next page while this one is scored
-    u += kScanWaves;
-    have = false;
-    if (u < u_end) {
-      while (u >= s_start[r + 1]) ++r;
-      const uint8_t *src;
-      have = page_of(u, r, src);
-      if (have) issue_loads(src);
-    }
-    __syncthreads();
-
-    if (chave) {
-      if (cr != cur_row) {
-        cur_row = cr;
-        cur_len = row_length(a, cr, max_tok, false);
-        const uint16_t *qr = reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)cr * kIdxHeads + n) * kIdxDim;
+    const int p = uu - __builtin_amdgcn_readfirstlane(s_start[rr]);
+    const int rem = cur_len - p * kPage;
+    float *out = a.scores + (int64_t)rr * a.ld + (int64_t)p * kPage;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8_t *>(qr + 64 * h + 8 * s);
+    for (int c2 = 0; c2 < 2; ++c2) {
+      if (32 * c2 >= rem) break;
+      const int tt = 32 * c2 + n;
+      const uint8_t *row = slot + tt * KR::kBytes;
+      f32x16_t acc = {};
+      float scale = 1.0f;
+      if constexpr (KEY_FMT == 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) wv[i] = a.w[(int64_t)cr * kIdxHeads + 8 * (i >> 2) + 4 * h + (i & 3)];
-      }
-      const int p = cu - s_start[cr];
-      const int rem = cur_len - p * kPage;  // valid tokens in this page, >= 1
-      float *out = a.scores + (int64_t)cr * a.ld + (int64_t)p * kPage;
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        if (32 * c2 >= rem) break;
-        const int tt = 32 * c2 + n;
-        const uint8_t *row = slot + tt * KR::kBytes;
-        f32x16_t acc = {};
-        float scale = 1.0f;
-        if constexpr (KEY_FMT == 0) {
-#pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            const uint32_t d0 = *reinterpret_cast<const uint32_t *>(row + 64 * h + 8 * s);
-            const uint32_t d1 = *reinterpret_cast<const uint32_t *>(row + 64 * h + 8 * s + 4);
-            acc = mfma_32x32x16_bf16(qf[s], e4m3x8_bf16(d0, d1), acc);
-          }
-          scale = *reinterpret_cast<const float *>(row + 128);
-        } else {
-          const uint32_t sc4 = *reinterpret_cast<const uint32_t *>(row + 64);
-#pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            const uint32_t dw = *reinterpret_cast<const uint32_t *>(row + 32 * h + 4 * s);
-            const float p2 = e8m0_pow2(sc4 >> (8 * (2 * h + (s >> 2))));
-            acc = mfma_32x32x16_bf16(qf[s], e2m1x8_bf16(dw, p2), acc);
-          }
+        for (int s = 0; s < 8; ++s) {
+          const uint32_t d0 = *reinterpret_cast<const uint32_t *>(row + 64 * h + 8 * s);
+          const uint32_t d1 = *reinterpret_cast<const uint32_t *>(row + 64 * h + 8 * s + 4);
+          acc = mfma_32x32x16_bf16(qf[s], e4m3x8_bf16(d0, d1), acc);
         }
-        // ReLU(x * scale) = scale * max(x, 0) for scale >= 0, scale * min(x, 0) otherwise
-        const bool neg = scale < 0.0f;
-        float sum = 0.0f;
+        scale = *reinterpret_cast<const float *>(row + 128);
+      } else {
+        const uint32_t sc4 = *reinterpret_cast<const uint32_t *>(row + 64);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float x = acc[i];
-          sum = fmaf(wv[i], neg ? fminf(x, 0.0f) : fmaxf(x, 0.0f), sum);
+        for (int s = 0; s < 8; ++s) {
+          const uint32_t dw = *reinterpret_cast<const uint32_t *>(row + 32 * h + 4 * s);
+          const float p2 = e8m0_pow2(sc4 >> (8 * (2 * h + (s >> 2))));
+          acc = mfma_32x32x16_bf16(qf[s], e2m1x8_bf16(dw, p2), acc);
         }
-        const float score = sum_halves(sum) * scale;
-        if (h == 0 && tt < rem) out[tt] = score;
       }
+      // ReLU(x * scale) = scale * med3(x, lo, hi): (lo, hi) = (0, inf) for scale >= 0, (-inf, 0) otherwise
+      const float lo = scale < 0.0f ? -INFINITY : 0.0f, hi = scale < 0.0f ? 0.0f : INFINITY;
+      float sum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum = fmaf(wv[i], __builtin_amdgcn_fmed3f(acc[i], lo, hi), sum);
+      const float score = sum_halves(sum) * scale;
+      if (h == 0 && tt < rem) out[tt] = score;
     }
-    __syncthreads();
+  };
+
+  // software pipeline: two pages in registers in flight while the third is scored from LDS
+  int u = u_beg;
+  int rl = row_of(u, r);
+  const uint8_t *s0 = src_of(u);
+  int r_0 = rl;
+  if (s0) load(b0, s0);
+  const uint8_t *s1 = nullptr;
+  int r_1 = rl;
+  if (u + 1 < u_end) {
+    rl = row_of(u + 1, rl);
+    s1 = src_of(u + 1);
+    r_1 = rl;
+    if (s1) load(b1, s1);
+  }
+  for (;;) {
+    // unit u lives in b0
+    if (s0) park(b0);
+    const bool c0 = s0 != nullptr;
+    const int cu0 = u, cr0 = r_0;
+    s0 = nullptr;
+    if (u + 2 < u_end) {
+      rl = row_of(u + 2, rl);
+      s0 = src_of(u + 2);
+      r_0 = rl;
+      if (s0) load(b0, s0);
+    }
+    if (c0) compute(cu0, cr0);
+    if (++u >= u_end) break;
+    // unit u lives in b1
+    if (s1) park(b1);
+    const bool c1 = s1 != nullptr;
+    const int cu1 = u, cr1 = r_1;
+    s1 = nullptr;
+    if (u + 2 < u_end) {
+      rl = row_of(u + 2, rl);
+      s1 = src_of(u + 2);
+      r_1 = rl;
+      if (s1) load(b1, s1);
+    }
+    if (c1) compute(cu1, cr1);
+    if (++u >= u_end) break;
   }
 }
 
@@ -216,8 +262,8 @@ hipError_t launch_indexer_scan(const ScoreArgs &a, hipStream_t s) {
   if (a.n_q > kScanMaxRows) return hipErrorInvalidValue;
   const int64_t max_tok = a.ld < a.off_ld * kPage ? a.ld : a.off_ld * kPage;
   const int64_t max_units = (int64_t)a.n_q * ((max_tok + kPage - 1) / kPage);
-  int64_t grid = (max_units + 7) / 8;
-  if (grid > 2048) grid = 2048;
+  int64_t grid = (max_units + 15) / 16;
+  if (grid > 512) grid = 512;
   if (grid < 1) grid = 1;
   const size_t dyn = sizeof(int) * (size_t)(a.n_q + 1);
   if (a.key_fmt == 0)
