@@ -122,16 +122,21 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
       }
       lane_off = a.key_off[(int64_t)a.q_req[lo] * a.off_ld + (uu - s_start[lo])];
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // drain on this rare path (see the query reload below)
   };
-  auto src_of = [&](int uu) -> const uint8_t * {
+  // Source of unit uu's page.  An invalid page is flagged and replaced by the pool's first page
+  // (in bounds: pool_bytes >= one page is checked above) so that every prefetch issues the same
+  // number of loads -- the compiler's wait counting then stays exact across loop iterations.
+  auto src_of = [&](int uu, bool &ok) -> const uint8_t * {
     if (uu - ob >= 64 || ob < 0) fill_offsets(uu);
     const int li = __builtin_amdgcn_readfirstlane(uu - ob);
     const uint32_t olo = __builtin_amdgcn_readlane((uint32_t)(uint64_t)lane_off, li);
     const uint32_t ohi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)lane_off >> 32), li);
     const int64_t off = (int64_t)(((uint64_t)ohi << 32) | olo);
-    if (off < 0 || off + KR::kPageBytes > a.pool_bytes || (off & 15)) {
+    ok = !(off < 0 || off + KR::kPageBytes > a.pool_bytes || (off & 15));
+    if (!ok) {
       if (lane == 0) flag_error(a.err, DSA_DEVERR_PAGE_OFFSET);
-      return nullptr;
+      return a.pool;
     }
     return a.pool + off;
   };
@@ -141,20 +146,21 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
   };
   u32x4_t b0[KR::kLoadsPerLane], b1[KR::kLoadsPerLane];
   // keys are read once per step: nontemporal loads keep them from displacing cached data
+  constexpr int kTail = KR::kChunks - 64 * KR::kFullLoads;  // 16-B chunks in the partial last load
   auto load = [&](u32x4_t (&buf)[KR::kLoadsPerLane], const uint8_t *src) {
-    const u32x4_t *p = reinterpret_cast<const u32x4_t *>(src) + lane;
+    const u32x4_t *p = reinterpret_cast<const u32x4_t *>(src);
 #pragma unroll
-    for (int i = 0; i < KR::kFullLoads; ++i) buf[i] = __builtin_nontemporal_load(p + 64 * i);
-    if constexpr (KR::kFullLoads < KR::kLoadsPerLane)
-      if (lane < KR::kChunks - 64 * KR::kFullLoads) buf[KR::kFullLoads] = __builtin_nontemporal_load(p + 64 * KR::kFullLoads);
+    for (int i = 0; i < KR::kFullLoads; ++i) buf[i] = __builtin_nontemporal_load(p + lane + 64 * i);
+    if constexpr (kTail > 0)  // every lane loads (lanes >= kTail re-read an in-page chunk)
+      buf[KR::kFullLoads] = __builtin_nontemporal_load(p + 64 * KR::kFullLoads + (lane < kTail ? lane : 0));
   };
   uint8_t *slot = s_page[wid];
   auto park = [&](const u32x4_t (&buf)[KR::kLoadsPerLane]) {
     u32x4_t *q = reinterpret_cast<u32x4_t *>(slot) + lane;
 #pragma unroll
     for (int i = 0; i < KR::kFullLoads; ++i) q[64 * i] = buf[i];
-    if constexpr (KR::kFullLoads < KR::kLoadsPerLane)
-      if (lane < KR::kChunks - 64 * KR::kFullLoads) q[64 * KR::kFullLoads] = buf[KR::kFullLoads];
+    if constexpr (kTail > 0)
+      if (lane < kTail) q[64 * KR::kFullLoads] = buf[KR::kFullLoads];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -173,6 +179,10 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
       for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8_t *>(qr + 64 * h + 8 * s);
 #pragma unroll
       for (int i = 0; i < 16; ++i) wv[i] = a.w[(int64_t)rr * kIdxHeads + 8 * (i >> 2) + 4 * h + (i & 3)];
+      // Drain here, on this rare path: loads still outstanding where it rejoins the common path
+      // would make the compiler put a vmcnt wait -- counting the page prefetches -- before
+      // every page's first MFMA.  (gfx9 s_waitcnt encoding: vmcnt 0, expcnt 7, lgkmcnt 15.)
+      __builtin_amdgcn_s_waitcnt(0x0F70);
     }
     const int p = uu - __builtin_amdgcn_readfirstlane(s_start[rr]);
     const int rem = cur_len - p * kPage;
@@ -211,47 +221,60 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
     }
   };
 
-  // software pipeline: two pages in registers in flight while the third is scored from LDS
+  // Software pipeline: two pages in registers in flight while the third is scored from LDS.
+  // The steady-state loop handles two units per trip and always issues two pages of loads.
+  if (a.pool_bytes < KR::kPageBytes) {  // no page can be valid
+    if (lane == 0) flag_error(a.err, DSA_DEVERR_PAGE_OFFSET);
+    return;
+  }
   int u = u_beg;
   int rl = row_of(u, r);
-  const uint8_t *s0 = src_of(u);
-  int r_0 = rl;
-  if (s0) load(b0, s0);
-  const uint8_t *s1 = nullptr;
-  int r_1 = rl;
+  bool ok0, ok1 = false;
+  int r_0 = rl, r_1 = rl;
+  load(b0, src_of(u, ok0));
+  const uint8_t *src1 = a.pool;  // a wave with one unit still issues this load (same count on every path)
   if (u + 1 < u_end) {
     rl = row_of(u + 1, rl);
-    s1 = src_of(u + 1);
     r_1 = rl;
-    if (s1) load(b1, s1);
+    src1 = src_of(u + 1, ok1);
   }
-  for (;;) {
-    // unit u lives in b0
-    if (s0) park(b0);
-    const bool c0 = s0 != nullptr;
-    const int cu0 = u, cr0 = r_0;
-    s0 = nullptr;
-    if (u + 2 < u_end) {
-      rl = row_of(u + 2, rl);
-      s0 = src_of(u + 2);
-      r_0 = rl;
-      if (s0) load(b0, s0);
+  load(b1, src1);
+  while (u + 3 < u_end) {
+    park(b0);
+    const bool c0 = ok0;
+    const int cr0 = r_0;
+    rl = row_of(u + 2, rl);
+    r_0 = rl;
+    load(b0, src_of(u + 2, ok0));
+    if (c0) compute(u, cr0);
+    ++u;
+    park(b1);
+    const bool c1 = ok1;
+    const int cr1 = r_1;
+    rl = row_of(u + 2, rl);
+    r_1 = rl;
+    load(b1, src_of(u + 2, ok1));
+    if (c1) compute(u, cr1);
+    ++u;
+  }
+  // the last one to three units
+  for (int t = 0; u < u_end; ++t, ++u) {
+    if ((t & 1) == 0) {
+      park(b0);
+      const bool c0 = ok0;
+      const int cr0 = r_0;
+      if (u + 2 < u_end) {
+        rl = row_of(u + 2, rl);
+        r_0 = rl;
+        load(b0, src_of(u + 2, ok0));
+      }
+      if (c0) compute(u, cr0);
+    } else {
+      park(b1);
+      const bool c1 = ok1;
+      const int cr1 = r_1;
+      if (c1) compute(u, cr1);
     }
-    if (c0) compute(cu0, cr0);
-    if (++u >= u_end) break;
-    // unit u lives in b1
-    if (s1) park(b1);
-    const bool c1 = s1 != nullptr;
-    const int cu1 = u, cr1 = r_1;
-    s1 = nullptr;
-    if (u + 2 < u_end) {
-      rl = row_of(u + 2, rl);
-      s1 = src_of(u + 2);
-      r_1 = rl;
-      if (s1) load(b1, s1);
-    }
-    if (c1) compute(cu1, cr1);
-    if (++u >= u_end) break;
   }
 }
 
