@@ -196,7 +196,9 @@ static dsa_status mla_common(const dsa_layout *layout, const uint8_t *pool, int6
   if (n_q < 0 || n_req < 0 || k < 0 || idx_ld < k || off_ld < 1 || pool_bytes < 0 || n_heads < 1)
     return DSA_ERR_BAD_SHAPE;
   if (n_heads > kMaxHeads || n_q > kMaxGridY) return DSA_ERR_UNSUPPORTED;
+  if (k > 64 * tps) return DSA_ERR_UNSUPPORTED;  // at most 64 token splits per row
   if (n_q == 0) return DSA_OK;
+  if (pool_bytes < layout->lat_page_bytes) return DSA_ERR_BAD_SHAPE;  // smaller than one page
   if (!pool || !lat_off || !ctx_len || !idx || !q || !out || !lse) return DSA_ERR_NULL_ARG;
   if (q_fmt == DSA_Q_FP8_E4M3 && !q_scale) return DSA_ERR_NULL_ARG;
   if (!aligned(pool, 16) || !aligned(q, 16) || !aligned(lat_off, 8) || !aligned(ctx_len, 4) || !aligned(idx, 4) ||
@@ -233,7 +235,11 @@ static dsa_status mla_common(const dsa_layout *layout, const uint8_t *pool, int6
   return launched(launch_mla(a, stream_of(stream)));
 }
 
-static int32_t prefill_tokens_per_split(int32_t k) { return k <= 32 ? 32 : (k + 31) / 32 * 32; }
+// Prefill: one split per row while k <= 2048 (whole 64-token subtiles).
+static int32_t prefill_tokens_per_split(int32_t k) {
+  const int32_t t = k <= 64 ? 64 : (k + 63) / 64 * 64;
+  return t > 2048 ? 2048 : t;
+}
 
 dsa_status dsa_sparse_mla_decode_workspace_size(int32_t n_req, int32_t n_heads, int32_t k, size_t *bytes) {
   if (!bytes) return DSA_ERR_NULL_ARG;

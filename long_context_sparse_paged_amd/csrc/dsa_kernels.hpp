@@ -80,7 +80,7 @@ struct MlaArgs {
   int32_t *err;
   int32_t lat_fmt, q_fmt;
   void *ws;
-  int32_t tokens_per_split;  // multiple of 32; nsplit = ceil(k / tokens_per_split)
+  int32_t tokens_per_split;  // multiple of 64, <= 2048; nsplit = ceil(k / tokens_per_split)
 };
 size_t mla_workspace_bytes(int32_t n_q, int32_t n_heads, int32_t k, int32_t tokens_per_split);
 hipError_t launch_mla(const MlaArgs &a, hipStream_t s);

@@ -9,20 +9,23 @@
 //    row over its local heads, reading the selected tokens straight from the cache.
 // Keys are all 576 latent dims, values the first 512 (the no-rope part).
 //
-// One workgroup = (query row, token split, 16-head tile); 4 waves.  Per 32-token
-// subtile:
-//   gather  the 32 selected latents (through the page table) are decoded to bf16
-//           (exact for e4m3 and NVFP4) into LDS twice: token-major Kt[32][576] for
-//           Q.K and dim-major Vt[512][32] for P.V (an MFMA fragment needs 8
-//           consecutive contraction elements per lane);
-//   QK      waves 0-1: S^T[16 tokens][16 heads] = Kt . Q^T, 18 v_mfma_f32_16x16x32_bf16;
-//   softmax online, per head, in log2 units; P is rounded to bf16 once and the
-//           same rounded values feed both P.V and the row sum;
-//   PV      all 4 waves: O^T[128 dims][16 heads] += Vt . P^T over the 32 tokens;
-//           the S^T accumulator layout is already the B-operand layout of P^T.
-// kv_scale and the query's FP8 scale are applied in fp32 (logits and output),
-// never folded into bf16 operands.  Token splits of fixed size are merged in
-// a fixed order, so a row's result does not depend on the batch.
+// One workgroup = (query row, token split, 16-head tile); 4 waves.  The split's token
+// offsets are resolved once (index -> page -> pool offset).  Then, per 64-token subtile:
+//   gather  the 64 latents (nontemporal 16-B loads, issued one subtile ahead into
+//           registers) are decoded to bf16 -- exact for e4m3 and NVFP4 -- into one
+//           token-major LDS tile Kt[64][576];
+//   QK      wave w: S^T[16 tokens][16 heads] = Kt[16w..] . Q^T, 18 v_mfma_f32_16x16x32_bf16;
+//   softmax online, per head, in log2 units; P is rounded to bf16 once and the same
+//           rounded values feed both P.V and the row sum;
+//   PV      wave w: O^T[128 dims][16 heads] += V^T . P^T over the 64 tokens.  The V^T
+//           operand (8 consecutive tokens of one dim per lane) is read from the same
+//           token-major tile with ds_read_b64_tr_b16: in each 16-lane group, source lane
+//           L points at row r0 + (L>>2), dims d0 + 4(L&3), and lane i receives rows
+//           r0..r0+3 of dim d0 + i.  The S^T accumulator layout is already the B-operand
+//           layout of P^T.
+// kv_scale and the query's FP8 scale are applied in fp32 (logits and output), never
+// folded into bf16 operands.  Token splits have a fixed size and are merged in a fixed
+// order, so a row's result does not depend on the batch.
 #include <math.h>
 
 #include "dsa_device.hpp"
@@ -32,9 +35,11 @@ namespace dsa {
 
 namespace {
 
-constexpr int kSub = 32;     // tokens per subtile
-constexpr int kKtLd = 584;   // bf16 per Kt row (576 + 8 pad) = 1168 B
-constexpr int kVtLd = 40;    // bf16 per Vt row (32 + 8 pad) = 80 B
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+
+constexpr int kSub = 64;     // tokens per subtile
+constexpr int kKtLd = 592;   // bf16 per Kt row (576 + 16 pad: rows land 8 banks apart)
+constexpr int kMaxTps = 2048;
 
 struct MlaWs {
   float *o;    // [n_q][nsplit][H][512] unnormalised partial outputs
@@ -52,17 +57,30 @@ __host__ __device__ inline MlaWs mla_carve(void *ws, int32_t n_q, int32_t H, int
   return w;
 }
 
-__device__ __forceinline__ uint32_t bf16_bits(__bf16 x) { return (uint32_t)__builtin_bit_cast(uint16_t, x); }
+// 16 raw bytes of a latent row chunk per gather item.
+template <int LAT_FMT>
+struct Gather {
+  // FP8: 36 chunks of 16 B per token (16 dims each).  NVFP4: 16 chunks of 16 B of e2m1
+  // (32 dims each, two 16-dim block scales) + 4 chunks of 16 B of rope e4m3 (16 dims each).
+  static constexpr int kChunks = LAT_FMT == 0 ? 36 : 20;
+  static constexpr int kItems = kSub * kChunks;          // 2304 / 1280
+  static constexpr int kPerThread = kItems / 256;        // 9 / 5
+  static_assert(kItems % 256 == 0, "gather items must tile the workgroup");
+};
+
+__device__ __forceinline__ i16x4_t tr16(const uint16_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t *)(const_cast<uint16_t *>(p)));
+}
 
 template <int LAT_FMT, int Q_FMT>
-__global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a, const int nsplit, const int tps, MlaWs w) {
+__global__ __launch_bounds__(256, 2) void mla_kernel(const MlaArgs a, const int nsplit, const int tps, MlaWs w) {
+  using G = Gather<LAT_FMT>;
   constexpr int LB = LAT_FMT == 0 ? 576 : 352;
   constexpr int64_t LPB = (int64_t)kPage * LB;
   __shared__ __align__(16) uint16_t s_kt[kSub * kKtLd];
-  __shared__ __align__(16) uint16_t s_vt[kVDim * kVtLd];
-  __shared__ __align__(16) uint16_t s_p[2][64 * 4];
-  __shared__ int64_t s_off[kSub];
-  __shared__ float s_red[2][2][16];
+  __shared__ __align__(16) uint16_t s_p[4][64 * 4];
+  __shared__ float s_red[2][4][16];
+  extern __shared__ int64_t s_off[];  // [tps]: pool offset of each of the split's tokens
 
   const int ht = blockIdx.x, sp = blockIdx.y, r = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -75,7 +93,28 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a, const int nsp
   if (!rvalid && tid == 0 && sp == 0 && ht == 0) flag_error(a.err, DSA_DEVERR_REQUEST);
   const int ctx = rvalid ? a.ctx_len[b] : 0;
   const int t_beg = sp * tps;
-  const int t_end = min(a.k, t_beg + tps);
+  const int n_tok = max(0, min(a.k, t_beg + tps) - t_beg);
+
+  // (0) pool offsets of the split's tokens (-1: padding or invalid)
+  for (int j = tid; j < n_tok; j += 256) {
+    int64_t off = -1;
+    if (rvalid) {
+      const int t = a.idx[(int64_t)r * a.idx_ld + t_beg + j];
+      if (t >= 0) {
+        const int pg = t >> 6;
+        if (t >= ctx || pg >= a.off_ld) {
+          flag_error(a.err, DSA_DEVERR_INDEX);
+        } else {
+          const int64_t po = a.lat_off[(int64_t)b * a.off_ld + pg];
+          if (po < 0 || po + LPB > a.pool_bytes || (po & 15))
+            flag_error(a.err, DSA_DEVERR_PAGE_OFFSET);
+          else
+            off = po + (int64_t)(t & 63) * LB;
+        }
+      }
+    }
+    s_off[j] = off;
+  }
 
   // Q^T fragments: lane (head hl, group g) holds q[h][32s + 8g .. +8] for s < 18
   bf16x8_t qf[18];
@@ -99,123 +138,130 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a, const int nsp
     for (int s = 0; s < 18; ++s) qf[s] = bf16x8_t{};
   }
   const float c2 = a.sm_scale * a.kv_scale * qscale * kLog2e;  // logits in log2 units
+  __syncthreads();  // s_off ready; query loads drained before the gather pipeline starts
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  // (1) gather pipeline: raw 16-B chunks of the next subtile live in registers
+  u32x4_t raw[G::kPerThread];
+  uint32_t bsc[G::kPerThread];  // NVFP4: the chunk's two e4m3 block scales (bytes 0, 1)
+  auto issue = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < G::kPerThread; ++i) {
+      const int item = tid + 256 * i;
+      const int tok = item / G::kChunks, c = item - tok * G::kChunks;
+      const int j = t0 + tok;
+      const int64_t off = j < n_tok ? s_off[j] : -1;
+      // every lane issues the load (an invalid token reads the pool's first bytes and is
+      // zeroed on decode), so the number of loads in flight is the same on every path
+      const uint8_t *base = a.pool + (off < 0 ? 0 : off);
+      if constexpr (LAT_FMT == 0) {
+        raw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(base + 16 * c));
+      } else {
+        const int boff = c < 16 ? 16 * c : 288 + 16 * (c - 16);
+        raw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(base + boff));
+        bsc[i] = *reinterpret_cast<const uint16_t *>(base + 256 + 2 * (c < 16 ? c : 0));
+      }
+    }
+  };
+  auto park = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < G::kPerThread; ++i) {
+      const int item = tid + 256 * i;
+      const int tok = item / G::kChunks, c = item - tok * G::kChunks;
+      const int j = t0 + tok;
+      const bool ok = j < n_tok && s_off[j] >= 0;
+      uint16_t *dst = s_kt + tok * kKtLd;
+      if constexpr (LAT_FMT == 0) {
+        bf16x8_t lo = e4m3x8_bf16(raw[i][0], raw[i][1]), hi = e4m3x8_bf16(raw[i][2], raw[i][3]);
+        if (!ok) lo = hi = bf16x8_t{};
+        *reinterpret_cast<bf16x8_t *>(dst + 16 * c) = lo;
+        *reinterpret_cast<bf16x8_t *>(dst + 16 * c + 8) = hi;
+      } else if (c < 16) {  // 32 no-rope dims: e2m1 x block scale
+        const float s0 = e4m3_f32(bsc[i] & 0xFFu), s1 = e4m3_f32((bsc[i] >> 8) & 0xFFu);
+        bf16x8_t v0 = nvfp4x8_bf16(raw[i][0], s0), v1 = nvfp4x8_bf16(raw[i][1], s0);
+        bf16x8_t v2 = nvfp4x8_bf16(raw[i][2], s1), v3 = nvfp4x8_bf16(raw[i][3], s1);
+        if (!ok) v0 = v1 = v2 = v3 = bf16x8_t{};
+        *reinterpret_cast<bf16x8_t *>(dst + 32 * c) = v0;
+        *reinterpret_cast<bf16x8_t *>(dst + 32 * c + 8) = v1;
+        *reinterpret_cast<bf16x8_t *>(dst + 32 * c + 16) = v2;
+        *reinterpret_cast<bf16x8_t *>(dst + 32 * c + 24) = v3;
+      } else {  // 16 rope dims, e4m3
+        bf16x8_t lo = e4m3x8_bf16(raw[i][0], raw[i][1]), hi = e4m3x8_bf16(raw[i][2], raw[i][3]);
+        if (!ok) lo = hi = bf16x8_t{};
+        *reinterpret_cast<bf16x8_t *>(dst + 512 + 16 * (c - 16)) = lo;
+        *reinterpret_cast<bf16x8_t *>(dst + 512 + 16 * (c - 16) + 8) = hi;
+      }
+    }
+  };
 
   float m_run = -INFINITY, l_run = 0.0f;
   f32x4_t o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4_t{};
 
-  for (int t0 = t_beg; t0 < t_end; t0 += kSub) {
-    // (a) pool offsets of this subtile's tokens (-1: padding or invalid)
-    if (tid < kSub) {
-      const int i = t0 + tid;
-      int64_t off = -1;
-      if (i < t_end && rvalid) {
-        const int t = a.idx[(int64_t)r * a.idx_ld + i];
-        if (t >= 0) {
-          const int pg = t >> 6;
-          if (t >= ctx || pg >= a.off_ld) {
-            flag_error(a.err, DSA_DEVERR_INDEX);
-          } else {
-            const int64_t po = a.lat_off[(int64_t)b * a.off_ld + pg];
-            if (po < 0 || po + LPB > a.pool_bytes || (po & 15))
-              flag_error(a.err, DSA_DEVERR_PAGE_OFFSET);
-            else
-              off = po + (int64_t)(t & 63) * LB;
-          }
-        }
-      }
-      s_off[tid] = off;
-    }
+  if (n_tok > 0) issue(0);
+  for (int t0 = 0; t0 < n_tok; t0 += kSub) {
+    park(t0);
     __syncthreads();
+    if (t0 + kSub < n_tok) issue(t0 + kSub);  // uniform; flies while this subtile is computed
 
-    // (b) gather + decode: item = (4-token group tg, 8-dim chunk c)
-    for (int item = tid; item < (kSub / 4) * 72; item += 256) {
-      const int tg = item / 72, c = item - tg * 72;
-      bf16x8_t v[4];
+    // (2) S^T = K Q^T, wave w: tokens 16w..16w+15
+    f32x4_t acc = {};
+    const uint16_t *krow = s_kt + (16 * wid + hl) * kKtLd + 8 * g;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t off = s_off[4 * tg + j];
-        if (off < 0) {
-          v[j] = bf16x8_t{};
-        } else if constexpr (LAT_FMT == 0) {
-          const u32x2_t d = *reinterpret_cast<const u32x2_t *>(a.pool + off + 8 * c);
-          v[j] = e4m3x8_bf16(d[0], d[1]);
-        } else {
-          if (c < 64) {
-            const uint32_t dw = *reinterpret_cast<const uint32_t *>(a.pool + off + 4 * c);
-            v[j] = nvfp4x8_bf16(dw, e4m3_f32(a.pool[off + 256 + (c >> 1)]));
-          } else {
-            const u32x2_t d = *reinterpret_cast<const u32x2_t *>(a.pool + off + 288 + 8 * (c - 64));
-            v[j] = e4m3x8_bf16(d[0], d[1]);
-          }
-        }
-        *reinterpret_cast<bf16x8_t *>(s_kt + (4 * tg + j) * kKtLd + 8 * c) = v[j];
-      }
-      if (c < 64) {
+    for (int s = 0; s < 18; ++s) acc = mfma_16x16x32_bf16(*reinterpret_cast<const bf16x8_t *>(krow + 32 * s), qf[s], acc);
+    float z[4], mx = -INFINITY;
 #pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-          u32x2_t pr;
-          pr[0] = bf16_bits(v[0][dd]) | (bf16_bits(v[1][dd]) << 16);
-          pr[1] = bf16_bits(v[2][dd]) | (bf16_bits(v[3][dd]) << 16);
-          *reinterpret_cast<u32x2_t *>(s_vt + (8 * c + dd) * kVtLd + 4 * tg) = pr;
-        }
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int j = t0 + 16 * wid + 4 * g + i;
+      z[i] = (j < n_tok && s_off[j] >= 0) ? acc[i] * c2 : -INFINITY;
+      mx = fmaxf(mx, z[i]);
     }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (g == 0) s_red[0][wid][hl] = mx;
     __syncthreads();
-
-    // (c) S^T = K Q^T on waves 0-1 (16 tokens each)
-    float z[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    if (wid < 2) {
-      f32x4_t acc = {};
-      const uint16_t *krow = s_kt + (16 * wid + hl) * kKtLd + 8 * g;
-#pragma unroll
-      for (int s = 0; s < 18; ++s) acc = mfma_16x16x32_bf16(*reinterpret_cast<const bf16x8_t *>(krow + 32 * s), qf[s], acc);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = 16 * wid + 4 * g + i;
-        z[i] = s_off[tok] >= 0 ? acc[i] * c2 : -INFINITY;
-        mx = fmaxf(mx, z[i]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (g == 0) s_red[0][wid][hl] = mx;
-    }
-    __syncthreads();
-    const float m_new = fmaxf(m_run, fmaxf(s_red[0][0][hl], s_red[0][1][hl]));
+    const float m_new =
+        fmaxf(m_run, fmaxf(fmaxf(s_red[0][0][hl], s_red[0][1][hl]), fmaxf(s_red[0][2][hl], s_red[0][3][hl])));
     const float alpha = m_new == -INFINITY ? 1.0f : exp2f(m_run - m_new);
-    if (wid < 2) {
-      float ps = 0.0f;
-      bf16x4_t pb;
+    float ps = 0.0f;
+    bf16x4_t pb;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = z[i] == -INFINITY ? 0.0f : exp2f(z[i] - m_new);
-        pb[i] = (__bf16)p;
-        ps += (float)pb[i];
-      }
-      *reinterpret_cast<bf16x4_t *>(s_p[wid] + 4 * lane) = pb;
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
-      if (g == 0) s_red[1][wid][hl] = ps;
+    for (int i = 0; i < 4; ++i) {
+      const float p = z[i] == -INFINITY ? 0.0f : exp2f(z[i] - m_new);
+      pb[i] = (__bf16)p;
+      ps += (float)pb[i];
     }
+    *reinterpret_cast<bf16x4_t *>(s_p[wid] + 4 * lane) = pb;
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    if (g == 0) s_red[1][wid][hl] = ps;
     __syncthreads();
-    l_run = l_run * alpha + s_red[1][0][hl] + s_red[1][1][hl];
+    l_run = l_run * alpha + ((s_red[1][0][hl] + s_red[1][1][hl]) + (s_red[1][2][hl] + s_red[1][3][hl]));
     m_run = m_new;
 
-    // (d) O^T += Vt . P^T; k-slot j of group g is token 4g+j (j<4) or 16+4g+j-4 (j>=4)
-    const bf16x8_t pf = cat4(*reinterpret_cast<const bf16x4_t *>(s_p[0] + 4 * lane),
-                             *reinterpret_cast<const bf16x4_t *>(s_p[1] + 4 * lane));
+    // (3) O^T += V^T P^T.  K-step ks covers tokens 32ks..32ks+31; k-slot j of group g is
+    // token 32ks + 4g + j (j < 4, from S^T tile 2ks) or 32ks + 16 + 4g + j - 4 (tile 2ks+1).
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const uint16_t *vrow = s_vt + (128 * wid + 16 * dt + hl) * kVtLd + 4 * g;
-      const bf16x8_t va = cat4(*reinterpret_cast<const bf16x4_t *>(vrow), *reinterpret_cast<const bf16x4_t *>(vrow + 16));
-      o[dt] = mfma_16x16x32_bf16(va, pf, o[dt] * alpha);
+    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8_t pf = cat4(*reinterpret_cast<const bf16x4_t *>(s_p[2 * ks] + 4 * lane),
+                               *reinterpret_cast<const bf16x4_t *>(s_p[2 * ks + 1] + 4 * lane));
+      const uint16_t *v0 = s_kt + (32 * ks + 4 * g + (hl >> 2)) * kKtLd + 4 * (hl & 3);
+      const uint16_t *v1 = v0 + 16 * kKtLd;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int d0 = 128 * wid + 16 * dt;
+        const i16x4_t x0 = tr16(v0 + d0), x1 = tr16(v1 + d0);
+        const bf16x8_t va = cat4(__builtin_bit_cast(bf16x4_t, x0), __builtin_bit_cast(bf16x4_t, x1));
+        o[dt] = mfma_16x16x32_bf16(va, pf, o[dt]);
+      }
     }
-    __syncthreads();
+    __syncthreads();  // s_kt and s_p are rewritten by the next subtile
   }
 
-  // (e) results: lane (head hl, group g) holds dims 128*wid + 16*dt + 4g + i
+  // (4) results: lane (head hl, group g) holds dims 128*wid + 16*dt + 4g + i
   if (!hvalid) return;
   if (nsplit == 1) {
     const float inv = l_run > 0.0f ? a.kv_scale / l_run : 0.0f;
@@ -237,35 +283,40 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a, const int nsp
   }
 }
 
-// Merge the token splits of one (row, head) in split order: 128 threads x 4 dims.
-__global__ __launch_bounds__(128) void mla_combine_kernel(const MlaArgs a, const int nsplit, MlaWs w) {
-  const int h = blockIdx.x, r = blockIdx.y, H = a.n_heads;
+// Merge the token splits of one row in split order.  Thread = (head, 4 dims).
+constexpr int kCombineMaxSplits = 64;
+__global__ __launch_bounds__(256) void mla_combine_kernel(const MlaArgs a, const int nsplit, MlaWs w) {
+  const int r = blockIdx.y, H = a.n_heads;
+  const int q = blockIdx.x * 256 + threadIdx.x;  // (head, dim quad)
+  if (q >= H * (kVDim / 4)) return;
+  const int h = q / (kVDim / 4), d4 = q % (kVDim / 4);
   const int64_t base = (int64_t)r * nsplit * H + h;
   float M = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, w.ml[base + (int64_t)s * H].x);
   float L = 0.0f;
   f32x4_t acc = {};
   if (M != -INFINITY) {
+#pragma unroll 8
     for (int s = 0; s < nsplit; ++s) {
-      const float2 ml = w.ml[base + (int64_t)s * H];
-      if (ml.x == -INFINITY) continue;
-      const float f = exp2f(ml.x - M);
+      const float2 ml = w.ml[base + (int64_t)s * H];  // second read hits the cache
+      const float f = ml.x == -INFINITY ? 0.0f : exp2f(ml.x - M);
       L += ml.y * f;
-      acc += *reinterpret_cast<const f32x4_t *>(w.o + (base + (int64_t)s * H) * kVDim + 4 * threadIdx.x) * f;
+      acc += *reinterpret_cast<const f32x4_t *>(w.o + (base + (int64_t)s * H) * kVDim + 4 * d4) * f;
     }
   }
   const float inv = L > 0.0f ? a.kv_scale / L : 0.0f;
   bf16x4_t v;
 #pragma unroll
   for (int i = 0; i < 4; ++i) v[i] = (__bf16)(acc[i] * inv);
-  *reinterpret_cast<bf16x4_t *>(a.out + ((int64_t)r * H + h) * kVDim + 4 * threadIdx.x) = v;
-  if (threadIdx.x == 0) a.lse[(int64_t)r * H + h] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  *reinterpret_cast<bf16x4_t *>(a.out + ((int64_t)r * H + h) * kVDim + 4 * d4) = v;
+  if (d4 == 0) a.lse[(int64_t)r * H + h] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 template <int LAT_FMT, int Q_FMT>
 void launch_mla_t(const MlaArgs &a, int nsplit, int tps, MlaWs w, hipStream_t s) {
   dim3 grid((a.n_heads + 15) / 16, nsplit, a.n_q);
-  hipLaunchKernelGGL((mla_kernel<LAT_FMT, Q_FMT>), grid, dim3(256), 0, s, a, nsplit, tps, w);
+  hipLaunchKernelGGL((mla_kernel<LAT_FMT, Q_FMT>), grid, dim3(256), sizeof(int64_t) * (size_t)tps, s, a, nsplit, tps, w);
 }
 
 int split_count(int32_t k, int32_t tps) { return k <= 0 ? 1 : (k + tps - 1) / tps; }
@@ -282,14 +333,17 @@ hipError_t launch_mla(const MlaArgs &a, hipStream_t s) {
   if (a.n_q == 0) return hipSuccess;
   const int tps = a.tokens_per_split;
   const int nsplit = split_count(a.k, tps);
+  if (tps > kMaxTps || tps % kSub != 0 || nsplit > kCombineMaxSplits) return hipErrorInvalidValue;
   const MlaWs w = mla_carve(a.ws, a.n_q, a.n_heads, nsplit);
   if (a.lat_fmt == 0) {
     if (a.q_fmt == 0) launch_mla_t<0, 0>(a, nsplit, tps, w, s); else launch_mla_t<0, 1>(a, nsplit, tps, w, s);
   } else {
     if (a.q_fmt == 0) launch_mla_t<1, 0>(a, nsplit, tps, w, s); else launch_mla_t<1, 1>(a, nsplit, tps, w, s);
   }
-  if (nsplit > 1)
-    hipLaunchKernelGGL(mla_combine_kernel, dim3(a.n_heads, a.n_q), dim3(128), 0, s, a, nsplit, w);
+  if (nsplit > 1) {
+    dim3 grid((a.n_heads * (kVDim / 4) + 255) / 256, a.n_q);
+    hipLaunchKernelGGL(mla_combine_kernel, grid, dim3(256), 0, s, a, nsplit, w);
+  }
   return hipGetLastError();
 }
 
