@@ -5,24 +5,34 @@
 //  * section "低延迟解码：融合的 DSA 解码路径": scorer and an exact top-k are two kernels;
 //  * section "流量减少 10× 的精确 top-k 合并": the global top-2048 is radix-selected
 //    from a candidate set, and the selection detects when a part held more of the
-//    top-k than it offered and redoes that row in full -- the same shape as here;
+//    top-k than it offered and redoes that part -- the same shape as here;
 //  * section "day 0 零失配 RL": a batch-invariant top-k (a token's result does not
 //    depend on its batch) -- here the result is a pure function of the row.
 //
 // Scores map to order-preserving uint32 keys (-0 -> +0), so the selection is an
-// integer problem on (key desc, index asc).  Three launches:
-//   1. sample   (one workgroup per long row): 64 evenly spread runs of 64 scores give
-//               4096 sample keys; the threshold `est` is the sample key whose rank
-//               predicts about 2k row elements >= est.
-//   2. collect  (one workgroup per 8192-score slice): every element with key >= est
-//               is appended, in index order, to the slice's candidate list.
-//   3. finalize (one workgroup per row): candidates of all slices, concatenated in
-//               slice order, are in index order; an LDS radix select finds the exact
-//               k-th key tau and how many ties at tau to keep; an ordered compaction
-//               writes the kept indices ascending.  Rows of <= 12288 scores skip 1-2
-//               and are loaded whole.  If the estimate failed (fewer than k
-//               candidates, a slice over capacity, too many in total) the row is
-//               selected exactly from the full row instead (always correct, slower).
+// integer problem on (key desc, index asc).  Launches:
+//   sample   (one workgroup per long row; skipped for a few short-enough rows, where
+//            every collect workgroup draws the same sample itself): runs of 64 scores
+//            spread evenly over the row give S sample keys; the threshold `est` is the
+//            sample key of rank m(k, len, S), set so that the row holds at least k
+//            elements >= est except with negligible probability, and a few k at most.
+//   collect  (one workgroup per 8192-score slice): the slice is loaded in one round trip
+//            and every element with key >= est is appended, in index order, to the
+//            slice's candidate list (ballot ranks; one barrier).
+//   finalize (one workgroup per row): the slices' candidates, concatenated in slice
+//            order, are in index order.  A slice that had more candidates than its list
+//            holds is filtered again from the scores.  An LDS radix select finds the
+//            exact k-th key tau and the number of ties at tau to keep; an ordered
+//            compaction writes the kept indices ascending.  Rows of <= 12288 scores skip
+//            sample and collect and are loaded whole.  If the candidates are fewer than k
+//            or more than LDS holds, the row is selected from the full row instead
+//            (always correct, slower).
+// The radix passes take their digits from key - min over the keys being selected,
+// starting at the top bit of max - min, and count into 16 copies of the histogram
+// (one per lane mod 16, odd stride): scores of one row share their leading bits, and a
+// plain histogram would send most of a wave's atomics to one address.
+// The result is exact whatever est is, so which launches a row goes through never
+// changes its output.
 #include "dsa_device.hpp"
 #include "dsa_kernels.hpp"
 
@@ -30,12 +40,20 @@ namespace dsa {
 
 namespace {
 
-constexpr int kSamples = 4096;
+constexpr int kOwnSamples = 4096;     // samples a collect workgroup draws itself
+constexpr int kOwnMaxLd = 262144;     // ... when rows are at most this long
+constexpr int kOwnMaxRows = 64;       // ... and there are at most this many
+constexpr int kMaxSamples = 16384;    // samples of the sample launch
 constexpr int kMaxSlices = 1024;
+constexpr int kRep = 16;              // histogram copies
+constexpr int kHistLd = 257;          // odd stride: the copies of one bin sit in different banks
+constexpr int kEstPasses = 2;         // 16 leading bits of the threshold are enough
+constexpr int kFinThreads = 512;
+constexpr int kFinPer = kShortRow / kFinThreads + 1;  // 25: candidates a finalize thread holds
 
 struct TopkWs {
   uint32_t *est;  // [n_rows]
-  uint32_t *cnt;  // [n_rows][n_slices]
+  uint32_t *cnt;  // [n_rows][n_slices] candidates of the slice (may exceed kSliceCap)
   uint2 *cand;    // [n_rows][n_slices][kSliceCap] (key, index)
 };
 
@@ -52,6 +70,14 @@ __host__ __device__ inline TopkWs carve(void *ws, int32_t n_rows, int32_t n_slic
   return w;
 }
 
+template <int NT>
+struct RadixLds {
+  int hist[2][kRep * kHistLd];  // double buffered: a pass clears the next one's
+  int tmp[NT / 64];
+  int sh[2];
+  uint32_t mm[2 * (NT / 64)];
+};
+
 __device__ __forceinline__ int row_len_of(const TopkArgs &a, int r) {
   int len = a.row_len[r];
   if (len < 0 || len > a.ld) {
@@ -61,104 +87,180 @@ __device__ __forceinline__ int row_len_of(const TopkArgs &a, int r) {
   return len;
 }
 
+// Sample rank of the threshold: with x = k S / len sample elements expected above the
+// row's k-th score, m = 1.25 x + 6 sqrt(x) + 8 puts the k-th score below est only if a
+// Poisson(x) count exceeds its mean by > 6 standard deviations.
+__device__ __forceinline__ int sample_rank(int keff, int len, int S) {
+  const float x = (float)keff * (float)S / (float)len;
+  return (int)ceilf(1.25f * x + 6.0f * sqrtf(x) + 8.0f);
+}
+
+// Block-wide inclusive scan of one int per thread; tmp holds NT / 64 ints.
+template <int NT>
+__device__ __forceinline__ int block_scan_incl(int v, int *tmp, int &total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
+  }
+  if (lane == 63) tmp[wid] = v;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int t = tmp[w];
+    base += w < wid ? t : 0;
+    total += t;
+  }
+  __syncthreads();
+  return v + base;
+}
+
+// Block-wide (min, max) of one key per thread.
+template <int NT>
+__device__ __forceinline__ void block_minmax(uint32_t &lo, uint32_t &hi, RadixLds<NT> &R) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, 64));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, 64));
+  }
+  if (lane == 0) {
+    R.mm[wid] = lo;
+    R.mm[NW + wid] = hi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    lo = min(lo, R.mm[w]);
+    hi = max(hi, R.mm[NW + w]);
+  }
+  __syncthreads();
+}
+
+// Radix select over keys in [kmin, kmax]: `visit(f)` calls f(key) for each of this
+// thread's keys.  Returns the m-th largest key (1-based) and in `gt` the number of keys
+// strictly larger, using 8-bit digits of key - kmin from the top bit of kmax - kmin down.
+// With max_passes below the number of digits the result is the lower edge of the bin that
+// holds the m-th largest key: at least m keys are >= it.
+template <int NT, class Visit>
+__device__ uint32_t radix_select(Visit visit, int m, uint32_t kmin, uint32_t kmax, int max_passes, RadixLds<NT> &R,
+                                 int &gt) {
+  const int tid = threadIdx.x;
+  gt = 0;
+  const uint32_t range = kmax - kmin;
+  if (range == 0) return kmin;
+  for (int i = tid; i < 2 * kRep * kHistLd; i += NT) (&R.hist[0][0])[i] = 0;
+  __syncthreads();
+  uint32_t prefix = 0;
+  int rem = m;
+  int hi = 31 - __clz((int)range);
+  for (int p = 0; hi >= 0 && p < max_passes; ++p, hi -= 8) {
+    const int lo = hi >= 7 ? hi - 7 : 0;
+    const uint32_t above = ~((2u << hi) - 1u);  // bits already decided
+    int *h = R.hist[p & 1];
+    int *my = h + (tid & (kRep - 1)) * kHistLd;
+    visit([&](uint32_t key) {
+      const uint32_t u = key - kmin;
+      if ((u & above) == prefix) atomicAdd(&my[(u >> lo) & 255u], 1);
+    });
+    __syncthreads();
+    // thread t < 256 sums bin 255 - t: an inclusive prefix over threads is a suffix over bins
+    int c = 0;
+    if (tid < 256) {
+#pragma unroll
+      for (int k = 0; k < kRep; ++k) c += h[k * kHistLd + 255 - tid];
+    }
+    int *o = R.hist[(p + 1) & 1];  // last read in the previous pass
+    for (int i = tid; i < kRep * kHistLd; i += NT) o[i] = 0;
+    int total;
+    const int incl = block_scan_incl<NT>(c, R.tmp, total);
+    const int excl = incl - c;
+    if (tid < 256 && excl < rem && incl >= rem) {
+      R.sh[0] = 255 - tid;
+      R.sh[1] = excl;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)R.sh[0] << lo;  // the digit's bits above hi repeat the prefix
+    rem -= R.sh[1];
+    gt += R.sh[1];
+  }
+  return kmin + prefix;
+}
+
 // Exclusive rank of `f` among the block's threads (thread order) and the block total.
-__device__ __forceinline__ int block_rank(bool f, int *s4, int &total) {
+template <int NT>
+__device__ __forceinline__ int block_rank(bool f, int *tmp, int &total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const unsigned long long bal = __ballot(f);
   const int rank = __popcll(bal & ((1ull << lane) - 1ull));
-  if (lane == 0) s4[wid] = __popcll(bal);
+  if (lane == 0) tmp[wid] = __popcll(bal);
   __syncthreads();
   int off = 0;
-  for (int w = 0; w < wid; ++w) off += s4[w];
-  total = s4[0] + s4[1] + s4[2] + s4[3];
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int t = tmp[w];
+    off += w < wid ? t : 0;
+    total += t;
+  }
   __syncthreads();
   return off + rank;
 }
 
-// Radix select, 8 bits per pass: the m-th largest key (1-based) among the n keys that
-// `load(i)` yields, and `gt` = how many keys are strictly larger.  blockDim.x == 256.
-template <class Load>
-__device__ uint32_t radix_select(Load load, int n, int m, int *s_hist, int *s_tmp, int *s_sh, int &gt) {
-  const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0;
-  int rem = m;
-  gt = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    s_hist[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += 256) {
-      const uint32_t key = load(i);
-      if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1);
-    }
-    __syncthreads();
-    // thread t looks at bin 255-t: an inclusive prefix over threads is a suffix over bins
-    const int c = s_hist[255 - tid];
-    int total;
-    const int incl = block_scan_incl_256(c, s_tmp, total);
-    const int excl = incl - c;
-    if (excl < rem && incl >= rem) {
-      s_sh[0] = 255 - tid;
-      s_sh[1] = excl;
-    }
-    __syncthreads();
-    const uint32_t digit = (uint32_t)s_sh[0];
-    rem -= s_sh[1];
-    gt += s_sh[1];
-    prefix |= digit << shift;
-    mask |= 0xFFu << shift;
-    __syncthreads();
-  }
-  return prefix;
-}
-
-// Ordered compaction: keep key > tau, and the first need_eq keys == tau in index order;
-// writes the kept indices to out[] ascending.
-template <class Load, class Index>
-__device__ void compact(Load load, Index index, int n, uint32_t tau, int need_eq, int32_t *out, int *s4) {
-  const int tid = threadIdx.x;
-  int written = 0, eq_seen = 0;
-  for (int c0 = 0; c0 < n; c0 += 256) {
-    const int i = c0 + tid;
-    uint32_t key = 0;
-    if (i < n) key = load(i);
-    const bool gtf = i < n && key > tau;
-    const bool eqf = i < n && key == tau;
-    int eq_tot, sel_tot;
-    const int eq_rank = block_rank(eqf, s4, eq_tot);
-    const bool sel = gtf || (eqf && eq_seen + eq_rank < need_eq);
-    const int pos = block_rank(sel, s4, sel_tot);
-    if (sel) out[written + pos] = index(i);
-    written += sel_tot;
-    eq_seen += eq_tot;
-  }
+// Sample position q (4 consecutive scores) of S: runs of 64 starting at multiples of 4,
+// spread evenly from 0 to len - 64.
+__device__ __forceinline__ float4 load_sample4(const float *row, bool vec, int len, int runs, int q) {
+  const int c = q >> 4, part = q & 15;
+  const int start = (int)((int64_t)(len - 64) * c / (runs - 1)) & ~3;
+  const float *p = row + start + 4 * part;
+  if (vec) return *reinterpret_cast<const float4 *>(p);
+  return make_float4(p[0], p[1], p[2], p[3]);
 }
 
 __global__ __launch_bounds__(256) void topk_sample_kernel(const TopkArgs a, TopkWs w) {
-  __shared__ uint32_t s_key[kSamples];
-  __shared__ int s_hist[256], s_tmp[4], s_sh[2];
+  __shared__ __align__(16) uint32_t s_smp[kMaxSamples];
+  __shared__ RadixLds<256> R;
   const int r = blockIdx.x;
   const int len = row_len_of(a, r);
   const int keff = min(a.k, len);
   if (len <= kShortRow || keff >= len) return;  // uniform
   const float *row = a.scores + (int64_t)r * a.ld;
-  for (int i = threadIdx.x; i < kSamples; i += 256) {
-    const int c = i >> 6, j = i & 63;
-    const int64_t start = (int64_t)(len - 64) * c / 63;
-    s_key[i] = score_key(row[start + j]);
+  const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+  int S = kOwnSamples;  // about len / 32, a power of two
+  while (S < kMaxSamples && S * 32 < len) S <<= 1;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  for (int q = threadIdx.x; q < S / 4; q += 256) {
+    const float4 v = load_sample4(row, vec, len, S / 64, q);
+    const uint4 k = make_uint4(score_key(v.x), score_key(v.y), score_key(v.z), score_key(v.w));
+    *reinterpret_cast<uint4 *>(s_smp + 4 * q) = k;
+    lo = min(min(lo, min(k.x, k.y)), min(k.z, k.w));
+    hi = max(max(hi, max(k.x, k.y)), max(k.z, k.w));
   }
-  __syncthreads();
-  // expect ~2k elements >= est: rank 2k*S/len among the samples, plus a margin
-  const int64_t m64 = (2 * (int64_t)keff * kSamples + len - 1) / len + 16;
-  uint32_t est = 0;
-  if (m64 < kSamples) {
+  block_minmax<256>(lo, hi, R);  // also orders the s_smp stores before the reads below
+  const int m = sample_rank(keff, len, S);
+  uint32_t est = 0u;
+  if (m < S) {
     int gt;
-    est = radix_select([&](int i) { return s_key[i]; }, kSamples, (int)m64, s_hist, s_tmp, s_sh, gt);
+    est = radix_select<256>(
+        [&](auto f) {
+          for (int i = threadIdx.x; i < S; i += 256) f(s_smp[i]);
+        },
+        m, lo, hi, kEstPasses, R, gt);
   }
   if (threadIdx.x == 0) w.est[r] = est;
 }
 
+// Slice element (chunk j, lane quad e) of thread t is beg + 1024 j + 4 t + e.
+template <bool OWN>
 __global__ __launch_bounds__(256) void topk_collect_kernel(const TopkArgs a, TopkWs w, int n_slices) {
-  __shared__ int s4[4][4];
+  __shared__ RadixLds<256> R;
+  __shared__ __align__(16) int s_tot[8][4];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int r = blockIdx.y, s = blockIdx.x;
   const int len = row_len_of(a, r);
@@ -171,50 +273,131 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(const TopkArgs a, Top
     return;
   }
   const int end = min(len, beg + kSlice);
-  const uint32_t thr = w.est[r];
   const float *row = a.scores + (int64_t)r * a.ld;
-  uint2 *out = w.cand + ((int64_t)r * n_slices + s) * kSliceCap;
-  int count = 0;
-  for (int c0 = beg; c0 < end; c0 += 1024) {
-    uint32_t key[4];
-    bool f[4];
+  const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+
+  // (1) the slice and (own threshold) the row's samples, all loads in flight at once
+  float4 v[8];
+  if (vec && end - beg == kSlice) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = c0 + 256 * j + tid;
-      f[j] = false;
-      key[j] = 0;
-      if (i < end) {
-        key[j] = score_key(row[i]);
-        f[j] = key[j] >= thr;
+    for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const float4 *>(row + beg + 1024 * j + 4 * tid);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = beg + 1024 * j + 4 * tid;
+      v[j].x = i < end ? row[i] : 0.0f;
+      v[j].y = i + 1 < end ? row[i + 1] : 0.0f;
+      v[j].z = i + 2 < end ? row[i + 2] : 0.0f;
+      v[j].w = i + 3 < end ? row[i + 3] : 0.0f;
+    }
+  }
+  uint32_t est;
+  if constexpr (OWN) {
+    constexpr int kQ = kOwnSamples / 4 / 256;  // 4 sample quads per thread
+    uint32_t sk[4 * kQ];
+#pragma unroll
+    for (int u = 0; u < kQ; ++u) {
+      const float4 t = load_sample4(row, vec, len, kOwnSamples / 64, tid + 256 * u);
+      sk[4 * u] = score_key(t.x);
+      sk[4 * u + 1] = score_key(t.y);
+      sk[4 * u + 2] = score_key(t.z);
+      sk[4 * u + 3] = score_key(t.w);
+    }
+    uint32_t lo = sk[0], hi = sk[0];
+#pragma unroll
+    for (int q = 1; q < 4 * kQ; ++q) {
+      lo = min(lo, sk[q]);
+      hi = max(hi, sk[q]);
+    }
+    block_minmax<256>(lo, hi, R);
+    const int m = sample_rank(keff, len, kOwnSamples);
+    est = 0u;
+    if (m < kOwnSamples) {
+      int gt;
+      est = radix_select<256>(
+          [&](auto f) {
+#pragma unroll
+            for (int q = 0; q < 4 * kQ; ++q) f(sk[q]);
+          },
+          m, lo, hi, kEstPasses, R, gt);
+    }
+    if (s == 0 && tid == 0) w.est[r] = est;
+  } else {
+    est = w.est[r];
+  }
+  // (2) ordered append of the elements >= est
+  uint32_t key[8][4];
+  unsigned long long bal[8][4];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = beg + 1024 * j + 4 * tid;
+    key[j][0] = score_key(v[j].x);
+    key[j][1] = score_key(v[j].y);
+    key[j][2] = score_key(v[j].z);
+    key[j][3] = score_key(v[j].w);
+    int cj = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bal[j][e] = __ballot(i + e < end && key[j][e] >= est);
+      cj += __popcll(bal[j][e]);
+    }
+    if (lane == 0) s_tot[j][wid] = cj;
+  }
+  __syncthreads();
+  int4 tot[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) tot[j] = *reinterpret_cast<const int4 *>(s_tot[j]);
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  uint2 *out = w.cand + ((int64_t)r * n_slices + s) * kSliceCap;
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int rank = base + (wid > 0 ? tot[j].x : 0) + (wid > 1 ? tot[j].y : 0) + (wid > 2 ? tot[j].z : 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rank += __popcll(bal[j][e] & lt);
+    const int i = beg + 1024 * j + 4 * tid;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if ((bal[j][e] >> lane) & 1ull) {
+        if (rank < kSliceCap) out[rank] = make_uint2(key[j][e], (uint32_t)(i + e));
+        ++rank;
       }
     }
-    unsigned long long bal[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bal[j] = __ballot(f[j]);
-      if (lane == 0) s4[j][wid] = __popcll(bal[j]);
-    }
-    __syncthreads();
-    int base = count;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int off = 0;
-      for (int v = 0; v < wid; ++v) off += s4[j][v];
-      const int pos = base + off + __popcll(bal[j] & ((1ull << lane) - 1ull));
-      if (f[j] && pos < kSliceCap) out[pos] = make_uint2(key[j], (uint32_t)(c0 + 256 * j + tid));
-      base += s4[j][0] + s4[j][1] + s4[j][2] + s4[j][3];
-    }
-    count = base;
-    __syncthreads();
+    base += tot[j].x + tot[j].y + tot[j].z + tot[j].w;
   }
-  if (tid == 0) *my_cnt = (uint32_t)count;
+  if (tid == 0) *my_cnt = (uint32_t)base;
 }
 
-__global__ __launch_bounds__(256) void topk_finalize_kernel(const TopkArgs a, TopkWs w, int n_slices) {
+// Ordered compaction, 512 elements per round: keep key > tau and the first need_eq keys
+// == tau in index order.  Used by the rare full-row path.
+template <class Load>
+__device__ void compact_rounds(Load load, int n, uint32_t tau, int need_eq, int32_t *out, int *tmp) {
+  const int tid = threadIdx.x;
+  int written = 0, eq_seen = 0;
+  for (int c0 = 0; c0 < n; c0 += kFinThreads) {
+    const int i = c0 + tid;
+    uint32_t key = 0;
+    if (i < n) key = load(i);
+    const bool gtf = i < n && key > tau;
+    const bool eqf = i < n && key == tau;
+    int eq_tot, sel_tot;
+    const int eq_rank = block_rank<kFinThreads>(eqf, tmp, eq_tot);
+    const bool sel = gtf || (eqf && eq_seen + eq_rank < need_eq);
+    const int pos = block_rank<kFinThreads>(sel, tmp, sel_tot);
+    if (sel) out[written + pos] = i;
+    written += sel_tot;
+    eq_seen += eq_tot;
+  }
+}
+
+__global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkArgs a, TopkWs w, int n_slices) {
+  constexpr int NT = kFinThreads;
+  constexpr int kBatch = 12;  // candidate loads in flight per thread
   __shared__ uint32_t s_key[kShortRow];
   __shared__ int32_t s_idx[kShortRow];
   __shared__ int s_base[kMaxSlices + 1];
-  __shared__ int s_hist[256], s_tmp[4], s4[4], s_sh[2], s_flag;
+  __shared__ RadixLds<NT> R;
+  __shared__ int s_flag;
   const int tid = threadIdx.x;
   const int r = blockIdx.x;
   const int len = row_len_of(a, r);
@@ -223,15 +406,27 @@ __global__ __launch_bounds__(256) void topk_finalize_kernel(const TopkArgs a, To
   const float *row = a.scores + (int64_t)r * a.ld;
 
   if (keff >= len) {  // keep everything (also len == 0)
-    for (int i = tid; i < a.k; i += 256) out[i] = i < len ? i : -1;
+    for (int i = tid; i < a.k; i += NT) out[i] = i < len ? i : -1;
     return;
   }
   int n = 0;
   bool ok;
   if (len <= kShortRow) {
-    for (int i = tid; i < len; i += 256) {
-      s_key[i] = score_key(row[i]);
-      s_idx[i] = i;
+    for (int i0 = 0; i0 < len; i0 += NT * kBatch) {
+      float x[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const int i = i0 + NT * q + tid;
+        x[q] = i < len ? row[i] : 0.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const int i = i0 + NT * q + tid;
+        if (i < len) {
+          s_key[i] = score_key(x[q]);
+          s_idx[i] = i;
+        }
+      }
     }
     n = len;
     ok = true;
@@ -241,52 +436,141 @@ __global__ __launch_bounds__(256) void topk_finalize_kernel(const TopkArgs a, To
     if (tid == 0) s_flag = 0;
     __syncthreads();
     int run = 0;
-    for (int s0 = 0; s0 < n_slices; s0 += 256) {
+    for (int s0 = 0; s0 < n_slices; s0 += NT) {
       const int s = s0 + tid;
-      int c = 0;
-      if (s < n_slices) {
-        c = (int)cnt[s];
-        if (c > kSliceCap) {
-          s_flag = 1;
-          c = kSliceCap;
-        }
-      }
+      const int c = s < n_slices ? (int)cnt[s] : 0;
+      if (c > kSliceCap) s_flag = 1;
       int total;
-      const int incl = block_scan_incl_256(c, s_tmp, total);
+      const int incl = block_scan_incl<NT>(c, R.tmp, total);
       if (s < n_slices) s_base[s] = run + incl - c;
       run += total;
     }
     if (tid == 0) s_base[n_slices] = run;
     __syncthreads();
     n = run;
-    ok = !s_flag && n >= keff && n <= kShortRow;
+    ok = n >= keff && n <= kShortRow;
     if (ok) {
       const uint2 *cand = w.cand + (int64_t)r * n_slices * kSliceCap;
-      for (int p = tid; p < n; p += 256) {
-        int lo = 0, hi = n_slices;  // slice s with s_base[s] <= p < s_base[s+1]
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (s_base[mid] <= p) lo = mid; else hi = mid;
+      int top = 1;  // largest power of two <= n_slices
+      while (2 * top <= n_slices) top <<= 1;
+      for (int p0 = 0; p0 < n; p0 += NT * kBatch) {
+        // slice sl[q] with s_base[sl] <= p < s_base[sl + 1], the batch's searches interleaved
+        int sl[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) sl[q] = 0;
+        for (int step = top; step > 0; step >>= 1) {
+#pragma unroll
+          for (int q = 0; q < kBatch; ++q) {
+            const int c = sl[q] + step;
+            if (c <= n_slices && s_base[c] <= p0 + NT * q + tid) sl[q] = c;
+          }
         }
-        const uint2 e = cand[(int64_t)lo * kSliceCap + (p - s_base[lo])];
-        s_key[p] = e.x;
-        s_idx[p] = (int32_t)e.y;
+        uint2 e[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+          const int p = p0 + NT * q + tid, lo = sl[q];
+          const bool take = p < n && s_base[lo + 1] - s_base[lo] <= kSliceCap;
+          e[q] = take ? cand[(int64_t)lo * kSliceCap + (p - s_base[lo])] : make_uint2(0u, 0xFFFFFFFFu);
+        }
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+          const int p = p0 + NT * q + tid;
+          if (p < n && e[q].y != 0xFFFFFFFFu) {
+            s_key[p] = e[q].x;
+            s_idx[p] = (int32_t)e[q].y;
+          }
+        }
+      }
+      if (s_flag) {  // slices whose list overflowed: filter them again from the scores
+        const uint32_t est = w.est[r];
+        for (int s = 0; s < n_slices; ++s) {
+          if (s_base[s + 1] - s_base[s] <= kSliceCap) continue;  // uniform
+          const int beg = s * kSlice, end = min(len, beg + kSlice);
+          int written = s_base[s];
+          for (int c0 = beg; c0 < end; c0 += NT) {
+            const int i = c0 + tid;
+            const uint32_t key = i < end ? score_key(row[i]) : 0u;
+            const bool f = i < end && key >= est;
+            int tot;
+            const int pos = written + block_rank<NT>(f, R.tmp, tot);
+            if (f && pos < s_base[s + 1]) {  // the same test as collect's: pos stays in the slice
+              s_key[pos] = key;
+              s_idx[pos] = i;
+            }
+            written += tot;
+          }
+        }
       }
     }
   }
   __syncthreads();
   if (ok) {
+    // thread t holds candidates [t per, t per + cnt) in registers; per is odd so the
+    // strided LDS reads of a wave hit distinct banks
+    const int per = ((n + NT - 1) / NT) | 1;
+    const int b0 = min(n, tid * per);
+    const int cnt = min(n, b0 + per) - b0;
+    uint32_t rk[kFinPer];
+    int32_t ri[kFinPer];
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int q = 0; q < kFinPer; ++q) {
+      rk[q] = q < cnt ? s_key[b0 + q] : 0u;
+      ri[q] = q < cnt ? s_idx[b0 + q] : 0;
+      if (q < cnt) {
+        lo = min(lo, rk[q]);
+        hi = max(hi, rk[q]);
+      }
+    }
+    block_minmax<NT>(lo, hi, R);
     int gt;
-    const uint32_t tau = radix_select([&](int i) { return s_key[i]; }, n, keff, s_hist, s_tmp, s_sh, gt);
-    compact([&](int i) { return s_key[i]; }, [&](int i) { return s_idx[i]; }, n, tau, keff - gt, out, s4);
+    const uint32_t tau = radix_select<NT>(
+        [&](auto f) {
+#pragma unroll
+          for (int q = 0; q < kFinPer; ++q)
+            if (q < cnt) f(rk[q]);
+        },
+        keff, lo, hi, 32, R, gt);
+    // ordered compaction
+    const int need_eq = keff - gt;
+    int ce = 0, cg = 0;
+#pragma unroll
+    for (int q = 0; q < kFinPer; ++q) {
+      cg += (q < cnt && rk[q] > tau) ? 1 : 0;
+      ce += (q < cnt && rk[q] == tau) ? 1 : 0;
+    }
+    int tot;
+    const int eq_excl = block_scan_incl<NT>(ce, R.tmp, tot) - ce;
+    const int cs = cg + min(ce, max(0, need_eq - eq_excl));
+    int pos = block_scan_incl<NT>(cs, R.tmp, tot) - cs;
+    int eq_seen = eq_excl;
+#pragma unroll
+    for (int q = 0; q < kFinPer; ++q) {
+      if (q < cnt) {
+        bool sel = rk[q] > tau;
+        if (rk[q] == tau) sel = eq_seen++ < need_eq;
+        if (sel) out[pos++] = ri[q];
+      }
+    }
   } else {
     // exact selection over the whole row, straight from global memory
     auto load = [&](int i) { return score_key(row[i]); };
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for (int i = tid; i < len; i += NT) {
+      const uint32_t k = load(i);
+      lo = min(lo, k);
+      hi = max(hi, k);
+    }
+    block_minmax<NT>(lo, hi, R);
     int gt;
-    const uint32_t tau = radix_select(load, len, keff, s_hist, s_tmp, s_sh, gt);
-    compact(load, [](int i) { return (int32_t)i; }, len, tau, keff - gt, out, s4);
+    const uint32_t tau = radix_select<NT>(
+        [&](auto f) {
+          for (int i = tid; i < len; i += NT) f(load(i));
+        },
+        keff, lo, hi, 32, R, gt);
+    compact_rounds(load, len, tau, keff - gt, out, R.tmp);
   }
-  for (int i = keff + tid; i < a.k; i += 256) out[i] = -1;
+  for (int i = keff + tid; i < a.k; i += NT) out[i] = -1;
 }
 
 }  // namespace
@@ -303,10 +587,14 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
   if (n_slices > kMaxSlices || a.n_rows > 65535) return hipErrorInvalidValue;
   const TopkWs w = carve(a.ws, a.n_rows, n_slices);
   if (a.ld > kShortRow) {
-    hipLaunchKernelGGL(topk_sample_kernel, dim3(a.n_rows), dim3(256), 0, s, a, w);
-    hipLaunchKernelGGL(topk_collect_kernel, dim3(n_slices, a.n_rows), dim3(256), 0, s, a, w, n_slices);
+    if (a.ld <= kOwnMaxLd && a.n_rows <= kOwnMaxRows) {
+      hipLaunchKernelGGL(topk_collect_kernel<true>, dim3(n_slices, a.n_rows), dim3(256), 0, s, a, w, n_slices);
+    } else {
+      hipLaunchKernelGGL(topk_sample_kernel, dim3(a.n_rows), dim3(256), 0, s, a, w);
+      hipLaunchKernelGGL(topk_collect_kernel<false>, dim3(n_slices, a.n_rows), dim3(256), 0, s, a, w, n_slices);
+    }
   }
-  hipLaunchKernelGGL(topk_finalize_kernel, dim3(a.n_rows), dim3(256), 0, s, a, w, n_slices);
+  hipLaunchKernelGGL(topk_finalize_kernel, dim3(a.n_rows), dim3(kFinThreads), 0, s, a, w, n_slices);
   return hipGetLastError();
 }
 

@@ -180,6 +180,36 @@ def test_topk_row_len_shorter_than_ld(d):
     assert np.array_equal(gpu_topk(d, s, lens, 2048), oracle.topk(s, lens, 2048))
 
 
+def test_topk_clustered_slice_overflow(d):
+    """Top scores packed into one 8192-score slice, so that slice's candidate list
+    overflows and is filtered again from the scores; other rows spread the top scores over
+    a few neighbouring slices, or over far-apart single tokens."""
+    rng = np.random.default_rng(13)
+    L = 131072
+    s = rng.standard_normal((3, L)).astype(np.float32)
+    s[0, 16384:16384 + 7000] = 10.0                      # ties at the threshold, one slice
+    s[0, rng.choice(np.arange(16384, 23384), 20, replace=False)] = 11.0
+    s[1, 40000:52000] += 6.0
+    s[2, ::977] += 8.0
+    log("[topk] clustered rows")
+    got = gpu_topk(d, s, [L] * 3, 2048)
+    assert np.array_equal(got, oracle.topk(s, [L] * 3, 2048))
+
+
+def test_topk_many_rows_and_long_rows(d):
+    """Batches that take the separate sample launch: many rows, and rows over 256K long."""
+    rng = np.random.default_rng(14)
+    s = (rng.standard_normal((80, 20000)) * 0.5 + 1.0).astype(np.float32)
+    lens = [int(x) for x in rng.integers(12289, 20001, 80)]
+    lens[3], lens[5] = 20000, 100
+    log("[topk] 80 rows")
+    assert np.array_equal(gpu_topk(d, s, lens, 2048), oracle.topk(s, lens, 2048))
+    L = 300_000
+    s = rng.standard_normal((2, L)).astype(np.float32)
+    log("[topk] 2 rows of 300000")
+    assert np.array_equal(gpu_topk(d, s, [L, L - 77], 2048), oracle.topk(s, [L, L - 77], 2048))
+
+
 # ------------------------------------------------------------------- attention
 
 def random_sets(rng, ctx, k, drop=0.0):
