@@ -37,6 +37,7 @@ namespace {
 
 constexpr int kScanWaves = 4;
 constexpr int kScanMaxRows = 4096;
+constexpr int kScoreBufUnits = 32;  // pages of scores a wave holds in LDS before writing them out
 
 template <int KEY_FMT>
 struct KeyRow {
@@ -68,6 +69,7 @@ template <int KEY_FMT>
 __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a) {
   using KR = KeyRow<KEY_FMT>;
   __shared__ __align__(16) uint8_t s_page[kScanWaves][KR::kPageBytes];
+  __shared__ __align__(16) float s_sc[kScanWaves][kScoreBufUnits][kPage];
   __shared__ int s_tmp[4];
   extern __shared__ int s_start[];  // [n_q + 1]: first unit of each row
 
@@ -166,6 +168,38 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
+  // Score write-back.  Scores written as the keys stream in interleave small writes with the
+  // read stream and cost HBM efficiency; instead each wave keeps up to kScoreBufUnits pages of
+  // scores in LDS and writes them out together (at the end of its range for most workloads).
+  int nb = 0, buf_lo = 0, buf_hi = 0, buf_rem = 0;
+  const bool vec_out = (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 && (a.ld & 3) == 0;
+  auto lds_sync = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  auto flush = [&]() {
+    lds_sync();
+    for (int k = 0; k < nb; k += 4) {  // four pages (16 lanes x 4 scores each) per pass
+      const int q = k + (lane >> 4), j = 4 * (lane & 15);
+      const int64_t dst = (int64_t)(((uint64_t)(uint32_t)__shfl(buf_hi, q, 64) << 32) | (uint32_t)__shfl(buf_lo, q, 64));
+      const int rq = __shfl(buf_rem, q, 64);
+      if (q < nb && j < rq) {
+        const f32x4_t s4 = *reinterpret_cast<const f32x4_t *>(&s_sc[wid][q][j]);
+        float *o = a.scores + dst + j;
+        if (vec_out && j + 4 <= rq) {
+          *reinterpret_cast<f32x4_t *>(o) = s4;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j + e < rq) o[e] = s4[e];
+        }
+      }
+    }
+    lds_sync();
+    nb = 0;
+  };
+
   int cur_row = -1, cur_len = 0;
   bf16x8_t qf[8];
   float wv[16];
@@ -187,11 +221,9 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
     const int p = uu - __builtin_amdgcn_readfirstlane(s_start[rr]);
     const int rem = cur_len - p * kPage;
     float *out = a.scores + (int64_t)rr * a.ld + (int64_t)p * kPage;
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      if (32 * c2 >= rem) break;
-      const int tt = 32 * c2 + n;
-      const uint8_t *row = slot + tt * KR::kBytes;
+    // score of token 32 c2 + n; both half-waves end up holding the same value
+    auto block = [&](int c2) {
+      const uint8_t *row = slot + (32 * c2 + n) * KR::kBytes;
       f32x16_t acc = {};
       float scale = 1.0f;
       if constexpr (KEY_FMT == 0) {
@@ -216,9 +248,23 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
       float sum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sum = fmaf(wv[i], __builtin_amdgcn_fmed3f(acc[i], lo, hi), sum);
-      const float score = sum_halves(sum) * scale;
-      if (h == 0 && tt < rem) out[tt] = score;
+      return sum_halves(sum) * scale;
+    };
+    // scores go to the wave's LDS buffer; lane nb keeps the page's destination and length
+    float *sb = s_sc[wid][nb];
+    if (rem >= kPage) {
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) sb[32 * c2 + n] = block(c2);  // both lanes of a token write the same value
+    } else {
+      for (int c2 = 0; c2 < 2 && 32 * c2 < rem; ++c2) sb[32 * c2 + n] = block(c2);
     }
+    const int64_t dst = (int64_t)rr * a.ld + (int64_t)p * kPage;
+    if (lane == nb) {
+      buf_lo = (int)(uint32_t)(uint64_t)dst;
+      buf_hi = (int)(uint32_t)((uint64_t)dst >> 32);
+      buf_rem = min(rem, kPage);
+    }
+    if (++nb == kScoreBufUnits) flush();
   };
 
   // Software pipeline: two pages in registers in flight while the third is scored from LDS.
@@ -246,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
     rl = row_of(u + 2, rl);
     r_0 = rl;
     load(b0, src_of(u + 2, ok0));
-    if (c0) compute(u, cr0);
+    if (c0) compute(u, cr0); else __builtin_amdgcn_s_waitcnt(0x0F70);
     ++u;
     park(b1);
     const bool c1 = ok1;
@@ -254,7 +300,7 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
     rl = row_of(u + 2, rl);
     r_1 = rl;
     load(b1, src_of(u + 2, ok1));
-    if (c1) compute(u, cr1);
+    if (c1) compute(u, cr1); else __builtin_amdgcn_s_waitcnt(0x0F70);
     ++u;
   }
   // the last one to three units
@@ -276,6 +322,7 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
       if (c1) compute(u, cr1);
     }
   }
+  if (nb > 0) flush();
 }
 
 }  // namespace
