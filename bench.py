@@ -104,8 +104,14 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s; pool {cache.pool.numel() / 1e9:.2f} GB")
 
-    scrub_src = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+    # cache scrub between steps: a plain elementwise pass (16-B vector loads and stores) over
+    # 512 MiB, which evicts the 256 MB MALL; it also serves as the copy of known size that
+    # scales the HBM traffic counters
+    scrub_src = torch.zeros(1 << 27, dtype=torch.float32, device=dev)
     scrub_dst = torch.empty_like(scrub_src)
+
+    def scrub():
+        torch.neg(scrub_src, out=scrub_dst)
     stages = [("resolve", step.resolve), ("score", step.score), ("topk", step.topk), ("attend", step.attend)]
 
     def one_step(ev):
@@ -115,7 +121,7 @@ def main():
         ev[len(stages)].record()
 
     for _ in range(args.warmup):
-        scrub_dst.copy_(scrub_src)
+        scrub()
         one_step([torch.cuda.Event(enable_timing=True) for _ in range(5)])
     torch.cuda.synchronize()
     assert int(step.err.item()) == 0, "device error flag set"
@@ -124,7 +130,7 @@ def main():
     torch.cuda.synchronize()
     tw = time.time()
     for _ in range(args.steps):
-        scrub_dst.copy_(scrub_src)
+        scrub()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
         one_step(ev)
         evs.append(ev)
@@ -153,7 +159,7 @@ def main():
                        "ctx_max": int(max(ctx)), "heads": wl["heads"], "topk": k,
                        "key_format": ["fp8_e4m3+fp32 scale (132 B)", "mxfp4 (68 B)"][wl["key_fmt"]],
                        "latent_format": ["fp8_e4m3 (576 B)", "nvfp4 (352 B)"][wl["lat_fmt"]], "page_tokens": 64,
-                       "pool_rows": cache.pool_rows, "scrub_between_steps_bytes": scrub_src.numel()},
+                       "pool_rows": cache.pool_rows, "scrub_between_steps_bytes": 4 * scrub_src.numel()},
             "kernels_us": {n: round(v * 1e3, 2) for n, v in per_stage.items()},
             "roofline": {"kernel": "indexer_scan (dsa_indexer_score, bf16 queries)", "bound": "hbm",
                          "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -255,5 +261,82 @@ def cpu_baseline(cache, step, wl, ctx, budget_s):
                       f"top-k {t_topk:.1f}s, attention {t_mla:.1f}s"}
 
 
+# --------------------------------------------------------------------------- profile summaries
+# These turn rocprofv3 output of `bench.py` runs into the short text files kept under profiles/.
+
+def _short_kernel(name):
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "").replace("dsa::", "")
+    return name.split("(")[0]
+
+
+def summarize_stats(argv):
+    """--summarize-stats <kernel_stats.csv> <out.txt> <title> <command>: the library's kernels."""
+    import csv
+    src, dst, title, cmd = argv
+    rows = [r for r in csv.DictReader(open(src)) if "dsa::" in r["Name"]]
+    out = [f"# rocprofv3 kernel statistics -- {title}", "#", "# command (repository root; TMPDIR=/tmp):",
+           f"#   {cmd}", "# rows: the library's kernels only (input generation and cache-scrub copies omitted)", "#",
+           f"{'kernel':44s} {'calls':>5s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    for r in rows:
+        out.append(f"{_short_kernel(r['Name']):44s} {r['Calls']:>5s} {float(r['AverageNs']) / 1e3:9.2f} "
+                   f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}")
+    open(dst, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+def summarize_pmc(argv):
+    """--summarize-pmc <fetch.csv> <write.csv> <workload> <command>: HBM traffic of the dominant kernel.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the kernel are scaled by what the same
+    counters read on the bench's cache-scrub copy, whose bytes are known (512 MiB read and
+    written), and written to profiles/traffic_<workload>.json beside a .txt summary."""
+    import csv
+    from collections import defaultdict
+    fetch_csv, write_csv, workload, cmd = argv
+    kern = "indexer_gemm_kernel" if workload == "prefill" else "indexer_scan_kernel"
+    src = ["indexer_gemm.hip" if workload == "prefill" else "indexer_scan.hip", "dsa_device.hpp"]
+    copy_bytes = 1 << 29
+
+    def per_dispatch(path, counter):
+        val, name = defaultdict(float), {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            val[r["Dispatch_Id"]] += float(r["Counter_Value"])
+            name[r["Dispatch_Id"]] = r["Kernel_Name"]
+        mine = [v for k, v in val.items() if kern in name[k]]
+        # the scrub pass (neg over 512 MiB): the largest dispatch outside the library
+        copies = [v for k, v in val.items() if "dsa::" not in name[k] and "neg" in name[k].lower()]
+        if not mine or not copies:
+            raise SystemExit(f"{path}: no {kern} or copy dispatch with {counter}")
+        return sum(mine) / len(mine), max(copies), len(mine)
+
+    f_k, f_c, nf = per_dispatch(fetch_csv, "FETCH_SIZE")
+    w_k, w_c, nw = per_dispatch(write_csv, "WRITE_SIZE")
+    ff, fw = (copy_bytes / 1024) / f_c, (copy_bytes / 1024) / w_c
+    traffic = (f_k * ff + w_k * fw) * 1024
+    rec = {"kernel": kern, "workload": workload, "source_sha": source_sha(*src),
+           "fetch_kib_per_dispatch": round(f_k, 1), "write_kib_per_dispatch": round(w_k, 1), "dispatches": [nf, nw],
+           "copy_fetch_kib": round(f_c, 1), "copy_write_kib": round(w_c, 1), "copy_bytes_each_way": copy_bytes,
+           "scale_fetch": round(ff, 4), "scale_write": round(fw, 4), "hbm_bytes_per_launch": int(traffic),
+           "command": cmd}
+    base = os.path.join(ROOT, "profiles", f"traffic_{workload}")
+    json.dump(rec, open(base + ".json", "w"), indent=1)
+    lines = [f"# HBM traffic of {kern} on workload '{workload}' (rocprofv3 --pmc)", "#",
+             "# commands (repository root; TMPDIR=/tmp), one counter per run:", f"#   {cmd}", "#",
+             f"FETCH_SIZE per dispatch        {f_k:14.1f} KiB  (mean of {nf} dispatches)",
+             f"WRITE_SIZE per dispatch        {w_k:14.1f} KiB  (mean of {nw} dispatches)",
+             f"scrub copy (512 MiB each way)  fetch {f_c:.1f} KiB, write {w_c:.1f} KiB",
+             f"scale factors                  fetch {ff:.4f}, write {fw:.4f}",
+             f"HBM bytes per launch           {traffic / 1e6:14.2f} MB", f"source sha                     {rec['source_sha']}"]
+    open(base + ".txt", "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
-    main()
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-stats":
+        summarize_stats(sys.argv[2:])
+    elif len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
+        summarize_pmc(sys.argv[2:])
+    else:
+        main()
