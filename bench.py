@@ -7,10 +7,13 @@ rows, 12 query heads (one TP8 GPU's share).  Inputs are seeded, synthetic and
 resident in HBM before timing starts.
 
 Timing: W untimed warmup steps, then K timed steps between device
-synchronisations.  A 1 GiB copy runs before every step (outside the per-step
-HIP events) so that no step finds the previous step's latents or scores in the
-256 MB Infinity Cache; ms_per_step is the mean of the per-step event times,
-wall_ms_per_step the bracketed wall time including the scrubs.
+synchronisations.  A 512 MiB elementwise pass (16-B loads and stores) runs before
+every step, outside its HIP events, so that no step finds the previous step's
+latents or scores in the 256 MB Infinity Cache.  ms_per_step is the mean of one
+event pair around the whole step; wall_ms_per_step is the bracketed wall time
+including the scrubs.  stage_us then times each stage on its own (scrub, earlier
+stages untimed, one event pair around the stage); the roofline uses the indexer
+scan's figure from there.
 
 Metric: algorithmic bytes of the layer-step (sum_b L_b*132 + min(2048, L_b)*576)
 divided by the step time, in GB/s, against the 8 TB/s HBM peak.  The roofline
@@ -114,30 +117,50 @@ def main():
         torch.neg(scrub_src, out=scrub_dst)
     stages = [("resolve", step.resolve), ("score", step.score), ("topk", step.topk), ("attend", step.attend)]
 
-    def one_step(ev):
-        for i, (_, fn) in enumerate(stages):
-            ev[i].record()
+    def run_step():
+        for _, fn in stages:
             fn()
-        ev[len(stages)].record()
 
     for _ in range(args.warmup):
         scrub()
-        one_step([torch.cuda.Event(enable_timing=True) for _ in range(5)])
+        run_step()
     torch.cuda.synchronize()
     assert int(step.err.item()) == 0, "device error flag set"
 
+    # (1) the step: one event pair around the four stages (events between stages would add
+    # their own gaps to the step)
     evs = []
     torch.cuda.synchronize()
     tw = time.time()
     for _ in range(args.steps):
         scrub()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-        one_step(ev)
-        evs.append(ev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run_step()
+        b.record()
+        evs.append((a, b))
     torch.cuda.synchronize()
     wall = time.time() - tw
-    per_stage = {n: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in evs])) for i, (n, _) in enumerate(stages)}
-    step_ms = float(np.mean([ev[0].elapsed_time(ev[4]) for ev in evs]))
+    step_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    # (2) each stage on its own, for attribution and the roofline: after a scrub, the stages
+    # before it run untimed (so its inputs sit where the step leaves them), then an event pair
+    # brackets just this stage
+    per_stage = {}
+    for i, (name, fn) in enumerate(stages):
+        evs_i = []
+        for _ in range(args.steps):
+            scrub()
+            for _, g in stages[:i]:
+                g()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs_i.append((a, b))
+        torch.cuda.synchronize()
+        per_stage[name] = float(np.mean([a.elapsed_time(b) for a, b in evs_i]))
+    assert int(step.err.item()) == 0, "device error flag set"
 
     out = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "scaling": "weak", "vs_baseline": None,
            "data": "synthetic (seeded; N(0,1) keys/latents/queries quantised to the cache formats)"}
@@ -160,7 +183,7 @@ def main():
                        "key_format": ["fp8_e4m3+fp32 scale (132 B)", "mxfp4 (68 B)"][wl["key_fmt"]],
                        "latent_format": ["fp8_e4m3 (576 B)", "nvfp4 (352 B)"][wl["lat_fmt"]], "page_tokens": 64,
                        "pool_rows": cache.pool_rows, "scrub_between_steps_bytes": 4 * scrub_src.numel()},
-            "kernels_us": {n: round(v * 1e3, 2) for n, v in per_stage.items()},
+            "stage_us": {n: round(v * 1e3, 2) for n, v in per_stage.items()},
             "roofline": {"kernel": "indexer_scan (dsa_indexer_score, bf16 queries)", "bound": "hbm",
                          "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_launch": key_bytes,
@@ -181,7 +204,7 @@ def main():
             "wall_ms_per_step": round(wall / args.steps * 1e3, 3), "dtype": "bf16",
             "config": {"workload": wl["name"], "rows": pq.n_q, "prefix": wl["prefix"], "heads": wl["heads"],
                        "topk": k, "scored_pairs": pairs, "query_format": "fp8_e4m3 + fp32 scale per (row, head)"},
-            "kernels_us": {n: round(v * 1e3, 2) for n, v in per_stage.items()},
+            "stage_us": {n: round(v * 1e3, 2) for n, v in per_stage.items()},
             "roofline": {"kernel": "indexer_gemm (dsa_indexer_score, fp8 queries, bf16 MFMA)", "bound": "mfma",
                          "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / BF16_PEAK_TFLOPS, 4), "frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),

@@ -107,21 +107,54 @@ __device__ __forceinline__ void flag_error(int32_t *err, uint32_t bits) {
   if (err) atomicOr(err, (int32_t)bits);
 }
 
-// Block-wide inclusive scan of one int per thread (blockDim.x == 256).  `tmp` holds >= 4 ints.
-__device__ __forceinline__ int block_scan_incl_256(int v, int *tmp, int &total) {
+// Wave-wide inclusive prefix sum (wave64): Hillis-Steele steps inside each 16-lane row with
+// DPP row shifts, then the row totals carried across rows with DPP row broadcasts.  Lanes
+// whose DPP source is out of range (or whose row is masked off) receive 0 through `old`.
+__device__ __forceinline__ int wave_scan_incl(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// Wave-wide max / min of uint32 (the result in every lane), same DPP pattern.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  int v = (int)x;
+  v = (int)max((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false));
+  v = (int)max((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false));
+  v = (int)max((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false));
+  v = (int)max((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false));
+  v = (int)max((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false));
+  v = (int)max((uint32_t)v, (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) { return ~wave_max_u32(~x); }
+
+// Block-wide inclusive scan of one int per thread (blockDim.x == NT).  `tmp` holds NT / 64 ints.
+template <int NT>
+__device__ __forceinline__ int block_scan_incl(int v, int *tmp, int &total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int t = __shfl_up(v, off, 64);
-    if (lane >= off) v += t;
-  }
+  v = wave_scan_incl(v);
   if (lane == 63) tmp[wid] = v;
   __syncthreads();
   int base = 0;
-  total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
-  for (int w = 0; w < wid; ++w) base += tmp[w];
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int t = tmp[w];
+    base += w < wid ? t : 0;
+    total += t;
+  }
   __syncthreads();
   return v + base;
+}
+
+__device__ __forceinline__ int block_scan_incl_256(int v, int *tmp, int &total) {
+  return block_scan_incl<256>(v, tmp, total);
 }
 
 }  // namespace dsa

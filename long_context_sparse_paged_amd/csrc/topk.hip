@@ -95,40 +95,13 @@ __device__ __forceinline__ int sample_rank(int keff, int len, int S) {
   return (int)ceilf(1.25f * x + 6.0f * sqrtf(x) + 8.0f);
 }
 
-// Block-wide inclusive scan of one int per thread; tmp holds NT / 64 ints.
-template <int NT>
-__device__ __forceinline__ int block_scan_incl(int v, int *tmp, int &total) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(v, off, 64);
-    if (lane >= off) v += t;
-  }
-  if (lane == 63) tmp[wid] = v;
-  __syncthreads();
-  int base = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int t = tmp[w];
-    base += w < wid ? t : 0;
-    total += t;
-  }
-  __syncthreads();
-  return v + base;
-}
-
 // Block-wide (min, max) of one key per thread.
 template <int NT>
 __device__ __forceinline__ void block_minmax(uint32_t &lo, uint32_t &hi, RadixLds<NT> &R) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, 64));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, 64));
-  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
   if (lane == 0) {
     R.mm[wid] = lo;
     R.mm[NW + wid] = hi;
@@ -393,6 +366,7 @@ __device__ void compact_rounds(Load load, int n, uint32_t tau, int need_eq, int3
 __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkArgs a, TopkWs w, int n_slices) {
   constexpr int NT = kFinThreads;
   constexpr int kBatch = 12;  // candidate loads in flight per thread
+  constexpr int kSpec = 16;   // speculative candidate loads per thread
   __shared__ uint32_t s_key[kShortRow];
   __shared__ int32_t s_idx[kShortRow];
   __shared__ int s_base[kMaxSlices + 1];
@@ -431,15 +405,29 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
     n = len;
     ok = true;
   } else {
-    // exclusive prefix of the slices' candidate counts
+    // One round trip for the counts and, speculatively, the first B entries of every slice's
+    // candidate list (B: a power of two, B x n_slices <= NT x kSpec); entries past a slice's
+    // count are read but not used (the lists are kSliceCap long, so every read is in bounds).
     const uint32_t *cnt = w.cnt + (int64_t)r * n_slices;
+    const uint2 *cand = w.cand + (int64_t)r * n_slices * kSliceCap;
+    int lgB = 4;
+    while ((2 << lgB) * n_slices <= NT * kSpec && (2 << lgB) <= kSliceCap) ++lgB;
+    uint2 e[kSpec];
+#pragma unroll
+    for (int q = 0; q < kSpec; ++q) {
+      const int x = tid + NT * q, s = x >> lgB, j = x & ((1 << lgB) - 1);
+      e[q] = s < n_slices ? cand[(int64_t)s * kSliceCap + j] : make_uint2(0u, 0u);
+    }
     if (tid == 0) s_flag = 0;
     __syncthreads();
+    // exclusive prefix of the slices' candidate counts; s_flag bit 0: a list overflowed,
+    // bit 1: a list is longer than B
     int run = 0;
     for (int s0 = 0; s0 < n_slices; s0 += NT) {
       const int s = s0 + tid;
       const int c = s < n_slices ? (int)cnt[s] : 0;
-      if (c > kSliceCap) s_flag = 1;
+      if (c > kSliceCap) atomicOr(&s_flag, 1);
+      else if (c > (1 << lgB)) atomicOr(&s_flag, 2);
       int total;
       const int incl = block_scan_incl<NT>(c, R.tmp, total);
       if (s < n_slices) s_base[s] = run + incl - c;
@@ -450,38 +438,50 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
     n = run;
     ok = n >= keff && n <= kShortRow;
     if (ok) {
-      const uint2 *cand = w.cand + (int64_t)r * n_slices * kSliceCap;
-      int top = 1;  // largest power of two <= n_slices
-      while (2 * top <= n_slices) top <<= 1;
-      for (int p0 = 0; p0 < n; p0 += NT * kBatch) {
-        // slice sl[q] with s_base[sl] <= p < s_base[sl + 1], the batch's searches interleaved
-        int sl[kBatch];
 #pragma unroll
-        for (int q = 0; q < kBatch; ++q) sl[q] = 0;
-        for (int step = top; step > 0; step >>= 1) {
-#pragma unroll
-          for (int q = 0; q < kBatch; ++q) {
-            const int c = sl[q] + step;
-            if (c <= n_slices && s_base[c] <= p0 + NT * q + tid) sl[q] = c;
-          }
-        }
-        uint2 e[kBatch];
-#pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-          const int p = p0 + NT * q + tid, lo = sl[q];
-          const bool take = p < n && s_base[lo + 1] - s_base[lo] <= kSliceCap;
-          e[q] = take ? cand[(int64_t)lo * kSliceCap + (p - s_base[lo])] : make_uint2(0u, 0xFFFFFFFFu);
-        }
-#pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-          const int p = p0 + NT * q + tid;
-          if (p < n && e[q].y != 0xFFFFFFFFu) {
-            s_key[p] = e[q].x;
-            s_idx[p] = (int32_t)e[q].y;
+      for (int q = 0; q < kSpec; ++q) {
+        const int x = tid + NT * q, s = x >> lgB, j = x & ((1 << lgB) - 1);
+        if (s < n_slices) {
+          const int c = s_base[s + 1] - s_base[s];
+          if (c <= kSliceCap && j < c) {
+            s_key[s_base[s] + j] = e[q].x;
+            s_idx[s_base[s] + j] = (int32_t)e[q].y;
           }
         }
       }
-      if (s_flag) {  // slices whose list overflowed: filter them again from the scores
+      if (s_flag & 2) {  // lists longer than B: their remaining entries
+        int top = 1;     // largest power of two <= n_slices
+        while (2 * top <= n_slices) top <<= 1;
+        for (int p0 = 0; p0 < n; p0 += NT * kBatch) {
+          // slice sl[q] with s_base[sl] <= p < s_base[sl + 1], the batch's searches interleaved
+          int sl[kBatch];
+#pragma unroll
+          for (int q = 0; q < kBatch; ++q) sl[q] = 0;
+          for (int step = top; step > 0; step >>= 1) {
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+              const int c = sl[q] + step;
+              if (c <= n_slices && s_base[c] <= p0 + NT * q + tid) sl[q] = c;
+            }
+          }
+          uint2 f[kBatch];
+#pragma unroll
+          for (int q = 0; q < kBatch; ++q) {
+            const int p = p0 + NT * q + tid, lo = sl[q], j = p - s_base[lo];
+            const bool take = p < n && s_base[lo + 1] - s_base[lo] <= kSliceCap && j >= (1 << lgB);
+            f[q] = take ? cand[(int64_t)lo * kSliceCap + j] : make_uint2(0u, 0xFFFFFFFFu);
+          }
+#pragma unroll
+          for (int q = 0; q < kBatch; ++q) {
+            const int p = p0 + NT * q + tid;
+            if (p < n && f[q].y != 0xFFFFFFFFu) {
+              s_key[p] = f[q].x;
+              s_idx[p] = (int32_t)f[q].y;
+            }
+          }
+        }
+      }
+      if (s_flag & 1) {  // slices whose list overflowed: filter them again from the scores
         const uint32_t est = w.est[r];
         for (int s = 0; s < n_slices; ++s) {
           if (s_base[s + 1] - s_base[s] <= kSliceCap) continue;  // uniform
