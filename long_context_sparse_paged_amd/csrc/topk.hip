@@ -45,8 +45,8 @@ constexpr int kOwnMaxLd = 262144;     // ... when rows are at most this long
 constexpr int kOwnMaxRows = 64;       // ... and there are at most this many
 constexpr int kMaxSamples = 16384;    // samples of the sample launch
 constexpr int kMaxSlices = 1024;
-constexpr int kRep = 16;              // histogram copies
-constexpr int kHistLd = 257;          // odd stride: the copies of one bin sit in different banks
+constexpr int kRep = 16;              // histogram copies (one per lane mod 16)
+constexpr int kBinLd = 20;            // ints per bin: 16 copies + 4 pad (80-B rows, 16-B aligned)
 constexpr int kEstPasses = 2;         // 16 leading bits of the threshold are enough
 constexpr int kFinThreads = 512;
 constexpr int kFinPer = kShortRow / kFinThreads + 1;  // 25: candidates a finalize thread holds
@@ -72,9 +72,11 @@ __host__ __device__ inline TopkWs carve(void *ws, int32_t n_rows, int32_t n_slic
 
 template <int NT>
 struct RadixLds {
-  int hist[2][kRep * kHistLd];  // double buffered: a pass clears the next one's
+  __align__(16) int hist[256 * kBinLd];  // [bin][copy]; never cleared (see radix_select)
   int tmp[NT / 64];
-  int sh[2];
+  int tmp2[2][NT / 64];
+  int sh[3];
+  int list_n;
   uint32_t mm[2 * (NT / 64)];
 };
 
@@ -115,52 +117,88 @@ __device__ __forceinline__ void block_minmax(uint32_t &lo, uint32_t &hi, RadixLd
   __syncthreads();
 }
 
+// Sum of the kRep copies of one histogram bin (one 80-B row), modulo 2^32.
+__device__ __forceinline__ uint32_t bin_total(const int *h, int bin) {
+  const uint4 *row = reinterpret_cast<const uint4 *>(h + bin * kBinLd);
+  uint32_t c = 0;
+#pragma unroll
+  for (int k = 0; k < kRep / 4; ++k) {
+    const uint4 x = row[k];
+    c += (x.x + x.y) + (x.z + x.w);
+  }
+  return c;
+}
+
 // Radix select over keys in [kmin, kmax]: `visit(f)` calls f(key) for each of this
 // thread's keys.  Returns the m-th largest key (1-based) and in `gt` the number of keys
 // strictly larger, using 8-bit digits of key - kmin from the top bit of kmax - kmin down.
 // With max_passes below the number of digits the result is the lower edge of the bin that
 // holds the m-th largest key: at least m keys are >= it.
+// `list` (optional, LDS, list_cap keys): after the first pass the keys of the chosen bin
+// are copied there, and later passes read only those.
+// The histogram is never cleared: thread t reads bin 255 - t before and after each pass
+// and takes the difference (wrap-around int arithmetic), which is cheaper than clearing
+// 20 KB of LDS per pass.
 template <int NT, class Visit>
 __device__ uint32_t radix_select(Visit visit, int m, uint32_t kmin, uint32_t kmax, int max_passes, RadixLds<NT> &R,
-                                 int &gt) {
-  const int tid = threadIdx.x;
+                                 int &gt, uint32_t *list = nullptr, int list_cap = 0) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   gt = 0;
   const uint32_t range = kmax - kmin;
   if (range == 0) return kmin;
-  for (int i = tid; i < 2 * kRep * kHistLd; i += NT) (&R.hist[0][0])[i] = 0;
-  __syncthreads();
+  int *my = R.hist + (tid & (kRep - 1));
+  uint32_t before = tid < 256 ? bin_total(R.hist, 255 - tid) : 0u;
+  __syncthreads();  // every snapshot is taken before the first increment
   uint32_t prefix = 0;
-  int rem = m;
+  int rem = m, nl = -1;  // nl >= 0: later passes read list[0, nl)
   int hi = 31 - __clz((int)range);
   for (int p = 0; hi >= 0 && p < max_passes; ++p, hi -= 8) {
     const int lo = hi >= 7 ? hi - 7 : 0;
     const uint32_t above = ~((2u << hi) - 1u);  // bits already decided
-    int *h = R.hist[p & 1];
-    int *my = h + (tid & (kRep - 1)) * kHistLd;
-    visit([&](uint32_t key) {
+    auto count = [&](uint32_t key) {
       const uint32_t u = key - kmin;
-      if ((u & above) == prefix) atomicAdd(&my[(u >> lo) & 255u], 1);
-    });
+      if ((u & above) == prefix) atomicAdd(&my[((u >> lo) & 255u) * kBinLd], 1);
+    };
+    if (nl >= 0) {
+      for (int i = tid; i < nl; i += NT) count(list[i]);
+    } else {
+      visit(count);
+    }
     __syncthreads();
-    // thread t < 256 sums bin 255 - t: an inclusive prefix over threads is a suffix over bins
+    // thread t < 256 owns bin 255 - t: an inclusive prefix over threads is a suffix over bins
     int c = 0;
     if (tid < 256) {
-#pragma unroll
-      for (int k = 0; k < kRep; ++k) c += h[k * kHistLd + 255 - tid];
+      const uint32_t after = bin_total(R.hist, 255 - tid);
+      c = (int)(after - before);
+      before = after;
     }
-    int *o = R.hist[(p + 1) & 1];  // last read in the previous pass
-    for (int i = tid; i < kRep * kHistLd; i += NT) o[i] = 0;
-    int total;
-    const int incl = block_scan_incl<NT>(c, R.tmp, total);
-    const int excl = incl - c;
+    int *tmp = R.tmp2[p & 1];  // alternating: no barrier needed before its reuse
+    const int incl0 = wave_scan_incl(c);
+    if (lane == 63) tmp[wid] = incl0;
+    __syncthreads();
+    int base = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) base += w < wid ? tmp[w] : 0;
+    const int incl = incl0 + base, excl = incl - c;
     if (tid < 256 && excl < rem && incl >= rem) {
       R.sh[0] = 255 - tid;
       R.sh[1] = excl;
+      R.sh[2] = c;
+      R.list_n = 0;
     }
     __syncthreads();
     prefix |= (uint32_t)R.sh[0] << lo;  // the digit's bits above hi repeat the prefix
     rem -= R.sh[1];
     gt += R.sh[1];
+    if (list != nullptr && nl < 0 && lo > 0 && p + 1 < max_passes && R.sh[2] <= list_cap) {
+      const uint32_t mask = ~((1u << lo) - 1u);
+      visit([&](uint32_t key) {
+        if (((key - kmin) & mask) == prefix) list[atomicAdd(&R.list_n, 1)] = key;
+      });
+      __syncthreads();
+      nl = R.sh[2];
+    }
   }
   return kmin + prefix;
 }
@@ -276,16 +314,36 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(const TopkArgs a, Top
       sk[4 * u + 2] = score_key(t.z);
       sk[4 * u + 3] = score_key(t.w);
     }
-    uint32_t lo = sk[0], hi = sk[0];
-#pragma unroll
-    for (int q = 1; q < 4 * kQ; ++q) {
-      lo = min(lo, sk[q]);
-      hi = max(hi, sk[q]);
-    }
-    block_minmax<256>(lo, hi, R);
     const int m = sample_rank(keff, len, kOwnSamples);
     est = 0u;
-    if (m < kOwnSamples) {
+    if (m <= 128) {
+      // the sample's m-th largest key is >= the m-th largest of the threads' top-2 keys
+      // (a subset), so the top-2 keys give a valid, slightly lower threshold from 8x
+      // fewer keys
+      uint32_t t1 = 0u, t2 = 0u;
+#pragma unroll
+      for (int q = 0; q < 4 * kQ; ++q) {
+        const uint32_t x = sk[q];
+        t2 = x > t1 ? t1 : max(t2, x);
+        t1 = max(t1, x);
+      }
+      uint32_t lo = t2, hi = t1;
+      block_minmax<256>(lo, hi, R);
+      int gt;
+      est = radix_select<256>(
+          [&](auto f) {
+            f(t1);
+            f(t2);
+          },
+          m, lo, hi, kEstPasses, R, gt);
+    } else if (m < kOwnSamples) {
+      uint32_t lo = sk[0], hi = sk[0];
+#pragma unroll
+      for (int q = 1; q < 4 * kQ; ++q) {
+        lo = min(lo, sk[q]);
+        hi = max(hi, sk[q]);
+      }
+      block_minmax<256>(lo, hi, R);
       int gt;
       est = radix_select<256>(
           [&](auto f) {
@@ -360,6 +418,60 @@ __device__ void compact_rounds(Load load, int n, uint32_t tau, int need_eq, int3
     if (sel) out[written + pos] = i;
     written += sel_tot;
     eq_seen += eq_tot;
+  }
+}
+
+// Exact selection and ordered output of the n candidates in s_key / s_idx (index order):
+// thread t holds candidates [t per, t per + cnt) in registers (cnt <= per <= PER).  s_key
+// doubles as the radix select's list once the registers are loaded.
+template <int PER>
+__device__ void select_write(uint32_t *s_key, const int32_t *s_idx, int n, int per, int keff,
+                             RadixLds<kFinThreads> &R, int32_t *out) {
+  constexpr int NT = kFinThreads;
+  const int tid = threadIdx.x;
+  const int b0 = min(n, tid * per);
+  const int cnt = min(n, b0 + per) - b0;
+  uint32_t rk[PER];
+  int32_t ri[PER];
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    rk[q] = q < cnt ? s_key[b0 + q] : 0u;
+    ri[q] = q < cnt ? s_idx[b0 + q] : 0;
+    if (q < cnt) {
+      lo = min(lo, rk[q]);
+      hi = max(hi, rk[q]);
+    }
+  }
+  block_minmax<NT>(lo, hi, R);  // its barriers also end every read of s_key above
+  int gt;
+  const uint32_t tau = radix_select<NT>(
+      [&](auto f) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+          if (q < cnt) f(rk[q]);
+      },
+      keff, lo, hi, 32, R, gt, s_key, kShortRow);
+  // ordered compaction: keep key > tau, and the first need_eq keys == tau in index order
+  const int need_eq = keff - gt;
+  int ce = 0, cg = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    cg += (q < cnt && rk[q] > tau) ? 1 : 0;
+    ce += (q < cnt && rk[q] == tau) ? 1 : 0;
+  }
+  int tot;
+  const int eq_excl = block_scan_incl<NT>(ce, R.tmp, tot) - ce;
+  const int cs = cg + min(ce, max(0, need_eq - eq_excl));
+  int pos = block_scan_incl<NT>(cs, R.tmp, tot) - cs;
+  int eq_seen = eq_excl;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    if (q < cnt) {
+      bool sel = rk[q] > tau;
+      if (rk[q] == tau) sel = eq_seen++ < need_eq;
+      if (sel) out[pos++] = ri[q];
+    }
   }
 }
 
@@ -505,53 +617,15 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
   }
   __syncthreads();
   if (ok) {
-    // thread t holds candidates [t per, t per + cnt) in registers; per is odd so the
-    // strided LDS reads of a wave hit distinct banks
+    // thread t takes candidates [t per, t per + cnt) into registers (per is odd, so the
+    // strided LDS reads of a wave hit distinct banks); the loops are unrolled for a bound
+    // on per picked from a few sizes
     const int per = ((n + NT - 1) / NT) | 1;
-    const int b0 = min(n, tid * per);
-    const int cnt = min(n, b0 + per) - b0;
-    uint32_t rk[kFinPer];
-    int32_t ri[kFinPer];
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-#pragma unroll
-    for (int q = 0; q < kFinPer; ++q) {
-      rk[q] = q < cnt ? s_key[b0 + q] : 0u;
-      ri[q] = q < cnt ? s_idx[b0 + q] : 0;
-      if (q < cnt) {
-        lo = min(lo, rk[q]);
-        hi = max(hi, rk[q]);
-      }
-    }
-    block_minmax<NT>(lo, hi, R);
-    int gt;
-    const uint32_t tau = radix_select<NT>(
-        [&](auto f) {
-#pragma unroll
-          for (int q = 0; q < kFinPer; ++q)
-            if (q < cnt) f(rk[q]);
-        },
-        keff, lo, hi, 32, R, gt);
-    // ordered compaction
-    const int need_eq = keff - gt;
-    int ce = 0, cg = 0;
-#pragma unroll
-    for (int q = 0; q < kFinPer; ++q) {
-      cg += (q < cnt && rk[q] > tau) ? 1 : 0;
-      ce += (q < cnt && rk[q] == tau) ? 1 : 0;
-    }
-    int tot;
-    const int eq_excl = block_scan_incl<NT>(ce, R.tmp, tot) - ce;
-    const int cs = cg + min(ce, max(0, need_eq - eq_excl));
-    int pos = block_scan_incl<NT>(cs, R.tmp, tot) - cs;
-    int eq_seen = eq_excl;
-#pragma unroll
-    for (int q = 0; q < kFinPer; ++q) {
-      if (q < cnt) {
-        bool sel = rk[q] > tau;
-        if (rk[q] == tau) sel = eq_seen++ < need_eq;
-        if (sel) out[pos++] = ri[q];
-      }
-    }
+    if (per <= 5) select_write<5>(s_key, s_idx, n, per, keff, R, out);
+    else if (per <= 9) select_write<9>(s_key, s_idx, n, per, keff, R, out);
+    else if (per <= 13) select_write<13>(s_key, s_idx, n, per, keff, R, out);
+    else if (per <= 17) select_write<17>(s_key, s_idx, n, per, keff, R, out);
+    else select_write<kFinPer>(s_key, s_idx, n, per, keff, R, out);
   } else {
     // exact selection over the whole row, straight from global memory
     auto load = [&](int i) { return score_key(row[i]); };
@@ -567,7 +641,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
         [&](auto f) {
           for (int i = tid; i < len; i += NT) f(load(i));
         },
-        keff, lo, hi, 32, R, gt);
+        keff, lo, hi, 32, R, gt, s_key, kShortRow);
     compact_rounds(load, len, tau, keff - gt, out, R.tmp);
   }
   for (int i = keff + tid; i < a.k; i += NT) out[i] = -1;
