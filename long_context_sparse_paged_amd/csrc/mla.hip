@@ -283,6 +283,227 @@ __global__ __launch_bounds__(256, 2) void mla_kernel(const MlaArgs a, const int 
   }
 }
 
+// Wide variant for many heads (prefill: 96): one workgroup per (query row, token split)
+// covers every head of the row, so each 64-token subtile is gathered and decoded once for
+// all heads instead of once per 16-head tile.  Wave w owns heads 16 w .. 16 w + 15 (waves
+// past the last head tile only help gather): QK over all 64 tokens of the subtile, an
+// in-wave online softmax, and P.V into all 512 value dims.  FP8 queries stay as e4m3 codes
+// in registers and are converted to bf16 per MFMA.
+constexpr int kWideThreads = 512;                  // 8 waves: up to 8 head tiles (128 heads)
+constexpr int kWideMaxTiles = kWideThreads / 64;
+
+template <int LAT_FMT>
+__global__ __launch_bounds__(kWideThreads) void mla_wide_kernel(const MlaArgs a, const int nsplit, const int tps,
+                                                                MlaWs w) {
+  constexpr int LB = LAT_FMT == 0 ? 576 : 352;
+  constexpr int64_t LPB = (int64_t)kPage * LB;
+  constexpr int kChunks = Gather<LAT_FMT>::kChunks;
+  constexpr int kItems = kSub * kChunks;
+  constexpr int kPer = (kItems + kWideThreads - 1) / kWideThreads;  // 5 / 3
+  __shared__ __align__(16) uint16_t s_kt[kSub * kKtLd];
+  __shared__ __align__(16) uint16_t s_p[kWideMaxTiles][4][64 * 4];
+  extern __shared__ int64_t s_off[];  // [tps]
+
+  const int sp = blockIdx.y, r = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int hl = lane & 15, g = lane >> 4;
+  const int H = a.n_heads;
+  const bool computes = wid * 16 < H;  // wave-uniform
+  const int h = wid * 16 + hl;
+  const bool hvalid = h < H;
+  const int b = a.q_req ? a.q_req[r] : r;
+  const bool rvalid = b >= 0 && b < a.n_req;
+  if (!rvalid && tid == 0 && sp == 0) flag_error(a.err, DSA_DEVERR_REQUEST);
+  const int ctx = rvalid ? a.ctx_len[b] : 0;
+  const int t_beg = sp * tps;
+  const int n_tok = max(0, min(a.k, t_beg + tps) - t_beg);
+
+  for (int j = tid; j < n_tok; j += kWideThreads) {
+    int64_t off = -1;
+    if (rvalid) {
+      const int t = a.idx[(int64_t)r * a.idx_ld + t_beg + j];
+      if (t >= 0) {
+        const int pg = t >> 6;
+        if (t >= ctx || pg >= a.off_ld) {
+          flag_error(a.err, DSA_DEVERR_INDEX);
+        } else {
+          const int64_t po = a.lat_off[(int64_t)b * a.off_ld + pg];
+          if (po < 0 || po + LPB > a.pool_bytes || (po & 15))
+            flag_error(a.err, DSA_DEVERR_PAGE_OFFSET);
+          else
+            off = po + (int64_t)(t & 63) * LB;
+        }
+      }
+    }
+    s_off[j] = off;
+  }
+
+  // e4m3 query codes: lane (head hl, group g) holds dims 32 s + 8 g .. + 8 of head h
+  u32x2_t qc[18];
+  float qscale = 0.0f;
+  if (hvalid) {
+    const uint8_t *qr = static_cast<const uint8_t *>(a.q) + ((int64_t)r * H + h) * kLatDim;
+#pragma unroll
+    for (int s = 0; s < 18; ++s) qc[s] = *reinterpret_cast<const u32x2_t *>(qr + 32 * s + 8 * g);
+    qscale = a.q_scale[(int64_t)r * H + h];
+  } else {
+#pragma unroll
+    for (int s = 0; s < 18; ++s) qc[s] = u32x2_t{};
+  }
+  const float c2 = a.sm_scale * a.kv_scale * qscale * kLog2e;
+  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  u32x4_t raw[kPer];
+  uint32_t bsc[kPer];
+  auto issue = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int item = tid + kWideThreads * i;
+      const int tok = item / kChunks, c = item - tok * kChunks;
+      const int j = t0 + tok;
+      const int64_t off = (item < kItems && j < n_tok) ? s_off[j] : -1;
+      const uint8_t *base = a.pool + (off < 0 ? 0 : off);  // every lane loads: fixed wait counts
+      const int cc = c < kChunks ? c : 0;
+      if constexpr (LAT_FMT == 0) {
+        raw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(base + 16 * cc));
+      } else {
+        const int boff = cc < 16 ? 16 * cc : 288 + 16 * (cc - 16);
+        raw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(base + boff));
+        bsc[i] = *reinterpret_cast<const uint16_t *>(base + 256 + 2 * (cc < 16 ? cc : 0));
+      }
+    }
+  };
+  auto park = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int item = tid + kWideThreads * i;
+      if (item >= kItems) continue;
+      const int tok = item / kChunks, c = item - tok * kChunks;
+      const int j = t0 + tok;
+      const bool ok = j < n_tok && s_off[j] >= 0;
+      uint16_t *dst = s_kt + tok * kKtLd;
+      if constexpr (LAT_FMT == 0) {
+        bf16x8_t lo = e4m3x8_bf16(raw[i][0], raw[i][1]), hi = e4m3x8_bf16(raw[i][2], raw[i][3]);
+        if (!ok) lo = hi = bf16x8_t{};
+        *reinterpret_cast<bf16x8_t *>(dst + 16 * c) = lo;
+        *reinterpret_cast<bf16x8_t *>(dst + 16 * c + 8) = hi;
+      } else if (c < 16) {
+        const float s0 = e4m3_f32(bsc[i] & 0xFFu), s1 = e4m3_f32((bsc[i] >> 8) & 0xFFu);
+        bf16x8_t v0 = nvfp4x8_bf16(raw[i][0], s0), v1 = nvfp4x8_bf16(raw[i][1], s0);
+        bf16x8_t v2 = nvfp4x8_bf16(raw[i][2], s1), v3 = nvfp4x8_bf16(raw[i][3], s1);
+        if (!ok) v0 = v1 = v2 = v3 = bf16x8_t{};
+        *reinterpret_cast<bf16x8_t *>(dst + 32 * c) = v0;
+        *reinterpret_cast<bf16x8_t *>(dst + 32 * c + 8) = v1;
+        *reinterpret_cast<bf16x8_t *>(dst + 32 * c + 16) = v2;
+        *reinterpret_cast<bf16x8_t *>(dst + 32 * c + 24) = v3;
+      } else {
+        bf16x8_t lo = e4m3x8_bf16(raw[i][0], raw[i][1]), hi = e4m3x8_bf16(raw[i][2], raw[i][3]);
+        if (!ok) lo = hi = bf16x8_t{};
+        *reinterpret_cast<bf16x8_t *>(dst + 512 + 16 * (c - 16)) = lo;
+        *reinterpret_cast<bf16x8_t *>(dst + 512 + 16 * (c - 16) + 8) = hi;
+      }
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4_t o[32];
+#pragma unroll
+  for (int dt = 0; dt < 32; ++dt) o[dt] = f32x4_t{};
+  uint16_t *my_p = s_p[wid][0];
+
+  if (n_tok > 0) issue(0);
+  for (int t0 = 0; t0 < n_tok; t0 += kSub) {
+    park(t0);
+    __syncthreads();
+    if (t0 + kSub < n_tok) issue(t0 + kSub);
+    if (computes) {
+      // S^T: 4 groups of 16 tokens x this wave's 16 heads
+      float z[4][4], mx = -INFINITY;
+#pragma unroll
+      for (int tg = 0; tg < 4; ++tg) {
+        // the codes are converted again for every token group: hoisting the bf16 query out
+        // of this loop would hold 72 registers instead of 36
+#pragma unroll
+        for (int s = 0; s < 18; ++s) asm volatile("" : "+v"(qc[s]));
+        const uint16_t *krow = s_kt + (16 * tg + hl) * kKtLd + 8 * g;
+        f32x4_t acc = {};
+#pragma unroll
+        for (int s = 0; s < 18; ++s)
+          acc = mfma_16x16x32_bf16(*reinterpret_cast<const bf16x8_t *>(krow + 32 * s), e4m3x8_bf16(qc[s][0], qc[s][1]),
+                                   acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = t0 + 16 * tg + 4 * g + i;
+          z[tg][i] = (j < n_tok && s_off[j] >= 0) ? acc[i] * c2 : -INFINITY;
+          mx = fmaxf(mx, z[tg][i]);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.0f : exp2f(m_run - m_new);
+      float ps = 0.0f;
+#pragma unroll
+      for (int tg = 0; tg < 4; ++tg) {
+        bf16x4_t pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = z[tg][i] == -INFINITY ? 0.0f : exp2f(z[tg][i] - m_new);
+          pb[i] = (__bf16)p;
+          ps += (float)pb[i];
+        }
+        *reinterpret_cast<bf16x4_t *>(my_p + 256 * tg + 4 * lane) = pb;
+      }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      l_run = l_run * alpha + ps;
+      m_run = m_new;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // P written by the whole wave
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // O^T += V^T P^T, 32-token K-steps
+#pragma unroll
+      for (int dt = 0; dt < 32; ++dt) o[dt] *= alpha;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8_t pf = cat4(*reinterpret_cast<const bf16x4_t *>(my_p + 256 * (2 * ks) + 4 * lane),
+                                 *reinterpret_cast<const bf16x4_t *>(my_p + 256 * (2 * ks + 1) + 4 * lane));
+        const uint16_t *v0 = s_kt + (32 * ks + 4 * g + (hl >> 2)) * kKtLd + 4 * (hl & 3);
+        const uint16_t *v1 = v0 + 16 * kKtLd;
+#pragma unroll
+        for (int dt = 0; dt < 32; ++dt) {
+          const i16x4_t x0 = tr16(v0 + 16 * dt), x1 = tr16(v1 + 16 * dt);
+          const bf16x8_t va = cat4(__builtin_bit_cast(bf16x4_t, x0), __builtin_bit_cast(bf16x4_t, x1));
+          o[dt] = mfma_16x16x32_bf16(va, pf, o[dt]);
+        }
+      }
+    }
+    __syncthreads();  // s_kt is rewritten by the next subtile
+  }
+
+  // lane (head hl, group g) holds dims 16 dt + 4 g + i
+  if (!computes || !hvalid) return;
+  if (nsplit == 1) {
+    const float inv = l_run > 0.0f ? a.kv_scale / l_run : 0.0f;
+    uint16_t *orow = a.out + ((int64_t)r * H + h) * kVDim;
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) {
+      bf16x4_t vv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vv[i] = (__bf16)(o[dt][i] * inv);
+      *reinterpret_cast<bf16x4_t *>(orow + 16 * dt + 4 * g) = vv;
+    }
+    if (g == 0) a.lse[(int64_t)r * H + h] = l_run > 0.0f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+  } else {
+    const int64_t slot = ((int64_t)r * nsplit + sp) * H + h;
+    float *po = w.o + slot * kVDim;
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<f32x4_t *>(po + 16 * dt + 4 * g) = o[dt];
+    if (g == 0) w.ml[slot] = make_float2(m_run, l_run);
+  }
+}
+
 // Merge the token splits of one row in split order.  Thread = (head, 4 dims).
 constexpr int kCombineMaxSplits = 64;
 __global__ __launch_bounds__(256) void mla_combine_kernel(const MlaArgs a, const int nsplit, MlaWs w) {
@@ -335,7 +556,16 @@ hipError_t launch_mla(const MlaArgs &a, hipStream_t s) {
   const int nsplit = split_count(a.k, tps);
   if (tps > kMaxTps || tps % kSub != 0 || nsplit > kCombineMaxSplits) return hipErrorInvalidValue;
   const MlaWs w = mla_carve(a.ws, a.n_q, a.n_heads, nsplit);
-  if (a.lat_fmt == 0) {
+  const int nht = (a.n_heads + 15) / 16;
+  if (a.q_fmt == 1 && nht > 2 && nht <= kWideMaxTiles) {
+    // every head of a row per workgroup: one gather per subtile for all heads
+    dim3 grid(1, nsplit, a.n_q);
+    const size_t dyn = sizeof(int64_t) * (size_t)tps;
+    if (a.lat_fmt == 0)
+      hipLaunchKernelGGL(mla_wide_kernel<0>, grid, dim3(kWideThreads), dyn, s, a, nsplit, tps, w);
+    else
+      hipLaunchKernelGGL(mla_wide_kernel<1>, grid, dim3(kWideThreads), dyn, s, a, nsplit, tps, w);
+  } else if (a.lat_fmt == 0) {
     if (a.q_fmt == 0) launch_mla_t<0, 0>(a, nsplit, tps, w, s); else launch_mla_t<0, 1>(a, nsplit, tps, w, s);
   } else {
     if (a.q_fmt == 0) launch_mla_t<1, 0>(a, nsplit, tps, w, s); else launch_mla_t<1, 1>(a, nsplit, tps, w, s);

@@ -99,3 +99,32 @@ def test_prefill_chain(d, q_fmt):
         q, qs = pq.q_mla_bf16, None
     ref_o, ref_l = oracle.sparse_mla(oc, got_idx, q, q_fmt, qs, pq.q_req, 96, pq.sm_scale)
     check_attention(step.out, step.lse, ref_o, ref_l)
+
+
+@pytest.mark.parametrize("lat_fmt,heads,k", [(0, 48, 2048), (1, 96, 2048), (0, 128, 4096), (1, 40, 4096)])
+def test_mla_prefill_all_heads_per_row(d, lat_fmt, heads, k):
+    """FP8 queries with more than two 16-head tiles take the kernel that serves every head of
+    a row from one gather; k = 4096 adds a second token split and the merge."""
+    cache, pq, step = make_prefill(d, 5000, 24, heads=heads, seed=40 + heads, q_fmt=1, k=k)
+    if lat_fmt == 1:  # same geometry, MXFP4 keys and NVFP4 latents
+        cache = W.build_cache([5000 + 24], key_fmt=1, lat_fmt=1, seed=41 + heads, device="cuda", spare_rows=3)
+        step = d.PrefillStep(cache, pq, k=k, q_fmt=1)
+    rng = np.random.default_rng(heads + k)
+    rl = pq.row_len.cpu().numpy()
+    idx = np.full((pq.n_q, k), -1, np.int32)
+    for r in range(pq.n_q):
+        n = min(k, int(rl[r]))
+        sel = np.sort(rng.choice(int(rl[r]), n, replace=False)).astype(np.int32)
+        sel = sel[rng.random(n) >= 0.05]  # some -1 padding
+        idx[r, :len(sel)] = sel
+    idx[3, :7] = 11                       # one token seven times
+    idx[5, :] = -1                        # an empty row
+    step.resolve()
+    step.idx.copy_(torch.from_numpy(idx))
+    step.attend()
+    torch.cuda.synchronize()
+    assert int(step.err.item()) == 0
+    oc = oracle.OracleCache(cache)
+    ref_o, ref_l = oracle.sparse_mla(oc, idx, pq.q_mla_fp8, 1, pq.q_mla_scale, pq.q_req, heads, pq.sm_scale)
+    check_attention(step.out, step.lse, ref_o, ref_l)
+    assert np.isneginf(step.lse[5].cpu().numpy()).all() and (step.out[5].float() == 0).all()
