@@ -19,8 +19,8 @@
 //
 // Workgroup tile: 32 query rows x 256 tokens (4 pages); wave w owns page w (64 tokens,
 // two 32-token MFMA columns).  The key fragments are decoded once per tile and stay in
-// registers for all 32 heads.  For each head the 32 rows' query codes are decoded once
-// into LDS (double buffered, sign of a negative qs folded in) and shared by the 4 waves.
+// registers for all 32 heads.  The 32 rows' query codes are decoded into LDS two heads at
+// a time (double buffered, sign of a negative qs folded in) and shared by the 4 waves.
 // Per head and 32x32 sub-tile: 8 MFMAs (K = 128), then in the accumulator layout
 //   acc += (w * |qs|) * sel(x),  sel = max(x,0) (ks >= 0) or min(x,0) (ks < 0);
 // the store multiplies by ks.  Lane (column n, half h) at K-step s holds dims
@@ -47,7 +47,7 @@ constexpr int kQLd = kIdxDim + 8;          // bf16 per LDS query row (pad agains
 
 __global__ __launch_bounds__(256, 2) void indexer_gemm_kernel(const ScoreArgs a, const int n_tok_tiles) {
   __shared__ __align__(16) uint8_t s_page[kGWaves][kKPB];
-  __shared__ __align__(16) uint16_t s_q[2][kGRows][kQLd];
+  __shared__ __align__(16) uint16_t s_q[2][2][kGRows][kQLd];  // [buffer][head of the pair][row][dim]
   __shared__ __align__(16) float s_w[kIdxHeads][kGRows];  // w * |qs|, [head][row]
   __shared__ uint32_t s_neg[kIdxHeads];                   // rows with qs < 0, per head
   __shared__ int s_req[kGRows], s_len[kGRows];
@@ -126,18 +126,20 @@ __global__ __launch_bounds__(256, 2) void indexer_gemm_kernel(const ScoreArgs a,
       }
     }
     // (2) head 0's query tile -> LDS as bf16
-    auto stage_q = [&](int j, u32x4_t raw, int buf) {
+    auto stage_q = [&](int j, u32x4_t raw, int buf, int hh) {
       const bf16x8_t lo = e4m3x8_bf16(raw[0], raw[1]), hi = e4m3x8_bf16(raw[2], raw[3]);
       u32x4_t x0 = __builtin_bit_cast(u32x4_t, lo), x1 = __builtin_bit_cast(u32x4_t, hi);
       if ((s_neg[j] >> qm) & 1u) {
         x0 ^= 0x80008000u;
         x1 ^= 0x80008000u;
       }
-      *reinterpret_cast<u32x4_t *>(&s_q[buf][qm][16 * qc]) = x0;
-      *reinterpret_cast<u32x4_t *>(&s_q[buf][qm][16 * qc + 8]) = x1;
+      *reinterpret_cast<u32x4_t *>(&s_q[buf][hh][qm][16 * qc]) = x0;
+      *reinterpret_cast<u32x4_t *>(&s_q[buf][hh][qm][16 * qc + 8]) = x1;
     };
-    u32x4_t qraw = q_ok ? *reinterpret_cast<const u32x4_t *>(qsrc) : u32x4_t{};
-    stage_q(0, qraw, 0);
+    u32x4_t qraw0 = q_ok ? *reinterpret_cast<const u32x4_t *>(qsrc) : u32x4_t{};
+    u32x4_t qraw1 = q_ok ? *reinterpret_cast<const u32x4_t *>(qsrc + kIdxDim) : u32x4_t{};
+    stage_q(0, qraw0, 0, 0);
+    stage_q(1, qraw1, 0, 1);
     __syncthreads();
 
     // (3) key fragments, decoded once, resident for all heads
@@ -157,31 +159,41 @@ __global__ __launch_bounds__(256, 2) void indexer_gemm_kernel(const ScoreArgs a,
       acc[c] = f32x16_t{};
     }
 
-    // (4) heads
-    for (int j = 0; j < kIdxHeads; ++j) {
-      const int buf = j & 1;
-      if (j + 1 < kIdxHeads && q_ok) qraw = *reinterpret_cast<const u32x4_t *>(qsrc + (j + 1) * kIdxDim);
+    // (4) heads, two per barrier: the pair's query tiles are staged together
+    for (int j0 = 0; j0 < kIdxHeads; j0 += 2) {
+      const int buf = (j0 >> 1) & 1;
+      if (j0 + 2 < kIdxHeads && q_ok) {
+        qraw0 = *reinterpret_cast<const u32x4_t *>(qsrc + (j0 + 2) * kIdxDim);
+        qraw1 = *reinterpret_cast<const u32x4_t *>(qsrc + (j0 + 3) * kIdxDim);
+      }
       if (page_ok) {
-        bf16x8_t af[8];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) af[s] = *reinterpret_cast<const bf16x8_t *>(&s_q[buf][n][64 * h + 8 * s]);
-        float wv[16];
+        for (int hh = 0; hh < 2; ++hh) {
+          const int j = j0 + hh;
+          bf16x8_t af[8];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4_t t4 = *reinterpret_cast<const f32x4_t *>(&s_w[j][8 * q4 + 4 * h]);
+          for (int s = 0; s < 8; ++s) af[s] = *reinterpret_cast<const bf16x8_t *>(&s_q[buf][hh][n][64 * h + 8 * s]);
+          float wv[16];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) wv[4 * q4 + i] = t4[i];
-        }
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4_t t4 = *reinterpret_cast<const f32x4_t *>(&s_w[j][8 * q4 + 4 * h]);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          f32x16_t x = {};
+            for (int i = 0; i < 4; ++i) wv[4 * q4 + i] = t4[i];
+          }
 #pragma unroll
-          for (int s = 0; s < 8; ++s) x = mfma_32x32x16_bf16(af[s], bf[c][s], x);
+          for (int c = 0; c < 2; ++c) {
+            f32x16_t x = {};
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[c][i] = fmaf(wv[i], __builtin_amdgcn_fmed3f(x[i], lo[c], hi[c]), acc[c][i]);
+            for (int s = 0; s < 8; ++s) x = mfma_32x32x16_bf16(af[s], bf[c][s], x);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[c][i] = fmaf(wv[i], __builtin_amdgcn_fmed3f(x[i], lo[c], hi[c]), acc[c][i]);
+          }
         }
       }
-      if (j + 1 < kIdxHeads) stage_q(j + 1, q_ok ? qraw : u32x4_t{}, buf ^ 1);
+      if (j0 + 2 < kIdxHeads) {
+        stage_q(j0 + 2, q_ok ? qraw0 : u32x4_t{}, buf ^ 1, 0);
+        stage_q(j0 + 3, q_ok ? qraw1 : u32x4_t{}, buf ^ 1, 1);
+      }
       __syncthreads();
     }
 
