@@ -95,6 +95,30 @@ __global__ __launch_bounds__(256, 2) void mla_kernel(const MlaArgs a, const int 
   const int t_beg = sp * tps;
   const int n_tok = max(0, min(a.k, t_beg + tps) - t_beg);
 
+  // Q^T fragments: lane (head hl, group g) holds q[h][32s + 8g .. +8] for s < 18.  Loaded
+  // first, so that they travel together with the index and page-offset reads below.
+  bf16x8_t qf[18];
+  u32x2_t qc8[18];
+  float qscale = 1.0f;
+  if (hvalid) {
+    if constexpr (Q_FMT == 0) {
+      const uint16_t *qr = static_cast<const uint16_t *>(a.q) + ((int64_t)r * H + h) * kLatDim;
+#pragma unroll
+      for (int s = 0; s < 18; ++s) qf[s] = *reinterpret_cast<const bf16x8_t *>(qr + 32 * s + 8 * g);
+    } else {
+      const uint8_t *qr = static_cast<const uint8_t *>(a.q) + ((int64_t)r * H + h) * kLatDim;
+#pragma unroll
+      for (int s = 0; s < 18; ++s) qc8[s] = *reinterpret_cast<const u32x2_t *>(qr + 32 * s + 8 * g);
+      qscale = a.q_scale[(int64_t)r * H + h];
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 18; ++s) {
+      qf[s] = bf16x8_t{};
+      qc8[s] = u32x2_t{};
+    }
+  }
+
   // (0) pool offsets of the split's tokens (-1: padding or invalid)
   for (int j = tid; j < n_tok; j += 256) {
     int64_t off = -1;
@@ -116,26 +140,9 @@ __global__ __launch_bounds__(256, 2) void mla_kernel(const MlaArgs a, const int 
     s_off[j] = off;
   }
 
-  // Q^T fragments: lane (head hl, group g) holds q[h][32s + 8g .. +8] for s < 18
-  bf16x8_t qf[18];
-  float qscale = 1.0f;
-  if (hvalid) {
-    if constexpr (Q_FMT == 0) {
-      const uint16_t *qr = static_cast<const uint16_t *>(a.q) + ((int64_t)r * H + h) * kLatDim;
+  if constexpr (Q_FMT == 1) {
 #pragma unroll
-      for (int s = 0; s < 18; ++s) qf[s] = *reinterpret_cast<const bf16x8_t *>(qr + 32 * s + 8 * g);
-    } else {
-      const uint8_t *qr = static_cast<const uint8_t *>(a.q) + ((int64_t)r * H + h) * kLatDim;
-#pragma unroll
-      for (int s = 0; s < 18; ++s) {
-        const u32x2_t d = *reinterpret_cast<const u32x2_t *>(qr + 32 * s + 8 * g);
-        qf[s] = e4m3x8_bf16(d[0], d[1]);
-      }
-      qscale = a.q_scale[(int64_t)r * H + h];
-    }
-  } else {
-#pragma unroll
-    for (int s = 0; s < 18; ++s) qf[s] = bf16x8_t{};
+    for (int s = 0; s < 18; ++s) qf[s] = e4m3x8_bf16(qc8[s][0], qc8[s][1]);
   }
   const float c2 = a.sm_scale * a.kv_scale * qscale * kLog2e;  // logits in log2 units
   __syncthreads();  // s_off ready; query loads drained before the gather pipeline starts
@@ -318,6 +325,19 @@ __global__ __launch_bounds__(kWideThreads) void mla_wide_kernel(const MlaArgs a,
   const int t_beg = sp * tps;
   const int n_tok = max(0, min(a.k, t_beg + tps) - t_beg);
 
+  // e4m3 query codes: lane (head hl, group g) holds dims 32 s + 8 g .. + 8 of head h; loaded
+  // first, so that they travel together with the index and page-offset reads below
+  u32x2_t qc[18];
+  float qscale = 0.0f;
+  if (hvalid) {
+    const uint8_t *qr = static_cast<const uint8_t *>(a.q) + ((int64_t)r * H + h) * kLatDim;
+#pragma unroll
+    for (int s = 0; s < 18; ++s) qc[s] = *reinterpret_cast<const u32x2_t *>(qr + 32 * s + 8 * g);
+    qscale = a.q_scale[(int64_t)r * H + h];
+  } else {
+#pragma unroll
+    for (int s = 0; s < 18; ++s) qc[s] = u32x2_t{};
+  }
   for (int j = tid; j < n_tok; j += kWideThreads) {
     int64_t off = -1;
     if (rvalid) {
@@ -338,18 +358,6 @@ __global__ __launch_bounds__(kWideThreads) void mla_wide_kernel(const MlaArgs a,
     s_off[j] = off;
   }
 
-  // e4m3 query codes: lane (head hl, group g) holds dims 32 s + 8 g .. + 8 of head h
-  u32x2_t qc[18];
-  float qscale = 0.0f;
-  if (hvalid) {
-    const uint8_t *qr = static_cast<const uint8_t *>(a.q) + ((int64_t)r * H + h) * kLatDim;
-#pragma unroll
-    for (int s = 0; s < 18; ++s) qc[s] = *reinterpret_cast<const u32x2_t *>(qr + 32 * s + 8 * g);
-    qscale = a.q_scale[(int64_t)r * H + h];
-  } else {
-#pragma unroll
-    for (int s = 0; s < 18; ++s) qc[s] = u32x2_t{};
-  }
   const float c2 = a.sm_scale * a.kv_scale * qscale * kLog2e;
   __syncthreads();
   __builtin_amdgcn_s_waitcnt(0x0F70);
