@@ -243,21 +243,49 @@ __global__ __launch_bounds__(256) void topk_sample_kernel(const TopkArgs a, Topk
   if (len <= kShortRow || keff >= len) return;  // uniform
   const float *row = a.scores + (int64_t)r * a.ld;
   const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
-  int S = kOwnSamples;  // about len / 32, a power of two
-  while (S < kMaxSamples && S * 32 < len) S <<= 1;
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  for (int q = threadIdx.x; q < S / 4; q += 256) {
-    const float4 v = load_sample4(row, vec, len, S / 64, q);
-    const uint4 k = make_uint4(score_key(v.x), score_key(v.y), score_key(v.z), score_key(v.w));
-    *reinterpret_cast<uint4 *>(s_smp + 4 * q) = k;
-    lo = min(min(lo, min(k.x, k.y)), min(k.z, k.w));
-    hi = max(max(hi, max(k.x, k.y)), max(k.z, k.w));
+  int lg = 12;  // S = 2^lg samples, about len / 32
+  while ((1 << lg) < kMaxSamples && (32 << lg) < len) ++lg;
+  const int S = 1 << lg, lg_runs = lg - 6;
+  // runs of 64 start at multiples of 4 spread over [0, len - 64): run c at (len - 64) c / runs
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u, t1 = 0u, t2 = 0u;
+  for (int q0 = threadIdx.x; q0 < S / 4; q0 += 4 * 256) {  // S / 4 is a multiple of 1024
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = q0 + 256 * u, c = q >> 4, part = q & 15;
+      const int start = (int)(((int64_t)(len - 64) * c) >> lg_runs) & ~3;
+      const float *p = row + start + 4 * part;
+      v[u] = vec ? *reinterpret_cast<const float4 *>(p) : make_float4(p[0], p[1], p[2], p[3]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint4 k = make_uint4(score_key(v[u].x), score_key(v[u].y), score_key(v[u].z), score_key(v[u].w));
+      *reinterpret_cast<uint4 *>(s_smp + 4 * (q0 + 256 * u)) = k;
+      const uint32_t kk[4] = {k.x, k.y, k.z, k.w};
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        lo = min(lo, kk[e2]);
+        hi = max(hi, kk[e2]);
+        t2 = kk[e2] > t1 ? t1 : max(t2, kk[e2]);
+        t1 = max(t1, kk[e2]);
+      }
+    }
   }
-  block_minmax<256>(lo, hi, R);  // also orders the s_smp stores before the reads below
   const int m = sample_rank(keff, len, S);
   uint32_t est = 0u;
-  if (m < S) {
-    int gt;
+  int gt;
+  if (m <= 128) {
+    // the threads' top-2 keys are a subset of the sample: their m-th key is a lower bound
+    uint32_t l2 = t2, h2 = t1;
+    block_minmax<256>(l2, h2, R);
+    est = radix_select<256>(
+        [&](auto f) {
+          f(t1);
+          f(t2);
+        },
+        m, l2, h2, kEstPasses, R, gt);
+  } else if (m < S) {
+    block_minmax<256>(lo, hi, R);  // also orders the s_smp stores before the reads below
     est = radix_select<256>(
         [&](auto f) {
           for (int i = threadIdx.x; i < S; i += 256) f(s_smp[i]);
