@@ -82,7 +82,12 @@ def main():
     import numpy as np
     import torch
 
-    from long_context_sparse_paged_amd import build as B
+    import importlib.util
+    # build.py by path: importing it through the package would first load the library
+    spec = importlib.util.spec_from_file_location("long_context_sparse_paged_amd_build",
+                                                  os.path.join(ROOT, "long_context_sparse_paged_amd", "build.py"))
+    B = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(B)
     B.ensure_built()
     import long_context_sparse_paged_amd as d
     from synth import workloads as W

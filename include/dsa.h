@@ -143,13 +143,20 @@ dsa_status dsa_resolve_pages(const dsa_layout *layout, int32_t layer, const int3
  *   q_req, row_len  device int32 [n_q]
  *   scores     device fp32 [n_q][ld] (out): entries t < row_len[r] written,
  *              the rest untouched.
+ *   workspace  device, >= dsa_indexer_score_workspace_size(n_q, q_fmt) bytes,
+ *              256-B aligned (0 bytes, may be NULL, for bf16 queries)
  * The BF16 path streams each row's keys (decode); the FP8 path is an MFMA
  * GEMM over tiles of consecutive rows and is fastest when consecutive rows
- * share a request (a prefill chunk).  Both accept any q_req. */
+ * share a request (a prefill chunk).  Both accept any q_req.  The FP8 path
+ * first writes the rows' sign-folded bf16 query heads, head weights and the
+ * bf16 pieces of sum_j w_j |q_scale_j| q_j into the workspace (about 9.3 KB
+ * per row). */
+dsa_status dsa_indexer_score_workspace_size(int32_t n_q, int32_t q_fmt, size_t *bytes);
 dsa_status dsa_indexer_score(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
                              const int64_t *key_off, int64_t off_ld, int32_t n_req, const void *q, int32_t q_fmt,
                              const float *q_scale, const float *w, const int32_t *q_req, const int32_t *row_len,
-                             int32_t n_q, float *scores, int64_t ld, int32_t *err_flag, dsa_stream_t stream);
+                             int32_t n_q, float *scores, int64_t ld, void *workspace, size_t workspace_bytes,
+                             int32_t *err_flag, dsa_stream_t stream);
 
 /* Top-k ([ZH] "K3.1 Pro 中的稀疏注意力": the top 2048 are kept; an exact top-k
  * per "低延迟解码：融合的 DSA 解码路径").  For each row r, the min(k, row_len[r])

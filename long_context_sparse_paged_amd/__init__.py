@@ -29,7 +29,7 @@ DSA_Q_BF16, DSA_Q_FP8_E4M3 = 0, 1
 
 __all__ = [
     "DsaError", "dsa_layout", "lib", "dsa_status_str", "dsa_version", "dsa_layout_make", "dsa_resolve_pages",
-    "dsa_indexer_score", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_decode_workspace_size",
+    "dsa_indexer_score_workspace_size", "dsa_indexer_score", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_decode_workspace_size",
     "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill_workspace_size", "dsa_sparse_mla_prefill",
 ]
 
@@ -52,7 +52,7 @@ class dsa_layout(C.Structure):
 
 def _load():
     if not _LIB_PATH.exists():
-        raise ImportError(f"{_LIB_PATH} is not built; run `python -m long_context_sparse_paged_amd.build` "
+        raise ImportError(f"{_LIB_PATH} is not built; run `python long_context_sparse_paged_amd/build.py` "
                           "(the DSA kernels have no CPU fallback)")
     L = C.CDLL(str(_LIB_PATH))
     P, I32, I64, SZ, F = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_float
@@ -62,7 +62,8 @@ def _load():
         "dsa_version": ([], C.c_char_p),
         "dsa_layout_make": ([I32, I32, I32, I32, I64, LP], I32),
         "dsa_resolve_pages": ([LP, I32, P, I64, P, I32, I32, I64, P, P, I64, P, P], I32),
-        "dsa_indexer_score": ([LP, P, I64, P, I64, I32, P, I32, P, P, P, P, I32, P, I64, P, P], I32),
+        "dsa_indexer_score_workspace_size": ([I32, I32, C.POINTER(SZ)], I32),
+        "dsa_indexer_score": ([LP, P, I64, P, I64, I32, P, I32, P, P, P, P, I32, P, I64, P, SZ, P, P], I32),
         "dsa_topk_workspace_size": ([I32, I64, I32, C.POINTER(SZ)], I32),
         "dsa_topk": ([P, I64, P, I32, I32, P, I64, P, SZ, P, P], I32),
         "dsa_sparse_mla_decode_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
@@ -135,14 +136,22 @@ def dsa_resolve_pages(layout: dsa_layout, layer: int, block_table, n_pages, pool
     _check("dsa_resolve_pages", st)
 
 
+def dsa_indexer_score_workspace_size(n_q: int, q_fmt: int) -> int:
+    out = C.c_size_t()
+    _check("dsa_indexer_score_workspace_size", lib.dsa_indexer_score_workspace_size(n_q, q_fmt, C.byref(out)))
+    return out.value
+
+
 def dsa_indexer_score(layout: dsa_layout, pool, key_off, n_req: int, q, q_fmt: int, q_scale, w, q_req, row_len,
-                      scores, err_flag=None, stream=None):
+                      scores, workspace=None, err_flag=None, stream=None):
     qd = BF16 if q_fmt == DSA_Q_BF16 else U8
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.dsa_indexer_score(C.byref(layout), _ptr(pool, U8, "pool"), pool.numel(), _ptr(key_off, I64, "key_off"),
                                key_off.shape[1], n_req, _ptr(q, qd, "q"), q_fmt, _ptr(q_scale, F32, "q_scale"),
                                _ptr(w, F32, "w"), _ptr(q_req, I32, "q_req"), _ptr(row_len, I32, "row_len"),
                                row_len.shape[0], _ptr(scores, F32, "scores"), scores.shape[1],
-                               _ptr(err_flag, I32, "err_flag"), _stream(stream))
+                               _ptr(workspace, None, "workspace"), ws_bytes, _ptr(err_flag, I32, "err_flag"),
+                               _stream(stream))
     _check("dsa_indexer_score", st)
 
 

@@ -1,6 +1,8 @@
 """Build libdsa.so (the gfx950 HIP kernels + C ABI) in-tree with hipcc.
 
-    python -m long_context_sparse_paged_amd.build
+    python long_context_sparse_paged_amd/build.py
+
+(run as a file, not with -m: importing the package loads the library it builds)
 
 Every source is compiled for gfx950 only, with packed-FP32 instruction
 selection disabled (-packed-fp32-ops).  The library lands in

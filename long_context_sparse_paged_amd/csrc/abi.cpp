@@ -114,7 +114,8 @@ dsa_status dsa_resolve_pages(const dsa_layout *layout, int32_t layer, const int3
 dsa_status dsa_indexer_score(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
                              const int64_t *key_off, int64_t off_ld, int32_t n_req, const void *q, int32_t q_fmt,
                              const float *q_scale, const float *w, const int32_t *q_req, const int32_t *row_len,
-                             int32_t n_q, float *scores, int64_t ld, int32_t *err_flag, dsa_stream_t stream) {
+                             int32_t n_q, float *scores, int64_t ld, void *workspace, size_t workspace_bytes,
+                             int32_t *err_flag, dsa_stream_t stream) {
   dsa_status st = check_layout(layout);
   if (st != DSA_OK) return st;
   if (q_fmt != DSA_Q_BF16 && q_fmt != DSA_Q_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
@@ -141,12 +142,25 @@ dsa_status dsa_indexer_score(const dsa_layout *layout, const uint8_t *pool, int6
   a.ld = ld;
   a.err = err_flag;
   a.key_fmt = layout->key_fmt;
+  a.ws = nullptr;
   if (q_fmt == DSA_Q_BF16) {
     if (n_q > 4096) return DSA_ERR_UNSUPPORTED;
     return launched(launch_indexer_scan(a, stream_of(stream)));
   }
   if (layout->key_fmt != DSA_KEY_FP8_E4M3_SCALED) return DSA_ERR_UNSUPPORTED;  // FP8 queries need FP8 keys
+  if (workspace_bytes < indexer_gemm_workspace_bytes(n_q)) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace) return DSA_ERR_NULL_ARG;
+  if (!aligned(workspace, 256)) return DSA_ERR_MISALIGNED;
+  a.ws = workspace;
   return launched(launch_indexer_gemm(a, stream_of(stream)));
+}
+
+dsa_status dsa_indexer_score_workspace_size(int32_t n_q, int32_t q_fmt, size_t *bytes) {
+  if (!bytes) return DSA_ERR_NULL_ARG;
+  if (n_q < 0) return DSA_ERR_BAD_SHAPE;
+  if (q_fmt != DSA_Q_BF16 && q_fmt != DSA_Q_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
+  *bytes = q_fmt == DSA_Q_BF16 ? 0 : indexer_gemm_workspace_bytes(n_q);
+  return DSA_OK;
 }
 
 dsa_status dsa_topk_workspace_size(int32_t n_rows, int64_t ld, int32_t k, size_t *bytes) {

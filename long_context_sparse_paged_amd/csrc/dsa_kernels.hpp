@@ -37,9 +37,11 @@ struct ScoreArgs {
   int64_t ld;
   int32_t *err;
   int32_t key_fmt;
+  void *ws;  // e4m3 queries: indexer_gemm_workspace_bytes(n_q) bytes, 256-B aligned
 };
 hipError_t launch_indexer_scan(const ScoreArgs &a, hipStream_t s);  // bf16 queries
 hipError_t launch_indexer_gemm(const ScoreArgs &a, hipStream_t s);  // e4m3 queries
+size_t indexer_gemm_workspace_bytes(int32_t n_q);
 
 // Top-k: slices of kSlice scores, candidates per slice <= kSliceCap, rows of up to
 // kShortRow scores are selected wholly in LDS.

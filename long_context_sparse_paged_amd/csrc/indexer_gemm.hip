@@ -17,17 +17,32 @@
 // is exact) accumulates in fp32 to ~1e-8.  So both operands are decoded to bf16 and the
 // contraction runs on v_mfma_f32_32x32x16_bf16.
 //
-// Workgroup tile: 32 query rows x 256 tokens (4 pages); wave w owns page w (64 tokens,
-// two 32-token MFMA columns).  The key fragments are decoded once per tile and stay in
-// registers for all 32 heads.  The 32 rows' query codes are decoded into LDS two heads at
-// a time (double buffered, sign of a negative qs folded in) and shared by the 4 waves.
-// Per head and 32x32 sub-tile: 8 MFMAs (K = 128), then in the accumulator layout
-//   acc += (w * |qs|) * sel(x),  sel = max(x,0) (ks >= 0) or min(x,0) (ks < 0);
-// the store multiplies by ks.  Lane (column n, half h) at K-step s holds dims
-// [64h + 8s, 64h + 8s + 8) of both operands (any dim order works if both agree).
-// Grid order is row-block-major, so a row block's 128 KB of query codes stays in L2
-// while its token tiles stream past.  Rows of one tile that belong to different
-// requests are handled one request at a time with masked stores.
+// The ReLU costs one VALU op per (row, token, head) instead of two.  With the sign of qs
+// folded into the query (q~ = sign(qs) qcode), s_j = w_j |qs_j|, x_j = q~_j . kcode and
+// sigma = sign(ks):
+//   score = |ks| sum_j s_j ReLU(sigma x_j) = |ks|/2 (sigma A + B),
+//   A = sum_j s_j x_j = Q' . kcode  with  Q' = sum_j s_j q~_j,     B = sum_j s_j |x_j|,
+// since ReLU(y) = (y + |y|) / 2.  B is one v_fma per element (|x| is a free source
+// modifier).  A is a linear form: Q' (computed in fp64 by a pre-pass) is split into three
+// bf16 pieces whose sum carries 24 significant bits (fp32's precision), and three extra
+// 8-MFMA chains accumulate them straight into A's accumulator -- 3/32 more MFMA work, no
+// VALU.
+//
+// Pre-pass (indexer_qprep_kernel), one workgroup per row, into the caller's workspace:
+//   qb[r][36][128] bf16: heads 0..31 = q~_j (exact), heads 32..34 = the pieces of Q',
+//     head 35 = zeros (pads the last staging group of four heads);
+//   sw[r/32][32][r%32] fp32: s_j, laid out as the GEMM's LDS weight tile.
+//
+// GEMM workgroup tile: 32 query rows x 256 tokens (4 pages); wave w owns page w (64
+// tokens, two 32-token MFMA columns).  The key fragments are decoded once per tile and
+// stay in registers for all 36 heads.  Query tiles move global -> LDS by direct LDS loads
+// two heads at a time (double buffered, no VALU, 16-B chunks XOR-swizzled by row so the
+// MFMA operand reads are conflict-free).  Per head pair: four 8-MFMA chains, each after
+// the first interleaved with the accumulation of the one before it.  Lane (column n, half
+// h) at K-step s holds dims [64h + 8s, 64h + 8s + 8) of both operands.  Grid order is
+// row-block-major, so a row block's 288 KB of query tiles stays in L2 while its token
+// tiles stream past.  Rows of one tile that belong to different requests are handled one
+// request at a time with masked stores.
 #include <math.h>
 
 #include "dsa_device.hpp"
@@ -39,192 +54,327 @@ namespace {
 
 constexpr int kGRows = 32;
 constexpr int kGWaves = 4;
-constexpr int kGTokWG = kGWaves * kPage;   // 256
-constexpr int kKB = 132;                   // FP8 key row
-constexpr int kKPB = kPage * kKB;          // 8448
-constexpr int kChunks = kKPB / 16;         // 528
-constexpr int kQLd = kIdxDim + 8;          // bf16 per LDS query row (pad against bank conflicts)
+constexpr int kGTokWG = kGWaves * kPage;         // 256
+constexpr int kKB = 132;                         // FP8 key row
+constexpr int kKPB = kPage * kKB;                // 8448
+constexpr int kChunks = kKPB / 16;               // 528
+constexpr int kPer = (kChunks + 63) / 64;        // 9 16-byte chunks per lane, the last partial
+constexpr int kPageLds = kPer * 1024;            // a wave's page region, padded to whole loads
+constexpr int kLinHeads = 3;                     // bf16 pieces of Q' (24 significant bits)
+constexpr int kQbHeads = kIdxHeads + 4;          // 36: the last head slot is padding
+constexpr int kGroup = 4;                        // heads staged per barrier
+constexpr int kGroups = kQbHeads / kGroup;       // 9: eight of query heads, one of Q' pieces
+constexpr int kHeadTile = kGRows * kIdxDim;      // bf16 per staged head tile (8 KB)
+static_assert(kGroup * kHeadTile * 2 <= kGWaves * kPageLds, "query buffer 1 fits in the page region");
+constexpr int64_t kQbRow = (int64_t)kQbHeads * kIdxDim;  // bf16 per workspace row
 
-__global__ __launch_bounds__(256, 2) void indexer_gemm_kernel(const ScoreArgs a, const int n_tok_tiles) {
-  __shared__ __align__(16) uint8_t s_page[kGWaves][kKPB];
-  __shared__ __align__(16) uint16_t s_q[2][2][kGRows][kQLd];  // [buffer][head of the pair][row][dim]
-  __shared__ __align__(16) float s_w[kIdxHeads][kGRows];  // w * |qs|, [head][row]
-  __shared__ uint32_t s_neg[kIdxHeads];                   // rows with qs < 0, per head
-  __shared__ int s_req[kGRows], s_len[kGRows];
+__device__ __forceinline__ uint16_t bf16_bits_rn(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// ---- pre-pass: sign-folded bf16 queries, Q' pieces and weights for one row ----
+__global__ __launch_bounds__(256) void indexer_qprep_kernel(const ScoreArgs a, uint16_t *qb, float *sw) {
+  __shared__ float s_qt[kIdxHeads][kIdxDim + 1];
+  __shared__ float s_s[kIdxHeads];
+  const int r = blockIdx.x, t = threadIdx.x, j = t >> 3, d0 = 16 * (t & 7);
+  const float qs = a.q_scale[(int64_t)r * kIdxHeads + j];
+  const float s = a.w[(int64_t)r * kIdxHeads + j] * fabsf(qs);
+  const u32x4_t raw = *reinterpret_cast<const u32x4_t *>(static_cast<const uint8_t *>(a.q) +
+                                                         ((int64_t)r * kIdxHeads + j) * kIdxDim + d0);
+  u32x4_t x0 = __builtin_bit_cast(u32x4_t, e4m3x8_bf16(raw[0], raw[1]));
+  u32x4_t x1 = __builtin_bit_cast(u32x4_t, e4m3x8_bf16(raw[2], raw[3]));
+  if (qs < 0.0f) {
+    x0 ^= 0x80008000u;
+    x1 ^= 0x80008000u;
+  }
+  uint16_t *dst = qb + (int64_t)r * kQbRow + (int64_t)j * kIdxDim + d0;
+  *reinterpret_cast<u32x4_t *>(dst) = x0;
+  *reinterpret_cast<u32x4_t *>(dst + 8) = x1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s_qt[j][d0 + 2 * i] = __uint_as_float(x0[i] << 16);
+    s_qt[j][d0 + 2 * i + 1] = __uint_as_float(x0[i] & 0xFFFF0000u);
+    s_qt[j][d0 + 8 + 2 * i] = __uint_as_float(x1[i] << 16);
+    s_qt[j][d0 + 8 + 2 * i + 1] = __uint_as_float(x1[i] & 0xFFFF0000u);
+  }
+  if ((t & 7) == 0) {
+    s_s[j] = s;
+    sw[((int64_t)(r / kGRows) * kIdxHeads + j) * kGRows + r % kGRows] = s;
+  }
+  __syncthreads();
+  if (t < kIdxDim) {
+    // Q'[t] in fp64 (each product is exact), then four bf16 pieces; each residual is exact
+    // in fp64 (a piece is within a factor of two of what it approximates)
+    double q = 0.0;
+#pragma unroll 8
+    for (int jj = 0; jj < kIdxHeads; ++jj) q += (double)s_s[jj] * (double)s_qt[jj][t];
+#pragma unroll
+    for (int p = 0; p < kLinHeads; ++p) {
+      const uint16_t b = bf16_bits_rn((float)q);
+      qb[(int64_t)r * kQbRow + (int64_t)(kIdxHeads + p) * kIdxDim + t] = b;
+      q -= (double)__uint_as_float((uint32_t)b << 16);
+    }
+    qb[(int64_t)r * kQbRow + (int64_t)(kQbHeads - 1) * kIdxDim + t] = 0;
+  }
+}
+
+// ---- GEMM ----
+__global__ __launch_bounds__(256, 2) void indexer_gemm_kernel(const ScoreArgs a, const int n_tok_tiles,
+                                                              const uint16_t *qb, const float *sw) {
+  // query tiles are double buffered four heads at a time; buffer 1 shares its LDS with the
+  // key pages, which are read only once per tile (to decode the key fragments)
+  __shared__ __align__(16) uint16_t s_q0[kGroup * kHeadTile];    // [head of the group][row][dim], swizzled
+  __shared__ __align__(16) uint8_t s_pg[kGWaves * kPageLds];     // key pages, then query buffer 1
+  __shared__ __align__(16) float s_w[kIdxHeads][kGRows];         // s_j, [head][row]
+  __shared__ int s_len[kGRows];
 
   const int tile = blockIdx.x % n_tok_tiles;
-  const int row0 = (blockIdx.x / n_tok_tiles) * kGRows;
+  const int rb = blockIdx.x / n_tok_tiles, row0 = rb * kGRows;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
   const int64_t max_tok = a.ld < a.off_ld * kPage ? a.ld : a.off_ld * kPage;
   const bool report = tile == 0;
 
-  if (tid < kIdxHeads) s_neg[tid] = 0;
-  if (tid < kGRows) {
-    const int r = row0 + tid;
-    int req = -1, len = 0;
+  typedef void __attribute__((address_space(1))) gvoid;
+  typedef void __attribute__((address_space(3))) lvoid;
+  auto qbuf = [&](int buf) -> uint16_t * { return buf ? reinterpret_cast<uint16_t *>(s_pg) : s_q0; };
+  // the block's workspace rows as a buffer: rows past n_q are out of range and read as zero
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(qb + (int64_t)row0 * kQbRow), 0, (int)(min(kGRows, a.n_q - row0) * kQbRow * 2), 0x00020000);
+  // query tiles of heads 4g .. 4g+3 -> buffer g & 1: wave w stages head 4g + w with eight
+  // direct LDS loads of 4 rows; the lane for row m, LDS chunk c' fetches chunk c' ^ (m & 15)
+  auto stage = [&](int g) {
+    uint16_t *dst = qbuf(g & 1) + wid * kHeadTile;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = 4 * i + (lane >> 4);
+      const int voff = 2 * (m * (int)kQbRow + wid * kIdxDim + 8 * ((lane & 15) ^ (m & 15)));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lvoid *)(dst + 4 * i * kIdxDim), 16, voff, 2 * kGroup * g * kIdxDim,
+                                               0, 0);
+    }
+  };
+  // the weight tile (4 KB, one 1-KB load per wave) and the first head pair go out before
+  // anything is waited on
+  __builtin_amdgcn_global_load_lds((const gvoid *)(sw + (int64_t)rb * kIdxHeads * kGRows + 256 * wid + 4 * lane),
+                                   (lvoid *)&s_w[8 * wid][0], 16, 0, 0);
+  stage(0);
+
+  // rows of the block: lane m < 32 of every wave holds row m's request and length
+  int my_req = -1, my_len = 0;
+  if (lane < kGRows) {
+    const int r = row0 + lane;
     if (r < a.n_q) {
       const int b = a.q_req[r];
-      len = a.row_len[r];
+      int len = a.row_len[r];
       uint32_t e = 0;
-      if (b < 0 || b >= a.n_req) e |= DSA_DEVERR_REQUEST; else req = b;
+      if (b < 0 || b >= a.n_req) e |= DSA_DEVERR_REQUEST; else my_req = b;
       if (len < 0 || len > max_tok) {
         e |= DSA_DEVERR_ROW_LEN;
         len = len < 0 ? 0 : (int)max_tok;
       }
-      if (e && report) flag_error(a.err, e);
+      if (e && report && wid == 0) flag_error(a.err, e);
+      my_len = my_req >= 0 ? len : 0;
     }
-    s_req[tid] = req;
-    s_len[tid] = req >= 0 ? len : 0;
+    if (wid == 0) s_len[lane] = my_len;
   }
-  __syncthreads();
-  for (int i = tid; i < kIdxHeads * kGRows; i += 256) {
-    const int j = i / kGRows, m = i % kGRows, r = row0 + m;
-    float v = 0.0f;
-    if (r < a.n_q) {
-      const float qs = a.q_scale[(int64_t)r * kIdxHeads + j];
-      v = a.w[(int64_t)r * kIdxHeads + j] * fabsf(qs);
-      if (qs < 0.0f) atomicOr(&s_neg[j], 1u << m);
-    }
-    s_w[j][m] = v;
-  }
-  __syncthreads();
-
-  uint32_t todo = 0;
-  for (int m = 0; m < kGRows; ++m)
-    if (s_req[m] >= 0) todo |= 1u << m;
-  const uint8_t *qbase = static_cast<const uint8_t *>(a.q);
-  // this thread's share of a head tile: row qm, codes [16 qc, 16 qc + 16)
-  const int qm = tid >> 3, qc = tid & 7;
-  const bool q_ok = row0 + qm < a.n_q;
-  const uint8_t *qsrc = qbase + ((int64_t)(row0 + qm) * kIdxHeads) * kIdxDim + 16 * qc;
+  uint32_t todo = (uint32_t)__ballot(lane < kGRows && my_req >= 0);
+  bool first = true;
 
   while (todo) {
-    const int b = s_req[__ffs(todo) - 1];
-    uint32_t rows = 0;
-    int lmax = 0;
-    for (int m = 0; m < kGRows; ++m)
-      if (s_req[m] == b) {
-        rows |= 1u << m;
-        lmax = max(lmax, s_len[m]);
-      }
+    const int b = __builtin_amdgcn_readlane(my_req, __ffs(todo) - 1);
+    const bool mine = lane < kGRows && my_req == b;
+    const uint32_t rows = (uint32_t)__ballot(mine);
+    const int lmax = (int)wave_max_u32(mine ? (uint32_t)my_len : 0u);
+    const int lmin = (int)wave_min_u32(mine ? (uint32_t)my_len : 0xFFFFFFFFu);
     todo &= ~rows;
     if (tile * kGTokWG >= lmax) continue;  // uniform: the tile lies past every row's length
+    if (!first) stage(0);  // a second request in this tile restarts the head loop
+    first = false;
 
-    // (1) this wave's key page -> LDS
+    // (1) this wave's key page -> LDS, all nine chunk loads in flight at once
     const int wtok0 = tile * kGTokWG + wid * kPage;
     bool page_ok = false;
     if (wtok0 < lmax) {
-      const int64_t off = a.key_off[(int64_t)b * a.off_ld + wtok0 / kPage];
+      int64_t off = a.key_off[(int64_t)b * a.off_ld + wtok0 / kPage];
+      // one page per wave: the offset is wave-uniform, so the descriptor lives in SGPRs
+      off = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(off >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)off));
       if (off < 0 || off + kKPB > a.pool_bytes || (off & 15)) {
         if (lane == 0) flag_error(a.err, DSA_DEVERR_PAGE_OFFSET);
       } else {
         page_ok = true;
-        const uint8_t *src = a.pool + off;
-        for (int c = lane; c < kChunks; c += 64)
-          *reinterpret_cast<u32x4_t *>(s_page[wid] + 16 * c) = *reinterpret_cast<const u32x4_t *>(src + 16 * c);
+        // the descriptor's range (one page) zero-fills the tail of the last load, which
+        // lands in the region's padding
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.pool + off), 0, kKPB, 0x00020000);
+        u32x4_t pg[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) pg[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * lane + 1024 * i, 0, 0);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) *reinterpret_cast<u32x4_t *>(s_pg + wid * kPageLds + 16 * lane + 1024 * i) = pg[i];
       }
     }
-    // (2) head 0's query tile -> LDS as bf16
-    auto stage_q = [&](int j, u32x4_t raw, int buf, int hh) {
-      const bf16x8_t lo = e4m3x8_bf16(raw[0], raw[1]), hi = e4m3x8_bf16(raw[2], raw[3]);
-      u32x4_t x0 = __builtin_bit_cast(u32x4_t, lo), x1 = __builtin_bit_cast(u32x4_t, hi);
-      if ((s_neg[j] >> qm) & 1u) {
-        x0 ^= 0x80008000u;
-        x1 ^= 0x80008000u;
-      }
-      *reinterpret_cast<u32x4_t *>(&s_q[buf][hh][qm][16 * qc]) = x0;
-      *reinterpret_cast<u32x4_t *>(&s_q[buf][hh][qm][16 * qc + 8]) = x1;
-    };
-    u32x4_t qraw0 = q_ok ? *reinterpret_cast<const u32x4_t *>(qsrc) : u32x4_t{};
-    u32x4_t qraw1 = q_ok ? *reinterpret_cast<const u32x4_t *>(qsrc + kIdxDim) : u32x4_t{};
-    stage_q(0, qraw0, 0, 0);
-    stage_q(1, qraw1, 0, 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the direct LDS loads (weights, group 0) landed
     __syncthreads();
 
-    // (3) key fragments, decoded once, resident for all heads
+    // (2) key fragments, decoded once, resident for all heads
     bf16x8_t bf[2][8];
-    float ks[2], lo[2], hi[2];
-    f32x16_t acc[2];
+    float ks[2];
+    f32x16_t acc[2], lin[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const uint8_t *kr = s_page[wid] + (32 * c + n) * kKB;
+      const uint8_t *kr = s_pg + wid * kPageLds + (32 * c + n) * kKB;
 #pragma unroll
       for (int s = 0; s < 8; ++s)
         bf[c][s] = e4m3x8_bf16(*reinterpret_cast<const uint32_t *>(kr + 64 * h + 8 * s),
                                *reinterpret_cast<const uint32_t *>(kr + 64 * h + 8 * s + 4));
       ks[c] = *reinterpret_cast<const float *>(kr + 128);
-      lo[c] = ks[c] < 0.0f ? -INFINITY : 0.0f;
-      hi[c] = ks[c] < 0.0f ? 0.0f : INFINITY;
       acc[c] = f32x16_t{};
+      lin[c] = f32x16_t{};
     }
 
-    // (4) heads, two per barrier: the pair's query tiles are staged together
-    for (int j0 = 0; j0 < kIdxHeads; j0 += 2) {
-      const int buf = (j0 >> 1) & 1;
-      if (j0 + 2 < kIdxHeads && q_ok) {
-        qraw0 = *reinterpret_cast<const u32x4_t *>(qsrc + (j0 + 2) * kIdxDim);
-        qraw1 = *reinterpret_cast<const u32x4_t *>(qsrc + (j0 + 3) * kIdxDim);
+    __syncthreads();  // every wave has its key fragments: the page region becomes query buffer 1
+    stage(1);
+
+    bf16x8_t af[8];
+    auto load_af = [&](int buf, int hh) {
+      const uint16_t *row = qbuf(buf) + hh * kHeadTile + n * kIdxDim;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) af[s] = *reinterpret_cast<const bf16x8_t *>(row + 8 * ((8 * h + s) ^ (n & 15)));
+    };
+    auto chain = [&](int c, f32x16_t x) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) x = mfma_32x32x16_bf16(af[s], bf[c][s], x);
+      return x;
+    };
+    auto load_w = [&](float *wv, int j) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4_t t4 = *reinterpret_cast<const f32x4_t *>(&s_w[j][8 * q4 + 4 * h]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wv[4 * q4 + i] = t4[i];
       }
+    };
+    auto accum = [&](int c, const f32x16_t &x, const float *wv) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[c][i] = fmaf(wv[i], fabsf(x[i]), acc[c][i]);
+    };
+    auto interleave = [] {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
+      }
+    };
+
+    // (3) the 32 heads, four per barrier: B accumulates s_j |x_j|.  Chain i of a group is
+    // (head i/2, column i%2); each chain after the first overlaps the accumulation of the
+    // one before it.
+    for (int g = 0; g < kGroups - 1; ++g) {
+      const int buf = g & 1;
+      if (g > 0) stage(g + 1);
       if (page_ok) {
+        // one set of weights: head hd's are read last by the accumulation that overlaps
+        // chain 2hd+2, just before head hd+1's are loaded
+        float wv[16];
+        load_af(buf, 0);
+        load_w(wv, kGroup * g);
+        f32x16_t xp = chain(0, f32x16_t{});
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int j = j0 + hh;
-          bf16x8_t af[8];
-#pragma unroll
-          for (int s = 0; s < 8; ++s) af[s] = *reinterpret_cast<const bf16x8_t *>(&s_q[buf][hh][n][64 * h + 8 * s]);
-          float wv[16];
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4_t t4 = *reinterpret_cast<const f32x4_t *>(&s_w[j][8 * q4 + 4 * h]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) wv[4 * q4 + i] = t4[i];
-          }
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            f32x16_t x = {};
-#pragma unroll
-            for (int s = 0; s < 8; ++s) x = mfma_32x32x16_bf16(af[s], bf[c][s], x);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[c][i] = fmaf(wv[i], __builtin_amdgcn_fmed3f(x[i], lo[c], hi[c]), acc[c][i]);
-          }
+        for (int i = 1; i < 2 * kGroup; ++i) {
+          const int hd = i >> 1, c = i & 1, cp = (i - 1) & 1;
+          if (c == 0) load_af(buf, hd);
+          if (c == 1 && hd > 0) load_w(wv, kGroup * g + hd);
+          const f32x16_t xn = chain(c, f32x16_t{});
+          accum(cp, xp, wv);
+          interleave();
+          __builtin_amdgcn_sched_barrier(0);
+          xp = xn;
         }
+        accum(1, xp, wv);
       }
-      if (j0 + 2 < kIdxHeads) {
-        stage_q(j0 + 2, q_ok ? qraw0 : u32x4_t{}, buf ^ 1, 0);
-        stage_q(j0 + 3, q_ok ? qraw1 : u32x4_t{}, buf ^ 1, 1);
-      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // the next group's tiles have landed in LDS
       __syncthreads();
     }
-
-    // (5) store: acc[c][i] is row 8*(i/4) + 4h + i%4, token wtok0 + 32c + n
+    // (4) the three pieces of Q': A accumulates in the MFMA accumulator itself
     if (page_ok) {
+#pragma unroll
+      for (int hh = 0; hh < kLinHeads; ++hh) {
+        load_af((kGroups - 1) & 1, hh);
+        lin[0] = chain(0, lin[0]);
+        lin[1] = chain(1, lin[1]);
+      }
+    }
+    __syncthreads();
+
+    // (5) store |ks|/2 (sigma A + B): element i is row 8*(i/4) + 4h + i%4, token wtok0 + 32c + n
+    if (page_ok) {
+      // row addresses are formed here, not hoisted out of the request loop where 16 of
+      // them would hold 32 VGPRs through the head loop
+      int64_t ld = a.ld;
+      uint32_t rws = rows;
+      int h4 = 4 * h;
+      asm volatile("" : "+s"(ld), "+s"(rws), "+v"(h4));
+      float *const out = a.scores + (int64_t)row0 * ld;
+      // the block's score rows as a buffer (32 ld floats fit 32-bit offsets, checked at
+      // launch): a lane offset for (row 4h, token t) plus a scalar offset per row step
+      const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(out, 0, 0x7FFFFFFF, 0x00020000);
+      const int ld32 = (int)ld;
+      // the common case: every row of the block is this request's and the wave's 64 tokens
+      // lie below every row's length, so no element needs a mask
+      const bool whole = rws == 0xFFFFFFFFu && wtok0 + kPage <= lmin;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int t = wtok0 + 32 * c + n;
+        const float sg = ks[c] < 0.0f ? -1.0f : 1.0f, half = 0.5f * fabsf(ks[c]);
+        if (whole) {
+          const int voff = 4 * (h4 * ld32 + t);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int m = 8 * (i >> 2) + 4 * h + (i & 3);
-          if (((rows >> m) & 1u) && t < s_len[m]) a.scores[(int64_t)(row0 + m) * a.ld + t] = ks[c] * acc[c][i];
+          for (int i = 0; i < 16; ++i)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(half * fmaf(sg, lin[c][i], acc[c][i])), ors, voff,
+                                                  4 * (8 * (i >> 2) + (i & 3)) * ld32, 0);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int m = 8 * (i >> 2) + h4 + (i & 3);
+            if (((rws >> m) & 1u) && t < s_len[m]) out[m * ld + t] = half * fmaf(sg, lin[c][i], acc[c][i]);
+          }
         }
       }
     }
     __syncthreads();  // s_page / s_q are refilled for the next request of this tile
   }
+  // no direct LDS load may still be in flight when the workgroup's LDS is released: a tile
+  // whose every request was skipped never waited for the prologue's loads
+  if (first) __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 }  // namespace
 
+size_t indexer_gemm_workspace_bytes(int32_t n_q) {
+  if (n_q <= 0) return 0;
+  const int64_t qb = ((int64_t)n_q * kQbRow * 2 + 255) & ~int64_t(255);
+  const int64_t sw = (int64_t)((n_q + kGRows - 1) / kGRows) * kIdxHeads * kGRows * 4;
+  return (size_t)(qb + sw);
+}
+
 hipError_t launch_indexer_gemm(const ScoreArgs &a, hipStream_t s) {
   if (a.n_q == 0) return hipSuccess;
-  if (a.key_fmt != 0) return hipErrorInvalidValue;
+  if (a.key_fmt != 0 || a.ws == nullptr) return hipErrorInvalidValue;
   const int64_t max_tok = a.ld < a.off_ld * kPage ? a.ld : a.off_ld * kPage;
   const int64_t n_tok_tiles = (max_tok + kGTokWG - 1) / kGTokWG;
   const int64_t n_row_blocks = (a.n_q + kGRows - 1) / kGRows;
   const int64_t grid = n_tok_tiles * n_row_blocks;
-  if (grid == 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(indexer_gemm_kernel, dim3((unsigned)grid), dim3(256), 0, s, a, (int)n_tok_tiles);
+  if ((int64_t)kGRows * a.ld * 4 > 0x7FFFFFFF) return hipErrorInvalidValue;  // 32-bit store offsets
+  uint16_t *qb = static_cast<uint16_t *>(a.ws);
+  float *sw = reinterpret_cast<float *>(static_cast<uint8_t *>(a.ws) +
+                                        (((int64_t)a.n_q * kQbRow * 2 + 255) & ~int64_t(255)));
+  hipLaunchKernelGGL(indexer_qprep_kernel, dim3(a.n_q), dim3(256), 0, s, a, qb, sw);
+  if (grid == 0) return hipGetLastError();
+  hipLaunchKernelGGL(indexer_gemm_kernel, dim3((unsigned)grid), dim3(256), 0, s, a, (int)n_tok_tiles, qb, sw);
   return hipGetLastError();
 }
 

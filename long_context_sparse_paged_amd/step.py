@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import torch
 
-from . import (DSA_Q_BF16, DSA_Q_FP8_E4M3, dsa_indexer_score, dsa_layout_make, dsa_resolve_pages, dsa_sparse_mla_decode,
+from . import (DSA_Q_BF16, DSA_Q_FP8_E4M3, dsa_indexer_score, dsa_indexer_score_workspace_size, dsa_layout_make, dsa_resolve_pages, dsa_sparse_mla_decode,
                dsa_sparse_mla_decode_workspace_size, dsa_sparse_mla_prefill, dsa_sparse_mla_prefill_workspace_size,
                dsa_topk, dsa_topk_workspace_size)
 
@@ -63,7 +63,7 @@ class DecodeStep(_Base):
     def score(self, stream=None):
         c = self.cache
         dsa_indexer_score(self.layout, c.pool, self.key_off, c.n_req, self.q_idx, DSA_Q_BF16, None, self.w, self.q_req,
-                          self.row_len, self.scores, self.err, stream)
+                          self.row_len, self.scores, None, self.err, stream)
 
     def attend(self, stream=None):
         c = self.cache
@@ -91,6 +91,8 @@ class PrefillStep(_Base):
         self.lse = torch.empty(pq.n_q, self.n_heads, dtype=torch.float32, device=device)
         nb = dsa_sparse_mla_prefill_workspace_size(pq.n_q, self.n_heads, k)
         self.ws_mla = torch.empty(nb, dtype=torch.uint8, device=device) if nb else None
+        nb = dsa_indexer_score_workspace_size(pq.n_q, q_fmt)
+        self.ws_score = torch.empty(nb, dtype=torch.uint8, device=device) if nb else None
 
     def score(self, stream=None):
         c, pq = self.cache, self.pq
@@ -99,7 +101,7 @@ class PrefillStep(_Base):
         else:
             q, qs = pq.q_idx_bf16, None
         dsa_indexer_score(self.layout, c.pool, self.key_off, c.n_req, q, self.q_fmt, qs, pq.w, pq.q_req, pq.row_len,
-                          self.scores, self.err, stream)
+                          self.scores, self.ws_score, self.err, stream)
 
     def attend(self, stream=None):
         c, pq = self.cache, self.pq

@@ -7,6 +7,18 @@ import torch
 from synth import workloads as W
 
 
+def ensure_lib():
+    """Build libdsa.so if it is absent.  build.py is loaded by path: importing it through
+    the package would first load the library."""
+    import importlib.util
+    from pathlib import Path
+    path = Path(__file__).resolve().parents[1] / "long_context_sparse_paged_amd" / "build.py"
+    spec = importlib.util.spec_from_file_location("long_context_sparse_paged_amd_build", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.ensure_built()
+
+
 def hand_cache(key_rows: np.ndarray, lat_rows: np.ndarray | None, key_fmt: int = 0, lat_fmt: int = 0,
                kv_scale: float = 1.0, perm_seed: int | None = None, n_layers: int = 1, layer: int = 0):
     """A one-request cache whose token t has exactly the given key/latent bytes.

@@ -12,8 +12,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 @pytest.fixture(scope="module")
 def d():
-    from long_context_sparse_paged_amd import build
-    build.ensure_built()
+    from tests.helpers import ensure_lib
+    ensure_lib()
     import long_context_sparse_paged_amd as d
     return d
 
@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(d):
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(d.lib, n), n
 
@@ -84,7 +84,8 @@ def test_resolve_errors(d):
 def test_score_errors(d):
     L = d.dsa_layout_make(64, 1, 0, 0, 0)
     f = d.lib.dsa_indexer_score
-    args = [C.byref(L), FAKE, 1 << 30, FAKE, 16, 1, FAKE, 0, None, FAKE, FAKE, FAKE, 4, FAKE, 1024, None, None]
+    args = [C.byref(L), FAKE, 1 << 30, FAKE, 16, 1, FAKE, 0, None, FAKE, FAKE, FAKE, 4, FAKE, 1024, None, 0, None,
+            None]
     a = list(args); a[1] = None
     assert f(*a) == d.DSA_ERR_NULL_ARG
     a = list(args); a[7] = 1        # FP8 queries without q_scale
@@ -102,6 +103,21 @@ def test_score_errors(d):
     assert f(*a) == d.DSA_ERR_UNSUPPORTED
     a = list(args); a[12] = 0       # nothing to do
     assert f(*a) == d.DSA_OK
+    # FP8 queries take a workspace: rows of bf16 query heads, weights, linear-term pieces
+    need = d.dsa_indexer_score_workspace_size(4, d.DSA_Q_FP8_E4M3)
+    assert need >= 4 * 36 * 128 * 2 + 32 * 32 * 4
+    assert d.dsa_indexer_score_workspace_size(4, d.DSA_Q_BF16) == 0
+    assert d.dsa_indexer_score_workspace_size(0, d.DSA_Q_FP8_E4M3) == 0
+    a = list(args); a[7] = 1; a[8] = FAKE; a[15] = FAKE; a[16] = need - 1
+    assert f(*a) == d.DSA_ERR_WORKSPACE_TOO_SMALL
+    a = list(args); a[7] = 1; a[8] = FAKE; a[15] = None; a[16] = need
+    assert f(*a) == d.DSA_ERR_NULL_ARG
+    a = list(args); a[7] = 1; a[8] = FAKE; a[15] = C.c_void_p(FAKE.value + 16); a[16] = need
+    assert f(*a) == d.DSA_ERR_MISALIGNED
+    out = C.c_size_t()
+    assert d.lib.dsa_indexer_score_workspace_size(-1, 1, C.byref(out)) == d.DSA_ERR_BAD_SHAPE
+    assert d.lib.dsa_indexer_score_workspace_size(4, 7, C.byref(out)) == d.DSA_ERR_UNSUPPORTED
+    assert d.lib.dsa_indexer_score_workspace_size(4, 1, None) == d.DSA_ERR_NULL_ARG
 
 
 def test_topk_errors(d):

@@ -25,8 +25,8 @@ pytestmark = pytest.mark.gpu
 
 @pytest.fixture(scope="module")
 def d(gpu):
-    from long_context_sparse_paged_amd import build
-    build.ensure_built()
+    from tests.helpers import ensure_lib
+    ensure_lib()
     import long_context_sparse_paged_amd as d
     return d
 

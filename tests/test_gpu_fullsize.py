@@ -25,8 +25,8 @@ SAMPLES = {1: [0, 17, 31], 2: [0, 7], 3: [0, 1, 40, 63], 4: [0, 1023, 2047]}
 
 @pytest.fixture(scope="module")
 def d(gpu):
-    from long_context_sparse_paged_amd import build
-    build.ensure_built()
+    from tests.helpers import ensure_lib
+    ensure_lib()
     import long_context_sparse_paged_amd as d
     return d
 

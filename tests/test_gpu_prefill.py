@@ -14,8 +14,8 @@ pytestmark = pytest.mark.gpu
 
 @pytest.fixture(scope="module")
 def d(gpu):
-    from long_context_sparse_paged_amd import build
-    build.ensure_built()
+    from tests.helpers import ensure_lib
+    ensure_lib()
     import long_context_sparse_paged_amd as d
     return d
 
@@ -71,8 +71,9 @@ def test_prefill_gemm_rows_of_several_requests(d):
     d.dsa_resolve_pages(layout, 0, cache.block_table, cache.n_pages, cache.pool_rows, lat_off, key_off)
     scores = torch.full((n_q, max(ctx)), float("nan"), device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(d.dsa_indexer_score_workspace_size(n_q, d.DSA_Q_FP8_E4M3), dtype=torch.uint8, device="cuda")
     d.dsa_indexer_score(layout, cache.pool, key_off, 3, codes.cuda(), d.DSA_Q_FP8_E4M3, qs.cuda(), w.cuda(),
-                        torch.from_numpy(q_req).cuda(), torch.from_numpy(row_len).cuda(), scores, err)
+                        torch.from_numpy(q_req).cuda(), torch.from_numpy(row_len).cuda(), scores, ws, err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     oc = oracle.OracleCache(cache)
