@@ -6,7 +6,7 @@ import torch
 import oracle
 from synth import formats as F
 from synth import workloads as W
-from tests.helpers import topk_set_ok
+from tests.helpers import topk_set_ok, torch_e4m3_values
 from tests.test_gpu_decode import check_attention, check_scores, log
 
 pytestmark = pytest.mark.gpu
@@ -129,3 +129,46 @@ def test_mla_prefill_all_heads_per_row(d, lat_fmt, heads, k):
     ref_o, ref_l = oracle.sparse_mla(oc, idx, pq.q_mla_fp8, 1, pq.q_mla_scale, pq.q_req, heads, pq.sm_scale)
     check_attention(step.out, step.lse, ref_o, ref_l)
     assert np.isneginf(step.lse[5].cpu().numpy()).all() and (step.out[5].float() == 0).all()
+
+
+def test_mla_prefill_reference_far_below_a_later_max(d):
+    """The FP8-latent prefill kernel fixes each head's softmax reference at its first subtile's
+    max.  Here row 2 head 0's first subtile scores far below a later token (log2 logit gap
+    > 64), so the row is computed again with the true max.  The logits stay small in absolute
+    terms (first subtile about -58, the later token about +8), so the comparison keeps the
+    usual tolerances; the result must be the oracle's exact softmax."""
+    cache, pq, step = make_prefill(d, 3000, 8, heads=96, seed=77, q_fmt=1, k=2048)
+    step.resolve()
+    torch.cuda.synchronize()
+    k, H = 2048, 96
+    rl = pq.row_len.cpu().numpy()
+    idx = np.full((pq.n_q, k), -1, np.int32)
+    for r in range(pq.n_q):
+        n = min(k, int(rl[r]))
+        idx[r, :n] = np.arange(n, dtype=np.int32)  # tokens 0 .. n-1 in order: 0 .. 31 is subtile 0
+    # e4m3 latent codes of one magnitude with the signs of row 2 head 0's query (or against them)
+    qd = pq.q_mla_fp8[2, 0].cpu().numpy()
+    qv = torch_e4m3_values(qd).astype(np.float64) * float(pq.q_mla_scale[2, 0])
+    base = abs(qv).sum() * pq.sm_scale * cache.kv_scale / np.log(2.0)  # log2 logit per unit code value
+    grid = [((c >> 3) & 15, c & 7) for c in range(1, 127)]
+    vals = sorted(((1 + mm / 8) * 2.0 ** (ee - 7) if ee else mm / 8 * 2.0 ** -6, (ee << 3) | mm) for ee, mm in grid)
+    m0, c0 = max((x for x in vals if base * x[0] <= 60.0), key=lambda x: x[0])
+    m1, c1 = min((x for x in vals if base * (m0 + x[0]) > 65.0), key=lambda x: x[0])
+    assert base * m0 > 50.0 and base * m1 < 16.0, f"no e4m3 pair fits: {base:.3g} per unit"
+    low = np.where(qv < 0, c0, c0 | 0x80).astype(np.uint8)   # against the query: logit -base m0
+    high = np.where(qv < 0, c1 | 0x80, c1).astype(np.uint8)  # along it: logit +base m1
+    lat_off = step.lat_off.cpu().numpy()
+    row_off = lambda t: int(lat_off[0, t >> 6]) + (t & 63) * 576
+    flat = cache.pool.view(-1)  # the offsets are bytes from the pool base; the pool is [rows, row_stride]
+    for t, codes in [(t, low) for t in range(32)] + [(1000, high)]:
+        o = row_off(t)
+        assert 0 <= o and o + 576 <= flat.numel()
+        flat[o:o + 576] = torch.from_numpy(codes).cuda()
+    step.idx.copy_(torch.from_numpy(idx))
+    step.attend()
+    torch.cuda.synchronize()
+    assert int(step.err.item()) == 0
+    oc = oracle.OracleCache(cache)
+    ref_o, ref_l = oracle.sparse_mla(oc, idx, pq.q_mla_fp8, 1, pq.q_mla_scale, pq.q_req, H, pq.sm_scale)
+    assert base * (m0 + m1) > 64.0  # the gap the second pass exists for
+    check_attention(step.out, step.lse, ref_o, ref_l)
