@@ -512,28 +512,39 @@ __global__ __launch_bounds__(kWideThreads) void mla_wide_kernel(const MlaArgs a,
   }
 }
 
-// ---- prefill, FP8 latents: every head of a row per workgroup, 32 heads per wave ----
+// ---- prefill, FP8 latents: every head of a row per workgroup ----
 //
-// One 256-thread workgroup per (row, split); wave w owns heads 32w .. 32w+31 (up to 128
-// heads) and keeps all 512 value dims of its 32 heads in MFMA accumulators (256 registers;
-// one wave per SIMD leaves 512).  The latent rows are used as gathered, FP8, with no decode
-// pass: per 32-token subtile
-//   S^T[token][head] = K Q^T     9 v_mfma_scale_f32_32x32x64_f8f6f4 (scales 1): A = 32 raw
-//                                e4m3 bytes of a K row per lane from LDS, B = 32 bytes of the
-//                                row's e4m3 query codes per lane from registers.  The FP8 MFMA
-//                                rounds inside its sums (~1e-5 of sum |q k|); the logits then
-//                                move the attention output far less than its 1e-2 tolerance.
-//   O^T[dim][head] += V^T P^T    32 v_mfma_f32_32x32x16_bf16: A = 8 tokens x 1 dim of V per
-//                                lane by ds_read_b64_tr_b8, decoded e4m3 -> bf16 (exact);
-//                                B = P^T, bf16, taken straight from S^T's accumulator.
+// One 256-thread workgroup per (row, split), one wave per SIMD.  The work of a 32-token
+// subtile is split two ways:
+//   QK  wave t < ceil(H / 32) owns head tile t (heads 32t .. 32t+31):
+//         S^T[token][head] = K Q^T   9 v_mfma_scale_f32_32x32x64_f8f6f4 (scales 1): A = 32 raw
+//                                    e4m3 bytes of a K row per lane from LDS, B = 32 bytes of
+//                                    the row's e4m3 query codes per lane from registers.  The
+//                                    FP8 MFMA rounds inside its sums (~1e-5 of sum |q k|); the
+//                                    logits then move the attention output far less than its
+//                                    1e-2 tolerance.
+//       then the softmax weights P (bf16, rounded once; the same rounded values feed the row
+//       sum) go to LDS as the P^T operand fragments of the tile.
+//   PV  wave w owns value dims 128w .. 128w+127 of every head:
+//         O^T[dim][head] += V^T P^T  8 x (head tiles) v_mfma_f32_32x32x16_bf16: A = 8 tokens x
+//                                    1 dim of V per lane by ds_read_b64_tr_b8, decoded e4m3 ->
+//                                    bf16 (exact) once per wave and used for every head tile;
+//                                    B = P^T of the tile from LDS.
+//       Its accumulators (4 dim blocks x up to 4 head tiles of 32 x 32 fp32) stay in the
+//       MFMA accumulator registers for the whole row.
+// So every SIMD takes part in P.V, and each value byte is decoded once per workgroup, where
+// a wave holding all 512 dims of its own heads would leave one SIMD idle at 96 heads and
+// decode every value byte once per head tile.
 // S^T's accumulator row rho = 8q + 4p + i holds token 16 (q / 2) + 8 p + 4 (q % 2) + i (the
 // K operand's lanes read their rows in that order), so lane half p's elements 8 s2 .. 8 s2+7
-// are the 8 consecutive tokens 16 s2 + 8 p .. + 7 -- the K order of one transposing read.
-// Gather: rows go straight to LDS by direct loads into a ring of subtile slots, six subtiles
-// ahead of the one being used; one barrier per subtile frees the oldest slot.  Rows sit 592 B
-// apart in a slot, which spreads the 16 rows of one K read over distinct banks.
+// are the 8 consecutive tokens 16 s2 + 8 p .. + 7 -- the K order of one transposing read, and
+// S^T's lane layout is already the B layout of P^T.
+// Gather: rows go straight to LDS by direct loads into a ring of subtile slots, five subtiles
+// ahead of the one being used.  Per subtile, one barrier frees the oldest slot and a second
+// one publishes P.  Rows sit 592 B apart in a slot, which spreads the 16 rows of one K read
+// over distinct banks.
 // Softmax reference: p = 2^(z - m_ref) with m_ref fixed at the head's max over its first
-// subtile with a valid token, so the 256 accumulator registers are never rescaled.  O / l and
+// subtile with a valid token, so the accumulators are never rescaled.  O / l and
 // m_ref + log2 l do not depend on the reference, and p <= 2^64 keeps p (bf16), l and O (fp32)
 // far from overflow.  If a later max passes m_ref by more than 2^64, the workgroup computes
 // the row again with m_ref = the row's true max (a second pass that real data never needs).
@@ -545,9 +556,10 @@ constexpr int kPfChunks = kPfRow / 16;              // 37 16-byte chunks, the la
 constexpr int kPfLoads = (kPfSub * kPfChunks + 63) / 64;  // 19 wave loads per subtile
 constexpr int kPfPer = (kPfLoads + 3) / 4;          // 5 per wave (padded to 20)
 constexpr int kPfSlot = 4 * kPfPer * 1024;          // 20 KB
-constexpr int kPfSlots = 7;                         // 140 KB; with s_off (16 KB) within 160 KB
+constexpr int kPfSlots = 6;                         // 120 KB; with P (<= 16 KB) and s_off (16 KB) within 160 KB
 constexpr int kPfAhead = kPfSlots - 1;
 constexpr int kPfMaxSubs = kMaxTps / kPfSub;        // 64
+constexpr int kPfBlocks = kVDim / 32 / 4;           // 32-dim blocks of V per wave: 4
 
 // s_waitcnt vmcnt(K), other counters untouched (K < 64)
 template <int K>
@@ -559,22 +571,28 @@ __device__ __forceinline__ void wait_vm() {
 typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 typedef __attribute__((ext_vector_type(2))) int i32x2_t;
 
-// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4; the wave's 64 lanes
-// fill lds .. lds + 1 KB).  Issued from inline asm: the compiler then does not make every
+// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4 with M0 = `lds`, a
+// wave-uniform LDS byte address; the wave's 64 lanes fill lds .. lds + 1 KB).  Issued from inline asm: the compiler then does not make every
 // later LDS read wait for all such loads in flight (it cannot tell ring slots apart), which
 // would expose the gather's full latency each subtile.  Every read of a ring slot is ordered
 // after its loads by an explicit vmcnt wait and a barrier instead.
-__device__ __forceinline__ void lds_dma16(const void *src, const void *lds) {
-  const unsigned base =
-      __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)(__attribute__((address_space(3))) const void *)lds);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base) : "memory", "m0");
+__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
 
+// 32-bit LDS address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+
+template <int NHT>  // head tiles of 32: 2..4
 __global__ __launch_bounds__(kPfThreads, 1) void mla_prefill_kernel(const MlaArgs a, const int nsplit, const int tps,
                                                                      MlaWs w) {
   constexpr int LB = 576;
   constexpr int64_t LPB = (int64_t)kPage * LB;
   __shared__ __align__(16) uint8_t s_raw[kPfSlots][kPfSlot];
+  __shared__ __align__(16) u32x4_t s_p[2][NHT][2][64];  // P^T fragments: [subtile & 1][head tile][K-step][lane]
+  __shared__ float s_l[NHT * 32];                    // row sums, for the PV waves' outputs
   __shared__ uint32_t s_ok[kPfMaxSubs];  // valid tokens of each subtile
   __shared__ int s_redo;                 // some head's max passed its reference by > 2^64
   extern __shared__ int64_t s_off[];     // [tps]
@@ -583,9 +601,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void mla_prefill_kernel(const MlaArg
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int n = lane & 31, g = lane >> 5;
   const int H = a.n_heads;
-  const bool computes = wid * 32 < H;  // wave-uniform
+  const bool computes = wid < NHT;        // this wave forms S and P of head tile wid
   const int h = wid * 32 + n;
-  const bool hvalid = h < H;
+  const bool hvalid = computes && h < H;
   const int b = a.q_req ? a.q_req[r] : r;
   const bool rvalid = b >= 0 && b < a.n_req;
   if (!rvalid && tid == 0 && sp == 0) flag_error(a.err, DSA_DEVERR_REQUEST);
@@ -637,125 +655,162 @@ __global__ __launch_bounds__(kPfThreads, 1) void mla_prefill_kernel(const MlaArg
     const uint32_t okm = (uint32_t)__ballot(lane < kPfSub && j < n_tok && s_off[j] >= 0);
     if (lane == 0) s_ok[sub] = okm;
   }
-
-  typedef void __attribute__((address_space(1))) gvoid;
-  typedef void __attribute__((address_space(3))) lvoid;
   // Subtile `sub`'s rows -> ring slot sub % kPfSlots, rows kPfRow bytes apart: load kk (of
   // 20; wave w issues kk = 5w .. 5w+4) fills slot chunks 64 kk .. 64 kk + 63.  Lanes on a row's
   // padding chunk, past the rows, or on an invalid token read the pool's first bytes instead.
+  // LDS address of this wave's first 1 KB in slot 0 (wave w fills loads 5w .. 5w+4 of a slot)
+  const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(lds_addr(s_raw[0]) + 1024 * kPfPer * wid);
   auto issue = [&](int sub) {
-    uint8_t *slot = s_raw[sub % kPfSlots];
+    const uint32_t slot_lds = wave_lds + kPfSlot * (uint32_t)(sub % kPfSlots);
+    // the row offsets first, all reads in flight together (the index is clamped into s_off;
+    // a clamped read is not used)
+    int64_t offs[kPfPer];
+#pragma unroll
+    for (int i = 0; i < kPfPer; ++i) {
+      const int tok = (64 * (wid * kPfPer + i) + lane) / kPfChunks;
+      offs[i] = s_off[min(sub * kPfSub + min(tok, kPfSub - 1), n_tok - 1)];
+    }
 #pragma unroll
     for (int i = 0; i < kPfPer; ++i) {
       const int kk = wid * kPfPer + i, q = 64 * kk + lane;
       const int tok = q / kPfChunks, c = q - tok * kPfChunks;
-      const int j = sub * kPfSub + tok;
-      const int64_t off = (tok < kPfSub && c < LB / 16 && j < n_tok) ? s_off[j] : -1;
-      const uint8_t *src = a.pool + (off < 0 ? 0 : off + 16 * c);
-      lds_dma16(src, slot + 1024 * kk);
+      const bool ok = tok < kPfSub && c < LB / 16 && sub * kPfSub + tok < n_tok && offs[i] >= 0;
+      lds_dma16(a.pool + (ok ? offs[i] + 16 * c : 0), slot_lds + 1024 * i);
     }
   };
-  // wait until this wave's loads of subtile `sub` have landed (kPfPer per subtile, in order;
-  // those of later subtiles may still fly)
-  auto wait_for = [&](int sub) {
-    switch (min(n_sub - 1 - sub, kPfAhead - 1)) {  // subtiles issued after it
+  // wait until this wave's loads of a subtile have landed, `later` subtiles issued after it
+  // still flying (kPfPer loads per subtile, in order)
+  auto wait_later = [&](int later) {
+    switch (later) {
       case 0: wait_vm<0>(); break;
       case 1: wait_vm<kPfPer>(); break;
       case 2: wait_vm<2 * kPfPer>(); break;
       case 3: wait_vm<3 * kPfPer>(); break;
-      case 4: wait_vm<4 * kPfPer>(); break;
-      default: wait_vm<5 * kPfPer>(); break;
+      default: wait_vm<4 * kPfPer>(); break;
     }
   };
-  static_assert(kPfAhead - 1 <= 5, "the wait ladder covers up to five later subtiles");
+  static_assert(kPfAhead - 1 <= 4, "the wait ladder covers up to four later subtiles");
 
   // lane rho of the K operand reads slot row pi(rho); S^T element e of half g is token
   // 16 (e / 8) + 8 g + e % 8
   const int krow = 16 * (n >> 4) + 8 * ((n >> 2) & 1) + 4 * ((n >> 3) & 1) + (n & 3);
 
+  // PV operand: lane l of a 16-lane group points at token row 16 s2 + 8 g + (l & 15) / 2 and
+  // dims 16 ((l >> 4) & 1) + 8 (l & 1) of a 32-dim block; the transposing read then gives
+  // lane l dim (l & 31) of the block at the 8 tokens 16 s2 + 8 g .. + 7.  This wave's blocks
+  // are 4 wid .. 4 wid + 3 (byte 128 wid of a row).
+  const int vofs = (8 * g + ((lane & 15) >> 1)) * kPfRow + 16 * ((lane >> 4) & 1) + 8 * (lane & 1) + 128 * wid;
+
   float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.0f;
-  f32x16_t o[16];
+  f32x16_t o[NHT][kPfBlocks];
   for (int pass = 0; pass < 2; ++pass) {
     bool over = false;
     l_run = 0.0f;
 #pragma unroll
-    for (int db = 0; db < 16; ++db) o[db] = f32x16_t{};
+    for (int t = 0; t < NHT; ++t)
+#pragma unroll
+      for (int db = 0; db < kPfBlocks; ++db) o[t][db] = f32x16_t{};
     for (int s = 0; s < kPfAhead && s < n_sub; ++s) issue(s);
-
+    // S^T of one subtile (head tile wid) on FP8: rows = the subtile's 32 tokens (permuted),
+    // columns = 32 heads; 9 MFMAs over the slot's rows
+    auto qk = [&](const uint8_t *ks) {
+      f32x16_t acc = {};
+      const uint8_t *kr = ks + krow * kPfRow + 32 * g;
+#pragma unroll
+      for (int s = 0; s < 9; ++s) {
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(kr + 64 * s);
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(kr + 64 * s + 16);
+        const i32x8_t ka = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qc[s], acc, 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
+      }
+      return acc;
+    };
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    f32x16_t sacc = {};
+    if (n_sub > 0) {
+      wait_later(min(n_sub - 1, kPfAhead - 1));
+      __syncthreads();  // subtile 0 has landed
+      if (computes) sacc = qk(s_raw[0]);
+    }
+    // Software pipeline: the MFMAs of subtile it + 1's logits are issued before subtile it's
+    // P.V, so the softmax of a subtile never waits on its logits' MFMA chain.
     for (int it = 0; it < n_sub; ++it) {
-      wait_for(it);
-      __syncthreads();  // subtile it has landed; every wave is done with the slot of it - 1
-      if (it + kPfAhead < n_sub) issue(it + kPfAhead);  // into that slot
       const uint8_t *slot = s_raw[it % kPfSlots];
       if (computes) {
-        // S^T = K Q^T on FP8: rows = this subtile's 32 tokens (permuted), columns = 32 heads
-        f32x16_t sacc = {};
-        const uint8_t *kr = slot + krow * kPfRow + 32 * g;
+        const uint32_t okm = s_ok[it];  // uniform
+        float z[16];
+        if (okm == 0xFFFFFFFFu) {
 #pragma unroll
-        for (int s = 0; s < 9; ++s) {
-          const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(kr + 64 * s);
-          const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(kr + 64 * s + 16);
-          const i32x8_t ka = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qc[s], sacc, 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
-        }
-        const uint32_t okm = s_ok[it];
-        float z[16], mx = -INFINITY;
+          for (int e = 0; e < 16; ++e) z[e] = sacc[e] * c2;
+        } else {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int tok = 16 * (e >> 3) + 8 * g + (e & 7);
-          z[e] = ((okm >> tok) & 1u) ? sacc[e] * c2 : -INFINITY;
-          mx = fmaxf(mx, z[e]);
+          for (int e = 0; e < 16; ++e) {
+            const int tok = 16 * (e >> 3) + 8 * g + (e & 7);
+            z[e] = ((okm >> tok) & 1u) ? sacc[e] * c2 : -INFINITY;
+          }
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(z[e], z[e + 1]));
+        {  // max with the other half-wave (lanes l and l ^ 32 hold the same head)
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
+          mx = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
+        }
         if (m_ref == -INFINITY) m_ref = mx;  // the head's first valid tokens: O and l are still 0
         m_true = fmaxf(m_true, mx);
         over |= mx > m_ref + kRefSlack;
-        bf16x8_t pf[2];
+        // p = 2^(z - m_ref), rounded to bf16 in pairs; the row sum adds the rounded values (a
+        // bf16 dot product with ones).  Invalid tokens (z = -inf) give 0, and so does a subtile
+        // before the head's first valid token (m_ref is still -inf and every z is -inf).
+        const float mr = m_ref == -INFINITY ? 0.0f : m_ref;
+        float ls = 0.0f;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
+          u32x4_t pk;
 #pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const float zz = z[8 * s2 + m];
-            const __bf16 pb = (__bf16)(zz == -INFINITY ? 0.0f : exp2f(zz - m_ref));
-            pf[s2][m] = pb;
-            l_run += (float)pb;
+          for (int m2 = 0; m2 < 4; ++m2) {
+            const f32x2_t pp = {__builtin_amdgcn_exp2f(z[8 * s2 + 2 * m2] - mr),
+                                __builtin_amdgcn_exp2f(z[8 * s2 + 2 * m2 + 1] - mr)};
+            const bf16x2_t pb = __builtin_convertvector(pp, bf16x2_t);
+            pk[m2] = __builtin_bit_cast(uint32_t, pb);
+            ls = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, ls, false);
           }
+          s_p[it & 1][wid][s2][lane] = pk;
         }
-        // O^T += V^T P^T: K-step s2 is tokens 16 s2 + 8 g' .. + 7 for lane half g'; a
-        // 16-lane group's transposing read takes 8 rows x 16 dims: lane L of the group points
-        // at row 16 s2 + 8 g' + L / 2, dims 16 (group half) + 8 (L % 2) of block db
-        // 32 steps (s2, db); the transposing reads run four steps ahead of their MFMAs
-        const uint8_t *vb = slot + (8 * g + ((lane & 15) >> 1)) * kPfRow + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
-        auto vread = [&](int st) {  // step st = 16 s2 + db
-          return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (__attribute__((address_space(3))) i32x2_t *)(vb + 16 * (st >> 4) * kPfRow + 32 * (st & 15)));
-        };
-        i32x2_t xv[4];
+        l_run += ls;
+      }
+      if (it + 1 < n_sub) wait_later(min(n_sub - 2 - it, kPfAhead - 2));
+      // P of subtile it is in LDS; subtile it + 1 has landed; every wave is done with subtile
+      // it - 1, its slot and its P buffer
+      __syncthreads();
+      if (it + kPfAhead < n_sub) issue(it + kPfAhead);  // into the slot of it - 1
+      __builtin_amdgcn_sched_barrier(0);
+      if (computes && it + 1 < n_sub) sacc = qk(s_raw[(it + 1) % kPfSlots]);
+      // O^T += V^T P^T over this wave's 4 dim blocks: step st = 4 s2 + db
+      const uint8_t *vb = slot + vofs;
+      i32x2_t xv[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xv[i] = vread(i);
+      for (int st = 0; st < 8; ++st)
+        xv[st] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2_t *)(vb + 16 * (st >> 2) * kPfRow + 32 * (st & 3)));
 #pragma unroll
-        for (int st0 = 0; st0 < 32; st0 += 4) {
-          i32x2_t xn[4];
-          if (st0 + 4 < 32) {
+      for (int s2 = 0; s2 < 2; ++s2) {
+        bf16x8_t pt[NHT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xn[i] = vread(st0 + 4 + i);
-          }
+        for (int t = 0; t < NHT; ++t) pt[t] = __builtin_bit_cast(bf16x8_t, s_p[it & 1][t][s2][lane]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int st = st0 + i;
-            o[st & 15] = mfma_32x32x16_bf16(e4m3x8_bf16((uint32_t)xv[i][0], (uint32_t)xv[i][1]), pf[st >> 4], o[st & 15]);
-          }
-          __builtin_amdgcn_sched_barrier(0);  // bounded lookahead keeps registers
-          if (st0 + 4 < 32) {
+        for (int db = 0; db < kPfBlocks; ++db) {
+          const bf16x8_t va = e4m3x8_bf16((uint32_t)xv[4 * s2 + db][0], (uint32_t)xv[4 * s2 + db][1]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xv[i] = xn[i];
-          }
+          for (int t = 0; t < NHT; ++t) o[t][db] = mfma_32x32x16_bf16(va, pt[t], o[t][db]);
         }
       }
       // O lives in the accumulator registers across subtiles (without this the loop-carried
       // values are kept in VGPRs and copied around every MFMA)
 #pragma unroll
-      for (int db = 0; db < 16; ++db) asm volatile("" : "+a"(o[db]));
+      for (int t = 0; t < NHT; ++t)
+#pragma unroll
+        for (int db = 0; db < kPfBlocks; ++db) asm volatile("" : "+a"(o[t][db]));
     }
     if (computes && __ballot(over) != 0 && lane == 0) s_redo = 1;
     __syncthreads();
@@ -766,38 +821,51 @@ __global__ __launch_bounds__(kPfThreads, 1) void mla_prefill_kernel(const MlaArg
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // nothing in flight into LDS
 
-  if (!computes) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (!hvalid) return;
-  // lane (head n, half g) holds dims 32 db + 8 (e / 4) + 4 g + e % 4
-  if (nsplit == 1) {
-    const float inv = l_tot > 0.0f ? a.kv_scale / l_tot : 0.0f;
-    uint16_t *orow = a.out + ((int64_t)r * H + h) * kVDim;
+  // row sums of every head, from the QK waves to all
+  float l_tot = 0.0f;
+  if (computes) {
+    l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (g == 0) s_l[32 * wid + n] = l_tot;
+  }
+  __syncthreads();
+  // lane (head 32 t + n, half g) holds dims 32 (4 wid + db) + 8 (e / 4) + 4 g + e % 4
 #pragma unroll
-    for (int db = 0; db < 16; ++db) {
+  for (int t = 0; t < NHT; ++t) {
+    const int ht = 32 * t + n;
+    if (ht >= H) continue;
+    if (nsplit == 1) {
+      const float lt = s_l[ht];
+      const float inv = lt > 0.0f ? a.kv_scale / lt : 0.0f;
+      uint16_t *orow = a.out + ((int64_t)r * H + ht) * kVDim + 128 * wid;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        bf16x4_t vv;
+      for (int db = 0; db < kPfBlocks; ++db) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vv[i] = (__bf16)(o[db][4 * q + i] * inv);
-        *reinterpret_cast<bf16x4_t *>(orow + 32 * db + 8 * q + 4 * g) = vv;
+        for (int q = 0; q < 4; ++q) {
+          bf16x4_t vv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vv[i] = (__bf16)(o[t][db][4 * q + i] * inv);
+          *reinterpret_cast<bf16x4_t *>(orow + 32 * db + 8 * q + 4 * g) = vv;
+        }
+      }
+    } else {
+      float *po = w.o + (((int64_t)r * nsplit + sp) * H + ht) * kVDim + 128 * wid;
+#pragma unroll
+      for (int db = 0; db < kPfBlocks; ++db) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4_t vv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vv[i] = o[t][db][4 * q + i];
+          *reinterpret_cast<f32x4_t *>(po + 32 * db + 8 * q + 4 * g) = vv;
+        }
       }
     }
-    if (g == 0) a.lse[(int64_t)r * H + h] = l_tot > 0.0f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
-  } else {
-    const int64_t slot = ((int64_t)r * nsplit + sp) * H + h;
-    float *po = w.o + slot * kVDim;
-#pragma unroll
-    for (int db = 0; db < 16; ++db) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f32x4_t vv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vv[i] = o[db][4 * q + i];
-        *reinterpret_cast<f32x4_t *>(po + 32 * db + 8 * q + 4 * g) = vv;
-      }
-    }
-    if (g == 0) w.ml[slot] = make_float2(m_ref, l_tot);
+  }
+  if (hvalid && g == 0) {
+    if (nsplit == 1)
+      a.lse[(int64_t)r * H + h] = l_tot > 0.0f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+    else
+      w.ml[((int64_t)r * nsplit + sp) * H + h] = make_float2(m_ref, l_tot);
   }
 }
 
@@ -858,9 +926,15 @@ hipError_t launch_mla(const MlaArgs &a, hipStream_t s) {
     // every head of a row per workgroup: one gather per subtile for all heads
     dim3 grid(1, nsplit, a.n_q);
     const size_t dyn = sizeof(int64_t) * (size_t)tps;
-    if (a.lat_fmt == 0)
-      hipLaunchKernelGGL(mla_prefill_kernel, grid, dim3(kPfThreads), dyn, s, a, nsplit, tps, w);
-    else
+    if (a.lat_fmt == 0) {
+      const int nht32 = (a.n_heads + 31) / 32;
+      if (nht32 == 2)
+        hipLaunchKernelGGL(mla_prefill_kernel<2>, grid, dim3(kPfThreads), dyn, s, a, nsplit, tps, w);
+      else if (nht32 == 3)
+        hipLaunchKernelGGL(mla_prefill_kernel<3>, grid, dim3(kPfThreads), dyn, s, a, nsplit, tps, w);
+      else
+        hipLaunchKernelGGL(mla_prefill_kernel<4>, grid, dim3(kPfThreads), dyn, s, a, nsplit, tps, w);
+    } else
       hipLaunchKernelGGL(mla_wide_kernel<1>, grid, dim3(kWideThreads), dyn, s, a, nsplit, tps, w);
   } else if (a.lat_fmt == 0) {
     if (a.q_fmt == 0) launch_mla_t<0, 0>(a, nsplit, tps, w, s); else launch_mla_t<0, 1>(a, nsplit, tps, w, s);
