@@ -28,6 +28,8 @@
 // order, so a row's result does not depend on the batch.
 #include <math.h>
 
+#include <type_traits>
+
 #include "dsa_device.hpp"
 #include "dsa_kernels.hpp"
 
@@ -557,7 +559,7 @@ constexpr int kPfLoads = (kPfSub * kPfChunks + 63) / 64;  // 19 wave loads per s
 constexpr int kPfPer = (kPfLoads + 3) / 4;          // 5 per wave (padded to 20)
 constexpr int kPfSlot = 4 * kPfPer * 1024;          // 20 KB
 constexpr int kPfSlots = 6;                         // 120 KB; with P (<= 16 KB) and s_off (16 KB) within 160 KB
-constexpr int kPfAhead = kPfSlots - 1;
+constexpr int kPfAhead = kPfSlots - 2;                // subtiles issued ahead of the one whose softmax runs
 constexpr int kPfMaxSubs = kMaxTps / kPfSub;        // 64
 constexpr int kPfBlocks = kVDim / 32 / 4;           // 32-dim blocks of V per wave: 4
 
@@ -576,9 +578,14 @@ typedef __attribute__((ext_vector_type(2))) int i32x2_t;
 // later LDS read wait for all such loads in flight (it cannot tell ring slots apart), which
 // would expose the gather's full latency each subtile.  Every read of a ring slot is ordered
 // after its loads by an explicit vmcnt wait and a barrier instead.
+// (m0 is set right before its one use here; the compiler also sets it before each of its own
+// uses, so the clobber is harmless)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // 32-bit LDS address of a __shared__ object
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
@@ -591,7 +598,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void mla_prefill_kernel(const MlaArg
   constexpr int LB = 576;
   constexpr int64_t LPB = (int64_t)kPage * LB;
   __shared__ __align__(16) uint8_t s_raw[kPfSlots][kPfSlot];
-  __shared__ __align__(16) u32x4_t s_p[2][NHT][2][64];  // P^T fragments: [subtile & 1][head tile][K-step][lane]
+  __shared__ __align__(16) u32x4_t s_p[2][4][2][64];  // P^T fragments: [subtile & 1][wave][K-step][lane]
   __shared__ float s_l[NHT * 32];                    // row sums, for the PV waves' outputs
   __shared__ uint32_t s_ok[kPfMaxSubs];  // valid tokens of each subtile
   __shared__ int s_redo;                 // some head's max passed its reference by > 2^64
@@ -678,19 +685,6 @@ __global__ __launch_bounds__(kPfThreads, 1) void mla_prefill_kernel(const MlaArg
       lds_dma16(a.pool + (ok ? offs[i] + 16 * c : 0), slot_lds + 1024 * i);
     }
   };
-  // wait until this wave's loads of a subtile have landed, `later` subtiles issued after it
-  // still flying (kPfPer loads per subtile, in order)
-  auto wait_later = [&](int later) {
-    switch (later) {
-      case 0: wait_vm<0>(); break;
-      case 1: wait_vm<kPfPer>(); break;
-      case 2: wait_vm<2 * kPfPer>(); break;
-      case 3: wait_vm<3 * kPfPer>(); break;
-      default: wait_vm<4 * kPfPer>(); break;
-    }
-  };
-  static_assert(kPfAhead - 1 <= 4, "the wait ladder covers up to four later subtiles");
-
   // lane rho of the K operand reads slot row pi(rho); S^T element e of half g is token
   // 16 (e / 8) + 8 g + e % 8
   const int krow = 16 * (n >> 4) + 8 * ((n >> 2) & 1) + 4 * ((n >> 3) & 1) + (n & 3);
@@ -710,12 +704,11 @@ __global__ __launch_bounds__(kPfThreads, 1) void mla_prefill_kernel(const MlaArg
     for (int t = 0; t < NHT; ++t)
 #pragma unroll
       for (int db = 0; db < kPfBlocks; ++db) o[t][db] = f32x16_t{};
-    for (int s = 0; s < kPfAhead && s < n_sub; ++s) issue(s);
-    // S^T of one subtile (head tile wid) on FP8: rows = the subtile's 32 tokens (permuted),
+    // S^T of subtile j (head tile wid) on FP8: rows = the subtile's 32 tokens (permuted),
     // columns = 32 heads; 9 MFMAs over the slot's rows
-    auto qk = [&](const uint8_t *ks) {
+    auto qk = [&](int j) {
       f32x16_t acc = {};
-      const uint8_t *kr = ks + krow * kPfRow + 32 * g;
+      const uint8_t *kr = s_raw[j % kPfSlots] + krow * kPfRow + 32 * g;
 #pragma unroll
       for (int s = 0; s < 9; ++s) {
         const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(kr + 64 * s);
@@ -725,69 +718,48 @@ __global__ __launch_bounds__(kPfThreads, 1) void mla_prefill_kernel(const MlaArg
       }
       return acc;
     };
+    // softmax of subtile j from its S^T: running max, p = 2^(S c2 - m_ref) rounded to bf16 in
+    // pairs, the row sum of the rounded values (a bf16 dot product with ones), and P^T to LDS.
+    // okm: the subtile's valid tokens (an invalid token's p is 0; with okm = 0 the call changes
+    // nothing but its P buffer).  Before the head's first valid token m_ref is -inf and every
+    // token of the subtile is invalid.
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-    f32x16_t sacc = {};
-    if (n_sub > 0) {
-      wait_later(min(n_sub - 1, kPfAhead - 1));
-      __syncthreads();  // subtile 0 has landed
-      if (computes) sacc = qk(s_raw[0]);
-    }
-    // Software pipeline: the MFMAs of subtile it + 1's logits are issued before subtile it's
-    // P.V, so the softmax of a subtile never waits on its logits' MFMA chain.
-    for (int it = 0; it < n_sub; ++it) {
-      const uint8_t *slot = s_raw[it % kPfSlots];
-      if (computes) {
-        const uint32_t okm = s_ok[it];  // uniform
-        float z[16];
-        if (okm == 0xFFFFFFFFu) {
+    auto softmax = [&](const f32x16_t &acc, int j, uint32_t okm) {
+      // this lane's 16 tokens 16 (e / 8) + 8 g + e % 8 as bits e of m16
+      const uint32_t m16 = ((okm >> (8 * g)) & 0xFFu) | ((okm >> (8 + 8 * g)) & 0xFF00u);
+      float z[16];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) z[e] = sacc[e] * c2;
-        } else {
+      for (int e = 0; e < 16; ++e) z[e] = ((m16 >> e) & 1u) ? acc[e] * c2 : -INFINITY;
+      float mx = -INFINITY;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int tok = 16 * (e >> 3) + 8 * g + (e & 7);
-            z[e] = ((okm >> tok) & 1u) ? sacc[e] * c2 : -INFINITY;
-          }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(z[e], z[e + 1]));
-        {  // max with the other half-wave (lanes l and l ^ 32 hold the same head)
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
-          mx = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
-        }
-        if (m_ref == -INFINITY) m_ref = mx;  // the head's first valid tokens: O and l are still 0
-        m_true = fmaxf(m_true, mx);
-        over |= mx > m_ref + kRefSlack;
-        // p = 2^(z - m_ref), rounded to bf16 in pairs; the row sum adds the rounded values (a
-        // bf16 dot product with ones).  Invalid tokens (z = -inf) give 0, and so does a subtile
-        // before the head's first valid token (m_ref is still -inf and every z is -inf).
-        const float mr = m_ref == -INFINITY ? 0.0f : m_ref;
-        float ls = 0.0f;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          u32x4_t pk;
-#pragma unroll
-          for (int m2 = 0; m2 < 4; ++m2) {
-            const f32x2_t pp = {__builtin_amdgcn_exp2f(z[8 * s2 + 2 * m2] - mr),
-                                __builtin_amdgcn_exp2f(z[8 * s2 + 2 * m2 + 1] - mr)};
-            const bf16x2_t pb = __builtin_convertvector(pp, bf16x2_t);
-            pk[m2] = __builtin_bit_cast(uint32_t, pb);
-            ls = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, ls, false);
-          }
-          s_p[it & 1][wid][s2][lane] = pk;
-        }
-        l_run += ls;
+      for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(z[e], z[e + 1]));
+      {  // max with the other half-wave (lanes l and l ^ 32 hold the same head)
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
+        mx = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
       }
-      if (it + 1 < n_sub) wait_later(min(n_sub - 2 - it, kPfAhead - 2));
-      // P of subtile it is in LDS; subtile it + 1 has landed; every wave is done with subtile
-      // it - 1, its slot and its P buffer
-      __syncthreads();
-      if (it + kPfAhead < n_sub) issue(it + kPfAhead);  // into the slot of it - 1
-      __builtin_amdgcn_sched_barrier(0);
-      if (computes && it + 1 < n_sub) sacc = qk(s_raw[(it + 1) % kPfSlots]);
-      // O^T += V^T P^T over this wave's 4 dim blocks: step st = 4 s2 + db
-      const uint8_t *vb = slot + vofs;
+      if (m_ref == -INFINITY) m_ref = mx;  // the head's first valid tokens: O and l are still 0
+      m_true = fmaxf(m_true, mx);
+      over |= mx > m_ref + kRefSlack;
+      const float mr = m_ref == -INFINITY ? 0.0f : m_ref;
+      float ls = 0.0f;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        u32x4_t pk;
+#pragma unroll
+        for (int m2 = 0; m2 < 4; ++m2) {
+          const f32x2_t pp = {__builtin_amdgcn_exp2f(z[8 * s2 + 2 * m2] - mr),
+                              __builtin_amdgcn_exp2f(z[8 * s2 + 2 * m2 + 1] - mr)};
+          const bf16x2_t pb = __builtin_convertvector(pp, bf16x2_t);
+          pk[m2] = __builtin_bit_cast(uint32_t, pb);
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, ls, false);
+        }
+        s_p[j & 1][wid][s2][lane] = pk;
+      }
+      l_run += ls;
+    };
+    // O^T += V^T P^T of subtile j over this wave's 4 dim blocks: step st = 4 s2 + db
+    auto pv = [&](int j) {
+      const uint8_t *vb = s_raw[j % kPfSlots] + vofs;
       i32x2_t xv[8];
 #pragma unroll
       for (int st = 0; st < 8; ++st)
@@ -797,7 +769,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void mla_prefill_kernel(const MlaArg
       for (int s2 = 0; s2 < 2; ++s2) {
         bf16x8_t pt[NHT];
 #pragma unroll
-        for (int t = 0; t < NHT; ++t) pt[t] = __builtin_bit_cast(bf16x8_t, s_p[it & 1][t][s2][lane]);
+        for (int t = 0; t < NHT; ++t) pt[t] = __builtin_bit_cast(bf16x8_t, s_p[j & 1][t][s2][lane]);
 #pragma unroll
         for (int db = 0; db < kPfBlocks; ++db) {
           const bf16x8_t va = e4m3x8_bf16((uint32_t)xv[4 * s2 + db][0], (uint32_t)xv[4 * s2 + db][1]);
@@ -805,12 +777,49 @@ __global__ __launch_bounds__(kPfThreads, 1) void mla_prefill_kernel(const MlaArg
           for (int t = 0; t < NHT; ++t) o[t][db] = mfma_32x32x16_bf16(va, pt[t], o[t][db]);
         }
       }
-      // O lives in the accumulator registers across subtiles (without this the loop-carried
-      // values are kept in VGPRs and copied around every MFMA)
+    };
+
+    // Pipeline over subtiles: iteration it runs P.V of subtile it - 1, the logits of it + 1,
+    // the softmax of it and the loads of it + kPfAhead, all in one basic block, so that the
+    // softmax and the load issue run between the matrix-core instructions.  P of it - 1 was
+    // published by the barrier that ends iteration it - 1, subtile it + 1 landed before it, and
+    // the logits of it were formed in iteration it - 1.  Every wave runs the same code: a wave
+    // past the last head tile forms logits of zero queries and its softmax output is not used.
+    // Past the last subtile the logits are formed from whatever a slot holds and discarded, the
+    // softmax sees no valid token, and the loads read the pool's first bytes into a free slot,
+    // so that every iteration issues the same loads and the wait counts stay fixed.
+    // Slots in use during iteration it: it - 1 .. it + kPfAhead (six); P buffers it & 1
+    // (written) and (it - 1) & 1 (read).
+    if (n_sub > 0) {
+      for (int s = 0; s < kPfAhead; ++s) issue(s);
+      wait_vm<(kPfAhead - 2) * kPfPer>();  // subtiles 0 and 1 have landed
+      __syncthreads();
+      f32x16_t acc = qk(0);
+      {  // iteration 0: no P.V yet
+        const f32x16_t an = qk(1);
+        softmax(acc, 0, s_ok[0]);
+        issue(kPfAhead);
+        acc = an;
+      }
+      for (int it = 1;; ++it) {
+        wait_vm<(kPfAhead - 2) * kPfPer>();  // subtile it + 1 has landed (all but the last two subtiles issued)
+        // P of subtile it - 1 is in LDS; every wave is done with subtile it - 2, its slot and
+        // its P buffer
+        __syncthreads();
+        pv(it - 1);
+        const f32x16_t an = qk(it + 1);
+        softmax(acc, it, it < n_sub ? s_ok[it] : 0u);
+        issue(it + kPfAhead);
+        acc = an;
+        // O lives in the accumulator registers across subtiles (without this the loop-carried
+        // values are kept in VGPRs and copied around every MFMA)
 #pragma unroll
-      for (int t = 0; t < NHT; ++t)
+        for (int t = 0; t < NHT; ++t)
 #pragma unroll
-        for (int db = 0; db < kPfBlocks; ++db) asm volatile("" : "+a"(o[t][db]));
+          for (int db = 0; db < kPfBlocks; ++db) asm volatile("" : "+a"(o[t][db]));
+        if (it == n_sub) break;
+      }
+      wait_vm<0>();  // no load into the ring still in flight
     }
     if (computes && __ballot(over) != 0 && lane == 0) s_redo = 1;
     __syncthreads();
