@@ -541,10 +541,10 @@ __global__ __launch_bounds__(kWideThreads) void mla_wide_kernel(const MlaArgs a,
 // K operand's lanes read their rows in that order), so lane half p's elements 8 s2 .. 8 s2+7
 // are the 8 consecutive tokens 16 s2 + 8 p .. + 7 -- the K order of one transposing read, and
 // S^T's lane layout is already the B layout of P^T.
-// Gather: rows go straight to LDS by direct loads into a ring of subtile slots, five subtiles
-// ahead of the one being used.  Per subtile, one barrier frees the oldest slot and a second
-// one publishes P.  Rows sit 592 B apart in a slot, which spreads the 16 rows of one K read
-// over distinct banks.
+// Gather: rows go straight to LDS by direct loads into a ring of six subtile slots, four
+// subtiles ahead of the one whose softmax runs; one barrier per subtile both frees the oldest
+// slot and publishes P (the pipeline is described at the loop).  Rows sit 592 B apart in a
+// slot, which spreads the 16 rows of one K read over distinct banks.
 // Softmax reference: p = 2^(z - m_ref) with m_ref fixed at the head's max over its first
 // subtile with a valid token, so the accumulators are never rescaled.  O / l and
 // m_ref + log2 l do not depend on the reference, and p <= 2^64 keeps p (bf16), l and O (fp32)
@@ -558,8 +558,8 @@ constexpr int kPfChunks = kPfRow / 16;              // 37 16-byte chunks, the la
 constexpr int kPfLoads = (kPfSub * kPfChunks + 63) / 64;  // 19 wave loads per subtile
 constexpr int kPfPer = (kPfLoads + 3) / 4;          // 5 per wave (padded to 20)
 constexpr int kPfSlot = 4 * kPfPer * 1024;          // 20 KB
-constexpr int kPfSlots = 6;                         // 120 KB; with P (<= 16 KB) and s_off (16 KB) within 160 KB
-constexpr int kPfAhead = kPfSlots - 2;                // subtiles issued ahead of the one whose softmax runs
+constexpr int kPfSlots = 6;                         // 120 KB; with P (16 KB) and s_off (16 KB) within 160 KB
+constexpr int kPfAhead = kPfSlots - 2;              // subtiles issued ahead of the one whose softmax runs
 constexpr int kPfMaxSubs = kMaxTps / kPfSub;        // 64
 constexpr int kPfBlocks = kVDim / 32 / 4;           // 32-dim blocks of V per wave: 4
 
@@ -811,6 +811,13 @@ __global__ __launch_bounds__(kPfThreads, 1) void mla_prefill_kernel(const MlaArg
         softmax(acc, it, it < n_sub ? s_ok[it] : 0u);
         issue(it + kPfAhead);
         acc = an;
+        // interleave: each of the 33 MFMAs (24 P.V, 9 logits) followed by up to 12 VALU
+        // instructions (softmax, decode of V, load addresses); measured best of 6-12
+#pragma unroll
+        for (int q = 0; q < 33; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+        }
         // O lives in the accumulator registers across subtiles (without this the loop-carried
         // values are kept in VGPRs and copied around every MFMA)
 #pragma unroll
