@@ -75,6 +75,9 @@ def lib():
         L.or_indexer_score.argtypes = [C.POINTER(OrLayout), I64, P, I64, P, I64, P, I64, P, I64, P, P, P,
                                        P, I64, P, I64, P]
         L.or_topk.argtypes = [P, I64, P, I64, I64, P, I64]
+        L.or_bf16_round.restype = D
+        L.or_bf16_round.argtypes = [C.c_float]
+        L.or_dcp_topk.argtypes = [P, I64, P, I64, I64, I64, P, I64, P]
         L.or_sparse_mla.argtypes = [C.POINTER(OrLayout), I64, P, I64, P, I64, P, P, I64, P, I64, I64, P, I64,
                                     P, P, I64, I64, D, D, P, P, P]
         _lib = L
@@ -196,6 +199,25 @@ def topk(scores, row_len, k: int) -> np.ndarray:
     if rc != OK:
         raise ValueError("or_topk failed: %d" % rc)
     return out
+
+
+def bf16_round(x: float) -> float:
+    """x (as fp32) rounded to the nearest BF16 value, ties to even (normal range)."""
+    return lib().or_bf16_round(float(x))
+
+
+def dcp_topk(scores, row_len, k: int, n_shards: int):
+    """Outcome of the exact top-k merge across n_shards decode-context-parallel shards
+    (token t on shard t mod n_shards): (idx [n_rows][k] ascending, -1 padded, under the
+    order BF16(score) desc then index asc; resend [n_rows] bit mask of flagged shards)."""
+    s = _np(scores, np.float32)
+    rl = _np(row_len, np.int32)
+    out = np.zeros((s.shape[0], k), np.int32)
+    rs = np.zeros(s.shape[0], np.uint32)
+    rc = lib().or_dcp_topk(_p(s), s.shape[1], _p(rl), s.shape[0], k, n_shards, _p(out), k, _p(rs))
+    if rc != OK:
+        raise ValueError("or_dcp_topk failed: %d" % rc)
+    return out, rs
 
 
 def sparse_mla(oc: OracleCache, idx, q, q_fmt: int, q_scale, q_req, n_heads: int, sm_scale: float,
