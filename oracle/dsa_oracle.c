@@ -426,11 +426,13 @@ int or_dcp_topk(const float *scores, int64_t ld, const int32_t *row_len, int64_t
     }
     qsort_r(order, (size_t)len, sizeof(int32_t), cmp_dval_desc_idx_asc, (void *)v);
     const int64_t keep = k < len ? k : len;
-    /* shard s's c-th best token is its c-th token met along the global order */
+    /* shard s's c-th best token is its c-th token met along the global order; a shard
+     * with at most c tokens sent them all and is never flagged */
     int64_t seen[32] = {0};
     for (int64_t p = 0; p < len; ++p) {
       const int64_t sh = order[p] % W;
-      if (++seen[sh] == c && p < keep) resend[r] |= 1u << sh;
+      const int64_t held = (len - 1 - sh) / W + 1; /* tokens of shard sh in the row */
+      if (++seen[sh] == c && p < keep && held > c) resend[r] |= 1u << sh;
     }
     qsort(order, (size_t)keep, sizeof(int32_t), cmp_int_asc);
     for (int64_t i = 0; i < k; ++i) out[i] = i < keep ? order[i] : -1;

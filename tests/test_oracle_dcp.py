@@ -100,6 +100,11 @@ def test_resend_closed_forms():
     s = np.where(np.arange(L) % w == 3, 1.0, 0.5).astype(np.float32)[None, :]
     idx, rs = oracle.dcp_topk(s, np.array([L], np.int32), k, w)
     assert np.array_equal(idx[0], 3 + w * np.arange(k)) and rs[0] == 1 << 3
+    # every shard holds exactly c = 1 token (k = 1, W = 8, three tokens): shards that sent all
+    # their tokens are never flagged, even when their last one is kept
+    s3 = np.array([[0.1, 0.5, 0.9]], np.float32)
+    idx, rs = oracle.dcp_topk(s3, np.array([3], np.int32), 1, w)
+    assert idx[0][0] == 2 and rs[0] == 0
     # fewer tokens than k: everything kept, nobody flagged
     idx, rs = oracle.dcp_topk(s, np.array([100], np.int32), k, w)
     assert np.array_equal(idx[0][:100], np.arange(100)) and (idx[0][100:] == -1).all() and rs[0] == 0
