@@ -13,6 +13,8 @@
  *   3. dsa_topk               the 2048 best tokens kept per query row
  *   4. dsa_sparse_mla_decode / dsa_sparse_mla_prefill
  *                             exact MLA attention over only those tokens
+ * and, for decode context parallelism emulated on one GPU:
+ *   dsa_dcp_topk              the exact top-k merge across token shards
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -210,6 +212,30 @@ dsa_status dsa_sparse_mla_prefill(const dsa_layout *layout, const uint8_t *pool,
                                   const float *q_scale, const int32_t *q_req, int32_t n_q, int32_t n_heads,
                                   float sm_scale, float kv_scale, uint16_t *out, float *lse, void *workspace,
                                   size_t workspace_bytes, int32_t *err_flag, dsa_stream_t stream);
+
+/* Exact top-k merge across decode-context-parallel shards, emulated on one GPU
+ * ([ZH] "长上下文：带稀疏 indexer 的 decode 上下文并行": shard s of W holds every
+ * W-th token, t mod W = s; "流量减少 10× 的精确 top-k 合并": each shard sends
+ * its best ceil(1.5 k / W) candidates taken from BF16 scores, each packed with
+ * its score into 32 bits; the same radix select over the gathered candidates
+ * gives the global top-k; a shard that held more of it than it sent resends
+ * its full local top-k for the row).
+ * Output idx[r][0..k): the min(k, row_len[r]) tokens first in the order
+ * (BF16 of the score, round to nearest even, descending; token index
+ * ascending), in ascending token order, then -1.  resend_mask[r] (optional,
+ * device uint32): bit s set when shard s had to resend for row r.  Four
+ * launches (candidates, merge, resend, merge of resent rows), all on `stream`.
+ *   scores  device fp32 [n_rows][ld]; row_len device int32 [n_rows]
+ *   idx     device int32 [n_rows][idx_ld] (out), idx_ld >= k
+ *   workspace  device, >= dsa_dcp_topk_workspace_size(n_rows, k, n_shards)
+ *              bytes, 16-B aligned
+ * 1 <= n_shards <= 8, 1 <= k <= 2048, ld <= 65536 * n_shards (each shard's
+ * local token index fits the 16 bits of a packed candidate), else
+ * DSA_ERR_UNSUPPORTED. */
+dsa_status dsa_dcp_topk_workspace_size(int32_t n_rows, int32_t k, int32_t n_shards, size_t *bytes);
+dsa_status dsa_dcp_topk(const float *scores, int64_t ld, const int32_t *row_len, int32_t n_rows, int32_t k,
+                        int32_t n_shards, int32_t *idx, int64_t idx_ld, uint32_t *resend_mask, void *workspace,
+                        size_t workspace_bytes, int32_t *err_flag, dsa_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -69,6 +69,8 @@ def _load():
         "dsa_sparse_mla_decode_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
         "dsa_sparse_mla_decode": ([LP, P, I64, P, I64, P, P, I64, I32, P, I32, I32, F, F, P, P, P, SZ, P, P], I32),
         "dsa_sparse_mla_prefill_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
+        "dsa_dcp_topk_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
+        "dsa_dcp_topk": ([P, I64, P, I32, I32, I32, P, I64, P, P, SZ, P, P], I32),
         "dsa_sparse_mla_prefill": ([LP, P, I64, P, I64, I32, P, P, I64, I32, P, I32, P, P, I32, I32, F, F, P, P, P,
                                     SZ, P, P], I32),
     }
@@ -213,6 +215,22 @@ def dsa_sparse_mla_prefill(layout: dsa_layout, pool, lat_off, n_req: int, ctx_le
                                     n_q, n_heads, float(sm_scale), float(kv_scale), _ptr(out, BF16, "out"),
                                     _ptr(lse, F32, "lse"), wp, wb, _ptr(err_flag, I32, "err_flag"), _stream(stream))
     _check("dsa_sparse_mla_prefill", st)
+
+
+def dsa_dcp_topk_workspace_size(n_rows: int, k: int, n_shards: int) -> int:
+    out = C.c_size_t()
+    _check("dsa_dcp_topk_workspace_size", lib.dsa_dcp_topk_workspace_size(n_rows, k, n_shards, C.byref(out)))
+    return out.value
+
+
+def dsa_dcp_topk(scores, row_len, k: int, n_shards: int, idx, workspace, resend_mask=None, err_flag=None,
+                 stream=None):
+    st = lib.dsa_dcp_topk(_ptr(scores, F32, "scores"), scores.shape[1], _ptr(row_len, I32, "row_len"),
+                          scores.shape[0], k, n_shards, _ptr(idx, I32, "idx"), idx.shape[1],
+                          _ptr(resend_mask, (torch.int32, torch.uint32), "resend_mask"),
+                          _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+                          _ptr(err_flag, I32, "err_flag"), _stream(stream))
+    _check("dsa_dcp_topk", st)
 
 
 from .step import DecodeStep, PrefillStep  # noqa: E402,F401

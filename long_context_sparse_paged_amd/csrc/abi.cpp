@@ -198,6 +198,44 @@ dsa_status dsa_topk(const float *scores, int64_t ld, const int32_t *row_len, int
   return launched(launch_topk(a, stream_of(stream)));
 }
 
+dsa_status dsa_dcp_topk_workspace_size(int32_t n_rows, int32_t k, int32_t n_shards, size_t *bytes) {
+  if (!bytes) return DSA_ERR_NULL_ARG;
+  if (n_rows < 0 || k < 1 || n_shards < 1) return DSA_ERR_BAD_SHAPE;
+  if (k > kDcpMaxK || n_shards > kDcpMaxShards) return DSA_ERR_UNSUPPORTED;
+  *bytes = dcp_workspace_bytes(n_rows, k, n_shards);
+  return DSA_OK;
+}
+
+dsa_status dsa_dcp_topk(const float *scores, int64_t ld, const int32_t *row_len, int32_t n_rows, int32_t k,
+                        int32_t n_shards, int32_t *idx, int64_t idx_ld, uint32_t *resend_mask, void *workspace,
+                        size_t workspace_bytes, int32_t *err_flag, dsa_stream_t stream) {
+  size_t need;
+  dsa_status st = dsa_dcp_topk_workspace_size(n_rows, k, n_shards, &need);
+  if (st != DSA_OK) return st;
+  if (ld < 0 || idx_ld < k) return DSA_ERR_BAD_SHAPE;
+  if (ld > (int64_t)65536 * n_shards) return DSA_ERR_UNSUPPORTED;
+  if (n_rows == 0) return DSA_OK;
+  if (!scores || !row_len || !idx || !workspace) return DSA_ERR_NULL_ARG;
+  if (n_rows > kMaxGridY) return DSA_ERR_UNSUPPORTED;
+  if (!aligned(scores, 4) || !aligned(row_len, 4) || !aligned(idx, 4) || !aligned(resend_mask, 4) ||
+      !aligned(workspace, 16) || !aligned(err_flag, 4))
+    return DSA_ERR_MISALIGNED;
+  if (workspace_bytes < need) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  DcpArgs a;
+  a.scores = scores;
+  a.ld = ld;
+  a.row_len = row_len;
+  a.n_rows = n_rows;
+  a.k = k;
+  a.n_shards = n_shards;
+  a.idx = idx;
+  a.idx_ld = idx_ld;
+  a.resend_mask = resend_mask;
+  a.ws = workspace;
+  a.err = err_flag;
+  return launched(launch_dcp_topk(a, stream_of(stream)));
+}
+
 static dsa_status mla_common(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
                              const int64_t *lat_off, int64_t off_ld, int32_t n_req, const int32_t *ctx_len,
                              const int32_t *idx, int64_t idx_ld, int32_t k, const void *q, int32_t q_fmt,

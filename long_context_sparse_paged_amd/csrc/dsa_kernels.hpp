@@ -87,4 +87,22 @@ struct MlaArgs {
 size_t mla_workspace_bytes(int32_t n_q, int32_t n_heads, int32_t k, int32_t tokens_per_split);
 hipError_t launch_mla(const MlaArgs &a, hipStream_t s);
 
+// Exact top-k merge across emulated decode-context-parallel shards.
+constexpr int kDcpMaxShards = 8;
+constexpr int kDcpMaxK = 2048;
+struct DcpArgs {
+  const float *scores;
+  int64_t ld;
+  const int32_t *row_len;
+  int32_t n_rows, k, n_shards;
+  int32_t *idx;
+  int64_t idx_ld;
+  uint32_t *resend_mask;  // may be NULL
+  void *ws;
+  int32_t *err;
+};
+int32_t dcp_candidates(int32_t k, int32_t n_shards);  // ceil(1.5 k / n_shards)
+size_t dcp_workspace_bytes(int32_t n_rows, int32_t k, int32_t n_shards);
+hipError_t launch_dcp_topk(const DcpArgs &a, hipStream_t s);
+
 }  // namespace dsa

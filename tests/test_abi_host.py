@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(d):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     for n in names:
         assert hasattr(d.lib, n), n
 
@@ -138,6 +138,32 @@ def test_topk_errors(d):
     assert f(*a) == d.DSA_ERR_MISALIGNED
     with pytest.raises(d.DsaError):
         d.dsa_topk_workspace_size(1, 1 << 30, 2048)
+
+
+def test_dcp_topk_errors(d):
+    f = d.lib.dsa_dcp_topk
+    need = d.dsa_dcp_topk_workspace_size(4, 2048, 8)
+    # counts, first candidate lists (c = 384), flags, resend counts and lists
+    assert need >= 4 * 8 * 4 * 2 + 4 * 8 * 384 * 4 + 4 * 4 + 4 * 8 * 2048 * 4
+    args = [FAKE, 131072, FAKE, 4, 2048, 8, FAKE, 2048, None, FAKE, need, None, None]
+    a = list(args); a[5] = 0
+    assert f(*a) == d.DSA_ERR_BAD_SHAPE
+    a = list(args); a[5] = 9
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED
+    a = list(args); a[4] = 4096
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED
+    a = list(args); a[1] = 65536 * 8 + 1   # local index past 16 bits
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED
+    a = list(args); a[7] = 100
+    assert f(*a) == d.DSA_ERR_BAD_SHAPE
+    a = list(args); a[10] = need - 1
+    assert f(*a) == d.DSA_ERR_WORKSPACE_TOO_SMALL
+    a = list(args); a[9] = None
+    assert f(*a) == d.DSA_ERR_NULL_ARG
+    a = list(args); a[8] = C.c_void_p((1 << 20) + 2)
+    assert f(*a) == d.DSA_ERR_MISALIGNED
+    a = list(args); a[3] = 0               # nothing to do
+    assert f(*a) == d.DSA_OK
 
 
 def test_mla_errors(d):
