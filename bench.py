@@ -166,6 +166,7 @@ def main():
         torch.cuda.synchronize()
         per_stage[name] = float(np.mean([a.elapsed_time(b) for a, b in evs_i]))
     assert int(step.err.item()) == 0, "device error flag set"
+    dcp = dcp_merge_timing(d, step, wl, scrub, args.steps) if wl["kind"] == "decode" else None
 
     out = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "scaling": "weak", "vs_baseline": None,
            "data": "synthetic (seeded; N(0,1) keys/latents/queries quantised to the cache formats)"}
@@ -189,6 +190,7 @@ def main():
                        "latent_format": ["fp8_e4m3 (576 B)", "nvfp4 (352 B)"][wl["lat_fmt"]], "page_tokens": 64,
                        "pool_rows": cache.pool_rows, "scrub_between_steps_bytes": 4 * scrub_src.numel()},
             "stage_us": {n: round(v * 1e3, 2) for n, v in per_stage.items()},
+            "dcp_merge": dcp,
             "roofline": {"kernel": "indexer_scan (dsa_indexer_score, bf16 queries)", "bound": "hbm",
                          "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_launch": key_bytes,
@@ -219,6 +221,41 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cache, step, wl, ctx, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def dcp_merge_timing(d, step, wl, scrub, steps, n_shards=8):
+    """The exact top-k merge across n_shards emulated decode-context-parallel shards
+    (dsa_dcp_topk) on the step's scores: its time per launch set (HIP events, after a
+    scrub), the candidate bytes one row puts on the wire against a merge that sends every
+    shard's full top-k as (fp32 score, int32 id), and the rows that needed a resend."""
+    import numpy as np
+    import torch
+    n, ld = step.scores.shape
+    k = wl["topk"]
+    if ld > 65536 * n_shards:
+        return None
+    ws = torch.empty(max(d.dsa_dcp_topk_workspace_size(n, k, n_shards), 16), dtype=torch.uint8, device="cuda")
+    idx = torch.empty(n, k, dtype=torch.int32, device="cuda")
+    rs = torch.zeros(n, dtype=torch.int32, device="cuda")
+    step.run()
+    evs = []
+    for i in range(steps + 1):
+        scrub()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        d.dsa_dcp_topk(step.scores, step.row_len, k, n_shards, idx, ws, rs, step.err)
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    c = (3 * k + 2 * n_shards - 1) // (2 * n_shards)
+    mask = rs.cpu().numpy().astype(np.uint32)
+    resent = int(sum(bin(int(m)).count("1") for m in mask))
+    sent = n_shards * c * 4
+    generic = n_shards * k * 8
+    return {"shards": n_shards, "us": round(float(np.mean([a.elapsed_time(b) for a, b in evs[1:]])) * 1e3, 2),
+            "candidates_per_shard": c, "candidate_bytes_per_row": sent, "generic_bytes_per_row": generic,
+            "traffic_ratio": round(generic / sent, 2), "rows_with_resend": int((mask != 0).sum()),
+            "resent_lists": resent}
 
 
 def cpu_baseline(cache, step, wl, ctx, budget_s):

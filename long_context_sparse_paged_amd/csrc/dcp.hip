@@ -16,8 +16,8 @@
 //   merge (row)         gathers the W lists and radix-selects the k-th largest word; words
 //                       equal to it (the same key and local index on several shards) are taken
 //                       in shard order.  Since t = W i + s with s < W, (word desc, shard asc)
-//                       is exactly (key desc, t asc).  A shard that sent c of more tokens and
-//                       whose smallest sent word is kept is flagged; a row without a flag
+//                       is exactly (key desc, t asc).  A shard that holds more than c tokens
+//                       (so it sent c) and whose smallest sent word is kept is flagged; a row without a flag
 //                       writes its output, a flagged row its flags;
 //   local again         flagged (row, shard) pairs only, with k candidates (the resend);
 //   merge again         flagged rows only, with the resent lists in place of the flagged
@@ -31,7 +31,7 @@ namespace dsa {
 
 namespace {
 
-constexpr int kLocThreads = 256;
+constexpr int kLocThreads = 1024;
 constexpr int kMrgThreads = 512;
 constexpr int kMaxCand = kDcpMaxShards * kDcpMaxK;          // 16384 words (64 KB)
 constexpr int kMaxBitWords = kDcpMaxShards * 65536 / 32;    // a row's token bitmap (64 KB)
@@ -77,13 +77,29 @@ __device__ __forceinline__ int row_len_checked(const DcpArgs &a, int r) {
   return len;
 }
 
-// Bin of a 256-bin histogram (h[b], counted over keys with the prefix fixed so far) that holds
-// the rem-th largest key: thread t < 256 owns bin 255 - t, so an inclusive scan over threads is
-// a suffix sum over bins.  Returns the bin and, in `above`, the count in higher bins.
+// 256-bin histograms are kept as kCopies copies (one per lane mod kCopies, kHistLd ints per
+// bin): the keys of one row share their leading bits, and one copy would send most of a
+// wave's atomics to the same address.
+constexpr int kCopies = 16;
+constexpr int kHistLd = kCopies + 1;
+
+__device__ __forceinline__ void hist_clear(int *h, int nt) {
+  for (int q = threadIdx.x; q < 256 * kHistLd; q += nt) h[q] = 0;
+}
+__device__ __forceinline__ void hist_add(int *h, uint32_t bin) {
+  atomicAdd(&h[bin * kHistLd + (threadIdx.x & (kCopies - 1))], 1);
+}
+
+// Bin of a 256-bin histogram (counted over keys with the prefix fixed so far) that holds the
+// rem-th largest key: thread t < 256 owns bin 255 - t, so an inclusive scan over threads is a
+// suffix sum over bins.  Returns the bin and, in `above`, the count in higher bins.
 template <int NT>
 __device__ int find_bin(const int *h, int rem, int *tmp, int *sh, int &above) {
   const int tid = threadIdx.x;
-  const int c = tid < 256 ? h[255 - tid] : 0;
+  int c = 0;
+  if (tid < 256)
+#pragma unroll
+    for (int q = 0; q < kCopies; ++q) c += h[(255 - tid) * kHistLd + q];
   int total;
   const int incl = block_scan_incl<NT>(c, tmp, total);
   if (tid < 256 && incl - c < rem && incl >= rem) {
@@ -98,36 +114,55 @@ __device__ int find_bin(const int *h, int rem, int *tmp, int *sh, int &above) {
 }
 
 // ---- local: one workgroup per (shard, row) ----
+// Workgroup ids go round-robin over the eight XCDs (id mod 8), each with its own L2.  A row's
+// shards read interleaved elements of the same score lines, so all shards of row r get ids
+// congruent to r mod 8: the row is fetched from HBM once, into one L2.
 __global__ __launch_bounds__(kLocThreads) void dcp_local_kernel(const DcpArgs a, DcpWs w, int cap, int resend) {
   constexpr int NT = kLocThreads;
-  __shared__ int s_hist[256];
+  __shared__ uint16_t s_key[65536];  // the shard's keys, local index order
+  __shared__ int s_hist[256 * kHistLd];
   __shared__ int s_tmp[NT / 64];
   __shared__ int s_sh[2];
-  const int s = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int W = a.n_shards;
+  const int m = blockIdx.x >> 3, q = m / W, s = m - q * W, r = (blockIdx.x & 7) + 8 * q;
+  if (r >= a.n_rows) return;                       // uniform
   if (resend && !((w.flag[r] >> s) & 1u)) return;  // uniform
   const int len = row_len_checked(a, r);
   const float *row = a.scores + (int64_t)r * a.ld;
   int32_t *n_out = (resend ? w.n2 : w.n1) + (int64_t)r * kDcpMaxShards + s;
   uint32_t *out = (resend ? w.c2 : w.c1) + ((int64_t)r * kDcpMaxShards + s) * cap;
-  const int ls = len > s ? (len - 1 - s) / W + 1 : 0;  // the shard's tokens in this row
-  auto word = [&](int i) { return (bf16_key(row[(int64_t)W * i + s]) << 16) | (uint32_t)(0xFFFF - i); };
+  const int ls = len > s ? (len - 1 - s) / W + 1 : 0;  // the shard's tokens in this row (<= 65536)
   if (ls <= cap) {  // the shard sends everything
-    for (int i = tid; i < ls; i += NT) out[i] = word(i);
+    for (int i = tid; i < ls; i += NT) out[i] = (bf16_key(row[(int64_t)W * i + s]) << 16) | (uint32_t)(0xFFFF - i);
     if (tid == 0) *n_out = ls;
     return;
+  }
+  // the keys to LDS, 16 loads in flight per thread
+  for (int i0 = 0; i0 < ls; i0 += 16 * NT) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = i0 + u * NT + tid;
+      v[u] = i < ls ? row[(int64_t)W * i + s] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = i0 + u * NT + tid;
+      if (i < ls) s_key[i] = (uint16_t)bf16_key(v[u]);
+    }
   }
   // the cap-th largest key: two 8-bit radix passes over the 16-bit keys
   int tau = 0, gt = 0;
   for (int pass = 0; pass < 2; ++pass) {
-    for (int b = tid; b < 256; b += NT) s_hist[b] = 0;
-    __syncthreads();
+    hist_clear(s_hist, NT);
+    __syncthreads();  // (the first time also: the keys are in LDS)
     for (int i = tid; i < ls; i += NT) {
-      const uint32_t kk = bf16_key(row[(int64_t)W * i + s]);
+      const uint32_t kk = s_key[i];
       if (pass == 0)
-        atomicAdd(&s_hist[kk >> 8], 1);
+        hist_add(s_hist, kk >> 8);
       else if ((int)(kk >> 8) == tau)
-        atomicAdd(&s_hist[kk & 255u], 1);
+        hist_add(s_hist, kk & 255u);
     }
     __syncthreads();
     int above;
@@ -141,7 +176,7 @@ __global__ __launch_bounds__(kLocThreads) void dcp_local_kernel(const DcpArgs a,
   const int i0 = min(ls, tid * chunk), i1 = min(ls, i0 + chunk);
   int ng = 0, ne = 0;
   for (int i = i0; i < i1; ++i) {
-    const int kk = (int)bf16_key(row[(int64_t)W * i + s]);
+    const int kk = s_key[i];
     ng += kk > tau;
     ne += kk == tau;
   }
@@ -152,9 +187,8 @@ __global__ __launch_bounds__(kLocThreads) void dcp_local_kernel(const DcpArgs a,
   int pos = block_scan_incl<NT>(cs, s_tmp, tot) - cs;
   int eq_seen = 0;
   for (int i = i0; i < i1; ++i) {
-    const uint32_t wd = word(i);
-    const int kk = (int)(wd >> 16);
-    if (kk > tau || (kk == tau && eq_seen++ < take_eq)) out[pos++] = wd;
+    const int kk = s_key[i];
+    if (kk > tau || (kk == tau && eq_seen++ < take_eq)) out[pos++] = ((uint32_t)kk << 16) | (uint32_t)(0xFFFF - i);
   }
   if (tid == 0) *n_out = cap;
 }
@@ -164,7 +198,7 @@ __global__ __launch_bounds__(kMrgThreads) void dcp_merge_kernel(const DcpArgs a,
   constexpr int NT = kMrgThreads;
   __shared__ uint32_t s_w[kMaxCand];
   __shared__ uint32_t s_bits[kMaxBitWords];
-  __shared__ int s_hist[256];
+  __shared__ int s_hist[256 * kHistLd];
   __shared__ int s_tmp[NT / 64];
   __shared__ int s_sh[2];
   __shared__ int s_off[kDcpMaxShards + 1];
@@ -188,34 +222,53 @@ __global__ __launch_bounds__(kMrgThreads) void dcp_merge_kernel(const DcpArgs a,
     return;
   }
   // (1) gather the shards' lists in shard order
+  if (tid < W)
+    s_tie[tid] = ((flagged >> tid) & 1u) ? w.n2[(int64_t)r * kDcpMaxShards + tid] : w.n1[(int64_t)r * kDcpMaxShards + tid];
+  if (tid < kDcpMaxShards) s_min[tid] = 0xFFFFFFFFu;
+  __syncthreads();
   if (tid == 0) {
     int o = 0;
     for (int s = 0; s < W; ++s) {
       s_off[s] = o;
-      o += ((flagged >> s) & 1u) ? w.n2[(int64_t)r * kDcpMaxShards + s] : w.n1[(int64_t)r * kDcpMaxShards + s];
+      o += s_tie[s];  // (s_tie holds the list lengths until the ties are collected)
     }
     s_off[W] = o;
     s_ntie = 0;
     s_flag = 0u;
   }
-  if (tid < kDcpMaxShards) s_min[tid] = 0xFFFFFFFFu;
   __syncthreads();
   const int n = s_off[W];
-  for (int s = 0; s < W; ++s) {
-    const bool re = (flagged >> s) & 1u;
-    const uint32_t *src = re ? w.c2 + ((int64_t)r * kDcpMaxShards + s) * k : w.c1 + ((int64_t)r * kDcpMaxShards + s) * c;
-    for (int j = tid; j < s_off[s + 1] - s_off[s]; j += NT) s_w[s_off[s] + j] = src[j];
+  // one flat pass over all lists, 8 loads in flight per thread
+  for (int j0 = 0; j0 < n; j0 += 8 * NT) {
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u * NT + tid;
+      v[u] = 0u;
+      if (j < n) {
+        int s = 0;
+        while (s + 1 < W && s_off[s + 1] <= j) ++s;
+        const int e = j - s_off[s];
+        v[u] = ((flagged >> s) & 1u) ? w.c2[((int64_t)r * kDcpMaxShards + s) * k + e]
+                                     : w.c1[((int64_t)r * kDcpMaxShards + s) * c + e];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u * NT + tid;
+      if (j < n) s_w[j] = v[u];
+    }
   }
   __syncthreads();
   // (2) the keep-th largest word: four 8-bit radix passes
   uint32_t prefix = 0u, mask = 0u;
   int rem = keep;
   for (int sh = 24; sh >= 0; sh -= 8) {
-    for (int b = tid; b < 256; b += NT) s_hist[b] = 0;
+    hist_clear(s_hist, NT);
     __syncthreads();
     for (int j = tid; j < n; j += NT) {
       const uint32_t x = s_w[j];
-      if ((x & mask) == prefix) atomicAdd(&s_hist[(x >> sh) & 255u], 1);
+      if ((x & mask) == prefix) hist_add(s_hist, (x >> sh) & 255u);
     }
     __syncthreads();
     int above;
@@ -226,13 +279,28 @@ __global__ __launch_bounds__(kMrgThreads) void dcp_merge_kernel(const DcpArgs a,
   }
   const uint32_t tau = prefix;
   const int need_eq = rem;  // words equal to tau to keep, in shard order
-  // (3) words equal to tau (at most one per shard) and each shard's smallest word
-  for (int s = 0; s < W; ++s)
-    for (int j = s_off[s] + tid; j < s_off[s + 1]; j += NT) {
-      const uint32_t x = s_w[j];
-      atomicMin(&s_min[s], x);
-      if (x == tau) s_tie[atomicAdd(&s_ntie, 1)] = s;
+  // (3) words equal to tau (at most one per shard) and each shard's smallest word: per-thread
+  // minima, then a wave minimum per shard, then one LDS atomic per wave and shard
+  uint32_t mn[kDcpMaxShards];
+#pragma unroll
+  for (int s = 0; s < kDcpMaxShards; ++s) mn[s] = 0xFFFFFFFFu;
+#pragma unroll
+  for (int s = 0; s < kDcpMaxShards; ++s) {
+    if (s < W) {
+      for (int j = s_off[s] + tid; j < s_off[s + 1]; j += NT) {
+        const uint32_t x = s_w[j];
+        mn[s] = min(mn[s], x);
+        if (x == tau) s_tie[atomicAdd(&s_ntie, 1)] = s;
+      }
     }
+  }
+#pragma unroll
+  for (int s = 0; s < kDcpMaxShards; ++s) {
+    if (s < W) {
+      const uint32_t m = wave_min_u32(mn[s]);
+      if ((tid & 63) == 0) atomicMin(&s_min[s], m);
+    }
+  }
   __syncthreads();
   // a tied word of shard s is kept iff fewer than need_eq tied words come from lower shards
   auto tie_kept = [&](int s) {
@@ -301,7 +369,7 @@ hipError_t launch_dcp_topk(const DcpArgs &a, hipStream_t st) {
   if (a.n_rows == 0) return hipSuccess;
   const int c = dcp_candidates(a.k, a.n_shards);
   const DcpWs w = dcp_carve(a.ws, a.n_rows, c, a.k);
-  const dim3 lg(a.n_shards, a.n_rows);
+  const dim3 lg(8 * ((a.n_rows + 7) / 8) * a.n_shards);
   hipLaunchKernelGGL(dcp_local_kernel, lg, dim3(kLocThreads), 0, st, a, w, c, 0);
   hipLaunchKernelGGL(dcp_merge_kernel, dim3(a.n_rows), dim3(kMrgThreads), 0, st, a, w, c, 0);
   hipLaunchKernelGGL(dcp_local_kernel, lg, dim3(kLocThreads), 0, st, a, w, a.k, 1);
