@@ -21,7 +21,12 @@ object is the indexer scan (the dominant kernel): its key bytes per launch over
 its own mean launch time.  cpu_baseline is the CPU oracle on a bounded sample of
 the same workload.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|mixed|long|prefill]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|mixed|long|prefill|verify]
+
+--workload verify is speculative verification on the same 32 x 131,072-token cache: 8 query
+rows per request (DSpark's 7 draft tokens), the indexer reading each key page once for all
+8 rows (dsa_indexer_score_verify); its roofline is the bf16 MFMA peak, because 8 rows of
+32 x 128 products per 132-byte key outrun HBM.
 """
 from __future__ import annotations
 
@@ -40,7 +45,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
 
-WORKLOADS = {"decode": 1, "long": 2, "mixed": 3, "prefill": 4}
+WORKLOADS = {"decode": 1, "long": 2, "mixed": 3, "prefill": 4, "verify": 5}
 
 
 def log(msg):
@@ -106,6 +111,9 @@ def main():
     if wl["kind"] == "decode":
         dq = W.decode_queries(len(ctx), wl["heads"], seed=cfg_id, device=dev)
         step = d.DecodeStep(cache, dq.q_idx, dq.w, dq.q_mla, dq.sm_scale, k=k)
+    elif wl["kind"] == "verify":
+        vq = W.verify_queries(ctx, wl["rows"], wl["heads"], seed=cfg_id, device=dev)
+        step = d.VerifyStep(cache, vq, k=k)
     else:
         pq = W.prefill_queries(wl["prefix"], wl["chunk"], wl["heads"], seed=cfg_id, device=dev)
         step = d.PrefillStep(cache, pq, k=k, q_fmt=d.DSA_Q_FP8_E4M3)
@@ -196,6 +204,33 @@ def main():
                          "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_launch": key_bytes,
                          "traffic": traffic},
         })
+    elif wl["kind"] == "verify":
+        m = wl["rows"]
+        alg = W.algorithmic_verify_bytes(ctx, m, kb, lb, k)
+        key_bytes = sum(ctx) * kb
+        rl = vq.row_len.cpu().numpy().astype(np.int64)
+        flop_idx = int(rl.sum()) * 32 * 128 * 2
+        gbs = alg / (step_ms * 1e-3) / 1e9
+        score_ms = per_stage["score"]
+        tf = flop_idx / (score_ms * 1e-3) / 1e12
+        out.update({
+            "metric": f"us/layer-step & HBM GB/s, DSA speculative-verify decode ({wl['name']}), one MI355X",
+            "value": round(gbs, 1), "unit": "GB/s", "higher_is_better": True,
+            "ms_per_step": round(step_ms, 4), "us_per_layer_step": round(step_ms * 1e3, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "wall_ms_per_step": round(wall / args.steps * 1e3, 3),
+            "algorithmic_bytes": alg, "dtype": "bf16",
+            "config": {"workload": wl["name"], "batch": len(ctx), "rows_per_request": m, "ctx_total": int(sum(ctx)),
+                       "heads": wl["heads"], "topk": k, "key_format": "fp8_e4m3+fp32 scale (132 B)",
+                       "latent_format": "fp8_e4m3 (576 B)", "page_tokens": 64, "pool_rows": cache.pool_rows,
+                       "scrub_between_steps_bytes": 4 * scrub_src.numel()},
+            "stage_us": {n: round(v * 1e3, 2) for n, v in per_stage.items()},
+            "roofline": {"kernel": "indexer_verify (dsa_indexer_score_verify, bf16 MFMA)", "bound": "mfma",
+                         "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / BF16_PEAK_TFLOPS, 4), "flop_per_launch": flop_idx,
+                         "key_bytes_per_launch": key_bytes,
+                         "key_gbs": round(key_bytes / (score_ms * 1e-3) / 1e9, 1),
+                         "traffic": None},
+        })
     else:
         rl = pq.row_len.cpu().numpy().astype(np.int64)
         pairs = int(rl.sum())
@@ -263,6 +298,7 @@ def cpu_baseline(cache, step, wl, ctx, budget_s):
     import numpy as np
 
     import oracle
+    from synth.workloads import algorithmic_verify_bytes as W_verify_bytes
     t0 = time.time()
     oc = oracle.OracleCache(cache)
     log(f"[bench] host copy for the oracle: {time.time() - t0:.1f}s")
@@ -295,6 +331,33 @@ def cpu_baseline(cache, step, wl, ctx, budget_s):
                 break
         return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
                 "sample": f"{done_units} of {len(ctx)} requests (full score + sort + attention each), "
+                          f"{spent:.1f}s: score {t_score:.1f}s, top-k {t_topk:.1f}s, attention {t_mla:.1f}s"}
+    if wl["kind"] == "verify":
+        vq = step.vq
+        m = vq.m
+        q_idx, w, q_mla = vq.q_idx.cpu(), vq.w.cpu(), vq.q_mla.cpu()
+        rl_all = vq.row_len.cpu().numpy()
+        for b in range(len(ctx)):
+            rows = np.arange(b * m, (b + 1) * m)
+            a = time.time()
+            s = oracle.indexer_score(oc, q_idx[b * m:(b + 1) * m], 0, None, w[b * m:(b + 1) * m],
+                                     np.full(m, b, np.int32), rl_all[rows])
+            t1 = time.time()
+            idx = oracle.topk(np.nan_to_num(s, nan=0.0), rl_all[rows], k)
+            t2 = time.time()
+            oracle.sparse_mla(oc, idx, q_mla[b * m:(b + 1) * m], 0, None, np.full(m, b, np.int32), q_mla.shape[1],
+                              vq.sm_scale)
+            t3 = time.time()
+            t_score += t1 - a
+            t_topk += t2 - t1
+            t_mla += t3 - t2
+            spent += t3 - a
+            done_bytes += W_verify_bytes([ctx[b]], m, kb, lb, k)
+            done_units += 1
+            if spent >= budget_s:
+                break
+        return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+                "sample": f"{done_units} of {len(ctx)} requests x {m} rows (full score + sort + attention each), "
                           f"{spent:.1f}s: score {t_score:.1f}s, top-k {t_topk:.1f}s, attention {t_mla:.1f}s"}
     pq = step.pq
     rows = pq.n_q

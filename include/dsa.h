@@ -160,6 +160,29 @@ dsa_status dsa_indexer_score(const dsa_layout *layout, const uint8_t *pool, int6
                              int32_t n_q, float *scores, int64_t ld, void *workspace, size_t workspace_bytes,
                              int32_t *err_flag, dsa_stream_t stream);
 
+/* Indexer score for speculative verification ([ZH] "量化：原生 MXFP4 索引器": while
+ * draft tokens are verified, the keys are reused across the query rows instead of
+ * being read again for each; "低延迟解码：融合的 DSA 解码路径": DSpark verifies 7
+ * draft tokens, 8 rows per request).  Request b owns the rows_per_req consecutive
+ * query rows r = b*rows_per_req + i; each row gets exactly the dsa_indexer_score
+ * (bf16 query) result for q_req[r] = r / rows_per_req, bit for bit, but every
+ * key page is read once for all rows of its request.  Row r scores tokens
+ * t < row_len[r] (for causal verification of m rows at context L:
+ * row_len = L - m + 1 + i).
+ *   pool       device uint8, pool_bytes long, 16-B aligned
+ *   key_off    device int64 [n_req][off_ld] from dsa_resolve_pages
+ *   q          device bf16 [n_req*rows_per_req][32][128], 16-B aligned
+ *   w          device fp32 [n_req*rows_per_req][32]
+ *   row_len    device int32 [n_req*rows_per_req]
+ *   scores     device fp32 [n_req*rows_per_req][ld] (out): entries t < row_len[r]
+ *              written, the rest untouched.
+ * 1 <= rows_per_req <= 8 and n_req <= 1024, else DSA_ERR_UNSUPPORTED.  A row_len
+ * outside [0, min(ld, 64*off_ld)] is clamped and flags DSA_DEVERR_ROW_LEN. */
+dsa_status dsa_indexer_score_verify(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                                    const int64_t *key_off, int64_t off_ld, int32_t n_req, int32_t rows_per_req,
+                                    const uint16_t *q, const float *w, const int32_t *row_len, float *scores,
+                                    int64_t ld, int32_t *err_flag, dsa_stream_t stream);
+
 /* Top-k ([ZH] "K3.1 Pro 中的稀疏注意力": the top 2048 are kept; an exact top-k
  * per "低延迟解码：融合的 DSA 解码路径").  For each row r, the min(k, row_len[r])
  * tokens with the largest scores[r][t]; a tie goes to the lower token index

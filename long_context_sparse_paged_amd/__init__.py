@@ -29,7 +29,7 @@ DSA_Q_BF16, DSA_Q_FP8_E4M3 = 0, 1
 
 __all__ = [
     "DsaError", "dsa_layout", "lib", "dsa_status_str", "dsa_version", "dsa_layout_make", "dsa_resolve_pages",
-    "dsa_indexer_score_workspace_size", "dsa_indexer_score", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_decode_workspace_size",
+    "dsa_indexer_score_workspace_size", "dsa_indexer_score", "dsa_indexer_score_verify", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_decode_workspace_size",
     "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill_workspace_size", "dsa_sparse_mla_prefill",
 ]
 
@@ -64,6 +64,7 @@ def _load():
         "dsa_resolve_pages": ([LP, I32, P, I64, P, I32, I32, I64, P, P, I64, P, P], I32),
         "dsa_indexer_score_workspace_size": ([I32, I32, C.POINTER(SZ)], I32),
         "dsa_indexer_score": ([LP, P, I64, P, I64, I32, P, I32, P, P, P, P, I32, P, I64, P, SZ, P, P], I32),
+        "dsa_indexer_score_verify": ([LP, P, I64, P, I64, I32, I32, P, P, P, P, I64, P, P], I32),
         "dsa_topk_workspace_size": ([I32, I64, I32, C.POINTER(SZ)], I32),
         "dsa_topk": ([P, I64, P, I32, I32, P, I64, P, SZ, P, P], I32),
         "dsa_sparse_mla_decode_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
@@ -157,6 +158,17 @@ def dsa_indexer_score(layout: dsa_layout, pool, key_off, n_req: int, q, q_fmt: i
     _check("dsa_indexer_score", st)
 
 
+def dsa_indexer_score_verify(layout: dsa_layout, pool, key_off, n_req: int, rows_per_req: int, q, w, row_len,
+                             scores, err_flag=None, stream=None):
+    """Rows r = b*rows_per_req + i belong to request b; each key page is read once per request."""
+    st = lib.dsa_indexer_score_verify(C.byref(layout), _ptr(pool, U8, "pool"), pool.numel(),
+                                      _ptr(key_off, I64, "key_off"), key_off.shape[1], n_req, rows_per_req,
+                                      _ptr(q, BF16, "q"), _ptr(w, F32, "w"), _ptr(row_len, I32, "row_len"),
+                                      _ptr(scores, F32, "scores"), scores.shape[1], _ptr(err_flag, I32, "err_flag"),
+                                      _stream(stream))
+    _check("dsa_indexer_score_verify", st)
+
+
 def dsa_topk_workspace_size(n_rows: int, ld: int, k: int) -> int:
     out = C.c_size_t()
     _check("dsa_topk_workspace_size", lib.dsa_topk_workspace_size(n_rows, ld, k, C.byref(out)))
@@ -233,4 +245,4 @@ def dsa_dcp_topk(scores, row_len, k: int, n_shards: int, idx, workspace, resend_
     _check("dsa_dcp_topk", st)
 
 
-from .step import DecodeStep, PrefillStep  # noqa: E402,F401
+from .step import DecodeStep, PrefillStep, VerifyStep  # noqa: E402,F401

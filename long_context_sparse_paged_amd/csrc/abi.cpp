@@ -155,6 +155,36 @@ dsa_status dsa_indexer_score(const dsa_layout *layout, const uint8_t *pool, int6
   return launched(launch_indexer_gemm(a, stream_of(stream)));
 }
 
+dsa_status dsa_indexer_score_verify(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                                    const int64_t *key_off, int64_t off_ld, int32_t n_req, int32_t rows_per_req,
+                                    const uint16_t *q, const float *w, const int32_t *row_len, float *scores,
+                                    int64_t ld, int32_t *err_flag, dsa_stream_t stream) {
+  dsa_status st = check_layout(layout);
+  if (st != DSA_OK) return st;
+  if (n_req < 0 || ld < 0 || off_ld < 1 || pool_bytes < 0 || rows_per_req < 1) return DSA_ERR_BAD_SHAPE;
+  if (rows_per_req > kVerifyMaxRows || n_req > kVerifyMaxReq) return DSA_ERR_UNSUPPORTED;
+  if (n_req == 0) return DSA_OK;
+  if (!pool || !key_off || !q || !w || !row_len || !scores) return DSA_ERR_NULL_ARG;
+  if (!aligned(pool, 16) || !aligned(q, 16) || !aligned(key_off, 8) || !aligned(w, 4) || !aligned(row_len, 4) ||
+      !aligned(scores, 4) || !aligned(err_flag, 4))
+    return DSA_ERR_MISALIGNED;
+  VerifyArgs a;
+  a.pool = pool;
+  a.pool_bytes = pool_bytes;
+  a.key_off = key_off;
+  a.off_ld = off_ld;
+  a.n_req = n_req;
+  a.m = rows_per_req;
+  a.q = q;
+  a.w = w;
+  a.row_len = row_len;
+  a.scores = scores;
+  a.ld = ld;
+  a.err = err_flag;
+  a.key_fmt = layout->key_fmt;
+  return launched(launch_indexer_verify(a, stream_of(stream)));
+}
+
 dsa_status dsa_indexer_score_workspace_size(int32_t n_q, int32_t q_fmt, size_t *bytes) {
   if (!bytes) return DSA_ERR_NULL_ARG;
   if (n_q < 0) return DSA_ERR_BAD_SHAPE;

@@ -43,6 +43,25 @@ hipError_t launch_indexer_scan(const ScoreArgs &a, hipStream_t s);  // bf16 quer
 hipError_t launch_indexer_gemm(const ScoreArgs &a, hipStream_t s);  // e4m3 queries
 size_t indexer_gemm_workspace_bytes(int32_t n_q);
 
+// Speculative-verify decode: m rows per request share each key page read.
+constexpr int kVerifyMaxRows = 8;
+constexpr int kVerifyMaxReq = 1024;
+struct VerifyArgs {
+  const uint8_t *pool;
+  int64_t pool_bytes;
+  const int64_t *key_off;
+  int64_t off_ld;
+  int32_t n_req, m;      // rows r = b*m + i belong to request b
+  const uint16_t *q;     // bf16 [n_req*m][32][128]
+  const float *w;        // [n_req*m][32]
+  const int32_t *row_len;
+  float *scores;
+  int64_t ld;
+  int32_t *err;
+  int32_t key_fmt;
+};
+hipError_t launch_indexer_verify(const VerifyArgs &a, hipStream_t s);
+
 // Top-k: slices of kSlice scores, candidates per slice <= kSliceCap, rows of up to
 // kShortRow scores are selected wholly in LDS.
 constexpr int kSlice = 8192;

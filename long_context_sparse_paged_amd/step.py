@@ -3,13 +3,15 @@
 ``DecodeStep`` / ``PrefillStep`` own the device buffers a step needs (page
 offsets, scores, selected indices, outputs, workspaces) and call
 dsa_resolve_pages -> dsa_indexer_score -> dsa_topk -> dsa_sparse_mla_* on one
-stream.  No arithmetic happens here.
+stream; ``VerifyStep`` does the same for speculative verification, with
+dsa_indexer_score_verify reading each key page once for all rows of a request.
+No arithmetic happens here.
 """
 from __future__ import annotations
 
 import torch
 
-from . import (DSA_Q_BF16, DSA_Q_FP8_E4M3, dsa_indexer_score, dsa_indexer_score_workspace_size, dsa_layout_make, dsa_resolve_pages, dsa_sparse_mla_decode,
+from . import (DSA_Q_BF16, DSA_Q_FP8_E4M3, dsa_indexer_score, dsa_indexer_score_verify, dsa_indexer_score_workspace_size, dsa_layout_make, dsa_resolve_pages, dsa_sparse_mla_decode,
                dsa_sparse_mla_decode_workspace_size, dsa_sparse_mla_prefill, dsa_sparse_mla_prefill_workspace_size,
                dsa_topk, dsa_topk_workspace_size)
 
@@ -112,6 +114,42 @@ class PrefillStep(_Base):
         dsa_sparse_mla_prefill(self.layout, c.pool, self.lat_off, c.n_req, c.ctx_len, self.idx, self.k, q, self.q_fmt,
                                qs, pq.q_req, pq.sm_scale, c.kv_scale, self.out, self.lse, self.ws_mla, self.err,
                                stream)
+
+    def run(self, stream=None):
+        self.resolve(stream)
+        self.score(stream)
+        self.topk(stream)
+        self.attend(stream)
+
+
+class VerifyStep(_Base):
+    """Speculative verification: m query rows per request (row b*m + i at position L_b - m + i,
+    row_len = L_b - m + 1 + i); the indexer reads each key page once for all m rows, then every
+    row gets its own top-k and attention."""
+
+    def __init__(self, cache, vq, k: int = 2048, device="cuda"):
+        n_req = cache.block_table.shape[0]
+        ld = int(cache.ctx_len.max().item()) if n_req else 1
+        super().__init__(cache, k, n_req * vq.m, ld, device)
+        self.vq = vq
+        self.m = vq.m
+        self.n_heads = vq.q_mla.shape[1]
+        self.row_len = vq.row_len
+        self.out = torch.empty(n_req * vq.m, self.n_heads, 512, dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty(n_req * vq.m, self.n_heads, dtype=torch.float32, device=device)
+        nb = dsa_sparse_mla_prefill_workspace_size(n_req * vq.m, self.n_heads, k)
+        self.ws_mla = torch.empty(nb, dtype=torch.uint8, device=device) if nb else None
+
+    def score(self, stream=None):
+        c, vq = self.cache, self.vq
+        dsa_indexer_score_verify(self.layout, c.pool, self.key_off, c.n_req, vq.m, vq.q_idx, vq.w, vq.row_len,
+                                 self.scores, self.err, stream)
+
+    def attend(self, stream=None):
+        c, vq = self.cache, self.vq
+        dsa_sparse_mla_prefill(self.layout, c.pool, self.lat_off, c.n_req, c.ctx_len, self.idx, self.k, vq.q_mla,
+                               DSA_Q_BF16, None, vq.q_req, vq.sm_scale, c.kv_scale, self.out, self.lse, self.ws_mla,
+                               self.err, stream)
 
     def run(self, stream=None):
         self.resolve(stream)

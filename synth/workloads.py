@@ -218,6 +218,34 @@ def prefill_queries(prefix: int, chunk: int, n_heads: int = 96, seed: int = 0, d
                           sm_scale=float(np.float32(1.0 / math.sqrt(LAT_DIM))))
 
 
+@dataclass
+class VerifyQueries:
+    """Speculative verification: m query rows per request (the last accepted token and m-1
+    drafts) at the request's last m positions; row i of request b is row b*m + i."""
+    m: int
+    q_req: torch.Tensor   # int32 [B*m]
+    row_len: torch.Tensor  # int32 [B*m]  causal: L_b - m + 1 + i
+    q_idx: torch.Tensor   # bf16 [B*m, 32, 128]
+    w: torch.Tensor       # fp32 [B*m, 32]
+    q_mla: torch.Tensor   # bf16 [B*m, H, 576]
+    sm_scale: float
+
+
+def verify_queries(ctx_lens, m: int, n_heads: int = 12, seed: int = 0, device="cpu") -> VerifyQueries:
+    """Indexer query bf16 ~ N(0,1), head weights ~ U(0,1)/32, MLA query bf16 ~ N(0,1), per row."""
+    ctx = [int(c) for c in ctx_lens]
+    n = len(ctx) * m
+    g = _gen(seed * 40503 + 17, device)
+    q_idx = torch.randn(n, IDX_HEADS, IDX_DIM, generator=g, device=device).to(torch.bfloat16)
+    w = torch.rand(n, IDX_HEADS, generator=g, device=device) / IDX_HEADS
+    q_mla = torch.randn(n, n_heads, LAT_DIM, generator=g, device=device).to(torch.bfloat16)
+    rl = [max(0, L - m + 1 + i) for L in ctx for i in range(m)]
+    return VerifyQueries(m=m, q_req=torch.arange(n, dtype=torch.int32, device=device) // m,
+                         row_len=torch.tensor(rl, dtype=torch.int32, device=device), q_idx=q_idx,
+                         w=w.float().contiguous(), q_mla=q_mla,
+                         sm_scale=float(np.float32(1.0 / math.sqrt(LAT_DIM))))
+
+
 def loguniform_lengths(n: int, lo: int, hi: int, seed: int) -> list[int]:
     """Context lengths round(exp(U[ln lo, ln hi])), seeded."""
     rng = np.random.default_rng(seed)
@@ -241,6 +269,11 @@ WORKLOADS = {
             key_fmt=1, lat_fmt=1, spare_rows=0, topk=2048, n=64, lo=4096, hi=524288),
     4: dict(name="prefill-2k-on-150k-fp8", kind="prefill", prefix=153600, chunk=2048, heads=96,
             key_fmt=0, lat_fmt=0, spare_rows=0, topk=2048),
+    # speculative verification: DSpark's 7 draft tokens, i.e. 8 query rows per request
+    # (section "低延迟解码：融合的 DSA 解码路径"), each key read once for all 8 rows
+    # (section "量化：原生 MXFP4 索引器"), on the batch-32 / 128K decode shape
+    5: dict(name="verify-b32x8-128k-fp8", kind="verify", ctx=[131072] * 32, rows=8, heads=12, key_fmt=0,
+            lat_fmt=0, spare_rows=0, topk=2048),
 }
 
 
@@ -252,6 +285,13 @@ def workload_ctx(cfg_id: int, seed: int | None = None) -> list[int]:
     if w["ctx"] == "loguniform":
         return loguniform_lengths(w["n"], w["lo"], w["hi"], s)
     return list(w["ctx"])
+
+
+def algorithmic_verify_bytes(ctx_lens, m: int, key_bytes: int, lat_bytes: int, k: int = 2048) -> int:
+    """Verify step with key reuse: each request's keys once, plus every row's selected latents
+    (row i of a request at context L has L - m + 1 + i tokens)."""
+    return int(sum(int(L) * key_bytes + sum(min(k, max(0, int(L) - m + 1 + i)) * lat_bytes for i in range(m))
+                   for L in ctx_lens))
 
 
 def algorithmic_decode_bytes(ctx_lens, key_bytes: int, lat_bytes: int, k: int = 2048) -> int:

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(d):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(d.lib, n), n
 
@@ -119,6 +119,36 @@ def test_score_errors(d):
     assert d.lib.dsa_indexer_score_workspace_size(4, 7, C.byref(out)) == d.DSA_ERR_UNSUPPORTED
     assert d.lib.dsa_indexer_score_workspace_size(4, 1, None) == d.DSA_ERR_NULL_ARG
 
+
+
+def test_score_verify_errors(d):
+    L = d.dsa_layout_make(64, 1, 0, 0, 0)
+    f = d.lib.dsa_indexer_score_verify
+    args = [C.byref(L), FAKE, 1 << 30, FAKE, 16, 2, 8, FAKE, FAKE, FAKE, FAKE, 1024, None, None]
+    a = list(args); a[0] = None
+    assert f(*a) == d.DSA_ERR_NULL_ARG
+    a = list(args); a[7] = None     # q
+    assert f(*a) == d.DSA_ERR_NULL_ARG
+    a = list(args); a[6] = 0        # rows per request
+    assert f(*a) == d.DSA_ERR_BAD_SHAPE
+    a = list(args); a[6] = 9        # more rows than the kernel stages
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED
+    a = list(args); a[5] = 1025     # requests
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED
+    a = list(args); a[5] = -1
+    assert f(*a) == d.DSA_ERR_BAD_SHAPE
+    a = list(args); a[4] = 0        # off_ld
+    assert f(*a) == d.DSA_ERR_BAD_SHAPE
+    a = list(args); a[7] = C.c_void_p((1 << 20) + 8)   # q must be 16-B aligned
+    assert f(*a) == d.DSA_ERR_MISALIGNED
+    a = list(args); a[10] = ODD     # scores
+    assert f(*a) == d.DSA_ERR_MISALIGNED
+    bad = d.dsa_layout_make(64, 1, 0, 0, 0)
+    bad.layer_stride += 256
+    a = list(args); a[0] = C.byref(bad)
+    assert f(*a) == d.DSA_ERR_BAD_SHAPE
+    a = list(args); a[5] = 0        # nothing to do
+    assert f(*a) == d.DSA_OK
 
 def test_topk_errors(d):
     f = d.lib.dsa_topk
