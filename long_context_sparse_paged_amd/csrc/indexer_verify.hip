@@ -12,18 +12,18 @@
 //
 // Rows r = b*m + i (i < m) belong to request b; row r scores tokens t < row_len[r].
 //
-// Work split: a tile is 4 consecutive pages (256 tokens) of one request; the tiles of all
+// Work split: a tile is NW consecutive pages (one per wave) of one request; the tiles of all
 // requests form one list and each workgroup takes an equal contiguous share, so the scan
 // stays key-balanced.  Wave w of the workgroup owns page w of each tile.  The request's m
-// query rows (m x 8 KB bf16) and head weights sit in LDS, shared by the four waves, and are
+// query rows (m x 8 KB bf16) and head weights sit in LDS, shared by the NW waves, and are
 // restaged (between two barriers) only when the workgroup's tile moves to another request.
 // Per page a wave
-//   1. loads the 64 keys with coalesced nontemporal 16-B loads, two pages ahead, and parks
+//   1. loads the 64 keys with coalesced nontemporal 16-B loads, one page ahead, and parks
 //      them in its LDS slot,
 //   2. decodes the B fragments of both 32-token blocks to bf16 once (exact),
-//   3. for each row of the request that reaches the page: 8 + 8 v_mfma_f32_32x32x16_bf16
-//      with A fragments read from LDS, then the weighted ReLU head sum in the accumulator
-//      layout and one 256-byte store of the page's 64 scores.
+//   3. for each row of the request: 8 + 8 v_mfma_f32_32x32x16_bf16 with A fragments read
+//      from LDS one row ahead, then the weighted ReLU head sum in the accumulator layout and
+//      one 256-byte store of the page's 64 scores.
 // The per-row arithmetic (operand order, accumulation order, epilogue) is the same as the
 // one-row scan's, so a row's scores do not depend on which of the two kernels made them.
 #include <math.h>
@@ -34,8 +34,6 @@
 namespace dsa {
 
 namespace {
-
-constexpr int kVWaves = 4;  // pages per tile, one per wave
 
 template <int KEY_FMT>
 struct VKeyRow {
@@ -56,16 +54,18 @@ __device__ __forceinline__ int vrow_length(const VerifyArgs &a, int r, int64_t m
   return len;
 }
 
-template <int KEY_FMT, int MMAX>
-__global__ __launch_bounds__(256, MMAX <= 4 ? 2 : 1) void indexer_verify_kernel(const VerifyArgs a) {
+// NW waves per workgroup, one page each per tile; MMAX = most rows per request staged.
+template <int KEY_FMT, int MMAX, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void indexer_verify_kernel(const VerifyArgs a) {
   using KR = VKeyRow<KEY_FMT>;
-  __shared__ __align__(16) uint8_t s_page[kVWaves][KR::kPageBytes];
+  constexpr int NT = 64 * NW;
+  __shared__ __align__(16) uint8_t s_page[NW][KR::kPageBytes];
   // query rows of the current request: [row][head][16 chunks of 8 dims], chunk c of head j
   // stored at chunk position c ^ (j & 15) so that the A-fragment reads are conflict-free
   __shared__ __align__(16) uint16_t s_q[MMAX][kIdxHeads][kIdxDim];
   __shared__ __align__(16) float s_w[MMAX][kIdxHeads];
   __shared__ int s_len[MMAX];
-  __shared__ int s_tmp[4];
+  __shared__ int s_tmp[NW];
   extern __shared__ int s_dyn[];  // [n_req + 1] first tile of each request, then [n_req] pages
   int *s_start = s_dyn, *s_pages = s_dyn + a.n_req + 1;
 
@@ -73,8 +73,8 @@ __global__ __launch_bounds__(256, MMAX <= 4 ? 2 : 1) void indexer_verify_kernel(
   const int n_req = a.n_req, m = a.m;
   const int64_t max_tok = a.ld < a.off_ld * kPage ? a.ld : a.off_ld * kPage;
 
-  // tiles per request: ceil(pages / 4), pages from the request's longest row
-  const int per = (n_req + 255) / 256;
+  // tiles per request: ceil(pages / NW), pages from the request's longest row
+  const int per = (n_req + NT - 1) / NT;
   const int r0 = min(n_req, tid * per), r1 = min(n_req, r0 + per);
   int mine = 0;
   for (int b = r0; b < r1; ++b) {
@@ -82,13 +82,13 @@ __global__ __launch_bounds__(256, MMAX <= 4 ? 2 : 1) void indexer_verify_kernel(
     for (int i = 0; i < m; ++i) len = max(len, vrow_length(a, b * m + i, max_tok, blockIdx.x == 0));
     const int pg = (len + kPage - 1) / kPage;
     s_pages[b] = pg;
-    mine += (pg + kVWaves - 1) / kVWaves;
+    mine += (pg + NW - 1) / NW;
   }
   int total;
-  int run = block_scan_incl_256(mine, s_tmp, total) - mine;
+  int run = block_scan_incl<NT>(mine, s_tmp, total) - mine;
   for (int b = r0; b < r1; ++b) {
     s_start[b] = run;
-    run += (s_pages[b] + kVWaves - 1) / kVWaves;
+    run += (s_pages[b] + NW - 1) / NW;
   }
   if (tid == 0) s_start[n_req] = total;
   __syncthreads();
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256, MMAX <= 4 ? 2 : 1) void indexer_verify_kernel(
     lane_off = -2;
     if (tt < t_end) {
       const int b = req_of(tt);
-      const int p = kVWaves * (tt - s_start[b]) + wid;
+      const int p = NW * (tt - s_start[b]) + wid;
       if (p < s_pages[b]) lane_off = a.key_off[(int64_t)b * a.off_ld + p];
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // drain on this rare path (vmcnt 0)
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256, MMAX <= 4 ? 2 : 1) void indexer_verify_kernel(
     return ok ? a.pool + off : a.pool;
   };
 
-  u32x4_t b0[KR::kLoadsPerLane], b1[KR::kLoadsPerLane];
+  u32x4_t b0[KR::kLoadsPerLane];
   constexpr int kTail = KR::kChunks - 64 * KR::kFullLoads;
   auto load = [&](u32x4_t (&buf)[KR::kLoadsPerLane], const uint8_t *src) {
     const u32x4_t *p = reinterpret_cast<const u32x4_t *>(src);
@@ -173,12 +173,12 @@ __global__ __launch_bounds__(256, MMAX <= 4 ? 2 : 1) void indexer_verify_kernel(
     __syncthreads();  // every wave has finished with the previous request's rows
     const int nch = m * kIdxHeads * (kIdxDim / 8);
     const u32x4_t *qg = reinterpret_cast<const u32x4_t *>(a.q) + (int64_t)b * nch;
-    for (int i = tid; i < nch; i += 256) {
+    for (int i = tid; i < nch; i += NT) {
       const int g = i >> 9, j = (i >> 4) & 31, c = i & 15;
       const u32x4_t v = qg[i];
       *reinterpret_cast<u32x4_t *>(&s_q[g][j][8 * (c ^ (j & 15))]) = v;
     }
-    for (int i = tid; i < m * kIdxHeads; i += 256) s_w[i >> 5][i & 31] = a.w[(int64_t)b * m * kIdxHeads + i];
+    for (int i = tid; i < m * kIdxHeads; i += NT) s_w[i >> 5][i & 31] = a.w[(int64_t)b * m * kIdxHeads + i];
     if (tid < m) s_len[tid] = vrow_length(a, b * m + tid, max_tok, false);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // drain here, off the common path
     __syncthreads();
@@ -186,12 +186,14 @@ __global__ __launch_bounds__(256, MMAX <= 4 ? 2 : 1) void indexer_verify_kernel(
 
   const int n = lane & 31, h = lane >> 5;
   auto compute = [&](int tt, int b, bool valid) {
+    b = __builtin_amdgcn_readfirstlane(b);
     if (b != cur_b) {
       stage(b);
       cur_b = b;
     }
     if (!valid) return;
-    const int p = kVWaves * (tt - s_start[b]) + wid;
+    // wave-uniform, so that the score stores' buffer descriptors live in scalar registers
+    const int p = __builtin_amdgcn_readfirstlane(NW * (tt - s_start[b]) + wid);
     // B fragments of both 32-token blocks, decoded once for all rows
     bf16x8_t kf[2][8];
     float scale[2];
@@ -222,90 +224,92 @@ __global__ __launch_bounds__(256, MMAX <= 4 ? 2 : 1) void indexer_verify_kernel(
       lo[c2] = scale[c2] < 0.0f ? -INFINITY : 0.0f;
       hi[c2] = scale[c2] < 0.0f ? 0.0f : INFINITY;
     }
-    for (int g = 0; g < m; ++g) {
-      const int rem = __builtin_amdgcn_readfirstlane(s_len[g]) - p * kPage;
-      if (rem <= 0) continue;
+    // Rows one after another, each with its A fragments read from LDS one row ahead, so that
+    // a row's 16 MFMAs issue back to back; the other wave on the SIMD fills the epilogue's
+    // VALU time.  Every row of the request runs its MFMAs; a row that does not reach this page
+    // stores nothing (its buffer range is empty), so the loop body has no branch.
+    auto load_a = [&](int g, bf16x8_t (&qa)[8]) {
       const uint16_t *qrow = &s_q[g][n][0];
-      f32x16_t acc0 = {}, acc1 = {};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qa[s] = *reinterpret_cast<const bf16x8_t *>(qrow + 8 * ((8 * h + s) ^ (n & 15)));
+    };
+    const int tok = 32 * h + n;  // lane (n, h) stores token 32 h + n of the page
+    auto row = [&](int g, const bf16x8_t (&qa)[8]) {
+      f32x16_t c0 = {}, c1 = {};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const bf16x8_t qa = *reinterpret_cast<const bf16x8_t *>(qrow + 8 * ((8 * h + s) ^ (n & 15)));
-        acc0 = mfma_32x32x16_bf16(qa, kf[0][s], acc0);
-        acc1 = mfma_32x32x16_bf16(qa, kf[1][s], acc1);
+        c0 = mfma_32x32x16_bf16(qa[s], kf[0][s], c0);
+        c1 = mfma_32x32x16_bf16(qa[s], kf[1][s], c1);
       }
+      const int rem = __builtin_amdgcn_readfirstlane(s_len[g]) - p * kPage;
       const float *wg = &s_w[g][4 * h];
       float sum0 = 0.0f, sum1 = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float wv = wg[8 * (i >> 2) + (i & 3)];
-        sum0 = fmaf(wv, __builtin_amdgcn_fmed3f(acc0[i], lo[0], hi[0]), sum0);
-        sum1 = fmaf(wv, __builtin_amdgcn_fmed3f(acc1[i], lo[1], hi[1]), sum1);
+        sum0 = fmaf(wv, __builtin_amdgcn_fmed3f(c0[i], lo[0], hi[0]), sum0);
+        sum1 = fmaf(wv, __builtin_amdgcn_fmed3f(c1[i], lo[1], hi[1]), sum1);
       }
       const float s0 = sum_halves(sum0) * scale[0], s1 = sum_halves(sum1) * scale[1];
-      // both half-waves hold both blocks' sums: lane (n, h) stores token 32 h + n
-      const int tok = 32 * h + n;
-      if (tok < rem) a.scores[(int64_t)(b * m + g) * a.ld + (int64_t)p * kPage + tok] = h ? s1 : s0;
+      // the page's part of the row as a buffer of max(0, min(rem, 64)) scores: stores past it
+      // are dropped by the range check
+      const int nv = __builtin_amdgcn_readfirstlane(rem < 0 ? 0 : (rem > kPage ? kPage : rem));
+      const uint64_t base = reinterpret_cast<uint64_t>(a.scores + (int64_t)(b * m + g) * a.ld + (int64_t)p * kPage);
+      const uint64_t ubase = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) << 32) |
+                             (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base);
+      const __amdgpu_buffer_rsrc_t ors =
+          __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<float *>(ubase), 0, 4 * nv, 0x00020000);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(h ? s1 : s0), ors, 4 * tok, 0, 0);
+    };
+    bf16x8_t qa[8], qb[8];
+    load_a(0, qa);
+    int g = 0;
+    for (; g + 1 < m; g += 2) {
+      load_a(g + 1, qb);
+      row(g, qa);
+      load_a(min(g + 2, m - 1), qa);  // past the last row: a harmless re-read
+      row(g + 1, qb);
     }
+    if (g < m) row(g, qa);
   };
 
-  // Software pipeline as in the one-row scan: two pages in flight in registers while the
-  // third is scored from LDS; every iteration issues the same loads.
+  // Pipeline: one page in flight in registers while the previous one is scored from LDS (the
+  // kernel is bound by the matrix cores, not by HBM, once several rows share a page); every
+  // iteration issues the same loads.
   int t = t_beg;
   int bl = req_of(t);
   auto adv = [&](int tt, int bb) {  // request of tile tt, walking forward from bb
     while (tt >= __builtin_amdgcn_readfirstlane(s_start[bb + 1])) ++bb;
     return bb;
   };
-  bool has0, ok0, has1 = false, ok1 = false;
-  int rq0 = bl, rq1 = bl;
+  bool has0, ok0;
+  int rq0 = bl;
   load(b0, src_of(t, has0, ok0));
-  const uint8_t *src1 = a.pool;
-  if (t + 1 < t_end) {
-    bl = adv(t + 1, bl);
-    rq1 = bl;
-    src1 = src_of(t + 1, has1, ok1);
-  }
-  load(b1, src1);
-  while (t + 3 < t_end) {
+  for (; t < t_end; ++t) {
     park(b0);
     const bool v0 = ok0;
     const int c0 = rq0;
-    bl = adv(t + 2, bl);
-    rq0 = bl;
-    load(b0, src_of(t + 2, has0, ok0));
-    compute(t, c0, v0);
-    ++t;
-    park(b1);
-    const bool v1 = ok1;
-    const int c1 = rq1;
-    bl = adv(t + 2, bl);
-    rq1 = bl;
-    load(b1, src_of(t + 2, has1, ok1));
-    compute(t, c1, v1);
-    ++t;
-  }
-  for (int k = 0; t < t_end; ++k, ++t) {
-    if ((k & 1) == 0) {
-      park(b0);
-      const bool v0 = ok0;
-      const int c0 = rq0;
-      if (t + 2 < t_end) {
-        bl = adv(t + 2, bl);
-        rq0 = bl;
-        load(b0, src_of(t + 2, has0, ok0));
-      }
-      compute(t, c0, v0);
-    } else {
-      park(b1);
-      compute(t, rq1, ok1);
+    if (t + 1 < t_end) {
+      bl = adv(t + 1, bl);
+      rq0 = bl;
+      load(b0, src_of(t + 1, has0, ok0));
     }
+    compute(t, c0, v0);
   }
 }
 
-template <int KEY_FMT, int MMAX>
-hipError_t launch_verify_t(const VerifyArgs &a, hipStream_t s, int64_t grid) {
+// m <= 4: two 4-wave workgroups per CU; m <= 8: one 8-wave workgroup per CU (one copy of the
+// 64 KB of query rows for eight pages).  Either way two waves per SIMD.
+template <int KEY_FMT, int MMAX, int NW>
+hipError_t launch_verify_t(const VerifyArgs &a, hipStream_t s) {
+  const int64_t max_tok = a.ld < a.off_ld * kPage ? a.ld : a.off_ld * kPage;
+  const int64_t max_tiles = (int64_t)a.n_req * (((max_tok + kPage - 1) / kPage + NW - 1) / NW);
+  int64_t grid = (max_tiles + 7) / 8;
+  const int64_t cap = NW == 4 ? 512 : 256;
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
   const size_t dyn = sizeof(int) * (size_t)(2 * a.n_req + 1);
-  hipLaunchKernelGGL((indexer_verify_kernel<KEY_FMT, MMAX>), dim3((unsigned)grid), dim3(256), dyn, s, a);
+  hipLaunchKernelGGL((indexer_verify_kernel<KEY_FMT, MMAX, NW>), dim3((unsigned)grid), dim3(64 * NW), dyn, s, a);
   return hipGetLastError();
 }
 
@@ -314,15 +318,8 @@ hipError_t launch_verify_t(const VerifyArgs &a, hipStream_t s, int64_t grid) {
 hipError_t launch_indexer_verify(const VerifyArgs &a, hipStream_t s) {
   if (a.n_req == 0) return hipSuccess;
   if (a.m < 1 || a.m > kVerifyMaxRows || a.n_req > kVerifyMaxReq) return hipErrorInvalidValue;
-  const int64_t max_tok = a.ld < a.off_ld * kPage ? a.ld : a.off_ld * kPage;
-  const int64_t max_tiles = (int64_t)a.n_req * (((max_tok + kPage - 1) / kPage + kVWaves - 1) / kVWaves);
-  const int per_cu = a.m <= 4 ? 2 : 1;
-  int64_t grid = (max_tiles + 7) / 8;
-  if (grid > 256 * per_cu) grid = 256 * per_cu;
-  if (grid < 1) grid = 1;
-  if (a.key_fmt == 0)
-    return a.m <= 4 ? launch_verify_t<0, 4>(a, s, grid) : launch_verify_t<0, 8>(a, s, grid);
-  return a.m <= 4 ? launch_verify_t<1, 4>(a, s, grid) : launch_verify_t<1, 8>(a, s, grid);
+  if (a.key_fmt == 0) return a.m <= 4 ? launch_verify_t<0, 4, 4>(a, s) : launch_verify_t<0, 8, 8>(a, s);
+  return a.m <= 4 ? launch_verify_t<1, 4, 4>(a, s) : launch_verify_t<1, 8, 8>(a, s);
 }
 
 }  // namespace dsa
