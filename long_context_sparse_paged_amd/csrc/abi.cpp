@@ -317,8 +317,12 @@ static dsa_status mla_common(const dsa_layout *layout, const uint8_t *pool, int6
   return launched(launch_mla(a, stream_of(stream)));
 }
 
-// Prefill: one split per row while k <= 2048 (whole 64-token subtiles).
-static int32_t prefill_tokens_per_split(int32_t k) {
+// Prefill: one split per row while k <= 2048 (whole 64-token subtiles).  Rows with at most
+// 16 heads (one head tile, e.g. the verify rows of speculative decoding) take short splits:
+// one workgroup per row would walk its whole set alone.  The split size depends only on k
+// and the head count, so a row's result never depends on the batch it is in.
+static int32_t prefill_tokens_per_split(int32_t k, int32_t n_heads) {
+  if (n_heads <= 16) return 256;
   const int32_t t = k <= 64 ? 64 : (k + 63) / 64 * 64;
   return t > 2048 ? 2048 : t;
 }
@@ -343,7 +347,7 @@ dsa_status dsa_sparse_mla_decode(const dsa_layout *layout, const uint8_t *pool, 
 dsa_status dsa_sparse_mla_prefill_workspace_size(int32_t n_q, int32_t n_heads, int32_t k, size_t *bytes) {
   if (!bytes) return DSA_ERR_NULL_ARG;
   if (n_q < 0 || n_heads < 1 || k < 0) return DSA_ERR_BAD_SHAPE;
-  *bytes = mla_workspace_bytes(n_q, n_heads, k, prefill_tokens_per_split(k));
+  *bytes = mla_workspace_bytes(n_q, n_heads, k, prefill_tokens_per_split(k, n_heads));
   return DSA_OK;
 }
 
@@ -356,7 +360,7 @@ dsa_status dsa_sparse_mla_prefill(const dsa_layout *layout, const uint8_t *pool,
   if (n_q > 0 && !q_req) return DSA_ERR_NULL_ARG;
   return mla_common(layout, pool, pool_bytes, lat_off, off_ld, n_req, ctx_len, idx, idx_ld, k, q, q_fmt, q_scale,
                     q_req, n_q, n_heads, sm_scale, kv_scale, out, lse, workspace, workspace_bytes, err_flag, stream,
-                    prefill_tokens_per_split(k));
+                    prefill_tokens_per_split(k, n_heads));
 }
 
 }  // extern "C"
