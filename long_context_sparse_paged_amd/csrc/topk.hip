@@ -224,6 +224,13 @@ __device__ __forceinline__ int block_rank(bool f, int *tmp, int &total) {
   return off + rank;
 }
 
+// log2 of the sample count of a row of length len: about len / 32, from 4096 to kMaxSamples.
+__host__ __device__ inline int sample_log2(int64_t len) {
+  int lg = 12;
+  while ((1 << lg) < kMaxSamples && ((int64_t)32 << lg) < len) ++lg;
+  return lg;
+}
+
 // Sample position q (4 consecutive scores) of S: runs of 64 starting at multiples of 4,
 // spread evenly from 0 to len - 64.
 __device__ __forceinline__ float4 load_sample4(const float *row, bool vec, int len, int runs, int q) {
@@ -234,8 +241,10 @@ __device__ __forceinline__ float4 load_sample4(const float *row, bool vec, int l
   return make_float4(p[0], p[1], p[2], p[3]);
 }
 
+// The sample buffer is dynamic LDS of 4 * sample_count(ld) bytes: a row never draws more
+// samples than a row of length ld, and short rows leave room for more workgroups per CU.
 __global__ __launch_bounds__(256) void topk_sample_kernel(const TopkArgs a, TopkWs w) {
-  __shared__ __align__(16) uint32_t s_smp[kMaxSamples];
+  extern __shared__ __align__(16) uint32_t s_smp[];
   __shared__ RadixLds<256> R;
   const int r = blockIdx.x;
   const int len = row_len_of(a, r);
@@ -243,8 +252,7 @@ __global__ __launch_bounds__(256) void topk_sample_kernel(const TopkArgs a, Topk
   if (len <= kShortRow || keff >= len) return;  // uniform
   const float *row = a.scores + (int64_t)r * a.ld;
   const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
-  int lg = 12;  // S = 2^lg samples, about len / 32
-  while ((1 << lg) < kMaxSamples && (32 << lg) < len) ++lg;
+  const int lg = sample_log2(len);  // S = 2^lg samples, about len / 32
   const int S = 1 << lg, lg_runs = lg - 6;
   // runs of 64 start at multiples of 4 spread over [0, len - 64): run c at (len - 64) c / runs
   uint32_t lo = 0xFFFFFFFFu, hi = 0u, t1 = 0u, t2 = 0u;
@@ -692,7 +700,8 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
     if (a.ld <= kOwnMaxLd && a.n_rows <= kOwnMaxRows) {
       hipLaunchKernelGGL(topk_collect_kernel<true>, dim3(n_slices, a.n_rows), dim3(256), 0, s, a, w, n_slices);
     } else {
-      hipLaunchKernelGGL(topk_sample_kernel, dim3(a.n_rows), dim3(256), 0, s, a, w);
+      const size_t smp = sizeof(uint32_t) * ((size_t)1 << sample_log2(a.ld));
+      hipLaunchKernelGGL(topk_sample_kernel, dim3(a.n_rows), dim3(256), smp, s, a, w);
       hipLaunchKernelGGL(topk_collect_kernel<false>, dim3(n_slices, a.n_rows), dim3(256), 0, s, a, w, n_slices);
     }
   }
