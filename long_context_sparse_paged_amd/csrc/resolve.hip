@@ -13,7 +13,10 @@ __global__ __launch_bounds__(256) void resolve_kernel(const ResolveArgs a) {
   const int32_t b = blockIdx.y;
   const int32_t p = blockIdx.x * 256 + threadIdx.x;
   if (p >= a.max_pages) return;
+  // both loads in flight together: the table entry is in bounds (p < max_pages <= bt_ld)
+  // whether or not the page is in use
   int32_t np = a.n_pages[b];
+  const int64_t row = a.bt[(int64_t)b * a.bt_ld + p];
   uint32_t err = 0;
   if (np < 0 || np > a.max_pages) {
     err |= DSA_DEVERR_PAGE_COUNT;
@@ -21,7 +24,6 @@ __global__ __launch_bounds__(256) void resolve_kernel(const ResolveArgs a) {
   }
   int64_t lo = -1, ko = -1;
   if (p < np) {
-    const int64_t row = a.bt[(int64_t)b * a.bt_ld + p];
     if (row >= 0 && row < a.pool_rows) {
       lo = row * a.row_stride + a.layer_off;
       ko = lo + a.lat_page_bytes;
