@@ -229,7 +229,7 @@ def main():
                          "frac": round(tf / BF16_PEAK_TFLOPS, 4), "flop_per_launch": flop_idx,
                          "key_bytes_per_launch": key_bytes,
                          "key_gbs": round(key_bytes / (score_ms * 1e-3) / 1e9, 1),
-                         "traffic": None},
+                         "traffic": counter_traffic(DOMINANT["verify"][1], args.workload)},
         })
     else:
         rl = pq.row_len.cpu().numpy().astype(np.int64)
@@ -412,6 +412,12 @@ def summarize_stats(argv):
     print("\n".join(out))
 
 
+# dominant kernel of each workload and the sources its traffic figures depend on
+DOMINANT = {w: ("indexer_scan_kernel", ["indexer_scan.hip", "dsa_device.hpp"]) for w in ("decode", "long", "mixed")}
+DOMINANT["prefill"] = ("indexer_gemm_kernel", ["indexer_gemm.hip", "dsa_device.hpp"])
+DOMINANT["verify"] = ("indexer_verify_kernel", ["indexer_verify.hip", "dsa_device.hpp"])
+
+
 def summarize_pmc(argv):
     """--summarize-pmc <fetch.csv> <write.csv> <workload> <command>: HBM traffic of the dominant kernel.
 
@@ -421,8 +427,7 @@ def summarize_pmc(argv):
     import csv
     from collections import defaultdict
     fetch_csv, write_csv, workload, cmd = argv
-    kern = "indexer_gemm_kernel" if workload == "prefill" else "indexer_scan_kernel"
-    src = ["indexer_gemm.hip" if workload == "prefill" else "indexer_scan.hip", "dsa_device.hpp"]
+    kern, src = DOMINANT[workload]
     copy_bytes = 1 << 29
 
     def per_dispatch(path, counter):
