@@ -54,23 +54,25 @@ __device__ __forceinline__ int vrow_length(const VerifyArgs &a, int r, int64_t m
   return len;
 }
 
-// NW waves per workgroup, one page each per tile; MMAX = most rows per request staged.
-template <int KEY_FMT, int MMAX, int NW>
+// NW waves per workgroup, one page each per tile; M rows per request (a compile-time
+// count, so the row loop unrolls and each row's LDS reads take the row as an immediate offset).
+template <int KEY_FMT, int M, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void indexer_verify_kernel(const VerifyArgs a) {
   using KR = VKeyRow<KEY_FMT>;
   constexpr int NT = 64 * NW;
   __shared__ __align__(16) uint8_t s_page[NW][KR::kPageBytes];
   // query rows of the current request: [row][head][16 chunks of 8 dims], chunk c of head j
   // stored at chunk position c ^ (j & 15) so that the A-fragment reads are conflict-free
-  __shared__ __align__(16) uint16_t s_q[MMAX][kIdxHeads][kIdxDim];
-  __shared__ __align__(16) float s_w[MMAX][kIdxHeads];
-  __shared__ int s_len[MMAX];
+  __shared__ __align__(16) uint16_t s_q[M][kIdxHeads][kIdxDim];
+  __shared__ __align__(16) float s_w[M][kIdxHeads];
+  __shared__ int s_len[M];
   __shared__ int s_tmp[NW];
   extern __shared__ int s_dyn[];  // [n_req + 1] first tile of each request, then [n_req] pages
   int *s_start = s_dyn, *s_pages = s_dyn + a.n_req + 1;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int n_req = a.n_req, m = a.m;
+  const int n_req = a.n_req;
+  constexpr int m = M;
   const int64_t max_tok = a.ld < a.off_ld * kPage ? a.ld : a.off_ld * kPage;
 
   // tiles per request: ceil(pages / NW), pages from the request's longest row
@@ -261,16 +263,13 @@ __global__ __launch_bounds__(64 * NW, 2) void indexer_verify_kernel(const Verify
           __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<float *>(ubase), 0, 4 * nv, 0x00020000);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(h ? s1 : s0), ors, 4 * tok, 0, 0);
     };
-    bf16x8_t qa[8], qb[8];
-    load_a(0, qa);
-    int g = 0;
-    for (; g + 1 < m; g += 2) {
-      load_a(g + 1, qb);
-      row(g, qa);
-      load_a(min(g + 2, m - 1), qa);  // past the last row: a harmless re-read
-      row(g + 1, qb);
+    bf16x8_t qa[2][8];
+    load_a(0, qa[0]);
+#pragma unroll
+    for (int g = 0; g < M; ++g) {
+      if (g + 1 < M) load_a(g + 1, qa[(g + 1) & 1]);
+      row(g, qa[g & 1]);
     }
-    if (g < m) row(g, qa);
   };
 
   // Pipeline: one page in flight in registers while the previous one is scored from LDS (the
@@ -299,8 +298,8 @@ __global__ __launch_bounds__(64 * NW, 2) void indexer_verify_kernel(const Verify
 }
 
 // m <= 4: two 4-wave workgroups per CU; m <= 8: one 8-wave workgroup per CU (one copy of the
-// 64 KB of query rows for eight pages).  Either way two waves per SIMD.
-template <int KEY_FMT, int MMAX, int NW>
+// query rows, up to 64 KB, for eight pages).  Either way two waves per SIMD.
+template <int KEY_FMT, int M, int NW = (M <= 4 ? 4 : 8)>
 hipError_t launch_verify_t(const VerifyArgs &a, hipStream_t s) {
   const int64_t max_tok = a.ld < a.off_ld * kPage ? a.ld : a.off_ld * kPage;
   const int64_t max_tiles = (int64_t)a.n_req * (((max_tok + kPage - 1) / kPage + NW - 1) / NW);
@@ -309,8 +308,22 @@ hipError_t launch_verify_t(const VerifyArgs &a, hipStream_t s) {
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
   const size_t dyn = sizeof(int) * (size_t)(2 * a.n_req + 1);
-  hipLaunchKernelGGL((indexer_verify_kernel<KEY_FMT, MMAX, NW>), dim3((unsigned)grid), dim3(64 * NW), dyn, s, a);
+  hipLaunchKernelGGL((indexer_verify_kernel<KEY_FMT, M, NW>), dim3((unsigned)grid), dim3(64 * NW), dyn, s, a);
   return hipGetLastError();
+}
+
+template <int KEY_FMT>
+hipError_t launch_verify_m(const VerifyArgs &a, hipStream_t s) {
+  switch (a.m) {
+    case 1: return launch_verify_t<KEY_FMT, 1>(a, s);
+    case 2: return launch_verify_t<KEY_FMT, 2>(a, s);
+    case 3: return launch_verify_t<KEY_FMT, 3>(a, s);
+    case 4: return launch_verify_t<KEY_FMT, 4>(a, s);
+    case 5: return launch_verify_t<KEY_FMT, 5>(a, s);
+    case 6: return launch_verify_t<KEY_FMT, 6>(a, s);
+    case 7: return launch_verify_t<KEY_FMT, 7>(a, s);
+    default: return launch_verify_t<KEY_FMT, 8>(a, s);
+  }
 }
 
 }  // namespace
@@ -318,8 +331,7 @@ hipError_t launch_verify_t(const VerifyArgs &a, hipStream_t s) {
 hipError_t launch_indexer_verify(const VerifyArgs &a, hipStream_t s) {
   if (a.n_req == 0) return hipSuccess;
   if (a.m < 1 || a.m > kVerifyMaxRows || a.n_req > kVerifyMaxReq) return hipErrorInvalidValue;
-  if (a.key_fmt == 0) return a.m <= 4 ? launch_verify_t<0, 4, 4>(a, s) : launch_verify_t<0, 8, 8>(a, s);
-  return a.m <= 4 ? launch_verify_t<1, 4, 4>(a, s) : launch_verify_t<1, 8, 8>(a, s);
+  return a.key_fmt == 0 ? launch_verify_m<0>(a, s) : launch_verify_m<1>(a, s);
 }
 
 }  // namespace dsa
