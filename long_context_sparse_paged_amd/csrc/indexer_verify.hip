@@ -66,6 +66,7 @@ __global__ __launch_bounds__(64 * NW, 2) void indexer_verify_kernel(const Verify
   __shared__ __align__(16) uint16_t s_q[M][kIdxHeads][kIdxDim];
   __shared__ __align__(16) float s_w[M][kIdxHeads];
   __shared__ int s_len[M];
+  __shared__ float s_out[NW][M][kPage];  // the wave's last page of scores, stored one iteration later
   __shared__ int s_tmp[NW];
   extern __shared__ int s_dyn[];  // [n_req + 1] first tile of each request, then [n_req] pages
   int *s_start = s_dyn, *s_pages = s_dyn + a.n_req + 1;
@@ -187,13 +188,36 @@ __global__ __launch_bounds__(64 * NW, 2) void indexer_verify_kernel(const Verify
   };
 
   const int n = lane & 31, h = lane >> 5;
+  const int tok = 32 * h + n;  // lane (n, h) handles token 32 h + n of a page
+  // Scores of the last page, per row: the row's page base and valid count (wave-uniform).
+  // They are stored at the top of the next iteration, before the next page load is issued,
+  // so that the wait for a page never has to wait for stores issued after it.
+  uint64_t pend_base[M];
+  int pend_nv[M];
+#pragma unroll
+  for (int g = 0; g < M; ++g) {
+    pend_base[g] = reinterpret_cast<uint64_t>(a.scores);
+    pend_nv[g] = 0;
+  }
+  auto flush = [&]() {
+#pragma unroll
+    for (int g = 0; g < M; ++g) {
+      const float v = s_out[wid][g][tok];
+      const __amdgpu_buffer_rsrc_t ors =
+          __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<float *>(pend_base[g]), 0, 4 * pend_nv[g], 0x00020000);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ors, 4 * tok, 0, 0);
+    }
+  };
   auto compute = [&](int tt, int b, bool valid) {
     b = __builtin_amdgcn_readfirstlane(b);
     if (b != cur_b) {
       stage(b);
       cur_b = b;
     }
-    if (!valid) return;
+    // An invalid page (none for this wave in the tile, or a bad offset) is scored like any
+    // other -- from the pool's first bytes -- and its stores get an empty range, so every
+    // iteration issues the same memory operations and the wait for the next page counts
+    // only the stores issued after it, not a drain of everything.
     // wave-uniform, so that the score stores' buffer descriptors live in scalar registers
     const int p = __builtin_amdgcn_readfirstlane(NW * (tt - s_start[b]) + wid);
     // B fragments of both 32-token blocks, decoded once for all rows
@@ -235,7 +259,6 @@ __global__ __launch_bounds__(64 * NW, 2) void indexer_verify_kernel(const Verify
 #pragma unroll
       for (int s = 0; s < 8; ++s) qa[s] = *reinterpret_cast<const bf16x8_t *>(qrow + 8 * ((8 * h + s) ^ (n & 15)));
     };
-    const int tok = 32 * h + n;  // lane (n, h) stores token 32 h + n of the page
     auto row = [&](int g, const bf16x8_t (&qa)[8]) {
       f32x16_t c0 = {}, c1 = {};
 #pragma unroll
@@ -253,22 +276,19 @@ __global__ __launch_bounds__(64 * NW, 2) void indexer_verify_kernel(const Verify
         sum1 = fmaf(wv, __builtin_amdgcn_fmed3f(c1[i], lo[1], hi[1]), sum1);
       }
       const float s0 = sum_halves(sum0) * scale[0], s1 = sum_halves(sum1) * scale[1];
-      // the page's part of the row as a buffer of max(0, min(rem, 64)) scores: stores past it
-      // are dropped by the range check
-      const int nv = __builtin_amdgcn_readfirstlane(rem < 0 ? 0 : (rem > kPage ? kPage : rem));
+      s_out[wid][g][tok] = h ? s1 : s0;
+      // the page's part of the row as a buffer of max(0, min(rem, 64)) scores: the later
+      // stores past it are dropped by the range check
+      pend_nv[g] = __builtin_amdgcn_readfirstlane(!valid || rem < 0 ? 0 : (rem > kPage ? kPage : rem));
       const uint64_t base = reinterpret_cast<uint64_t>(a.scores + (int64_t)(b * m + g) * a.ld + (int64_t)p * kPage);
-      const uint64_t ubase = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) << 32) |
-                             (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base);
-      const __amdgpu_buffer_rsrc_t ors =
-          __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<float *>(ubase), 0, 4 * nv, 0x00020000);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(h ? s1 : s0), ors, 4 * tok, 0, 0);
+      pend_base[g] = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base);
     };
-    bf16x8_t qa[2][8];
-    load_a(0, qa[0]);
 #pragma unroll
     for (int g = 0; g < M; ++g) {
-      if (g + 1 < M) load_a(g + 1, qa[(g + 1) & 1]);
-      row(g, qa[g & 1]);
+      bf16x8_t qa[8];
+      load_a(g, qa);
+      row(g, qa);
     }
   };
 
@@ -288,13 +308,18 @@ __global__ __launch_bounds__(64 * NW, 2) void indexer_verify_kernel(const Verify
     park(b0);
     const bool v0 = ok0;
     const int c0 = rq0;
+    // past the last tile the load reads the pool's first page (in bounds) and is not used
+    const uint8_t *nsrc = a.pool;
     if (t + 1 < t_end) {
       bl = adv(t + 1, bl);
       rq0 = bl;
-      load(b0, src_of(t + 1, has0, ok0));
+      nsrc = src_of(t + 1, has0, ok0);
     }
+    flush();  // the previous page's scores (an empty range before the first page)
+    load(b0, nsrc);
     compute(t, c0, v0);
   }
+  flush();
 }
 
 // m <= 4: two 4-wave workgroups per CU; m <= 8: one 8-wave workgroup per CU (one copy of the
