@@ -256,19 +256,25 @@ __global__ __launch_bounds__(256) void topk_sample_kernel(const TopkArgs a, Topk
   const int S = 1 << lg, lg_runs = lg - 6;
   // runs of 64 start at multiples of 4 spread over [0, len - 64): run c at (len - 64) c / runs
   uint32_t lo = 0xFFFFFFFFu, hi = 0u, t1 = 0u, t2 = 0u;
-  for (int q0 = threadIdx.x; q0 < S / 4; q0 += 4 * 256) {  // S / 4 is a multiple of 1024
-    float4 v[4];
+  // every sample load in flight at once (S / 1024 = 4, 8 or 16 quads per thread): one round
+  // trip instead of one per batch of four
+  constexpr int kMaxQuads = kMaxSamples / 1024;
+  const int nq = S >> 10;  // wave-uniform
+  float4 v[kMaxQuads];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = q0 + 256 * u, c = q >> 4, part = q & 15;
+  for (int u = 0; u < kMaxQuads; ++u) {
+    if (u < nq) {
+      const int q = threadIdx.x + 256 * u, c = q >> 4, part = q & 15;
       const int start = (int)(((int64_t)(len - 64) * c) >> lg_runs) & ~3;
       const float *p = row + start + 4 * part;
       v[u] = vec ? *reinterpret_cast<const float4 *>(p) : make_float4(p[0], p[1], p[2], p[3]);
     }
+  }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < kMaxQuads; ++u) {
+    if (u < nq) {
       const uint4 k = make_uint4(score_key(v[u].x), score_key(v[u].y), score_key(v[u].z), score_key(v[u].w));
-      *reinterpret_cast<uint4 *>(s_smp + 4 * (q0 + 256 * u)) = k;
+      *reinterpret_cast<uint4 *>(s_smp + 4 * (threadIdx.x + 256 * u)) = k;
       const uint32_t kk[4] = {k.x, k.y, k.z, k.w};
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
