@@ -220,7 +220,6 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
     }
     const int p = uu - __builtin_amdgcn_readfirstlane(s_start[rr]);
     const int rem = cur_len - p * kPage;
-    float *out = a.scores + (int64_t)rr * a.ld + (int64_t)p * kPage;
     // score of token 32 c2 + n; both half-waves end up holding the same value
     auto block = [&](int c2) {
       const uint8_t *row = slot + (32 * c2 + n) * KR::kBytes;
