@@ -41,7 +41,7 @@ namespace dsa {
 namespace {
 
 constexpr int kOwnSamples = 4096;     // samples a collect workgroup draws itself
-constexpr int kOwnMaxLd = 262144;     // ... when rows are at most this long
+constexpr int kOwnMaxLd = 524288;     // ... when rows are at most this long
 constexpr int kOwnMaxRows = 64;       // ... and there are at most this many
 constexpr int kMaxSamples = 16384;    // samples of the sample launch
 constexpr int kMaxSlices = 1024;
