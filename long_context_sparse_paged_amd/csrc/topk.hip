@@ -592,15 +592,21 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
     n = run;
     ok = n >= keff && n <= kShortRow;
     if (ok) {
+      // every slice base first (all LDS reads in flight together), then the placements
+      int sb0[kSpec], sb1[kSpec];
+#pragma unroll
+      for (int q = 0; q < kSpec; ++q) {
+        const int s = min((tid + NT * q) >> lgB, n_slices - 1);
+        sb0[q] = s_base[s];
+        sb1[q] = s_base[s + 1];
+      }
 #pragma unroll
       for (int q = 0; q < kSpec; ++q) {
         const int x = tid + NT * q, s = x >> lgB, j = x & ((1 << lgB) - 1);
-        if (s < n_slices) {
-          const int c = s_base[s + 1] - s_base[s];
-          if (c <= kSliceCap && j < c) {
-            s_key[s_base[s] + j] = e[q].x;
-            s_idx[s_base[s] + j] = (int32_t)e[q].y;
-          }
+        const int c = sb1[q] - sb0[q];
+        if (s < n_slices && c <= kSliceCap && j < c) {
+          s_key[sb0[q] + j] = e[q].x;
+          s_idx[sb0[q] + j] = (int32_t)e[q].y;
         }
       }
       if (s_flag & 2) {  // lists longer than B: their remaining entries
