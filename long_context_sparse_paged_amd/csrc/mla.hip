@@ -154,12 +154,20 @@ __global__ __launch_bounds__(256, 2) void mla_kernel(const MlaArgs a, const int 
   u32x4_t raw[G::kPerThread];
   uint32_t bsc[G::kPerThread];  // NVFP4: the chunk's two e4m3 block scales (bytes 0, 1)
   auto issue = [&](int t0) {
+    // the tokens' pool offsets first (clamped reads, no branch: all LDS reads in flight
+    // together), then the loads
+    int64_t offs[G::kPerThread];
+#pragma unroll
+    for (int i = 0; i < G::kPerThread; ++i) {
+      const int j = t0 + (tid + 256 * i) / G::kChunks;
+      const int64_t o = s_off[min(j, n_tok - 1)];
+      offs[i] = j < n_tok ? o : -1;
+    }
 #pragma unroll
     for (int i = 0; i < G::kPerThread; ++i) {
       const int item = tid + 256 * i;
       const int tok = item / G::kChunks, c = item - tok * G::kChunks;
-      const int j = t0 + tok;
-      const int64_t off = j < n_tok ? s_off[j] : -1;
+      const int64_t off = offs[i];
       // every lane issues the load (an invalid token reads the pool's first bytes and is
       // zeroed on decode), so the number of loads in flight is the same on every path
       const uint8_t *base = a.pool + (off < 0 ? 0 : off);
@@ -367,12 +375,20 @@ __global__ __launch_bounds__(kWideThreads) void mla_wide_kernel(const MlaArgs a,
   u32x4_t raw[kPer];
   uint32_t bsc[kPer];
   auto issue = [&](int t0) {
+    // the tokens' pool offsets first (clamped reads: all LDS reads in flight together)
+    int64_t offs[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int item = tid + kWideThreads * i;
+      const int j = t0 + item / kChunks;
+      const int64_t o = s_off[min(j, n_tok - 1)];
+      offs[i] = (item < kItems && j < n_tok) ? o : -1;
+    }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int item = tid + kWideThreads * i;
       const int tok = item / kChunks, c = item - tok * kChunks;
-      const int j = t0 + tok;
-      const int64_t off = (item < kItems && j < n_tok) ? s_off[j] : -1;
+      const int64_t off = offs[i];
       const uint8_t *base = a.pool + (off < 0 ? 0 : off);  // every lane loads: fixed wait counts
       const int cc = c < kChunks ? c : 0;
       if constexpr (LAT_FMT == 0) {
