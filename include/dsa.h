@@ -176,8 +176,11 @@ dsa_status dsa_indexer_score(const dsa_layout *layout, const uint8_t *pool, int6
  *   row_len    device int32 [n_req*rows_per_req]
  *   scores     device fp32 [n_req*rows_per_req][ld] (out): entries t < row_len[r]
  *              written, the rest untouched.
- * 1 <= rows_per_req <= 8 and n_req <= 1024, else DSA_ERR_UNSUPPORTED.  A row_len
- * outside [0, min(ld, 64*off_ld)] is clamped and flags DSA_DEVERR_ROW_LEN. */
+ * rows_per_req < 1, n_req < 0, ld < 0 or off_ld < 1: DSA_ERR_BAD_SHAPE; rows_per_req
+ * > 8 or n_req > 1024: DSA_ERR_UNSUPPORTED.  A row_len outside [0, min(ld, 64*off_ld)]
+ * is clamped and flags DSA_DEVERR_ROW_LEN; a page a row needs whose offset is negative,
+ * misaligned or past the pool is skipped (its scores are not written) and flags
+ * DSA_DEVERR_PAGE_OFFSET. */
 dsa_status dsa_indexer_score_verify(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
                                     const int64_t *key_off, int64_t off_ld, int32_t n_req, int32_t rows_per_req,
                                     const uint16_t *q, const float *w, const int32_t *row_len, float *scores,
