@@ -69,3 +69,36 @@ def test_full_size_step_sampled_rows(d, cfg):
         topk_set_ok(ref_s, oracle.topk(ref_s, np.array([L], np.int32), k), got_idx, [L], k)
         ref_o, ref_l = oracle.sparse_mla(oc, got_idx, qm, fmt, qms, req, H, sm)
         check_attention(step.out[r:r + 1], step.lse[r:r + 1], ref_o, ref_l)
+
+
+def test_scans_past_one_offset_batch(d):
+    """Both key scans cache their pages' offsets 64 units at a time (one per lane).  With
+    9 requests of ~1M tokens a wave of the one-row scan takes 72 pages and a workgroup of the
+    verify scan (2 rows per request) 72 tiles, so both refill that cache mid-range: sampled
+    rows are checked against the oracle over their whole length."""
+    ctx = [1048576 + 37 * i for i in range(9)]
+    log(f"[case] offset-cache refill: {len(ctx)} requests, {sum(ctx)} tokens")
+    cache = W.build_cache(ctx, key_fmt=0, lat_fmt=0, seed=77, device="cuda")
+    dq = W.decode_queries(len(ctx), 12, seed=77, device="cuda")
+    step = d.DecodeStep(cache, dq.q_idx, dq.w, dq.q_mla, dq.sm_scale, k=2048)
+    step.resolve()
+    step.score()
+    vq = W.verify_queries(ctx, 2, 12, seed=78, device="cuda")
+    vs = d.VerifyStep(cache, vq, k=2048)
+    vs.resolve()
+    vs.score()
+    torch.cuda.synchronize()
+    assert int(step.err.item()) == 0 and int(vs.err.item()) == 0
+    oc = oracle.OracleCache(cache)
+    for r in (0, 8):
+        L = ctx[r]
+        log(f"[row] one-row scan row {r} length {L}")
+        ref = oracle.indexer_score(oc, dq.q_idx[r:r + 1], 0, None, dq.w[r:r + 1], np.array([r], np.int32),
+                                   np.array([L], np.int32))
+        check_scores(step.scores[r:r + 1, :L].cpu().numpy(), ref, [L])
+    for r in (1, 16):
+        L = int(vq.row_len[r].item())
+        log(f"[row] verify scan row {r} length {L}")
+        ref = oracle.indexer_score(oc, vq.q_idx[r:r + 1], 0, None, vq.w[r:r + 1], vq.q_req[r:r + 1].cpu().numpy(),
+                                   np.array([L], np.int32))
+        check_scores(vs.scores[r:r + 1, :L].cpu().numpy(), ref, [L])
