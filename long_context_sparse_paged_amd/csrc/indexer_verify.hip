@@ -21,9 +21,11 @@
 //   1. loads the 64 keys with coalesced nontemporal 16-B loads, one page ahead, and parks
 //      them in its LDS slot,
 //   2. decodes the B fragments of both 32-token blocks to bf16 once (exact),
-//   3. for each row of the request: 8 + 8 v_mfma_f32_32x32x16_bf16 with A fragments read
-//      from LDS one row ahead, then the weighted ReLU head sum in the accumulator layout and
-//      one 256-byte store of the page's 64 scores.
+//   3. for each row of the request (m is a compile-time count, so the rows unroll): 8 + 8
+//      v_mfma_f32_32x32x16_bf16 with A fragments read from LDS at immediate offsets, then
+//      the weighted ReLU head sum in the accumulator layout into a per-wave LDS buffer,
+//   4. stores the previous page's m x 64 scores at the top of the next iteration, before the
+//      next page load, so that waiting for a page never waits for score stores.
 // The per-row arithmetic (operand order, accumulation order, epilogue) is the same as the
 // one-row scan's, so a row's scores do not depend on which of the two kernels made them.
 #include <math.h>
@@ -250,10 +252,10 @@ __global__ __launch_bounds__(64 * NW, 2) void indexer_verify_kernel(const Verify
       lo[c2] = scale[c2] < 0.0f ? -INFINITY : 0.0f;
       hi[c2] = scale[c2] < 0.0f ? 0.0f : INFINITY;
     }
-    // Rows one after another, each with its A fragments read from LDS one row ahead, so that
-    // a row's 16 MFMAs issue back to back; the other wave on the SIMD fills the epilogue's
-    // VALU time.  Every row of the request runs its MFMAs; a row that does not reach this page
-    // stores nothing (its buffer range is empty), so the loop body has no branch.
+    // Rows one after another (unrolled: each row's A-fragment reads take the row as an
+    // immediate LDS offset); the other wave on the SIMD fills one wave's epilogue time.  Every
+    // row of the request runs its MFMAs; a row that does not reach this page stores nothing
+    // (its buffer range is empty), so the row loop has no branch.
     auto load_a = [&](int g, bf16x8_t (&qa)[8]) {
       const uint16_t *qrow = &s_q[g][n][0];
 #pragma unroll
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(64 * NW, 2) void indexer_verify_kernel(const Verify
 
   // Pipeline: one page in flight in registers while the previous one is scored from LDS (the
   // kernel is bound by the matrix cores, not by HBM, once several rows share a page); every
-  // iteration issues the same loads.
+  // iteration issues the same loads and stores, so the compiler's wait for a page is exact.
   int t = t_beg;
   int bl = req_of(t);
   auto adv = [&](int tt, int bb) {  // request of tile tt, walking forward from bb
