@@ -20,7 +20,9 @@
 //            and every element with key >= est is appended, in index order, to the
 //            slice's candidate list (ballot ranks; one barrier).
 //   finalize (one workgroup per row): the slices' candidates, concatenated in slice
-//            order, are in index order.  A slice that had more candidates than its list
+//            order, are in index order.  The first B entries of every list come in one
+//            round trip with the counts; the entries past B, numbered through a prefix
+//            over the slices, in a second.  A slice that had more candidates than its list
 //            holds is filtered again from the scores.  An LDS radix select finds the
 //            exact k-th key tau and the number of ties at tau to keep; an ordered
 //            compaction writes the kept indices ascending.  Rows of <= 12288 scores skip
@@ -519,11 +521,13 @@ __device__ void select_write(uint32_t *s_key, const int32_t *s_idx, int n, int p
 
 __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkArgs a, TopkWs w, int n_slices) {
   constexpr int NT = kFinThreads;
-  constexpr int kBatch = 12;  // candidate loads in flight per thread
+  constexpr int kBatch = 12;  // row-score loads in flight per thread (short rows)
   constexpr int kSpec = 16;   // speculative candidate loads per thread
+  constexpr int kXBatch = 4;  // loads of entries past B in flight per thread
   __shared__ uint32_t s_key[kShortRow];
   __shared__ int32_t s_idx[kShortRow];
   __shared__ int s_base[kMaxSlices + 1];
+  __shared__ int s_xbase[kMaxSlices + 1];
   __shared__ RadixLds<NT> R;
   __shared__ int s_flag;
   const int tid = threadIdx.x;
@@ -609,34 +613,53 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
           s_idx[sb0[q] + j] = (int32_t)e[q].y;
         }
       }
-      if (s_flag & 2) {  // lists longer than B: their remaining entries
-        int top = 1;     // largest power of two <= n_slices
+      if (s_flag & 2) {  // lists longer than B: only their entries past the first B
+        // x(s) = entries of slice s past B (0 for short and for overflowed lists); the
+        // extras are numbered 0..X-1 in slice order through the exclusive prefix s_xbase
+        const int B = 1 << lgB;
+        int xrun = 0;
+        for (int s0 = 0; s0 < n_slices; s0 += NT) {
+          const int s = s0 + tid;
+          const int c = s < n_slices ? s_base[s + 1] - s_base[s] : 0;
+          const int x = c > B && c <= kSliceCap ? c - B : 0;
+          int total;
+          const int incl = block_scan_incl<NT>(x, R.tmp, total);
+          if (s < n_slices) s_xbase[s] = xrun + incl - x;
+          xrun += total;
+        }
+        if (tid == 0) s_xbase[n_slices] = xrun;
+        __syncthreads();
+        int top = 1;  // largest power of two <= n_slices
         while (2 * top <= n_slices) top <<= 1;
-        for (int p0 = 0; p0 < n; p0 += NT * kBatch) {
-          // slice sl[q] with s_base[sl] <= p < s_base[sl + 1], the batch's searches interleaved
-          int sl[kBatch];
+        for (int p0 = 0; p0 < xrun; p0 += NT * kXBatch) {
+          // extra p lies in the last slice sl with s_xbase[sl] <= p (the batch's searches
+          // interleaved); positions past X load entry 0 of slice 0, so every load is in
+          // bounds and none waits on a branch
+          int sl[kXBatch];
 #pragma unroll
-          for (int q = 0; q < kBatch; ++q) sl[q] = 0;
+          for (int q = 0; q < kXBatch; ++q) sl[q] = 0;
           for (int step = top; step > 0; step >>= 1) {
 #pragma unroll
-            for (int q = 0; q < kBatch; ++q) {
+            for (int q = 0; q < kXBatch; ++q) {
               const int c = sl[q] + step;
-              if (c <= n_slices && s_base[c] <= p0 + NT * q + tid) sl[q] = c;
+              if (c <= n_slices && s_xbase[c] <= p0 + NT * q + tid) sl[q] = c;
             }
           }
-          uint2 f[kBatch];
+          int dst[kXBatch];
+          uint2 f[kXBatch];
 #pragma unroll
-          for (int q = 0; q < kBatch; ++q) {
-            const int p = p0 + NT * q + tid, lo = sl[q], j = p - s_base[lo];
-            const bool take = p < n && s_base[lo + 1] - s_base[lo] <= kSliceCap && j >= (1 << lgB);
-            f[q] = take ? cand[(int64_t)lo * kSliceCap + j] : make_uint2(0u, 0xFFFFFFFFu);
+          for (int q = 0; q < kXBatch; ++q) {
+            const int p = p0 + NT * q + tid;
+            const bool v = p < xrun;
+            const int lo = v ? sl[q] : 0, j = v ? B + p - s_xbase[lo] : 0;
+            dst[q] = v ? s_base[lo] + j : -1;
+            f[q] = cand[(int64_t)lo * kSliceCap + j];
           }
 #pragma unroll
-          for (int q = 0; q < kBatch; ++q) {
-            const int p = p0 + NT * q + tid;
-            if (p < n && f[q].y != 0xFFFFFFFFu) {
-              s_key[p] = f[q].x;
-              s_idx[p] = (int32_t)f[q].y;
+          for (int q = 0; q < kXBatch; ++q) {
+            if (dst[q] >= 0) {
+              s_key[dst[q]] = f[q].x;
+              s_idx[dst[q]] = (int32_t)f[q].y;
             }
           }
         }

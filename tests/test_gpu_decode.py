@@ -196,6 +196,24 @@ def test_topk_clustered_slice_overflow(d):
     assert np.array_equal(got, oracle.topk(s, [L] * 3, 2048))
 
 
+def test_topk_lists_longer_than_their_share(d):
+    """Rows of 2^20 scores (128 slices): finalize reads the first 64 entries of every slice's
+    candidate list in its first round trip and fetches the entries past 64 afterwards.  With
+    k = 4096 most lists are longer than 64; in row 1 two lists (first and last slice) hold
+    thousands of entries each, so the entries past 64 take several batches; row 2 has an
+    overflowed slice (re-filtered from the scores) next to a long list."""
+    rng = np.random.default_rng(15)
+    L = 1 << 20
+    s = rng.standard_normal((3, L)).astype(np.float32)
+    s[1, :3000] += 3.0
+    s[1, -3000:] += 3.0
+    s[2, 500000:509000] = 9.0
+    s[2, :200] += 4.0
+    log("[topk] 3 rows of 2^20, k=4096")
+    got = gpu_topk(d, s, [L, L, L - 5], 4096)
+    assert np.array_equal(got, oracle.topk(s, [L, L, L - 5], 4096))
+
+
 def test_topk_many_rows_and_long_rows(d):
     """Batches that take the separate sample launch: many rows, and rows over 256K long."""
     rng = np.random.default_rng(14)
