@@ -532,6 +532,25 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
   __shared__ int s_flag;
   const int tid = threadIdx.x;
   const int r = blockIdx.x;
+  // When rows may be long, one round trip loads the row's length, the slice counts and,
+  // speculatively, the first B entries of every slice's candidate list (B: a power of two,
+  // B x n_slices <= NT x kSpec).  None of these addresses depends on the length, and all
+  // are in bounds for every row: the lists are kSliceCap long, and entries past a slice's
+  // count (or the whole of a short row's lists) are read but not used.
+  const uint32_t *cnt = w.cnt + (int64_t)r * n_slices;
+  const uint2 *cand = w.cand + (int64_t)r * n_slices * kSliceCap;
+  int lgB = 4;
+  while ((2 << lgB) * n_slices <= NT * kSpec && (2 << lgB) <= kSliceCap) ++lgB;
+  uint2 e[kSpec];
+  int c_first = 0;  // count of slice tid
+  if (a.ld > kShortRow) {  // uniform
+#pragma unroll
+    for (int q = 0; q < kSpec; ++q) {
+      const int x = tid + NT * q, s = x >> lgB, j = x & ((1 << lgB) - 1);
+      e[q] = s < n_slices ? cand[(int64_t)s * kSliceCap + j] : make_uint2(0u, 0u);
+    }
+    c_first = tid < n_slices ? (int)cnt[tid] : 0;
+  }
   const int len = row_len_of(a, r);
   const int keff = min(a.k, len);
   int32_t *out = a.idx + (int64_t)r * a.idx_ld;
@@ -563,19 +582,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
     n = len;
     ok = true;
   } else {
-    // One round trip for the counts and, speculatively, the first B entries of every slice's
-    // candidate list (B: a power of two, B x n_slices <= NT x kSpec); entries past a slice's
-    // count are read but not used (the lists are kSliceCap long, so every read is in bounds).
-    const uint32_t *cnt = w.cnt + (int64_t)r * n_slices;
-    const uint2 *cand = w.cand + (int64_t)r * n_slices * kSliceCap;
-    int lgB = 4;
-    while ((2 << lgB) * n_slices <= NT * kSpec && (2 << lgB) <= kSliceCap) ++lgB;
-    uint2 e[kSpec];
-#pragma unroll
-    for (int q = 0; q < kSpec; ++q) {
-      const int x = tid + NT * q, s = x >> lgB, j = x & ((1 << lgB) - 1);
-      e[q] = s < n_slices ? cand[(int64_t)s * kSliceCap + j] : make_uint2(0u, 0u);
-    }
+    // (len > kShortRow implies ld > kShortRow: e[] and c_first are loaded)
     if (tid == 0) s_flag = 0;
     __syncthreads();
     // exclusive prefix of the slices' candidate counts; s_flag bit 0: a list overflowed,
@@ -583,7 +590,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
     int run = 0;
     for (int s0 = 0; s0 < n_slices; s0 += NT) {
       const int s = s0 + tid;
-      const int c = s < n_slices ? (int)cnt[s] : 0;
+      const int c = s0 == 0 ? c_first : s < n_slices ? (int)cnt[s] : 0;
       if (c > kSliceCap) atomicOr(&s_flag, 1);
       else if (c > (1 << lgB)) atomicOr(&s_flag, 2);
       int total;
