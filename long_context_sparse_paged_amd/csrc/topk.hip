@@ -527,6 +527,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
   constexpr int kBatch = 12;  // row-score loads in flight per thread (short rows)
   constexpr int kSpec = 16;   // speculative candidate loads per thread
   constexpr int kXBatch = 4;  // loads of entries past B in flight per thread
+  static_assert(8 * kMaxSlices <= NT * kSpec, "a speculative share of 8 entries must cover every slice");
   __shared__ uint32_t s_key[kShortRow];
   __shared__ int32_t s_idx[kShortRow];
   __shared__ int s_base[kMaxSlices + 1];
@@ -542,7 +543,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
   // count (or the whole of a short row's lists) are read but not used.
   const uint32_t *cnt = w.cnt + (int64_t)r * n_slices;
   const uint2 *cand = w.cand + (int64_t)r * n_slices * kSliceCap;
-  int lgB = 4;
+  int lgB = 3;  // B = 8 keeps B x n_slices <= NT x kSpec up to kMaxSlices = 1024 slices
   while ((2 << lgB) * n_slices <= NT * kSpec && (2 << lgB) <= kSliceCap) ++lgB;
   uint2 e[kSpec];
   int c_first = 0;  // count of slice tid

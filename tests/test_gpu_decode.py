@@ -214,6 +214,24 @@ def test_topk_lists_longer_than_their_share(d):
     assert np.array_equal(got, oracle.topk(s, [L, L, L - 5], 4096))
 
 
+def test_topk_rows_past_512_slices(d):
+    """Rows of more than 512 slices, up to the largest ld the entry point takes (1024 slices
+    of 8192 scores): finalize's speculative share of every candidate list drops to 8 entries
+    so that one round trip still covers every slice.  The 5M-score row (both k) and the
+    8M-score row at k = 1000 take the candidate path; the 8M row at k = 2048 holds more
+    candidates than LDS and is selected from the whole row."""
+    rng = np.random.default_rng(16)
+    ld = 1024 * 8192
+    lens = [5_000_000, ld]
+    s = np.zeros((2, ld), np.float32)
+    for r, L in enumerate(lens):
+        s[r, :L] = rng.standard_normal(L).astype(np.float32)
+    for k in (2048, 1000):
+        log(f"[topk] rows of {lens} scores, k={k}")
+        got = gpu_topk(d, s, lens, k)
+        assert np.array_equal(got, oracle.topk(s, lens, k))
+
+
 def test_topk_many_rows_and_long_rows(d):
     """Batches that take the separate sample launch: many rows, and rows over 256K long."""
     rng = np.random.default_rng(14)
