@@ -55,7 +55,7 @@ typedef int32_t dsa_status;
 #define DSA_ERR_NULL_ARG 1            /* a required pointer is NULL */
 #define DSA_ERR_BAD_SHAPE 2           /* a size, count or leading dimension is invalid */
 #define DSA_ERR_MISALIGNED 3          /* a pointer lacks the alignment stated for it */
-#define DSA_ERR_UNSUPPORTED 4         /* a format, head count or size this build does not run */
+#define DSA_ERR_UNSUPPORTED 4         /* a format, head count or size the library does not run */
 #define DSA_ERR_WORKSPACE_TOO_SMALL 5 /* workspace_bytes < the *_workspace_size answer */
 #define DSA_ERR_HIP 6                 /* a HIP launch failed */
 
@@ -89,7 +89,7 @@ typedef int32_t dsa_status;
  *   key_page(row, layer) = lat_page(row, layer) + lat_page_bytes
  *   token slot s of a page: + s*lat_bytes (latent) / + s*key_bytes (key)   */
 typedef struct dsa_layout {
-  int32_t page_size; /* tokens per page (64 on this build) */
+  int32_t page_size; /* tokens per page (64 in this library) */
   int32_t n_layers;
   int32_t key_fmt; /* DSA_KEY_* */
   int32_t lat_fmt; /* DSA_LAT_* */
