@@ -211,3 +211,24 @@ def test_verify_empty_and_single_token_requests(d, m):
     check_scores(got, ref, rl)
     for r, L in enumerate(rl):
         assert np.isnan(got[r, L:]).all(), f"row {r} written past its length"
+
+
+def test_verify_max_requests(d):
+    """The largest request count the entry point takes (1024) at 8 rows each with FP8 keys:
+    the request table in LDS then brings the workgroup to 158,788 of 163,840 bytes of LDS."""
+    rng = np.random.default_rng(60)
+    m = 8
+    ctx = [int(x) for x in rng.integers(m, 100, size=1024)]
+    cache, vq, step = make(d, ctx, m, seed=61)
+    step.scores.fill_(float("nan"))
+    step.resolve()
+    step.score()
+    torch.cuda.synchronize()
+    assert int(step.err.item()) == 0
+    got = step.scores.cpu().numpy()
+    rl = vq.row_len.cpu().numpy()
+    oc = oracle.OracleCache(cache)
+    ref = oracle.indexer_score(oc, vq.q_idx, 0, None, vq.w, vq.q_req, rl, ld=step.scores.shape[1])
+    check_scores(got, ref, rl)
+    for r, L in enumerate(rl):
+        assert np.isnan(got[r, L:]).all(), f"row {r} written past its length"
