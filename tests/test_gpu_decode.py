@@ -127,6 +127,25 @@ def test_scores_many_rows_key_balanced(d):
     check_scores(step.scores.cpu().numpy(), ref, ctx)
 
 
+def test_scores_max_rows(d):
+    """The largest row count the one-row scan takes (4096 requests, one row each): its row
+    table in LDS grows to 16 KB, and the key-balanced split spreads many short rows over
+    the waves."""
+    rng = np.random.default_rng(8)
+    ctx = [int(x) for x in rng.integers(1, 200, size=4096)]
+    cache, dq, step = make(d, ctx, seed=8)
+    step.scores.fill_(float("nan"))
+    step.resolve()
+    step.score()
+    torch.cuda.synchronize()
+    assert int(step.err.item()) == 0
+    got = step.scores.cpu().numpy()
+    _, ref = oracle_scores(cache, dq)
+    check_scores(got, ref, ctx)
+    for r, L in enumerate(ctx):
+        assert np.isnan(got[r, L:]).all(), f"row {r} written past its length"
+
+
 # ------------------------------------------------------------------- top-k
 
 def gpu_topk(d, scores, row_len, k):
