@@ -366,6 +366,15 @@ def test_chain_ragged_batch(d, fmt):
     run_chain_and_check(d, cache, dq, step)
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_chain_largest_k(d, fmt):
+    """k = 4096, the largest the entry points take: 32 token splits per decode row and a
+    combine over 32 partial results; rows shorter than k keep every token."""
+    ctx = [20000, 4096, 4095, 9000, 1]
+    cache, dq, step = make(d, ctx, key_fmt=fmt, lat_fmt=fmt, seed=45 + fmt, spare_rows=5, k=4096)
+    run_chain_and_check(d, cache, dq, step, k=4096)
+
+
 def test_determinism_and_batch_invariance(d):
     ctx = [3000, 20000, 700]
     cache, dq, step = make(d, ctx, seed=50, spare_rows=4)
