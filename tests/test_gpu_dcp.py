@@ -98,3 +98,14 @@ def test_decode_workload_scores(d):
     scores = step.scores.cpu().numpy()
     rl = cache.ctx_len.cpu().numpy()
     check(d, scores, rl, 2048, 8)
+
+
+@pytest.mark.parametrize("n_shards", [1, 8])
+def test_largest_shards(d, n_shards):
+    """Shards of 65,536 tokens, the most a shard may hold (ld = 65,536 W): random rows, a row
+    of coarse values with many BF16 ties, and a row one token short."""
+    rng = np.random.default_rng(110 + n_shards)
+    L = 65536 * n_shards
+    s = rng.standard_normal((3, L)).astype(np.float32)
+    s[1] = (np.round(s[1] * 8) / 8).astype(np.float32)
+    check(d, s, np.array([L, L, L - 1], np.int32), 2048, n_shards)
