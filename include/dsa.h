@@ -244,12 +244,17 @@ dsa_status dsa_sparse_mla_prefill(const dsa_layout *layout, const uint8_t *pool,
  * W-th token, t mod W = s; "流量减少 10× 的精确 top-k 合并": each shard sends
  * its best ceil(1.5 k / W) candidates taken from BF16 scores, each packed with
  * its score into 32 bits; the same radix select over the gathered candidates
- * gives the global top-k; a shard that held more of it than it sent resends
- * its full local top-k for the row).
+ * gives the global top-k; a shard that may hold more of it than it sent
+ * resends its full local top-k for the row).
  * Output idx[r][0..k): the min(k, row_len[r]) tokens first in the order
  * (BF16 of the score, round to nearest even, descending; token index
  * ascending), in ascending token order, then -1.  resend_mask[r] (optional,
- * device uint32): bit s set when shard s had to resend for row r.  Four
+ * device uint32): bit s set when shard s resent for row r, which is when
+ * shard s holds more than c = ceil(1.5 k / W) of the row's tokens and its
+ * c-th (last sent) candidate is among the min(k, row_len[r]) best of all
+ * shards' candidates; that is the test a shard can make from the gathered
+ * candidates alone, and it never misses a shard holding unsent top-k tokens
+ * (it may flag shards that hold none).  Four
  * launches (candidates, merge, resend, merge of resent rows), all on `stream`.
  *   scores  device fp32 [n_rows][ld]; row_len device int32 [n_rows]
  *   idx     device int32 [n_rows][idx_ld] (out), idx_ld >= k

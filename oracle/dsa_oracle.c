@@ -358,20 +358,22 @@ int or_topk(const float *scores, int64_t ld, const int32_t *row_len, int64_t n_r
  * shard t mod W), and the global top-2048 must be merged across shards before
  * attention.  Section "流量减少 10× 的精确 top-k 合并": each shard picks its
  * best 1.5 * 2048 / W candidates straight from BF16 scores and packs each with
- * its score into 32 bits; every shard radix-selects the same global top-2048
- * from the gathered candidates; the merge stays exact because a shard that held
- * more of the top-2048 than it sent is detected and resends its full local
- * top-k for that row.
+ * its score into 32 bits; every shard selects the same global top-2048 from the
+ * gathered candidates; a shard that may hold more of the top-2048 than it sent
+ * is detected and resends its full local top-k for that row.
  * Readings taken here:
  *   - the order is the BF16 value of the score (fp32 rounded to nearest, ties
  *     to even) descending, then token index ascending (the tie rule of or_topk);
- *   - c = ceil(1.5 k / W) candidates per shard;
- *   - shard r is flagged when it holds more than c tokens of the row and its
- *     c-th best token (in that order) is among the kept tokens: then, and only
- *     then, tokens it did not send may belong to the top-k.
- * The outcome is computed from those definitions with one full sort:
- *   idx[r]    the min(k, len) first tokens of the order, ascending, -1 padded;
- *   resend[r] bit s set when shard s is flagged. */
+ *   - c = ceil(1.5 k / W) candidates per shard; a shard holding at most c
+ *     tokens sends them all;
+ *   - detection uses only what the gathered candidates show: shard s is flagged
+ *     when it holds more than c tokens and its c-th (last sent) candidate is
+ *     among the min(k, len) first of the candidate union.  Otherwise every
+ *     token it kept back ranks below that candidate, hence below the union's
+ *     k-th, hence (the union being a subset of the row) below the true k-th;
+ *   - a flagged shard resends its first min(k, held) tokens, and the output is
+ *     the min(k, len) first of the second union, ascending, -1 padded.
+ * The steps are carried out literally, each with a full sort. */
 static double bf16_round(double x) {
   /* 8 significant bits, round to nearest, ties to even (normal range; the
    * BF16 subnormal range below 2^-126 keeps fewer bits and is not covered) */
@@ -389,6 +391,18 @@ static int cmp_dval_desc_idx_asc(const void *a, const void *b, void *ctx) {
   if (v[ia] > v[ib]) return -1;
   if (v[ia] < v[ib]) return 1;
   return (ia > ib) - (ia < ib);
+}
+
+/* The row's tokens on shard sh, first `take` of them in the order: the shard's
+ * candidate list.  Appends to list[*n] and returns the number appended. */
+static int64_t dcp_shard_list(const double *v, int64_t len, int64_t W, int64_t sh, int64_t take, int32_t *tmp,
+                              int32_t *list, int64_t *n) {
+  int64_t held = 0;
+  for (int64_t t = sh; t < len; t += W) tmp[held++] = (int32_t)t;
+  qsort_r(tmp, (size_t)held, sizeof(int32_t), cmp_dval_desc_idx_asc, (void *)v);
+  const int64_t m = take < held ? take : held;
+  for (int64_t i = 0; i < m; ++i) list[(*n)++] = tmp[i];
+  return m;
 }
 
 int or_dcp_topk(const float *scores, int64_t ld, const int32_t *row_len, int64_t n_rows, int64_t k, int64_t n_shards,
@@ -409,35 +423,52 @@ int or_dcp_topk(const float *scores, int64_t ld, const int32_t *row_len, int64_t
       continue;
     }
     const float *s = scores + r * ld;
-    double *v = (double *)malloc(sizeof(double) * (size_t)(len > 0 ? len : 1));
-    int32_t *order = (int32_t *)malloc(sizeof(int32_t) * (size_t)(len > 0 ? len : 1));
+    const size_t cap = (size_t)(len > 0 ? len : 1);
+    double *v = (double *)malloc(sizeof(double) * cap);
+    int32_t *tmp = (int32_t *)malloc(sizeof(int32_t) * cap);
+    int32_t *uni = (int32_t *)malloc(sizeof(int32_t) * cap);
+    int32_t *last = (int32_t *)malloc(sizeof(int32_t) * (size_t)W); /* each shard's last sent token */
+    int64_t *held = (int64_t *)malloc(sizeof(int64_t) * (size_t)W);
+    char *kept = (char *)calloc(cap, 1);
     int bad = 0;
     for (int64_t t = 0; t < len; ++t) {
       if (!isfinite(s[t])) bad = 1;
       v[t] = bf16_round((double)s[t]);
-      order[t] = (int32_t)t;
     }
     if (bad) {
 #pragma omp atomic write
       rc = OR_ERR_NONFINITE;
-      free(v);
-      free(order);
-      continue;
+      len = 0;
     }
-    qsort_r(order, (size_t)len, sizeof(int32_t), cmp_dval_desc_idx_asc, (void *)v);
     const int64_t keep = k < len ? k : len;
-    /* shard s's c-th best token is its c-th token met along the global order; a shard
-     * with at most c tokens sent them all and is never flagged */
-    int64_t seen[32] = {0};
-    for (int64_t p = 0; p < len; ++p) {
-      const int64_t sh = order[p] % W;
-      const int64_t held = (len - 1 - sh) / W + 1; /* tokens of shard sh in the row */
-      if (++seen[sh] == c && p < keep && held > c) resend[r] |= 1u << sh;
+    /* (1) every shard sends its first c tokens; the union is sorted in the order */
+    int64_t n = 0;
+    for (int64_t sh = 0; sh < W; ++sh) {
+      held[sh] = sh < len ? (len - 1 - sh) / W + 1 : 0;
+      const int64_t m = dcp_shard_list(v, len, W, sh, c, tmp, uni, &n);
+      last[sh] = m > 0 ? uni[n - 1] : -1;
     }
-    qsort(order, (size_t)keep, sizeof(int32_t), cmp_int_asc);
-    for (int64_t i = 0; i < k; ++i) out[i] = i < keep ? order[i] : -1;
+    qsort_r(uni, (size_t)n, sizeof(int32_t), cmp_dval_desc_idx_asc, (void *)v);
+    /* (2) flags: a shard that kept tokens back and whose last sent token is among
+     * the union's keep first */
+    for (int64_t p = 0; p < keep; ++p) kept[uni[p]] = 1;
+    for (int64_t sh = 0; sh < W; ++sh)
+      if (held[sh] > c && kept[last[sh]]) resend[r] |= 1u << sh;
+    /* (3) the flagged shards resend their first k tokens; the second union decides */
+    if (resend[r]) {
+      n = 0;
+      for (int64_t sh = 0; sh < W; ++sh)
+        dcp_shard_list(v, len, W, sh, ((resend[r] >> sh) & 1u) ? k : c, tmp, uni, &n);
+      qsort_r(uni, (size_t)n, sizeof(int32_t), cmp_dval_desc_idx_asc, (void *)v);
+    }
+    qsort(uni, (size_t)keep, sizeof(int32_t), cmp_int_asc);
+    for (int64_t i = 0; i < k; ++i) out[i] = i < keep ? uni[i] : -1;
     free(v);
-    free(order);
+    free(tmp);
+    free(uni);
+    free(last);
+    free(held);
+    free(kept);
   }
   return rc;
 }

@@ -2,7 +2,9 @@
 (dsa_dcp_topk) against the oracle, through the C ABI.
 
 Both the kept indices and the resend mask must match the oracle bit for bit: the order
-(BF16 score desc, token asc) is total, so the answer is unique.  Cases: several shard
+(BF16 score desc, token asc) is total, and a shard is flagged exactly when it kept tokens
+back and its last sent candidate is among the k best of all candidates, so both answers are
+unique.  Cases: several shard
 counts, row lengths that are empty, shorter than k, not multiples of W, and full size;
 scores with many BF16 ties; rows whose best tokens sit on one shard (forcing resends);
 and the indexer scores of the 32 x 128K decode workload.
@@ -13,6 +15,7 @@ import torch
 
 import oracle
 from synth import workloads as W
+from tests.test_oracle_dcp import brute_resend, skew_row
 
 pytestmark = pytest.mark.gpu
 
@@ -109,3 +112,25 @@ def test_largest_shards(d, n_shards):
     s = rng.standard_normal((3, L)).astype(np.float32)
     s[1] = (np.round(s[1] * 8) / 8).astype(np.float32)
     check(d, s, np.array([L, L, L - 1], np.int32), 2048, n_shards)
+
+
+@pytest.mark.parametrize("W_,second,expect", [(8, [1, 2, 3, 4], 0b11111), (3, [1], 0b011)])
+def test_skew_rows_flag_what_the_candidates_show(d, W_, second, expect):
+    """Shard 0 holds 3000 tokens at 10 (more than k, so the true top-k is all its own), and
+    the shards in `second` hold c tokens each at 5: the candidates cannot show that shard 0
+    alone fills the top-k, so those shards are flagged too (masks derived by hand in the
+    oracle's pins).  A two-tier row of the same kind (shard 0 +20, shard 1 +10 on N(0,1)
+    scores) runs beside it."""
+    k = 2048
+    c = -(-3 * k // (2 * W_))
+    L = 4000 * W_
+    rows = [skew_row(W_, 3000, second, c, L)]
+    t = np.arange(L)
+    two = np.random.default_rng(31).standard_normal(L).astype(np.float32)
+    two[t % W_ == 0] += 20.0
+    two[t % W_ == 1] += 10.0
+    rows.append(two)
+    s = np.stack(rows)
+    rs = check(d, s, np.array([L, L], np.int32), k, W_)
+    assert rs[0] == expect
+    assert rs[1] == brute_resend(s[1], L, k, W_)

@@ -12,8 +12,10 @@ full sort); these tests pin it to things other than itself:
 - the kept set does not depend on the number of shards;
 - the resend mask: closed forms (one shard never resends; a score that falls
   with the token index spreads the top-k evenly; a row whose best tokens all
-  sit on one shard flags exactly that shard) and brute force per shard on
-  small rows.
+  sit on one shard flags exactly that shard), constructed skew rows where the
+  protocol's detectable rule flags shards that hold none of the true top-k
+  (masks derived by hand), and a brute force of the protocol on small rows;
+- the output after the resend round: the plain top-k in the BF16 order.
 """
 import numpy as np
 import pytest
@@ -37,16 +39,22 @@ def lexsort_topk(s, length, k):
 
 
 def brute_resend(s, length, k, n_shards):
-    """Shard r flagged iff it holds more than c tokens and its c-th best is kept."""
+    """The protocol played out shard by shard: each shard sends its c best tokens (all of
+    them when it holds at most c); shard r is flagged iff it held more than c and its
+    last sent token is among the min(k, len) best of everything sent."""
     c = -(-3 * k // (2 * n_shards))
     v = torch_bf16(s[:length])
-    kept = set(np.lexsort((np.arange(length), -v))[:min(k, length)].tolist())
-    mask = 0
+    sent, last = [], {}
     for r in range(n_shards):
-        toks = sorted(range(r, length, n_shards), key=lambda t: (-v[t], t))
-        if len(toks) > c and toks[c - 1] in kept:
-            mask |= 1 << r
-    return mask
+        toks = list(range(r, length, n_shards))
+        toks.sort(key=lambda t: (-v[t], t))
+        mine = toks[:c]
+        sent += mine
+        if len(toks) > c:
+            last[r] = mine[-1]
+    sent.sort(key=lambda t: (-v[t], t))
+    top = set(sent[:min(k, length)])
+    return sum(1 << r for r, t in last.items() if t in top)
 
 
 def test_bf16_round_matches_torch():
@@ -130,3 +138,34 @@ def test_resend_brute_force(n_shards):
         assert rs[r] == brute_resend(s, L, k, n_shards), r
         assert np.array_equal(idx[r], lexsort_topk(s, L, k))
     assert rs.any()  # the skewed rows exercise the flag
+
+
+def skew_row(W, n_top, second, n_second, L):
+    """Shard 0's first n_top tokens score 10, each shard in `second` has its first n_second
+    tokens at 5, everything else scores 1."""
+    s = np.ones(L, np.float32)
+    t = np.arange(L)
+    sh, i = t % W, t // W
+    s[(sh == 0) & (i < n_top)] = 10.0
+    s[np.isin(sh, second) & (i < n_second)] = 5.0
+    return s
+
+
+@pytest.mark.parametrize("W,second,expect", [(8, [1, 2, 3, 4], 0b11111), (3, [1], 0b011)])
+def test_resend_flags_what_the_candidates_show(W, second, expect):
+    """k = 2048, c = ceil(1.5 k / W) (384 at W = 8, 1024 at W = 3).  Shard 0 holds 3000
+    tokens at 10, more than k, so the true top-k is shard 0's first 2048 tokens alone.  The
+    candidates show less: shard 0's c at 10, then c per shard at 5 for shards 1..4 (W = 8:
+    4 x 384 = 1536; W = 3: shard 1's 1024, shard 2 holds none at 5).  At W = 8 the union's
+    2048 best are 384 + 1536 at 10 and 5 and 128 at 1, so the last sent token of shards 0..4
+    is kept and shards 5..7's (at 1) are not: 0b11111.  At W = 3 the union's 2048 best are
+    shard 0's 1024 and shard 1's 1024: 0b011.  After the resend the output is shard 0's
+    first 2048 tokens either way."""
+    k = 2048
+    c = -(-3 * k // (2 * W))
+    L = 4000 * W
+    s = skew_row(W, 3000, second, c, L)[None, :]
+    idx, rs = oracle.dcp_topk(s, np.array([L], np.int32), k, W)
+    assert rs[0] == expect
+    assert rs[0] == brute_resend(s[0], L, k, W)
+    assert np.array_equal(idx[0], W * np.arange(k))
