@@ -150,9 +150,8 @@ dsa_status dsa_resolve_pages(const dsa_layout *layout, int32_t layer, const int3
  * The BF16 path streams each row's keys (decode); the FP8 path is an MFMA
  * GEMM over tiles of consecutive rows and is fastest when consecutive rows
  * share a request (a prefill chunk).  Both accept any q_req.  The FP8 path
- * first writes the rows' sign-folded bf16 query heads, head weights and the
- * bf16 pieces of sum_j w_j |q_scale_j| q_j into the workspace (about 9.3 KB
- * per row). */
+ * first writes the rows' sign-folded bf16 query heads and head weights into
+ * the workspace (about 8.2 KB per row). */
 dsa_status dsa_indexer_score_workspace_size(int32_t n_q, int32_t q_fmt, size_t *bytes);
 dsa_status dsa_indexer_score(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
                              const int64_t *key_off, int64_t off_ld, int32_t n_req, const void *q, int32_t q_fmt,

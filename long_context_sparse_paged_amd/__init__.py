@@ -17,7 +17,11 @@ from pathlib import Path
 
 import torch
 
-from .build import LIB as _LIB_PATH
+from .build import LIB as _BUILT_LIB
+
+# DSA_LIB selects another build of the same library (e.g. a host-sanitizer build for CPU-only
+# checks of argument validation); by default the in-tree build is loaded.
+_LIB_PATH = Path(os.environ.get("DSA_LIB", str(_BUILT_LIB)))
 
 DSA_OK, DSA_ERR_NULL_ARG, DSA_ERR_BAD_SHAPE, DSA_ERR_MISALIGNED = 0, 1, 2, 3
 DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE_TOO_SMALL, DSA_ERR_HIP = 4, 5, 6
@@ -31,6 +35,7 @@ __all__ = [
     "DsaError", "dsa_layout", "lib", "dsa_status_str", "dsa_version", "dsa_layout_make", "dsa_resolve_pages",
     "dsa_indexer_score_workspace_size", "dsa_indexer_score", "dsa_indexer_score_verify", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_decode_workspace_size",
     "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill_workspace_size", "dsa_sparse_mla_prefill",
+    "dsa_dcp_topk_workspace_size", "dsa_dcp_topk",
 ]
 
 

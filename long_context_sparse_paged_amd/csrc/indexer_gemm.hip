@@ -17,25 +17,21 @@
 // is exact) accumulates in fp32 to ~1e-8.  So both operands are decoded to bf16 and the
 // contraction runs on v_mfma_f32_32x32x16_bf16.
 //
-// The ReLU costs one VALU op per (row, token, head) instead of two.  With the sign of qs
-// folded into the query (q~ = sign(qs) qcode), s_j = w_j |qs_j|, x_j = q~_j . kcode and
-// sigma = sign(ks):
-//   score = |ks| sum_j s_j ReLU(sigma x_j) = |ks|/2 (sigma A + B),
-//   A = sum_j s_j x_j = Q' . kcode  with  Q' = sum_j s_j q~_j,     B = sum_j s_j |x_j|,
-// since ReLU(y) = (y + |y|) / 2.  B is one v_fma per element (|x| is a free source
-// modifier).  A is a linear form: Q' (computed in fp64 by a pre-pass) is split into three
-// bf16 pieces whose sum carries 24 significant bits (fp32's precision), and three extra
-// 8-MFMA chains accumulate them straight into A's accumulator -- 3/32 more MFMA work, no
-// VALU.
+// The ReLU is applied per head, exactly as in the decode scan.  With the sign of qs folded
+// into the query (q~ = sign(qs) qcode), s_j = w_j |qs_j| and x_j = q~_j . kcode:
+//   score = sum_j s_j ReLU(ks x_j) = ks sum_j s_j med3(x_j, lo, hi),
+// (lo, hi) = (0, inf) for ks >= 0 and (-inf, 0) otherwise.  Every term is >= 0, so a row
+// where no head is positive scores exactly +0 and a small score next to large per-head
+// terms keeps fp32's relative precision (a split into a linear part and sum_j s_j |x_j|
+// saves one VALU op per element but cancels in both cases).
 //
 // Pre-pass (indexer_qprep_kernel), one workgroup per row, into the caller's workspace:
-//   qb[r][36][128] bf16: heads 0..31 = q~_j (exact), heads 32..34 = the pieces of Q',
-//     head 35 = zeros (pads the last staging group of four heads);
+//   qb[r][32][128] bf16: q~_j (exact);
 //   sw[r/32][32][r%32] fp32: s_j, laid out as the GEMM's LDS weight tile.
 //
 // GEMM workgroup tile: 32 query rows x 256 tokens (4 pages); wave w owns page w (64
 // tokens, two 32-token MFMA columns).  The key fragments are decoded once per tile and
-// stay in registers for all 36 heads.  Query tiles move global -> LDS by direct LDS loads
+// stay in registers for all 32 heads.  Query tiles move global -> LDS by direct LDS loads
 // two heads at a time (double buffered, no VALU, 16-B chunks XOR-swizzled by row so the
 // MFMA operand reads are conflict-free).  Per head pair: four 8-MFMA chains, each after
 // the first interleaved with the accumulation of the one before it.  Lane (column n, half
@@ -60,23 +56,15 @@ constexpr int kKPB = kPage * kKB;                // 8448
 constexpr int kChunks = kKPB / 16;               // 528
 constexpr int kPer = (kChunks + 63) / 64;        // 9 16-byte chunks per lane, the last partial
 constexpr int kPageLds = kPer * 1024;            // a wave's page region, padded to whole loads
-constexpr int kLinHeads = 3;                     // bf16 pieces of Q' (24 significant bits)
-constexpr int kQbHeads = kIdxHeads + 4;          // 36: the last head slot is padding
+constexpr int kQbHeads = kIdxHeads;              // 32
 constexpr int kGroup = 4;                        // heads staged per barrier
-constexpr int kGroups = kQbHeads / kGroup;       // 9: eight of query heads, one of Q' pieces
+constexpr int kGroups = kQbHeads / kGroup;       // 8
 constexpr int kHeadTile = kGRows * kIdxDim;      // bf16 per staged head tile (8 KB)
 static_assert(kGroup * kHeadTile * 2 <= kGWaves * kPageLds, "query buffer 1 fits in the page region");
 constexpr int64_t kQbRow = (int64_t)kQbHeads * kIdxDim;  // bf16 per workspace row
 
-__device__ __forceinline__ uint16_t bf16_bits_rn(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
-
-// ---- pre-pass: sign-folded bf16 queries, Q' pieces and weights for one row ----
+// ---- pre-pass: sign-folded bf16 queries and weights for one row ----
 __global__ __launch_bounds__(256) void indexer_qprep_kernel(const ScoreArgs a, uint16_t *qb, float *sw) {
-  __shared__ float s_qt[kIdxHeads][kIdxDim + 1];
-  __shared__ float s_s[kIdxHeads];
   const int r = blockIdx.x, t = threadIdx.x, j = t >> 3, d0 = 16 * (t & 7);
   const float qs = a.q_scale[(int64_t)r * kIdxHeads + j];
   const float s = a.w[(int64_t)r * kIdxHeads + j] * fabsf(qs);
@@ -91,32 +79,7 @@ __global__ __launch_bounds__(256) void indexer_qprep_kernel(const ScoreArgs a, u
   uint16_t *dst = qb + (int64_t)r * kQbRow + (int64_t)j * kIdxDim + d0;
   *reinterpret_cast<u32x4_t *>(dst) = x0;
   *reinterpret_cast<u32x4_t *>(dst + 8) = x1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    s_qt[j][d0 + 2 * i] = __uint_as_float(x0[i] << 16);
-    s_qt[j][d0 + 2 * i + 1] = __uint_as_float(x0[i] & 0xFFFF0000u);
-    s_qt[j][d0 + 8 + 2 * i] = __uint_as_float(x1[i] << 16);
-    s_qt[j][d0 + 8 + 2 * i + 1] = __uint_as_float(x1[i] & 0xFFFF0000u);
-  }
-  if ((t & 7) == 0) {
-    s_s[j] = s;
-    sw[((int64_t)(r / kGRows) * kIdxHeads + j) * kGRows + r % kGRows] = s;
-  }
-  __syncthreads();
-  if (t < kIdxDim) {
-    // Q'[t] in fp64 (each product is exact), then four bf16 pieces; each residual is exact
-    // in fp64 (a piece is within a factor of two of what it approximates)
-    double q = 0.0;
-#pragma unroll 8
-    for (int jj = 0; jj < kIdxHeads; ++jj) q += (double)s_s[jj] * (double)s_qt[jj][t];
-#pragma unroll
-    for (int p = 0; p < kLinHeads; ++p) {
-      const uint16_t b = bf16_bits_rn((float)q);
-      qb[(int64_t)r * kQbRow + (int64_t)(kIdxHeads + p) * kIdxDim + t] = b;
-      q -= (double)__uint_as_float((uint32_t)b << 16);
-    }
-    qb[(int64_t)r * kQbRow + (int64_t)(kQbHeads - 1) * kIdxDim + t] = 0;
-  }
+  if ((t & 7) == 0) sw[((int64_t)(r / kGRows) * kIdxHeads + j) * kGRows + r % kGRows] = s;
 }
 
 // ---- GEMM ----
@@ -220,8 +183,8 @@ __global__ __launch_bounds__(256, 2) void indexer_gemm_kernel(const ScoreArgs a,
 
     // (2) key fragments, decoded once, resident for all heads
     bf16x8_t bf[2][8];
-    float ks[2];
-    f32x16_t acc[2], lin[2];
+    float ks[2], lo[2], hi[2];
+    f32x16_t acc[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const uint8_t *kr = s_pg + wid * kPageLds + (32 * c + n) * kKB;
@@ -230,8 +193,9 @@ __global__ __launch_bounds__(256, 2) void indexer_gemm_kernel(const ScoreArgs a,
         bf[c][s] = e4m3x8_bf16(*reinterpret_cast<const uint32_t *>(kr + 64 * h + 8 * s),
                                *reinterpret_cast<const uint32_t *>(kr + 64 * h + 8 * s + 4));
       ks[c] = *reinterpret_cast<const float *>(kr + 128);
+      lo[c] = ks[c] < 0.0f ? -INFINITY : 0.0f;
+      hi[c] = ks[c] < 0.0f ? 0.0f : INFINITY;
       acc[c] = f32x16_t{};
-      lin[c] = f32x16_t{};
     }
 
     __syncthreads();  // every wave has its key fragments: the page region becomes query buffer 1
@@ -258,22 +222,22 @@ __global__ __launch_bounds__(256, 2) void indexer_gemm_kernel(const ScoreArgs a,
     };
     auto accum = [&](int c, const f32x16_t &x, const float *wv) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[c][i] = fmaf(wv[i], fabsf(x[i]), acc[c][i]);
+      for (int i = 0; i < 16; ++i) acc[c][i] = fmaf(wv[i], __builtin_amdgcn_fmed3f(x[i], lo[c], hi[c]), acc[c][i]);
     };
     auto interleave = [] {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
       }
     };
 
-    // (3) the 32 heads, four per barrier: B accumulates s_j |x_j|.  Chain i of a group is
-    // (head i/2, column i%2); each chain after the first overlaps the accumulation of the
+    // (3) the 32 heads, four per barrier: acc accumulates s_j med3(x_j).  Chain i of a group
+    // is (head i/2, column i%2); each chain after the first overlaps the accumulation of the
     // one before it.
-    for (int g = 0; g < kGroups - 1; ++g) {
+    for (int g = 0; g < kGroups; ++g) {
       const int buf = g & 1;
-      if (g > 0) stage(g + 1);
+      if (g > 0 && g + 1 < kGroups) stage(g + 1);
       if (page_ok) {
         // one set of weights: head hd's are read last by the accumulation that overlaps
         // chain 2hd+2, just before head hd+1's are loaded
@@ -298,18 +262,8 @@ __global__ __launch_bounds__(256, 2) void indexer_gemm_kernel(const ScoreArgs a,
       __builtin_amdgcn_s_waitcnt(0x0F70);  // the next group's tiles have landed in LDS
       __syncthreads();
     }
-    // (4) the three pieces of Q': A accumulates in the MFMA accumulator itself
-    if (page_ok) {
-#pragma unroll
-      for (int hh = 0; hh < kLinHeads; ++hh) {
-        load_af((kGroups - 1) & 1, hh);
-        lin[0] = chain(0, lin[0]);
-        lin[1] = chain(1, lin[1]);
-      }
-    }
-    __syncthreads();
 
-    // (5) store |ks|/2 (sigma A + B): element i is row 8*(i/4) + 4h + i%4, token wtok0 + 32c + n
+    // (4) store ks * acc: element i is row 8*(i/4) + 4h + i%4, token wtok0 + 32c + n
     if (page_ok) {
       // row addresses are formed here, not hoisted out of the request loop where 16 of
       // them would hold 32 VGPRs through the head loop
@@ -328,18 +282,17 @@ __global__ __launch_bounds__(256, 2) void indexer_gemm_kernel(const ScoreArgs a,
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int t = wtok0 + 32 * c + n;
-        const float sg = ks[c] < 0.0f ? -1.0f : 1.0f, half = 0.5f * fabsf(ks[c]);
         if (whole) {
           const int voff = 4 * (h4 * ld32 + t);
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(half * fmaf(sg, lin[c][i], acc[c][i])), ors, voff,
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ks[c] * acc[c][i]), ors, voff,
                                                   4 * (8 * (i >> 2) + (i & 3)) * ld32, 0);
         } else {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int m = 8 * (i >> 2) + h4 + (i & 3);
-            if (((rws >> m) & 1u) && t < s_len[m]) out[m * ld + t] = half * fmaf(sg, lin[c][i], acc[c][i]);
+            if (((rws >> m) & 1u) && t < s_len[m]) out[m * ld + t] = ks[c] * acc[c][i];
           }
         }
       }

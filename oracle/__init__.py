@@ -25,7 +25,8 @@ import numpy as np
 
 _HERE = Path(__file__).resolve().parent
 _SRC = _HERE / "dsa_oracle.c"
-_LIB_PATH = _HERE / "_build" / "libdsa_oracle.so"
+# DSA_ORACLE_LIB selects another build of the oracle (e.g. a sanitizer build)
+_LIB_PATH = Path(os.environ.get("DSA_ORACLE_LIB", str(_HERE / "_build" / "libdsa_oracle.so")))
 
 OK, ERR_ARG, ERR_RANGE, ERR_NONFINITE = 0, 1, 2, 3
 

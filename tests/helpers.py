@@ -82,7 +82,8 @@ def topk_set_ok(ref_scores: np.ndarray, ref_idx: np.ndarray, got_idx: np.ndarray
         diff = R ^ G
         if diff:
             s = ref_scores[r, :L].astype(np.float64)
-            order = sorted(range(L), key=lambda t: (-s[t], t))
+            order = np.lexsort((np.arange(L), -s))   # score desc, index asc
             T = s[order[keep - 1]]
-            bad = [t for t in diff if abs(s[t] - T) > rel * abs(T)]
-            assert not bad, f"row {r}: {len(bad)} tokens outside the tie window, e.g. {bad[:5]}"
+            d = np.fromiter(diff, np.int64)
+            bad = d[np.abs(s[d] - T) > rel * abs(T)]
+            assert bad.size == 0, f"row {r}: {bad.size} tokens outside the tie window, e.g. {bad[:5].tolist()}"

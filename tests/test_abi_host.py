@@ -103,9 +103,9 @@ def test_score_errors(d):
     assert f(*a) == d.DSA_ERR_UNSUPPORTED
     a = list(args); a[12] = 0       # nothing to do
     assert f(*a) == d.DSA_OK
-    # FP8 queries take a workspace: rows of bf16 query heads, weights, linear-term pieces
+    # FP8 queries take a workspace: rows of bf16 query heads, and the weights
     need = d.dsa_indexer_score_workspace_size(4, d.DSA_Q_FP8_E4M3)
-    assert need >= 4 * 36 * 128 * 2 + 32 * 32 * 4
+    assert need >= 4 * 32 * 128 * 2 + 32 * 32 * 4
     assert d.dsa_indexer_score_workspace_size(4, d.DSA_Q_BF16) == 0
     assert d.dsa_indexer_score_workspace_size(0, d.DSA_Q_FP8_E4M3) == 0
     a = list(args); a[7] = 1; a[8] = FAKE; a[15] = FAKE; a[16] = need - 1

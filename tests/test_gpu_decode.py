@@ -54,13 +54,17 @@ def check_scores(got, ref, row_len):
 
 
 def check_attention(out, lse, ref_o, ref_l):
+    """The bar per query row (stricter than over the whole tensor): max|dout| <= 1e-2 of the
+    row's max|ref|, and |dlse| <= 1e-3."""
     o = out.float().cpu().numpy().astype(np.float64)
     l = lse.cpu().numpy().astype(np.float64)
     finite = np.isfinite(ref_l)
     assert np.array_equal(np.isfinite(l), finite), "empty sets must give lse = -inf exactly where the oracle does"
     assert (o[~finite] == 0).all()
-    scale = np.abs(ref_o).max()
-    assert np.abs(o - ref_o).max() <= 1e-2 * scale, f"out err {np.abs(o - ref_o).max():.3g} vs {scale:.3g}"
+    for r in range(o.shape[0]):
+        scale = np.abs(ref_o[r]).max()
+        err = np.abs(o[r] - ref_o[r]).max()
+        assert err <= 1e-2 * scale, f"row {r}: out err {err:.3g} vs {scale:.3g}"
     if finite.any():
         assert np.abs(l[finite] - ref_l[finite]).max() <= 1e-3
 

@@ -2,11 +2,13 @@
 
 Each workload (the decode configurations at 32 x 128K, 8 x 1M and 64 mixed MXFP4/NVFP4
 requests, and the 2048-row prefill chunk on a 153,600-token prefix) is built with the same
-seeds and runs the same four calls as bench.py.  Sampled rows are then checked against the
-oracle: the whole row of scores (tolerance 1e-5 of each score + 1e-5 of the row's rms), the
-top-k (bit-exact selection on the GPU's own scores, and within the 1e-5 tie window of the
-oracle's k-th score), and attention on the GPU's index set (max|dout| <= 1e-2 max|ref|,
-|dlse| <= 1e-3).
+seeds and runs the same four calls as bench.py.  Then, for EVERY row of the decode
+workloads: the whole row of scores against the oracle (tolerance 1e-5 of each score + 1e-5
+of the row's rms), the top-k (bit-exact selection on the GPU's own scores, and within the
+1e-5 tie window of the oracle's k-th score), and attention on the GPU's index set (per row,
+max|dout| <= 1e-2 max|ref|, |dlse| <= 1e-3).  The prefill chunk is checked the same way on
+all 2048 rows for scores and top-k (in eight tests of 256 rows, each a few seconds of oracle
+work), and on a seeded sample of 128 rows for attention.
 """
 import numpy as np
 import pytest
@@ -19,8 +21,8 @@ from tests.test_gpu_decode import check_attention, check_scores, log
 
 pytestmark = pytest.mark.gpu
 
-# rows checked against the oracle, per workload (first, last and a few between)
-SAMPLES = {1: [0, 17, 31], 2: [0, 7], 3: [0, 1, 40, 63], 4: [0, 1023, 2047]}
+PREFILL_CHUNK = 256
+PREFILL_ATTN_SAMPLE = 128
 
 
 @pytest.fixture(scope="module")
@@ -31,44 +33,82 @@ def d(gpu):
     return d
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
-def test_full_size_step_sampled_rows(d, cfg):
+def build_step(d, cfg):
     wl = W.WORKLOADS[cfg]
     ctx = W.workload_ctx(cfg)
-    k = wl["topk"]
     log(f"[case] full size {wl['name']}: {len(ctx)} cache requests, {sum(ctx)} tokens")
     cache = W.build_cache(ctx, key_fmt=wl["key_fmt"], lat_fmt=wl["lat_fmt"], seed=cfg, device="cuda",
                           spare_rows=wl["spare_rows"])
-    decode = wl["kind"] == "decode"
-    if decode:
-        dq = W.decode_queries(len(ctx), wl["heads"], seed=cfg, device="cuda")
-        step = d.DecodeStep(cache, dq.q_idx, dq.w, dq.q_mla, dq.sm_scale, k=k)
+    if wl["kind"] == "decode":
+        qs = W.decode_queries(len(ctx), wl["heads"], seed=cfg, device="cuda")
+        step = d.DecodeStep(cache, qs.q_idx, qs.w, qs.q_mla, qs.sm_scale, k=wl["topk"])
     else:
-        pq = W.prefill_queries(wl["prefix"], wl["chunk"], wl["heads"], seed=cfg, device="cuda")
-        step = d.PrefillStep(cache, pq, k=k, q_fmt=d.DSA_Q_FP8_E4M3)
+        qs = W.prefill_queries(wl["prefix"], wl["chunk"], wl["heads"], seed=cfg, device="cuda")
+        step = d.PrefillStep(cache, qs, k=wl["topk"], q_fmt=d.DSA_Q_FP8_E4M3)
     step.run()
     torch.cuda.synchronize()
     assert int(step.err.item()) == 0
+    return wl, ctx, cache, qs, step
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_full_size_decode_every_row(d, cfg):
+    wl, ctx, cache, dq, step = build_step(d, cfg)
+    k, n = wl["topk"], len(ctx)
     oc = oracle.OracleCache(cache)
-    for r in SAMPLES[cfg]:
-        if decode:
-            L = int(ctx[r])
-            q, fmt, qs, w, req = dq.q_idx[r:r + 1], 0, None, dq.w[r:r + 1], np.array([r], np.int32)
-            qm, qms, H, sm = dq.q_mla[r:r + 1], None, wl["heads"], dq.sm_scale
-        else:
-            L = int(pq.row_len[r].item())
-            q, fmt, qs, w = pq.q_idx_fp8[r:r + 1], 1, pq.q_idx_scale[r:r + 1], pq.w[r:r + 1]
-            req = pq.q_req[r:r + 1].cpu().numpy()
-            qm, qms, H, sm = pq.q_mla_fp8[r:r + 1], pq.q_mla_scale[r:r + 1], wl["heads"], pq.sm_scale
-        log(f"[row] {wl['name']} row {r} length {L}")
-        ref_s = oracle.indexer_score(oc, q, fmt, qs, w, req, np.array([L], np.int32))
-        got_s = step.scores[r:r + 1, :L].cpu().numpy()
-        check_scores(got_s, ref_s, [L])
-        got_idx = step.idx[r:r + 1].cpu().numpy()
-        assert np.array_equal(got_idx, oracle.topk(got_s, np.array([L], np.int32), k))
-        topk_set_ok(ref_s, oracle.topk(ref_s, np.array([L], np.int32), k), got_idx, [L], k)
-        ref_o, ref_l = oracle.sparse_mla(oc, got_idx, qm, fmt, qms, req, H, sm)
-        check_attention(step.out[r:r + 1], step.lse[r:r + 1], ref_o, ref_l)
+    rl = np.asarray(ctx, np.int32)
+    req = np.arange(n, dtype=np.int32)
+    ld = int(step.scores.shape[1])
+    got_s = step.scores.cpu().numpy()
+    got_idx = step.idx.cpu().numpy()
+    log(f"[rows] {wl['name']}: oracle scores of all {n} rows")
+    ref_s = oracle.indexer_score(oc, dq.q_idx, 0, None, dq.w, req, rl, ld=ld)
+    check_scores(got_s, ref_s, ctx)
+    log(f"[rows] {wl['name']}: top-k of all {n} rows")
+    assert np.array_equal(got_idx, oracle.topk(np.nan_to_num(got_s), rl, k))
+    topk_set_ok(ref_s, oracle.topk(ref_s, rl, k), got_idx, ctx, k)
+    log(f"[rows] {wl['name']}: attention of all {n} rows")
+    ref_o, ref_l = oracle.sparse_mla(oc, got_idx, dq.q_mla, 0, None, req, wl["heads"], dq.sm_scale)
+    check_attention(step.out, step.lse, ref_o, ref_l)
+
+
+@pytest.fixture(scope="module")
+def prefill(d):
+    wl, ctx, cache, pq, step = build_step(d, 4)
+    host = dict(scores=step.scores.cpu().numpy(), idx=step.idx.cpu().numpy(),
+                row_len=pq.row_len.cpu().numpy().astype(np.int32), q_req=pq.q_req.cpu().numpy())
+    return wl, cache, pq, step, oracle.OracleCache(cache), host
+
+
+@pytest.mark.parametrize("chunk", range(2048 // PREFILL_CHUNK))
+def test_full_size_prefill_scores_and_topk(prefill, chunk):
+    """Rows [256 chunk, 256 chunk + 256) of the 2048-row prefill chunk: whole score rows, and
+    the top-k bit-exact on the GPU's scores and within the tie window of the oracle's."""
+    wl, cache, pq, step, oc, h = prefill
+    k = wl["topk"]
+    rows = slice(chunk * PREFILL_CHUNK, (chunk + 1) * PREFILL_CHUNK)
+    rl = h["row_len"][rows]
+    ld = int(rl.max())
+    log(f"[rows] prefill rows {rows.start}..{rows.stop - 1}, lengths {rl.min()}..{rl.max()}")
+    ref_s = oracle.indexer_score(oc, pq.q_idx_fp8[rows], 1, pq.q_idx_scale[rows], pq.w[rows], h["q_req"][rows], rl,
+                                 ld=ld)
+    got_s = h["scores"][rows, :ld]
+    check_scores(got_s, ref_s, rl)
+    got_idx = h["idx"][rows]
+    assert np.array_equal(got_idx, oracle.topk(np.nan_to_num(got_s), rl, k))
+    topk_set_ok(ref_s, oracle.topk(ref_s, rl, k), got_idx, rl, k)
+
+
+def test_full_size_prefill_attention_sample(prefill):
+    """Attention of a seeded sample of 128 of the 2048 prefill rows (a sample: the other rows
+    run the same kernel on the same launch)."""
+    wl, cache, pq, step, oc, h = prefill
+    rows = np.sort(np.random.default_rng(2048).choice(2048, PREFILL_ATTN_SAMPLE, replace=False))
+    rows[0], rows[-1] = 0, 2047
+    log(f"[rows] prefill attention on {len(rows)} sampled rows")
+    ref_o, ref_l = oracle.sparse_mla(oc, h["idx"][rows], pq.q_mla_fp8[rows], 1, pq.q_mla_scale[rows],
+                                     h["q_req"][rows], wl["heads"], pq.sm_scale)
+    check_attention(step.out[rows], step.lse[rows], ref_o, ref_l)
 
 
 def test_scans_past_one_offset_batch(d):
