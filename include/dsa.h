@@ -58,6 +58,7 @@ typedef int32_t dsa_status;
 #define DSA_ERR_UNSUPPORTED 4         /* a format, head count or size the library does not run */
 #define DSA_ERR_WORKSPACE_TOO_SMALL 5 /* workspace_bytes < the *_workspace_size answer */
 #define DSA_ERR_HIP 6                 /* a HIP launch failed */
+#define DSA_ERR_SCRATCH_LIMIT 7       /* needs more than the static scratch of the *_noalloc calls */
 
 /* Bits kernels OR into *err_flag. */
 #define DSA_DEVERR_BLOCK_RANGE 1u  /* block id outside [0, pool_rows) */
@@ -237,6 +238,25 @@ dsa_status dsa_sparse_mla_prefill(const dsa_layout *layout, const uint8_t *pool,
                                   const float *q_scale, const int32_t *q_req, int32_t n_q, int32_t n_heads,
                                   float sm_scale, float kv_scale, uint16_t *out, float *lse, void *workspace,
                                   size_t workspace_bytes, int32_t *err_flag, dsa_stream_t stream);
+
+/* Sparse MLA decode that allocates nothing and takes no workspace: for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments and result
+ * as dsa_sparse_mla_decode, bit for bit (the same kernels), minus the
+ * workspace.  The split partials go to a static device array of
+ * DSA_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends; a call whose
+ * partials would not fit (dsa_sparse_mla_decode_workspace_size answers more)
+ * returns DSA_ERR_SCRATCH_LIMIT and enqueues nothing (32 MiB covers 64 requests
+ * x 12 heads x k = 2048).  Every call on a GPU shares that GPU's array:
+ * calls that overlap on one GPU (other streams, other threads) race and must
+ * be serialised by the caller.  The array's device address is looked up with
+ * hipGetSymbolAddress on a device's first call (DSA_ERR_HIP if that fails). */
+#define DSA_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+dsa_status dsa_sparse_mla_decode_noalloc(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                                         const int64_t *lat_off, int64_t off_ld, const int32_t *ctx_len,
+                                         const int32_t *idx, int64_t idx_ld, int32_t k, const uint16_t *q,
+                                         int32_t n_req, int32_t n_heads, float sm_scale, float kv_scale,
+                                         uint16_t *out, float *lse, int32_t *err_flag, dsa_stream_t stream);
 
 /* Exact top-k merge across decode-context-parallel shards, emulated on one GPU
  * ([ZH] "长上下文：带稀疏 indexer 的 decode 上下文并行": shard s of W holds every

@@ -24,7 +24,8 @@ from .build import LIB as _BUILT_LIB
 _LIB_PATH = Path(os.environ.get("DSA_LIB", str(_BUILT_LIB)))
 
 DSA_OK, DSA_ERR_NULL_ARG, DSA_ERR_BAD_SHAPE, DSA_ERR_MISALIGNED = 0, 1, 2, 3
-DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE_TOO_SMALL, DSA_ERR_HIP = 4, 5, 6
+DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE_TOO_SMALL, DSA_ERR_HIP, DSA_ERR_SCRATCH_LIMIT = 4, 5, 6, 7
+DSA_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 DSA_DEVERR_BLOCK_RANGE, DSA_DEVERR_PAGE_COUNT, DSA_DEVERR_PAGE_OFFSET = 1, 2, 4
 DSA_DEVERR_ROW_LEN, DSA_DEVERR_INDEX, DSA_DEVERR_REQUEST = 8, 16, 32
 DSA_KEY_FP8_E4M3_SCALED, DSA_KEY_MXFP4 = 0, 1
@@ -35,7 +36,7 @@ __all__ = [
     "DsaError", "dsa_layout", "lib", "dsa_status_str", "dsa_version", "dsa_layout_make", "dsa_resolve_pages",
     "dsa_indexer_score_workspace_size", "dsa_indexer_score", "dsa_indexer_score_verify", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_decode_workspace_size",
     "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill_workspace_size", "dsa_sparse_mla_prefill",
-    "dsa_dcp_topk_workspace_size", "dsa_dcp_topk",
+    "dsa_dcp_topk_workspace_size", "dsa_dcp_topk", "dsa_sparse_mla_decode_noalloc",
 ]
 
 
@@ -74,6 +75,7 @@ def _load():
         "dsa_topk": ([P, I64, P, I32, I32, P, I64, P, SZ, P, P], I32),
         "dsa_sparse_mla_decode_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
         "dsa_sparse_mla_decode": ([LP, P, I64, P, I64, P, P, I64, I32, P, I32, I32, F, F, P, P, P, SZ, P, P], I32),
+        "dsa_sparse_mla_decode_noalloc": ([LP, P, I64, P, I64, P, P, I64, I32, P, I32, I32, F, F, P, P, P, P], I32),
         "dsa_sparse_mla_prefill_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
         "dsa_dcp_topk_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
         "dsa_dcp_topk": ([P, I64, P, I32, I32, I32, P, I64, P, P, SZ, P, P], I32),
@@ -210,6 +212,20 @@ def dsa_sparse_mla_decode(layout: dsa_layout, pool, lat_off, ctx_len, idx, k: in
                                    float(sm_scale), float(kv_scale), _ptr(out, BF16, "out"), _ptr(lse, F32, "lse"),
                                    wp, wb, _ptr(err_flag, I32, "err_flag"), _stream(stream))
     _check("dsa_sparse_mla_decode", st)
+
+
+def dsa_sparse_mla_decode_noalloc(layout: dsa_layout, pool, lat_off, ctx_len, idx, k: int, q, sm_scale: float,
+                                  kv_scale: float, out, lse, err_flag=None, stream=None):
+    """dsa_sparse_mla_decode without a workspace: the library's static per-GPU scratch holds
+    the split partials (calls that overlap on one GPU race)."""
+    n_req, n_heads = q.shape[0], q.shape[1]
+    st = lib.dsa_sparse_mla_decode_noalloc(C.byref(layout), _ptr(pool, U8, "pool"), pool.numel(),
+                                           _ptr(lat_off, I64, "lat_off"), lat_off.shape[1],
+                                           _ptr(ctx_len, I32, "ctx_len"), _ptr(idx, I32, "idx"), idx.shape[1], k,
+                                           _ptr(q, BF16, "q"), n_req, n_heads, float(sm_scale), float(kv_scale),
+                                           _ptr(out, BF16, "out"), _ptr(lse, F32, "lse"),
+                                           _ptr(err_flag, I32, "err_flag"), _stream(stream))
+    _check("dsa_sparse_mla_decode_noalloc", st)
 
 
 def dsa_sparse_mla_prefill_workspace_size(n_q: int, n_heads: int, k: int) -> int:

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "dsa_device.hpp"
 #include "dsa_kernels.hpp"
 
@@ -50,6 +52,7 @@ const char *dsa_status_str(dsa_status s) {
     case DSA_ERR_UNSUPPORTED: return "format, head count or size not supported";
     case DSA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the *_workspace_size answer";
     case DSA_ERR_HIP: return "HIP launch failed";
+    case DSA_ERR_SCRATCH_LIMIT: return "the call needs more scratch than the library's static scratch array holds";
     default: return "unknown status";
   }
 }
@@ -361,6 +364,51 @@ dsa_status dsa_sparse_mla_prefill(const dsa_layout *layout, const uint8_t *pool,
   return mla_common(layout, pool, pool_bytes, lat_off, off_ld, n_req, ctx_len, idx, idx_ld, k, q, q_fmt, q_scale,
                     q_req, n_q, n_heads, sm_scale, kv_scale, out, lse, workspace, workspace_bytes, err_flag, stream,
                     prefill_tokens_per_split(k, n_heads));
+}
+
+// ---- decode attention without a caller workspace ----
+// The split partials live in one file-scope device array per GPU.  Host code must not pass
+// the array's name to a kernel (on the host it is only a stand-in symbol): its device address
+// is looked up once per device with hipGetSymbolAddress, with that device current, and only
+// that address is used.  Calls on one GPU share the array, so calls that overlap on a GPU race;
+// nothing in it needs clearing (every partial slot a call reads is written by that call).
+static __device__ __align__(256) uint8_t scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on its first use), or nullptr on a HIP error.
+void *scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+dsa_status dsa_sparse_mla_decode_noalloc(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                                         const int64_t *lat_off, int64_t off_ld, const int32_t *ctx_len,
+                                         const int32_t *idx, int64_t idx_ld, int32_t k, const uint16_t *q,
+                                         int32_t n_req, int32_t n_heads, float sm_scale, float kv_scale,
+                                         uint16_t *out, float *lse, int32_t *err_flag, dsa_stream_t stream) {
+  if (n_req < 0 || n_heads < 1 || k < 0) return DSA_ERR_BAD_SHAPE;
+  const size_t need = mla_workspace_bytes(n_req, n_heads, k, kDecodeTokensPerSplit);
+  if (need > (size_t)DSA_NOALLOC_SCRATCH_BYTES) return DSA_ERR_SCRATCH_LIMIT;
+  void *ws = nullptr;
+  if (need > 0 && n_req > 0) {
+    ws = scratch_of_current_device();
+    if (!ws) return DSA_ERR_HIP;
+  }
+  return mla_common(layout, pool, pool_bytes, lat_off, off_ld, n_req, ctx_len, idx, idx_ld, k, q, DSA_Q_BF16, nullptr,
+                    nullptr, n_req, n_heads, sm_scale, kv_scale, out, lse, ws, need, err_flag, stream,
+                    kDecodeTokensPerSplit);
 }
 
 }  // extern "C"

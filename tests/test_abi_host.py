@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(d):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(d.lib, n), n
 
@@ -221,8 +221,8 @@ def test_mla_errors(d):
 
 
 def test_status_strings(d):
-    for s in range(7):
-        assert d.dsa_status_str(s)
+    for s in range(8):
+        assert d.dsa_status_str(s) and "unknown" not in d.dsa_status_str(s)
     assert "unknown" in d.dsa_status_str(99)
 
 
@@ -232,3 +232,17 @@ def test_binding_refuses_cpu_tensors(d):
     with pytest.raises(TypeError):
         d.dsa_resolve_pages(L, 0, torch.zeros(1, 4, dtype=torch.int32), torch.zeros(1, dtype=torch.int32), 4,
                             torch.zeros(1, 4, dtype=torch.int64), torch.zeros(1, 4, dtype=torch.int64))
+
+
+def test_noalloc_rejects_beyond_its_scratch(d):
+    """The no-allocation decode checks its partials against the static scratch size before
+    any HIP call: 1000 requests x 128 heads at k = 2048 need about 4.2 GB."""
+    L = d.dsa_layout_make(64, 1, 0, 0, 0)
+    f = d.lib.dsa_sparse_mla_decode_noalloc
+    args = [C.byref(L), FAKE, 1 << 30, FAKE, 2048, FAKE, FAKE, 2048, 2048, FAKE, 1000, 128, 0.1, 1.0, FAKE, FAKE,
+            None, None]
+    assert f(*args) == d.DSA_ERR_SCRATCH_LIMIT
+    need = d.dsa_sparse_mla_decode_workspace_size(64, 12, 2048)
+    assert need <= d.DSA_NOALLOC_SCRATCH_BYTES   # the largest decode batch of the workloads fits
+    a = list(args); a[10] = -1
+    assert f(*a) == d.DSA_ERR_BAD_SHAPE
