@@ -1,7 +1,9 @@
 """Benchmark of the DSA hot path on one MI355X.
 
-Default workload: one decode layer-step (resolve -> indexer scan -> top-2048 ->
-sparse MLA) for 32 requests at 131,072 tokens of context each, FP8 index keys
+Default workload: one decode layer-step (page resolve, indexer scan, top-2048 and
+sparse MLA, through the fused path: dsa_indexer_select, whose scan finds the pages
+through the block table and whose one select kernel emits physical rows, then
+dsa_sparse_mla_decode_phys) for 32 requests at 131,072 tokens of context each, FP8 index keys
 (132 B/token) and FP8 latents (576 B/token) in a block-packed pool of 65,536
 rows, 12 query heads (one TP8 GPU's share).  Inputs are seeded, synthetic and
 resident in HBM before timing starts.
@@ -108,9 +110,11 @@ def main():
     cache = W.build_cache(ctx, key_fmt=wl["key_fmt"], lat_fmt=wl["lat_fmt"], seed=cfg_id, device=dev,
                           spare_rows=wl["spare_rows"])
     kb, lb = cache.layout["key_bytes"], cache.layout["lat_bytes"]
+    four_call = None
     if wl["kind"] == "decode":
         dq = W.decode_queries(len(ctx), wl["heads"], seed=cfg_id, device=dev)
-        step = d.DecodeStep(cache, dq.q_idx, dq.w, dq.q_mla, dq.sm_scale, k=k)
+        step = d.FusedDecodeStep(cache, dq.q_idx, dq.w, dq.q_mla, dq.sm_scale, k=k)
+        four_call = d.DecodeStep(cache, dq.q_idx, dq.w, dq.q_mla, dq.sm_scale, k=k)
     elif wl["kind"] == "verify":
         vq = W.verify_queries(ctx, wl["rows"], wl["heads"], seed=cfg_id, device=dev)
         step = d.VerifyStep(cache, vq, k=k)
@@ -128,11 +132,17 @@ def main():
 
     def scrub():
         torch.neg(scrub_src, out=scrub_dst)
-    stages = [("resolve", step.resolve), ("score", step.score), ("topk", step.topk), ("attend", step.attend)]
+    if wl["kind"] == "decode":
+        # fused path: dsa_indexer_select (its halves are the score and top-k stages) then
+        # attention over physical rows
+        stages = [("score", step.score), ("topk", step.topk), ("attend", step.attend)]
+        run_step = step.run
+    else:
+        stages = [("resolve", step.resolve), ("score", step.score), ("topk", step.topk), ("attend", step.attend)]
 
-    def run_step():
-        for _, fn in stages:
-            fn()
+        def run_step():
+            for _, fn in stages:
+                fn()
 
     for _ in range(args.warmup):
         scrub()
@@ -175,6 +185,19 @@ def main():
         per_stage[name] = float(np.mean([a.elapsed_time(b) for a, b in evs_i]))
     assert int(step.err.item()) == 0, "device error flag set"
     dcp = dcp_merge_timing(d, step, wl, scrub, args.steps) if wl["kind"] == "decode" else None
+    four_call_ms = None
+    if four_call is not None:  # the same step through the four separate calls, for comparison
+        evs_f = []
+        for i in range(args.steps + 1):
+            scrub()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            four_call.run()
+            b.record()
+            evs_f.append((a, b))
+        torch.cuda.synchronize()
+        four_call_ms = float(np.mean([a.elapsed_time(b) for a, b in evs_f[1:]]))
+        assert torch.equal(four_call.idx, step.idx), "fused and four-call top-k differ"
 
     out = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "scaling": "weak", "vs_baseline": None,
            "data": "synthetic (seeded; N(0,1) keys/latents/queries quantised to the cache formats)"}
@@ -198,8 +221,12 @@ def main():
                        "latent_format": ["fp8_e4m3 (576 B)", "nvfp4 (352 B)"][wl["lat_fmt"]], "page_tokens": 64,
                        "pool_rows": cache.pool_rows, "scrub_between_steps_bytes": 4 * scrub_src.numel()},
             "stage_us": {n: round(v * 1e3, 2) for n, v in per_stage.items()},
+            "path": "fused: dsa_indexer_select (scan via block table + page records, select with physical rows)"
+                    " -> dsa_sparse_mla_decode_phys",
+            "four_call_us_per_step": round(four_call_ms * 1e3, 1),
             "dcp_merge": dcp,
-            "roofline": {"kernel": "indexer_scan (dsa_indexer_score, bf16 queries)", "bound": "hbm",
+            "roofline": {"kernel": "indexer_scan (dsa_indexer_score_pages: block table, page records)",
+                         "bound": "hbm",
                          "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_launch": key_bytes,
                          "traffic": traffic},

@@ -37,6 +37,8 @@ __all__ = [
     "dsa_indexer_score_workspace_size", "dsa_indexer_score", "dsa_indexer_score_verify", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_decode_workspace_size",
     "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill_workspace_size", "dsa_sparse_mla_prefill",
     "dsa_dcp_topk_workspace_size", "dsa_dcp_topk", "dsa_sparse_mla_decode_noalloc",
+    "dsa_indexer_select_workspace_size", "dsa_indexer_select", "dsa_sparse_mla_decode_phys",
+    "dsa_indexer_score_pages", "dsa_topk_pages",
 ]
 
 
@@ -76,6 +78,12 @@ def _load():
         "dsa_sparse_mla_decode_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
         "dsa_sparse_mla_decode": ([LP, P, I64, P, I64, P, P, I64, I32, P, I32, I32, F, F, P, P, P, SZ, P, P], I32),
         "dsa_sparse_mla_decode_noalloc": ([LP, P, I64, P, I64, P, P, I64, I32, P, I32, I32, F, F, P, P, P, P], I32),
+        "dsa_indexer_select_workspace_size": ([I32, I64, C.POINTER(SZ)], I32),
+        "dsa_indexer_select": ([LP, I32, P, I64, P, I64, I32, P, P, P, P, I32, I32, P, I64, P, P, I64, P, SZ, P, P],
+                               I32),
+        "dsa_sparse_mla_decode_phys": ([LP, I32, P, I64, P, I64, I32, P, I32, I32, F, F, P, P, P, SZ, P, P], I32),
+        "dsa_indexer_score_pages": ([LP, I32, P, I64, P, I64, I32, P, P, P, P, I32, P, I64, P, SZ, P, P], I32),
+        "dsa_topk_pages": ([LP, I64, P, I64, I32, P, P, I64, P, I32, I32, P, SZ, P, P, I64, P, P], I32),
         "dsa_sparse_mla_prefill_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
         "dsa_dcp_topk_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
         "dsa_dcp_topk": ([P, I64, P, I32, I32, I32, P, I64, P, P, SZ, P, P], I32),
@@ -189,6 +197,62 @@ def dsa_topk(scores, row_len, k: int, idx, workspace, err_flag=None, stream=None
     _check("dsa_topk", st)
 
 
+def dsa_indexer_select_workspace_size(n_q: int, ld: int) -> int:
+    out = C.c_size_t()
+    _check("dsa_indexer_select_workspace_size", lib.dsa_indexer_select_workspace_size(n_q, ld, C.byref(out)))
+    return out.value
+
+
+def dsa_indexer_select(layout: dsa_layout, layer: int, pool, block_table, n_req: int, q, w, q_req, row_len, k: int,
+                       scores, idx, phys, workspace, err_flag=None, stream=None):
+    """Fused decode indexer: scores, the exact top-k (ascending) and their physical rows."""
+    n_q = q.shape[0]
+    st = lib.dsa_indexer_select(C.byref(layout), layer, _ptr(pool, U8, "pool"), pool.numel(),
+                                _ptr(block_table, I32, "block_table"), block_table.shape[1], n_req,
+                                _ptr(q, BF16, "q"), _ptr(w, F32, "w"), _ptr(q_req, I32, "q_req"),
+                                _ptr(row_len, I32, "row_len"), n_q, k, _ptr(scores, F32, "scores"), scores.shape[1],
+                                _ptr(idx, I32, "idx"), _ptr(phys, I32, "phys"), idx.shape[1],
+                                _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+                                _ptr(err_flag, I32, "err_flag"), _stream(stream))
+    _check("dsa_indexer_select", st)
+
+
+def dsa_indexer_score_pages(layout: dsa_layout, layer: int, pool, block_table, n_req: int, q, w, q_req, row_len,
+                            scores, workspace, err_flag=None, stream=None):
+    """First half of dsa_indexer_select: the scan, with the per-page records in `workspace`."""
+    st = lib.dsa_indexer_score_pages(C.byref(layout), layer, _ptr(pool, U8, "pool"), pool.numel(),
+                                     _ptr(block_table, I32, "block_table"), block_table.shape[1], n_req,
+                                     _ptr(q, BF16, "q"), _ptr(w, F32, "w"), _ptr(q_req, I32, "q_req"),
+                                     _ptr(row_len, I32, "row_len"), q.shape[0], _ptr(scores, F32, "scores"),
+                                     scores.shape[1], _ptr(workspace, None, "workspace"),
+                                     workspace.numel() * workspace.element_size(), _ptr(err_flag, I32, "err_flag"),
+                                     _stream(stream))
+    _check("dsa_indexer_score_pages", st)
+
+
+def dsa_topk_pages(layout: dsa_layout, pool, block_table, n_req: int, q_req, scores, row_len, k: int, workspace, idx,
+                   phys=None, err_flag=None, stream=None):
+    """Second half of dsa_indexer_select: the exact top-k from the records and the scores."""
+    st = lib.dsa_topk_pages(C.byref(layout), pool.numel(), _ptr(block_table, I32, "block_table"), block_table.shape[1],
+                            n_req, _ptr(q_req, I32, "q_req"), _ptr(scores, F32, "scores"), scores.shape[1],
+                            _ptr(row_len, I32, "row_len"), scores.shape[0], k, _ptr(workspace, None, "workspace"),
+                            workspace.numel() * workspace.element_size(), _ptr(idx, I32, "idx"),
+                            _ptr(phys, I32, "phys"), idx.shape[1], _ptr(err_flag, I32, "err_flag"), _stream(stream))
+    _check("dsa_topk_pages", st)
+
+
+def dsa_sparse_mla_decode_phys(layout: dsa_layout, layer: int, pool, phys, k: int, q, sm_scale: float,
+                               kv_scale: float, out, lse, workspace=None, err_flag=None, stream=None):
+    n_req, n_heads = q.shape[0], q.shape[1]
+    wp, wb = _ws(workspace)
+    st = lib.dsa_sparse_mla_decode_phys(C.byref(layout), layer, _ptr(pool, U8, "pool"), pool.numel(),
+                                        _ptr(phys, I32, "phys"), phys.shape[1], k, _ptr(q, BF16, "q"), n_req, n_heads,
+                                        float(sm_scale), float(kv_scale), _ptr(out, BF16, "out"),
+                                        _ptr(lse, F32, "lse"), wp, wb, _ptr(err_flag, I32, "err_flag"),
+                                        _stream(stream))
+    _check("dsa_sparse_mla_decode_phys", st)
+
+
 def dsa_sparse_mla_decode_workspace_size(n_req: int, n_heads: int, k: int) -> int:
     out = C.c_size_t()
     _check("dsa_sparse_mla_decode_workspace_size",
@@ -266,4 +330,4 @@ def dsa_dcp_topk(scores, row_len, k: int, n_shards: int, idx, workspace, resend_
     _check("dsa_dcp_topk", st)
 
 
-from .step import DecodeStep, PrefillStep, VerifyStep  # noqa: E402,F401
+from .step import DecodeStep, FusedDecodeStep, PrefillStep, VerifyStep  # noqa: E402,F401

@@ -16,7 +16,9 @@
 //           token-major LDS tile Kt[64][576];
 //   QK      wave w: S^T[16 tokens][16 heads] = Kt[16w..] . Q^T, 18 v_mfma_f32_16x16x32_bf16;
 //   softmax online, per head, in log2 units; P is rounded to bf16 once and the same
-//           rounded values feed both P.V and the row sum;
+//           rounded values feed both P.V and the row sum that normalises O; the LSE takes
+//           a second row sum of the unrounded p (with few tokens the rounding of P would
+//           not average out of the LSE);
 //   PV      wave w: O^T[128 dims][16 heads] += V^T . P^T over the 64 tokens.  The V^T
 //           operand (8 consecutive tokens of one dim per lane) is read from the same
 //           token-major tile with ds_read_b64_tr_b16: in each 16-lane group, source lane
@@ -45,7 +47,7 @@ constexpr int kMaxTps = 2048;
 
 struct MlaWs {
   float *o;    // [n_q][nsplit][H][512] unnormalised partial outputs
-  float2 *ml;  // [n_q][nsplit][H] (running max in log2 units, sum)
+  float4 *ml;  // [n_q][nsplit][H] (running max in log2 units, sum of the bf16-rounded p, fp32 sum of p, 0)
 };
 
 __host__ __device__ inline int64_t a16(int64_t x) { return (x + 15) & ~int64_t(15); }
@@ -55,7 +57,7 @@ __host__ __device__ inline MlaWs mla_carve(void *ws, int32_t n_q, int32_t H, int
   uint8_t *p = static_cast<uint8_t *>(ws);
   w.o = reinterpret_cast<float *>(p);
   p += a16(4 * (int64_t)n_q * nsplit * H * kVDim);
-  w.ml = reinterpret_cast<float2 *>(p);
+  w.ml = reinterpret_cast<float4 *>(p);
   return w;
 }
 
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(256, 2) void mla_kernel(const MlaArgs a, const int 
   constexpr int64_t LPB = (int64_t)kPage * LB;
   __shared__ __align__(16) uint16_t s_kt[kSub * kKtLd];
   __shared__ __align__(16) uint16_t s_p[4][64 * 4];
-  __shared__ float s_red[2][4][16];
+  __shared__ float s_red[3][4][16];
   extern __shared__ int64_t s_off[];  // [tps]: pool offset of each of the split's tokens
 
   const int ht = blockIdx.x, sp = blockIdx.y, r = blockIdx.z;
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(256, 2) void mla_kernel(const MlaArgs a, const int 
   const int b = a.q_req ? a.q_req[r] : r;
   const bool rvalid = b >= 0 && b < a.n_req;
   if (!rvalid && tid == 0 && sp == 0 && ht == 0) flag_error(a.err, DSA_DEVERR_REQUEST);
-  const int ctx = rvalid ? a.ctx_len[b] : 0;
+  const int ctx = rvalid && !a.phys ? a.ctx_len[b] : 0;
   const int t_beg = sp * tps;
   const int n_tok = max(0, min(a.k, t_beg + tps) - t_beg);
 
@@ -124,7 +126,16 @@ __global__ __launch_bounds__(256, 2) void mla_kernel(const MlaArgs a, const int 
   // (0) pool offsets of the split's tokens (-1: padding or invalid)
   for (int j = tid; j < n_tok; j += 256) {
     int64_t off = -1;
-    if (rvalid) {
+    if (rvalid && a.phys) {  // physical rows: the address needs no page-table read
+      const int pr = a.idx[(int64_t)r * a.idx_ld + t_beg + j];
+      if (pr >= 0) {
+        const int64_t o = (int64_t)(pr >> 6) * a.row_stride + a.layer_off + (int64_t)(pr & 63) * LB;
+        if ((pr >> 6) >= a.pool_rows || o + LB > a.pool_bytes)
+          flag_error(a.err, DSA_DEVERR_BLOCK_RANGE);
+        else
+          off = o;
+      }
+    } else if (rvalid) {
       const int t = a.idx[(int64_t)r * a.idx_ld + t_beg + j];
       if (t >= 0) {
         const int pg = t >> 6;
@@ -211,7 +222,7 @@ __global__ __launch_bounds__(256, 2) void mla_kernel(const MlaArgs a, const int 
     }
   };
 
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f, lf_run = 0.0f;
   f32x4_t o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4_t{};
@@ -241,20 +252,27 @@ __global__ __launch_bounds__(256, 2) void mla_kernel(const MlaArgs a, const int 
     const float m_new =
         fmaxf(m_run, fmaxf(fmaxf(s_red[0][0][hl], s_red[0][1][hl]), fmaxf(s_red[0][2][hl], s_red[0][3][hl])));
     const float alpha = m_new == -INFINITY ? 1.0f : exp2f(m_run - m_new);
-    float ps = 0.0f;
+    float ps = 0.0f, pf = 0.0f;
     bf16x4_t pb;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float p = z[i] == -INFINITY ? 0.0f : exp2f(z[i] - m_new);
       pb[i] = (__bf16)p;
       ps += (float)pb[i];
+      pf += p;
     }
     *reinterpret_cast<bf16x4_t *>(s_p[wid] + 4 * lane) = pb;
     ps += __shfl_xor(ps, 16, 64);
     ps += __shfl_xor(ps, 32, 64);
-    if (g == 0) s_red[1][wid][hl] = ps;
+    pf += __shfl_xor(pf, 16, 64);
+    pf += __shfl_xor(pf, 32, 64);
+    if (g == 0) {
+      s_red[1][wid][hl] = ps;
+      s_red[2][wid][hl] = pf;
+    }
     __syncthreads();
     l_run = l_run * alpha + ((s_red[1][0][hl] + s_red[1][1][hl]) + (s_red[1][2][hl] + s_red[1][3][hl]));
+    lf_run = lf_run * alpha + ((s_red[2][0][hl] + s_red[2][1][hl]) + (s_red[2][2][hl] + s_red[2][3][hl]));
     m_run = m_new;
 
     // (3) O^T += V^T P^T.  K-step ks covers tokens 32ks..32ks+31; k-slot j of group g is
@@ -290,13 +308,13 @@ __global__ __launch_bounds__(256, 2) void mla_kernel(const MlaArgs a, const int 
       for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[dt][i] * inv);
       *reinterpret_cast<bf16x4_t *>(orow + 128 * wid + 16 * dt + 4 * g) = v;
     }
-    if (wid == 0 && g == 0) a.lse[(int64_t)r * H + h] = l_run > 0.0f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+    if (wid == 0 && g == 0) a.lse[(int64_t)r * H + h] = lf_run > 0.0f ? (m_run + log2f(lf_run)) * kLn2 : -INFINITY;
   } else {
     const int64_t slot = ((int64_t)r * nsplit + sp) * H + h;
     float *po = w.o + slot * kVDim;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4_t *>(po + 128 * wid + 16 * dt + 4 * g) = o[dt];
-    if (wid == 0 && g == 0) w.ml[slot] = make_float2(m_run, l_run);
+    if (wid == 0 && g == 0) w.ml[slot] = make_float4(m_run, l_run, lf_run, 0.0f);
   }
 }
 
@@ -432,7 +450,7 @@ __global__ __launch_bounds__(kWideThreads) void mla_wide_kernel(const MlaArgs a,
     }
   };
 
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f, lf_run = 0.0f;
   f32x4_t o[32];
 #pragma unroll
   for (int dt = 0; dt < 32; ++dt) o[dt] = f32x4_t{};
@@ -469,7 +487,7 @@ __global__ __launch_bounds__(kWideThreads) void mla_wide_kernel(const MlaArgs a,
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_run, mx);
       const float alpha = m_new == -INFINITY ? 1.0f : exp2f(m_run - m_new);
-      float ps = 0.0f;
+      float ps = 0.0f, pf = 0.0f;
 #pragma unroll
       for (int tg = 0; tg < 4; ++tg) {
         bf16x4_t pb;
@@ -478,12 +496,16 @@ __global__ __launch_bounds__(kWideThreads) void mla_wide_kernel(const MlaArgs a,
           const float p = z[tg][i] == -INFINITY ? 0.0f : exp2f(z[tg][i] - m_new);
           pb[i] = (__bf16)p;
           ps += (float)pb[i];
+          pf += p;
         }
         *reinterpret_cast<bf16x4_t *>(my_p + 256 * tg + 4 * lane) = pb;
       }
       ps += __shfl_xor(ps, 16, 64);
       ps += __shfl_xor(ps, 32, 64);
+      pf += __shfl_xor(pf, 16, 64);
+      pf += __shfl_xor(pf, 32, 64);
       l_run = l_run * alpha + ps;
+      lf_run = lf_run * alpha + pf;
       m_run = m_new;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // P written by the whole wave
       __builtin_amdgcn_wave_barrier();
@@ -520,13 +542,13 @@ __global__ __launch_bounds__(kWideThreads) void mla_wide_kernel(const MlaArgs a,
       for (int i = 0; i < 4; ++i) vv[i] = (__bf16)(o[dt][i] * inv);
       *reinterpret_cast<bf16x4_t *>(orow + 16 * dt + 4 * g) = vv;
     }
-    if (g == 0) a.lse[(int64_t)r * H + h] = l_run > 0.0f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+    if (g == 0) a.lse[(int64_t)r * H + h] = lf_run > 0.0f ? (m_run + log2f(lf_run)) * kLn2 : -INFINITY;
   } else {
     const int64_t slot = ((int64_t)r * nsplit + sp) * H + h;
     float *po = w.o + slot * kVDim;
 #pragma unroll
     for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<f32x4_t *>(po + 16 * dt + 4 * g) = o[dt];
-    if (g == 0) w.ml[slot] = make_float2(m_run, l_run);
+    if (g == 0) w.ml[slot] = make_float4(m_run, l_run, lf_run, 0.0f);
   }
 }
 
@@ -711,11 +733,12 @@ __global__ __launch_bounds__(kPfThreads, 1) void mla_prefill_kernel(const MlaArg
   // are 4 wid .. 4 wid + 3 (byte 128 wid of a row).
   const int vofs = (8 * g + ((lane & 15) >> 1)) * kPfRow + 16 * ((lane >> 4) & 1) + 8 * (lane & 1) + 128 * wid;
 
-  float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.0f;
+  float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.0f, lf_run = 0.0f;
   f32x16_t o[NHT][kPfBlocks];
   for (int pass = 0; pass < 2; ++pass) {
     bool over = false;
     l_run = 0.0f;
+    lf_run = 0.0f;
 #pragma unroll
     for (int t = 0; t < NHT; ++t)
 #pragma unroll
@@ -757,7 +780,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void mla_prefill_kernel(const MlaArg
       m_true = fmaxf(m_true, mx);
       over |= mx > m_ref + kRefSlack;
       const float mr = m_ref == -INFINITY ? 0.0f : m_ref;
-      float ls = 0.0f;
+      float ls = 0.0f, lf = 0.0f;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         u32x4_t pk;
@@ -768,10 +791,12 @@ __global__ __launch_bounds__(kPfThreads, 1) void mla_prefill_kernel(const MlaArg
           const bf16x2_t pb = __builtin_convertvector(pp, bf16x2_t);
           pk[m2] = __builtin_bit_cast(uint32_t, pb);
           ls = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, ls, false);
+          lf += pp[0] + pp[1];
         }
         s_p[j & 1][wid][s2][lane] = pk;
       }
       l_run += ls;
+      lf_run += lf;
     };
     // O^T += V^T P^T of subtile j over this wave's 4 dim blocks: step st = 4 s2 + db
     auto pv = [&](int j) {
@@ -854,9 +879,10 @@ __global__ __launch_bounds__(kPfThreads, 1) void mla_prefill_kernel(const MlaArg
   __builtin_amdgcn_s_waitcnt(0x0F70);  // nothing in flight into LDS
 
   // row sums of every head, from the QK waves to all
-  float l_tot = 0.0f;
+  float l_tot = 0.0f, lf_tot = 0.0f;
   if (computes) {
     l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    lf_tot = lf_run + __shfl_xor(lf_run, 32, 64);
     if (g == 0) s_l[32 * wid + n] = l_tot;
   }
   __syncthreads();
@@ -895,9 +921,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void mla_prefill_kernel(const MlaArg
   }
   if (hvalid && g == 0) {
     if (nsplit == 1)
-      a.lse[(int64_t)r * H + h] = l_tot > 0.0f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+      a.lse[(int64_t)r * H + h] = lf_tot > 0.0f ? (m_ref + log2f(lf_tot)) * kLn2 : -INFINITY;
     else
-      w.ml[((int64_t)r * nsplit + sp) * H + h] = make_float2(m_ref, l_tot);
+      w.ml[((int64_t)r * nsplit + sp) * H + h] = make_float4(m_ref, l_tot, lf_tot, 0.0f);
   }
 }
 
@@ -912,14 +938,15 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const MlaArgs a, const
   float M = -INFINITY;
 #pragma unroll 8
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, w.ml[base + (int64_t)s * H].x);
-  float L = 0.0f;
+  float L = 0.0f, LF = 0.0f;
   f32x4_t acc = {};
   if (M != -INFINITY) {
 #pragma unroll 8
     for (int s = 0; s < nsplit; ++s) {
-      const float2 ml = w.ml[base + (int64_t)s * H];  // second read hits the cache
+      const float4 ml = w.ml[base + (int64_t)s * H];  // second read hits the cache
       const float f = ml.x == -INFINITY ? 0.0f : exp2f(ml.x - M);
       L += ml.y * f;
+      LF += ml.z * f;
       acc += *reinterpret_cast<const f32x4_t *>(w.o + (base + (int64_t)s * H) * kVDim + 4 * d4) * f;
     }
   }
@@ -928,7 +955,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const MlaArgs a, const
 #pragma unroll
   for (int i = 0; i < 4; ++i) v[i] = (__bf16)(acc[i] * inv);
   *reinterpret_cast<bf16x4_t *>(a.out + ((int64_t)r * H + h) * kVDim + 4 * d4) = v;
-  if (d4 == 0) a.lse[(int64_t)r * H + h] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  if (d4 == 0) a.lse[(int64_t)r * H + h] = LF > 0.0f ? (M + log2f(LF)) * kLn2 : -INFINITY;
 }
 
 template <int LAT_FMT, int Q_FMT>
@@ -944,7 +971,7 @@ int split_count(int32_t k, int32_t tps) { return k <= 0 ? 1 : (k + tps - 1) / tp
 size_t mla_workspace_bytes(int32_t n_q, int32_t n_heads, int32_t k, int32_t tokens_per_split) {
   const int nsplit = split_count(k, tokens_per_split);
   if (nsplit == 1) return 0;
-  return (size_t)(a16(4 * (int64_t)n_q * nsplit * n_heads * kVDim) + 8 * (int64_t)n_q * nsplit * n_heads);
+  return (size_t)(a16(4 * (int64_t)n_q * nsplit * n_heads * kVDim) + 16 * (int64_t)n_q * nsplit * n_heads);
 }
 
 hipError_t launch_mla(const MlaArgs &a, hipStream_t s) {
@@ -954,6 +981,7 @@ hipError_t launch_mla(const MlaArgs &a, hipStream_t s) {
   if (tps > kMaxTps || tps % kSub != 0 || nsplit > kCombineMaxSplits) return hipErrorInvalidValue;
   const MlaWs w = mla_carve(a.ws, a.n_q, a.n_heads, nsplit);
   const int nht = (a.n_heads + 15) / 16;
+  if (a.phys && a.q_fmt != 0) return hipErrorInvalidValue;  // physical rows: the decode kernel only
   if (a.q_fmt == 1 && nht > 2 && nht <= kWideMaxTiles) {
     // every head of a row per workgroup: one gather per subtile for all heads
     dim3 grid(1, nsplit, a.n_q);

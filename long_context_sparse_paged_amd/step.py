@@ -1,19 +1,23 @@
-"""One DSA layer-step, as a sequence of the four C entry points.
+"""One DSA layer-step, as a sequence of the C entry points.
 
 ``DecodeStep`` / ``PrefillStep`` own the device buffers a step needs (page
 offsets, scores, selected indices, outputs, workspaces) and call
 dsa_resolve_pages -> dsa_indexer_score -> dsa_topk -> dsa_sparse_mla_* on one
 stream; ``VerifyStep`` does the same for speculative verification, with
 dsa_indexer_score_verify reading each key page once for all rows of a request.
+``FusedDecodeStep`` is the fused decode path: dsa_indexer_select (page resolve,
+scores, exact top-k and physical rows in two kernels) -> dsa_sparse_mla_decode_phys.
 No arithmetic happens here.
 """
 from __future__ import annotations
 
 import torch
 
-from . import (DSA_Q_BF16, DSA_Q_FP8_E4M3, dsa_indexer_score, dsa_indexer_score_verify, dsa_indexer_score_workspace_size, dsa_layout_make, dsa_resolve_pages, dsa_sparse_mla_decode,
+from . import (DSA_Q_BF16, DSA_Q_FP8_E4M3, dsa_indexer_score, dsa_indexer_score_pages, dsa_indexer_score_verify,
+               dsa_indexer_score_workspace_size, dsa_indexer_select, dsa_indexer_select_workspace_size,
+               dsa_layout_make, dsa_resolve_pages, dsa_sparse_mla_decode, dsa_sparse_mla_decode_phys,
                dsa_sparse_mla_decode_workspace_size, dsa_sparse_mla_prefill, dsa_sparse_mla_prefill_workspace_size,
-               dsa_topk, dsa_topk_workspace_size)
+               dsa_topk, dsa_topk_pages, dsa_topk_workspace_size)
 
 
 def _layout_of(cache):
@@ -155,4 +159,59 @@ class VerifyStep(_Base):
         self.resolve(stream)
         self.score(stream)
         self.topk(stream)
+        self.attend(stream)
+
+
+class FusedDecodeStep:
+    """Fused decode: the scan reads pages through the block table and records each page's
+    best scores, one select kernel emits the exact top-k with physical rows, and attention
+    reads those rows directly.  The same results as DecodeStep (bit for bit)."""
+
+    def __init__(self, cache, q_idx, w, q_mla, sm_scale: float, k: int = 2048, device="cuda"):
+        self.cache = cache
+        self.layout = _layout_of(cache)
+        self.k = k
+        n_req = cache.block_table.shape[0]
+        ld = int(cache.ctx_len.max().item()) if n_req else 1
+        ld = max(4, (ld + 3) // 4 * 4)  # score rows start on 16 B
+        self.q_idx, self.w, self.q_mla = q_idx, w, q_mla
+        self.sm_scale = sm_scale
+        self.n_heads = q_mla.shape[1]
+        self.q_req = torch.arange(n_req, dtype=torch.int32, device=device)
+        self.row_len = cache.ctx_len
+        self.scores = torch.empty(n_req, ld, dtype=torch.float32, device=device)
+        self.idx = torch.empty(n_req, k, dtype=torch.int32, device=device)
+        self.phys = torch.empty(n_req, k, dtype=torch.int32, device=device)
+        self.ws_sel = torch.empty(max(dsa_indexer_select_workspace_size(n_req, ld), 256), dtype=torch.uint8,
+                                  device=device)
+        self.out = torch.empty(n_req, self.n_heads, 512, dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty(n_req, self.n_heads, dtype=torch.float32, device=device)
+        nb = dsa_sparse_mla_decode_workspace_size(n_req, self.n_heads, k)
+        self.ws_mla = torch.empty(nb, dtype=torch.uint8, device=device) if nb else None
+        self.err = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def select(self, stream=None):
+        c = self.cache
+        dsa_indexer_select(self.layout, c.layer, c.pool, c.block_table, c.n_req, self.q_idx, self.w, self.q_req,
+                           self.row_len, self.k, self.scores, self.idx, self.phys, self.ws_sel, self.err, stream)
+
+    def score(self, stream=None):
+        """The select's first half alone (scan and page records)."""
+        c = self.cache
+        dsa_indexer_score_pages(self.layout, c.layer, c.pool, c.block_table, c.n_req, self.q_idx, self.w, self.q_req,
+                                self.row_len, self.scores, self.ws_sel, self.err, stream)
+
+    def topk(self, stream=None):
+        """The select's second half alone (needs score() first)."""
+        c = self.cache
+        dsa_topk_pages(self.layout, c.pool, c.block_table, c.n_req, self.q_req, self.scores, self.row_len, self.k,
+                       self.ws_sel, self.idx, self.phys, self.err, stream)
+
+    def attend(self, stream=None):
+        c = self.cache
+        dsa_sparse_mla_decode_phys(self.layout, c.layer, c.pool, self.phys, self.k, self.q_mla, self.sm_scale,
+                                   c.kv_scale, self.out, self.lse, self.ws_mla, self.err, stream)
+
+    def run(self, stream=None):
+        self.select(stream)
         self.attend(stream)

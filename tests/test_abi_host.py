@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(d):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 21
     for n in names:
         assert hasattr(d.lib, n), n
 
@@ -246,3 +246,61 @@ def test_noalloc_rejects_beyond_its_scratch(d):
     assert need <= d.DSA_NOALLOC_SCRATCH_BYTES   # the largest decode batch of the workloads fits
     a = list(args); a[10] = -1
     assert f(*a) == d.DSA_ERR_BAD_SHAPE
+
+
+def test_fused_select_errors(d):
+    """dsa_indexer_select and its two halves reject bad arguments before any launch."""
+    L = d.dsa_layout_make(64, 2, 0, 0, 0)
+    need = d.dsa_indexer_select_workspace_size(4, 1024)
+    assert need >= 4 * 16 * 20                    # 20 B of page records per page and row
+    f = d.lib.dsa_indexer_select
+    # layout, layer, pool, pool_bytes, bt, bt_ld, n_req, q, w, q_req, row_len, n_q, k, scores, ld,
+    # idx, phys, idx_ld, ws, ws_bytes, err, stream
+    args = [C.byref(L), 0, FAKE, 1 << 30, FAKE, 16, 4, FAKE, FAKE, FAKE, FAKE, 4, 2048, FAKE, 1024, FAKE, FAKE, 2048,
+            FAKE, need, None, None]
+    a = list(args); a[1] = 2
+    assert f(*a) == d.DSA_ERR_BAD_SHAPE           # layer past n_layers
+    a = list(args); a[14] = 1022
+    assert f(*a) == d.DSA_ERR_BAD_SHAPE           # ld not a multiple of 4
+    a = list(args); a[14] = (1 << 20) + 4
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED         # rows past 2^20 tokens
+    a = list(args); a[12] = 4097; a[17] = 4097
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED
+    a = list(args); a[12] = 0
+    assert f(*a) == d.DSA_ERR_BAD_SHAPE
+    a = list(args); a[17] = 100
+    assert f(*a) == d.DSA_ERR_BAD_SHAPE           # idx_ld < k
+    a = list(args); a[19] = need - 1
+    assert f(*a) == d.DSA_ERR_WORKSPACE_TOO_SMALL
+    a = list(args); a[13] = ODD
+    assert f(*a) == d.DSA_ERR_MISALIGNED          # scores must be 16-B aligned
+    a = list(args); a[4] = None
+    assert f(*a) == d.DSA_ERR_NULL_ARG
+    a = list(args); a[11] = 0
+    assert f(*a) == d.DSA_OK                      # nothing to do
+    a = list(args); a[11] = 5000
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED
+    # phys output needs pool_row * 64 + slot to fit int32
+    a = list(args); a[3] = (1 << 25) * L.row_stride
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED
+    g = d.lib.dsa_topk_pages
+    targs = [C.byref(L), 1 << 30, FAKE, 16, 4, FAKE, FAKE, 1024, FAKE, 4, 2048, FAKE, need, FAKE, FAKE, 2048, None,
+             None]
+    a = list(targs); a[10] = 0
+    assert g(*a) == d.DSA_ERR_BAD_SHAPE
+    a = list(targs); a[12] = 0
+    assert g(*a) == d.DSA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_mla_phys_errors(d):
+    L = d.dsa_layout_make(64, 1, 0, 0, 0)
+    f = d.lib.dsa_sparse_mla_decode_phys
+    args = [C.byref(L), 0, FAKE, 1 << 30, FAKE, 2048, 2048, FAKE, 4, 12, 0.1, 1.0, FAKE, FAKE, FAKE, 1 << 30, None, None]
+    a = list(args); a[1] = 1
+    assert f(*a) == d.DSA_ERR_BAD_SHAPE
+    a = list(args); a[9] = 129
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED
+    a = list(args); a[15] = 16
+    assert f(*a) == d.DSA_ERR_WORKSPACE_TOO_SMALL
+    a = list(args); a[4] = None
+    assert f(*a) == d.DSA_ERR_NULL_ARG
