@@ -1,9 +1,9 @@
 """Benchmark of the DSA hot path on one MI355X.
 
-Default workload: one decode layer-step (page resolve, indexer scan, top-2048 and
-sparse MLA, through the fused path: dsa_indexer_select, whose scan finds the pages
-through the block table and whose one select kernel emits physical rows, then
-dsa_sparse_mla_decode_phys) for 32 requests at 131,072 tokens of context each, FP8 index keys
+Default workload: one decode layer-step (indexer scan, top-2048 and sparse MLA, through
+the fused path: dsa_indexer_select, whose scan finds the pages through the block table and
+whose top-k emits physical rows, then dsa_sparse_mla_decode_phys) for 32 requests at
+131,072 tokens of context each, FP8 index keys
 (132 B/token) and FP8 latents (576 B/token) in a block-packed pool of 65,536
 rows, 12 query heads (one TP8 GPU's share).  Inputs are seeded, synthetic and
 resident in HBM before timing starts.
@@ -221,11 +221,11 @@ def main():
                        "latent_format": ["fp8_e4m3 (576 B)", "nvfp4 (352 B)"][wl["lat_fmt"]], "page_tokens": 64,
                        "pool_rows": cache.pool_rows, "scrub_between_steps_bytes": 4 * scrub_src.numel()},
             "stage_us": {n: round(v * 1e3, 2) for n, v in per_stage.items()},
-            "path": "fused: dsa_indexer_select (scan via block table + page records, select with physical rows)"
+            "path": "fused: dsa_indexer_select (scan via block table, top-k with physical rows)"
                     " -> dsa_sparse_mla_decode_phys",
             "four_call_us_per_step": round(four_call_ms * 1e3, 1),
             "dcp_merge": dcp,
-            "roofline": {"kernel": "indexer_scan (dsa_indexer_score_pages: block table, page records)",
+            "roofline": {"kernel": "indexer_scan (dsa_indexer_score_pages: pages via the block table)",
                          "bound": "hbm",
                          "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_launch": key_bytes,

@@ -245,9 +245,9 @@ dsa_status dsa_sparse_mla_prefill(const dsa_layout *layout, const uint8_t *pool,
 
 /* Fused indexer for decode: score -> exact top-k -> physical rows
  * ([ZH] "低延迟解码：融合的 DSA 解码路径": the fused indexer is a key-balanced
- * scorer and an exact top-k selection in two kernels, and it outputs the
- * physical KV rows attention reads; "面向三种状态的 KV 缓存": the pages are
- * found through the block table).  For each row r (request b = q_req[r]):
+ * scorer and an exact top-k selection, and it outputs the physical KV rows
+ * attention reads; "面向三种状态的 KV 缓存": the pages are found through the
+ * block table).  For each row r (request b = q_req[r]):
  *   scores[r][t] for t < row_len[r] exactly as dsa_indexer_score with bf16
  *   queries (same kernel, bit for bit), with each key page read through the
  *   block table (pool row * row_stride + layer * layer_stride + the latent
@@ -259,42 +259,37 @@ dsa_status dsa_sparse_mla_prefill(const dsa_layout *layout, const uint8_t *pool,
  *   block_table[b][t / 64] * 64 + t % 64, or -1 (padding; also for a block
  *   id outside [0, pool_rows), which flags DSA_DEVERR_BLOCK_RANGE), with
  *   pool_rows = pool_bytes / row_stride.
- * Two launches on `stream`: the scan, which also records each page's four
- * largest scores, then one selection kernel per row, which bounds the k-th
- * score from those records and reads in full only the pages that may hold
- * more than their four best (rows of up to 12,288 tokens, and rows whose
- * records cannot bound it closely, are selected from the whole row).
+ * Launches on `stream`: the scan, then dsa_topk's kernels, whose last one
+ * looks up each kept token's block as it writes it.  No page-offset table and
+ * no separate resolve launch.
  *   pool         device uint8, pool_bytes long, 16-B aligned
- *   block_table  device int32 [n_req][bt_ld]; row_len[r] <= 64 * bt_ld
+ *   block_table  device int32 [n_req][bt_ld]; row_len[r] <= 64 * bt_ld (else
+ *                DSA_DEVERR_ROW_LEN and the row is cut there)
  *   q            device bf16 [n_q][32][128], 16-B aligned; w device fp32 [n_q][32]
  *   q_req, row_len  device int32 [n_q]
- *   scores       device fp32 [n_q][ld] (out), 16-B aligned, ld a multiple of 4
+ *   scores       device fp32 [n_q][ld] (out)
  *   idx, phys    device int32 [n_q][idx_ld] (out), idx_ld >= k
  *   workspace    device, >= dsa_indexer_select_workspace_size(n_q, ld) bytes
- *                (20 B per 64-token page of each row), 256-B aligned
- * 1 <= k <= 4096, n_q <= 4096, ld <= 2^20 (else DSA_ERR_UNSUPPORTED); with
+ *                (the same as dsa_topk's), 16-B aligned
+ * 1 <= k <= 4096, n_q <= 4096, ld <= 2^23 (else DSA_ERR_UNSUPPORTED); with
  * phys, pool_rows * 64 must fit int32. */
 dsa_status dsa_indexer_select_workspace_size(int32_t n_q, int64_t ld, size_t *bytes);
-/* The two halves of dsa_indexer_select, for callers that time or reuse them:
- * dsa_indexer_score_pages runs the scan (scores plus the per-page records, in
- * `workspace`); dsa_topk_pages selects from those records and the scores.
- * Arguments as for dsa_indexer_select; dsa_topk_pages needs the workspace a
- * dsa_indexer_score_pages call with the same n_q, ld and row lengths filled. */
-dsa_status dsa_indexer_score_pages(const dsa_layout *layout, int32_t layer, const uint8_t *pool, int64_t pool_bytes,
-                                   const int32_t *block_table, int64_t bt_ld, int32_t n_req, const uint16_t *q,
-                                   const float *w, const int32_t *q_req, const int32_t *row_len, int32_t n_q,
-                                   float *scores, int64_t ld, void *workspace, size_t workspace_bytes,
-                                   int32_t *err_flag, dsa_stream_t stream);
-dsa_status dsa_topk_pages(const dsa_layout *layout, int64_t pool_bytes, const int32_t *block_table, int64_t bt_ld,
-                          int32_t n_req, const int32_t *q_req, const float *scores, int64_t ld,
-                          const int32_t *row_len, int32_t n_q, int32_t k, const void *workspace,
-                          size_t workspace_bytes, int32_t *idx, int32_t *phys, int64_t idx_ld, int32_t *err_flag,
-                          dsa_stream_t stream);
 dsa_status dsa_indexer_select(const dsa_layout *layout, int32_t layer, const uint8_t *pool, int64_t pool_bytes,
                               const int32_t *block_table, int64_t bt_ld, int32_t n_req, const uint16_t *q,
                               const float *w, const int32_t *q_req, const int32_t *row_len, int32_t n_q, int32_t k,
                               float *scores, int64_t ld, int32_t *idx, int32_t *phys, int64_t idx_ld,
                               void *workspace, size_t workspace_bytes, int32_t *err_flag, dsa_stream_t stream);
+/* The two halves of dsa_indexer_select, for callers that time or reuse them
+ * (arguments as there): dsa_indexer_score_pages is the scan alone (no
+ * workspace); dsa_topk_pages is dsa_topk with the physical-row output. */
+dsa_status dsa_indexer_score_pages(const dsa_layout *layout, int32_t layer, const uint8_t *pool, int64_t pool_bytes,
+                                   const int32_t *block_table, int64_t bt_ld, int32_t n_req, const uint16_t *q,
+                                   const float *w, const int32_t *q_req, const int32_t *row_len, int32_t n_q,
+                                   float *scores, int64_t ld, int32_t *err_flag, dsa_stream_t stream);
+dsa_status dsa_topk_pages(const dsa_layout *layout, int64_t pool_bytes, const int32_t *block_table, int64_t bt_ld,
+                          int32_t n_req, const int32_t *q_req, const float *scores, int64_t ld,
+                          const int32_t *row_len, int32_t n_q, int32_t k, void *workspace, size_t workspace_bytes,
+                          int32_t *idx, int32_t *phys, int64_t idx_ld, int32_t *err_flag, dsa_stream_t stream);
 
 /* Sparse MLA decode over physical rows ([ZH] "低延迟解码：融合的 DSA 解码路径":
  * attention reads the physical KV rows the fused indexer emits).  The result

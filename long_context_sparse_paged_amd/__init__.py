@@ -82,7 +82,7 @@ def _load():
         "dsa_indexer_select": ([LP, I32, P, I64, P, I64, I32, P, P, P, P, I32, I32, P, I64, P, P, I64, P, SZ, P, P],
                                I32),
         "dsa_sparse_mla_decode_phys": ([LP, I32, P, I64, P, I64, I32, P, I32, I32, F, F, P, P, P, SZ, P, P], I32),
-        "dsa_indexer_score_pages": ([LP, I32, P, I64, P, I64, I32, P, P, P, P, I32, P, I64, P, SZ, P, P], I32),
+        "dsa_indexer_score_pages": ([LP, I32, P, I64, P, I64, I32, P, P, P, P, I32, P, I64, P, P], I32),
         "dsa_topk_pages": ([LP, I64, P, I64, I32, P, P, I64, P, I32, I32, P, SZ, P, P, I64, P, P], I32),
         "dsa_sparse_mla_prefill_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
         "dsa_dcp_topk_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
@@ -218,21 +218,19 @@ def dsa_indexer_select(layout: dsa_layout, layer: int, pool, block_table, n_req:
 
 
 def dsa_indexer_score_pages(layout: dsa_layout, layer: int, pool, block_table, n_req: int, q, w, q_req, row_len,
-                            scores, workspace, err_flag=None, stream=None):
-    """First half of dsa_indexer_select: the scan, with the per-page records in `workspace`."""
+                            scores, err_flag=None, stream=None):
+    """First half of dsa_indexer_select: the scan, pages read through the block table."""
     st = lib.dsa_indexer_score_pages(C.byref(layout), layer, _ptr(pool, U8, "pool"), pool.numel(),
                                      _ptr(block_table, I32, "block_table"), block_table.shape[1], n_req,
                                      _ptr(q, BF16, "q"), _ptr(w, F32, "w"), _ptr(q_req, I32, "q_req"),
                                      _ptr(row_len, I32, "row_len"), q.shape[0], _ptr(scores, F32, "scores"),
-                                     scores.shape[1], _ptr(workspace, None, "workspace"),
-                                     workspace.numel() * workspace.element_size(), _ptr(err_flag, I32, "err_flag"),
-                                     _stream(stream))
+                                     scores.shape[1], _ptr(err_flag, I32, "err_flag"), _stream(stream))
     _check("dsa_indexer_score_pages", st)
 
 
 def dsa_topk_pages(layout: dsa_layout, pool, block_table, n_req: int, q_req, scores, row_len, k: int, workspace, idx,
                    phys=None, err_flag=None, stream=None):
-    """Second half of dsa_indexer_select: the exact top-k from the records and the scores."""
+    """Second half of dsa_indexer_select: dsa_topk plus each kept token's physical row."""
     st = lib.dsa_topk_pages(C.byref(layout), pool.numel(), _ptr(block_table, I32, "block_table"), block_table.shape[1],
                             n_req, _ptr(q_req, I32, "q_req"), _ptr(scores, F32, "scores"), scores.shape[1],
                             _ptr(row_len, I32, "row_len"), scores.shape[0], k, _ptr(workspace, None, "workspace"),

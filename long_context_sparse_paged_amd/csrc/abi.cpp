@@ -97,7 +97,7 @@ dsa_status dsa_resolve_pages(const dsa_layout *layout, int32_t layer, const int3
   if (!aligned(block_table, 4) || !aligned(n_pages, 4) || !aligned(lat_off, 8) || !aligned(key_off, 8) ||
       !aligned(err_flag, 4))
     return DSA_ERR_MISALIGNED;
-  ResolveArgs a;
+  ResolveArgs a{};
   a.bt = block_table;
   a.bt_ld = bt_ld;
   a.n_pages = n_pages;
@@ -171,7 +171,7 @@ dsa_status dsa_indexer_score_verify(const dsa_layout *layout, const uint8_t *poo
   if (!aligned(pool, 16) || !aligned(q, 16) || !aligned(key_off, 8) || !aligned(w, 4) || !aligned(row_len, 4) ||
       !aligned(scores, 4) || !aligned(err_flag, 4))
     return DSA_ERR_MISALIGNED;
-  VerifyArgs a;
+  VerifyArgs a{};
   a.pool = pool;
   a.pool_bytes = pool_bytes;
   a.key_off = key_off;
@@ -218,7 +218,7 @@ dsa_status dsa_topk(const float *scores, int64_t ld, const int32_t *row_len, int
       !aligned(err_flag, 4))
     return DSA_ERR_MISALIGNED;
   if (workspace_bytes < need) return DSA_ERR_WORKSPACE_TOO_SMALL;
-  TopkArgs a;
+  TopkArgs a{};
   a.scores = scores;
   a.ld = ld;
   a.row_len = row_len;
@@ -254,7 +254,7 @@ dsa_status dsa_dcp_topk(const float *scores, int64_t ld, const int32_t *row_len,
       !aligned(workspace, 16) || !aligned(err_flag, 4))
     return DSA_ERR_MISALIGNED;
   if (workspace_bytes < need) return DSA_ERR_WORKSPACE_TOO_SMALL;
-  DcpArgs a;
+  DcpArgs a{};
   a.scores = scores;
   a.ld = ld;
   a.row_len = row_len;
@@ -367,53 +367,55 @@ dsa_status dsa_sparse_mla_prefill(const dsa_layout *layout, const uint8_t *pool,
 }
 
 // ---- fused score -> select (decode) ----
-// 32-token units of a row: two per 64-token page (the scan writes both units of every page)
-static int64_t select_units(int64_t ld) { return 2 * ((ld + kPage - 1) / kPage); }
-static int64_t select_sum_bytes(int32_t n_q, int64_t ld) { return round_up_256(16 * (int64_t)n_q * select_units(ld)); }
-
 dsa_status dsa_indexer_select_workspace_size(int32_t n_q, int64_t ld, size_t *bytes) {
   if (!bytes) return DSA_ERR_NULL_ARG;
   if (n_q < 0 || ld < 0) return DSA_ERR_BAD_SHAPE;
-  *bytes = (size_t)(select_sum_bytes(n_q, ld) + round_up_256(4 * (int64_t)n_q * select_units(ld)));
+  if (ld > (int64_t)1024 * kSlice) return DSA_ERR_UNSUPPORTED;
+  *bytes = topk_workspace_bytes(n_q, ld);
   return DSA_OK;
 }
 
-// Checks shared by the fused calls; fills the page-record pointers.
-static dsa_status select_common(const dsa_layout *layout, int64_t pool_bytes, const int32_t *block_table, int64_t bt_ld,
-                                int32_t n_req, const int32_t *q_req, const int32_t *row_len, int32_t n_q,
-                                const float *scores, int64_t ld, const void *workspace, size_t workspace_bytes,
-                                int32_t *err_flag, uint32_t **sum_key, uint32_t **sum_slot) {
+// Checks shared by the fused calls (block table, rows, scores).
+static dsa_status fused_common(const dsa_layout *layout, int64_t pool_bytes, const int32_t *block_table, int64_t bt_ld,
+                               int32_t n_req, const int32_t *q_req, const int32_t *row_len, int32_t n_q,
+                               const float *scores, int64_t ld, int32_t *err_flag) {
   dsa_status st = check_layout(layout);
   if (st != DSA_OK) return st;
   if (n_q < 0 || n_req < 0 || ld < 0 || bt_ld < 1 || pool_bytes < 0) return DSA_ERR_BAD_SHAPE;
-  if (ld % 4 != 0) return DSA_ERR_BAD_SHAPE;  // score rows start on 16 B
-  if (n_q > 4096 || select_units(ld) > kSelectMaxUnits) return DSA_ERR_UNSUPPORTED;
+  if (n_q > 4096 || ld > (int64_t)1024 * kSlice) return DSA_ERR_UNSUPPORTED;
   if (n_q == 0) return DSA_OK;
   if (!block_table || !q_req || !row_len || !scores) return DSA_ERR_NULL_ARG;
-  if (!aligned(block_table, 4) || !aligned(q_req, 4) || !aligned(row_len, 4) || !aligned(scores, 16) ||
-      !aligned(err_flag, 4) || !aligned(workspace, 256))
+  if (!aligned(block_table, 4) || !aligned(q_req, 4) || !aligned(row_len, 4) || !aligned(scores, 4) ||
+      !aligned(err_flag, 4))
     return DSA_ERR_MISALIGNED;
-  size_t need = 0;
-  dsa_indexer_select_workspace_size(n_q, ld, &need);
-  if (!workspace) return DSA_ERR_NULL_ARG;
-  if (workspace_bytes < need) return DSA_ERR_WORKSPACE_TOO_SMALL;
-  *sum_key = static_cast<uint32_t *>(const_cast<void *>(workspace));
-  *sum_slot = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(const_cast<void *>(workspace)) + select_sum_bytes(n_q, ld));
   return DSA_OK;
 }
 
-dsa_status dsa_indexer_score_pages(const dsa_layout *layout, int32_t layer, const uint8_t *pool, int64_t pool_bytes,
-                                   const int32_t *block_table, int64_t bt_ld, int32_t n_req, const uint16_t *q,
-                                   const float *w, const int32_t *q_req, const int32_t *row_len, int32_t n_q,
-                                   float *scores, int64_t ld, void *workspace, size_t workspace_bytes,
-                                   int32_t *err_flag, dsa_stream_t stream) {
-  uint32_t *sum_key = nullptr, *sum_slot = nullptr;
-  dsa_status st = select_common(layout, pool_bytes, block_table, bt_ld, n_req, q_req, row_len, n_q, scores, ld,
-                                workspace, workspace_bytes, err_flag, &sum_key, &sum_slot);
-  if (st != DSA_OK || n_q == 0) return st;
+static dsa_status score_pages_check(const dsa_layout *layout, int32_t layer, const uint8_t *pool, const uint16_t *q,
+                                    const float *w) {
   if (layer < 0 || layer >= layout->n_layers) return DSA_ERR_BAD_SHAPE;
   if (!pool || !q || !w) return DSA_ERR_NULL_ARG;
   if (!aligned(pool, 16) || !aligned(q, 16) || !aligned(w, 4)) return DSA_ERR_MISALIGNED;
+  return DSA_OK;
+}
+
+static dsa_status topk_pages_check(const dsa_layout *layout, int64_t pool_bytes, int32_t n_q, int32_t k, int64_t ld,
+                                   const void *workspace, size_t workspace_bytes, const int32_t *idx,
+                                   const int32_t *phys, int64_t idx_ld) {
+  if (k < 1 || idx_ld < k) return DSA_ERR_BAD_SHAPE;
+  if (k > kMaxTopK || n_q > kMaxGridY) return DSA_ERR_UNSUPPORTED;
+  if (phys && pool_bytes / layout->row_stride > (int64_t)(INT32_MAX / kPage)) return DSA_ERR_UNSUPPORTED;
+  if (!idx || !workspace) return DSA_ERR_NULL_ARG;
+  if (!aligned(idx, 4) || !aligned(phys, 4) || !aligned(workspace, 16)) return DSA_ERR_MISALIGNED;
+  if (workspace_bytes < topk_workspace_bytes(n_q, ld)) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  return DSA_OK;
+}
+
+static dsa_status launch_score_pages(const dsa_layout *layout, int32_t layer, const uint8_t *pool,
+                                     int64_t pool_bytes, const int32_t *block_table, int64_t bt_ld, int32_t n_req,
+                                     const uint16_t *q, const float *w, const int32_t *q_req,
+                                     const int32_t *row_len, int32_t n_q, float *scores, int64_t ld,
+                                     int32_t *err_flag, dsa_stream_t stream) {
   ScoreArgs a{};
   a.pool = pool;
   a.pool_bytes = pool_bytes;
@@ -434,47 +436,59 @@ dsa_status dsa_indexer_score_pages(const dsa_layout *layout, int32_t layer, cons
   a.pool_rows = pool_bytes / layout->row_stride;
   a.row_stride = layout->row_stride;
   a.key_base = (int64_t)layer * layout->layer_stride + layout->lat_page_bytes;
-  a.sum_key = sum_key;
-  a.sum_slot = sum_slot;
-  a.sum_ld = select_units(ld);
   return launched(launch_indexer_scan(a, stream_of(stream)));
+}
+
+static dsa_status launch_topk_pages(const dsa_layout *layout, int64_t pool_bytes, const int32_t *block_table,
+                                    int64_t bt_ld, int32_t n_req, const int32_t *q_req, const float *scores,
+                                    int64_t ld, const int32_t *row_len, int32_t n_q, int32_t k, void *workspace,
+                                    int32_t *idx, int32_t *phys, int64_t idx_ld, int32_t *err_flag,
+                                    dsa_stream_t stream) {
+  TopkArgs a{};
+  a.scores = scores;
+  a.ld = ld;
+  a.row_len = row_len;
+  a.n_rows = n_q;
+  a.k = k;
+  a.idx = idx;
+  a.idx_ld = idx_ld;
+  a.ws = workspace;
+  a.err = err_flag;
+  a.phys = phys;
+  a.q_req = q_req;
+  a.n_req = n_req;
+  a.bt = block_table;
+  a.bt_ld = bt_ld;
+  a.pool_rows = pool_bytes / layout->row_stride;
+  return launched(launch_topk(a, stream_of(stream)));
+}
+
+dsa_status dsa_indexer_score_pages(const dsa_layout *layout, int32_t layer, const uint8_t *pool, int64_t pool_bytes,
+                                   const int32_t *block_table, int64_t bt_ld, int32_t n_req, const uint16_t *q,
+                                   const float *w, const int32_t *q_req, const int32_t *row_len, int32_t n_q,
+                                   float *scores, int64_t ld, int32_t *err_flag, dsa_stream_t stream) {
+  dsa_status st = fused_common(layout, pool_bytes, block_table, bt_ld, n_req, q_req, row_len, n_q, scores, ld,
+                               err_flag);
+  if (st != DSA_OK || n_q == 0) return st;
+  st = score_pages_check(layout, layer, pool, q, w);
+  if (st != DSA_OK) return st;
+  return launch_score_pages(layout, layer, pool, pool_bytes, block_table, bt_ld, n_req, q, w, q_req, row_len, n_q,
+                            scores, ld, err_flag, stream);
 }
 
 dsa_status dsa_topk_pages(const dsa_layout *layout, int64_t pool_bytes, const int32_t *block_table, int64_t bt_ld,
                           int32_t n_req, const int32_t *q_req, const float *scores, int64_t ld,
-                          const int32_t *row_len, int32_t n_q, int32_t k, const void *workspace,
-                          size_t workspace_bytes, int32_t *idx, int32_t *phys, int64_t idx_ld, int32_t *err_flag,
-                          dsa_stream_t stream) {
-  uint32_t *sum_key = nullptr, *sum_slot = nullptr;
-  dsa_status st = select_common(layout, pool_bytes, block_table, bt_ld, n_req, q_req, row_len, n_q, scores, ld,
-                                workspace, workspace_bytes, err_flag, &sum_key, &sum_slot);
+                          const int32_t *row_len, int32_t n_q, int32_t k, void *workspace, size_t workspace_bytes,
+                          int32_t *idx, int32_t *phys, int64_t idx_ld, int32_t *err_flag, dsa_stream_t stream) {
+  dsa_status st = fused_common(layout, pool_bytes, block_table, bt_ld, n_req, q_req, row_len, n_q, scores, ld,
+                               err_flag);
   if (st != DSA_OK) return st;
   if (k < 1 || idx_ld < k) return DSA_ERR_BAD_SHAPE;
-  if (k > kMaxTopK) return DSA_ERR_UNSUPPORTED;
-  const int64_t pool_rows = pool_bytes / layout->row_stride;
-  if (phys && pool_rows > (int64_t)(INT32_MAX / kPage)) return DSA_ERR_UNSUPPORTED;  // pool_row * 64 + slot in int32
-  if (n_q == 0) return DSA_OK;
-  if (!idx) return DSA_ERR_NULL_ARG;
-  if (!aligned(idx, 4) || !aligned(phys, 4)) return DSA_ERR_MISALIGNED;
-  SelectArgs s{};
-  s.scores = scores;
-  s.ld = ld;
-  s.row_len = row_len;
-  s.n_rows = n_q;
-  s.k = k;
-  s.sum_key = sum_key;
-  s.sum_slot = sum_slot;
-  s.sum_ld = select_units(ld);
-  s.q_req = q_req;
-  s.n_req = n_req;
-  s.bt = block_table;
-  s.bt_ld = bt_ld;
-  s.pool_rows = pool_rows;
-  s.idx = idx;
-  s.phys = phys;
-  s.idx_ld = idx_ld;
-  s.err = err_flag;
-  return launched(launch_select(s, stream_of(stream)));
+  if (n_q == 0) return k > kMaxTopK ? DSA_ERR_UNSUPPORTED : DSA_OK;
+  st = topk_pages_check(layout, pool_bytes, n_q, k, ld, workspace, workspace_bytes, idx, phys, idx_ld);
+  if (st != DSA_OK) return st;
+  return launch_topk_pages(layout, pool_bytes, block_table, bt_ld, n_req, q_req, scores, ld, row_len, n_q, k,
+                           workspace, idx, phys, idx_ld, err_flag, stream);
 }
 
 dsa_status dsa_indexer_select(const dsa_layout *layout, int32_t layer, const uint8_t *pool, int64_t pool_bytes,
@@ -483,22 +497,20 @@ dsa_status dsa_indexer_select(const dsa_layout *layout, int32_t layer, const uin
                               float *scores, int64_t ld, int32_t *idx, int32_t *phys, int64_t idx_ld,
                               void *workspace, size_t workspace_bytes, int32_t *err_flag, dsa_stream_t stream) {
   // every argument of both halves is checked before the first launch
-  uint32_t *sk = nullptr, *ss = nullptr;
-  dsa_status st = select_common(layout, pool_bytes, block_table, bt_ld, n_req, q_req, row_len, n_q, scores, ld,
-                                workspace, workspace_bytes, err_flag, &sk, &ss);
+  dsa_status st = fused_common(layout, pool_bytes, block_table, bt_ld, n_req, q_req, row_len, n_q, scores, ld,
+                               err_flag);
   if (st != DSA_OK) return st;
-  if (layer < 0 || layer >= layout->n_layers || k < 1 || idx_ld < k) return DSA_ERR_BAD_SHAPE;
-  if (k > kMaxTopK) return DSA_ERR_UNSUPPORTED;
-  if (phys && pool_bytes / layout->row_stride > (int64_t)(INT32_MAX / kPage)) return DSA_ERR_UNSUPPORTED;
-  if (n_q == 0) return DSA_OK;
-  if (!pool || !q || !w || !idx) return DSA_ERR_NULL_ARG;
-  if (!aligned(pool, 16) || !aligned(q, 16) || !aligned(w, 4) || !aligned(idx, 4) || !aligned(phys, 4))
-    return DSA_ERR_MISALIGNED;
-  st = dsa_indexer_score_pages(layout, layer, pool, pool_bytes, block_table, bt_ld, n_req, q, w, q_req, row_len, n_q,
-                               scores, ld, workspace, workspace_bytes, err_flag, stream);
+  if (k < 1 || idx_ld < k) return DSA_ERR_BAD_SHAPE;
+  if (layer < 0 || layer >= layout->n_layers) return DSA_ERR_BAD_SHAPE;
+  if (n_q == 0) return k > kMaxTopK ? DSA_ERR_UNSUPPORTED : DSA_OK;
+  st = score_pages_check(layout, layer, pool, q, w);
+  if (st == DSA_OK) st = topk_pages_check(layout, pool_bytes, n_q, k, ld, workspace, workspace_bytes, idx, phys, idx_ld);
   if (st != DSA_OK) return st;
-  return dsa_topk_pages(layout, pool_bytes, block_table, bt_ld, n_req, q_req, scores, ld, row_len, n_q, k, workspace,
-                        workspace_bytes, idx, phys, idx_ld, err_flag, stream);
+  st = launch_score_pages(layout, layer, pool, pool_bytes, block_table, bt_ld, n_req, q, w, q_req, row_len, n_q,
+                          scores, ld, err_flag, stream);
+  if (st != DSA_OK) return st;
+  return launch_topk_pages(layout, pool_bytes, block_table, bt_ld, n_req, q_req, scores, ld, row_len, n_q, k,
+                           workspace, idx, phys, idx_ld, err_flag, stream);
 }
 
 dsa_status dsa_sparse_mla_decode_phys(const dsa_layout *layout, int32_t layer, const uint8_t *pool, int64_t pool_bytes,

@@ -43,14 +43,6 @@ struct ScoreArgs {
   // of off_ld; a block id outside [0, pool_rows) flags DSA_DEVERR_BLOCK_RANGE.
   const int32_t *bt;
   int64_t bt_ld, pool_rows, row_stride, key_base;
-  // Unit records (sum_key != NULL): for row r and 32-token unit u (tokens 32u .. 32u + 31),
-  // four of its keys (score_key order; 0 = no token) at sum_key[(r * sum_ld + u) * 4 ..], and
-  // their slots within the unit, one byte each in the same order (255 = no token), at
-  // sum_slot[r * sum_ld + u].  They are the unit's four largest up to the lowest five bits:
-  // every key of the unit is <= (first | 31), and every key left out is <= (fourth | 31).
-  uint32_t *sum_key;
-  uint32_t *sum_slot;
-  int64_t sum_ld;
 };
 hipError_t launch_indexer_scan(const ScoreArgs &a, hipStream_t s);  // bf16 queries
 hipError_t launch_indexer_gemm(const ScoreArgs &a, hipStream_t s);  // e4m3 queries
@@ -91,30 +83,16 @@ struct TopkArgs {
   int64_t idx_ld;
   void *ws;
   int32_t *err;
+  // Physical rows (phys != NULL): phys[r][i] = bt[q_req[r] * bt_ld + t / 64] * 64 + t % 64 for
+  // the kept token t = idx[r][i], -1 where idx is -1 or the block id is outside [0, pool_rows)
+  // (which flags DSA_DEVERR_BLOCK_RANGE).
+  int32_t *phys;
+  const int32_t *q_req;  // request of each row, in [0, n_req) (else DSA_DEVERR_REQUEST)
+  int32_t n_req;
+  const int32_t *bt;     // [n_req][bt_ld]; a row longer than 64 bt_ld flags DSA_DEVERR_ROW_LEN
+  int64_t bt_ld, pool_rows;
 };
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
-
-// Fused select (after the scan's SUM mode): exact top-k of each row from its page summaries,
-// the few pages that need a full look, and the row's scores; logical and physical output.
-constexpr int kSelectMaxUnits = 32768;  // 32-token units: rows of at most 2^20 tokens
-struct SelectArgs {
-  const float *scores;
-  int64_t ld;
-  const int32_t *row_len;
-  int32_t n_rows, k;
-  const uint32_t *sum_key;   // [n_rows][sum_ld][4] unit records (see ScoreArgs)
-  const uint32_t *sum_slot;  // [n_rows][sum_ld]
-  int64_t sum_ld;
-  const int32_t *q_req;      // request of each row
-  int32_t n_req;
-  const int32_t *bt;         // [n_req][bt_ld] pool row of each page
-  int64_t bt_ld, pool_rows;
-  int32_t *idx;              // [n_rows][idx_ld] logical token ids, ascending, -1 padded
-  int32_t *phys;             // [n_rows][idx_ld] pool_row * 64 + slot, same order (may be NULL)
-  int64_t idx_ld;
-  int32_t *err;
-};
-hipError_t launch_select(const SelectArgs &a, hipStream_t s);
 
 struct MlaArgs {
   const uint8_t *pool;

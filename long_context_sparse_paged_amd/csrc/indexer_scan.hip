@@ -27,15 +27,10 @@
 // (n, h) at K-step s takes dims [64h + 8s, 64h + 8s + 8), which makes both the
 // query fragment and the key fragment contiguous runs of bytes.
 //
-// Two options serve the fused score -> select path (section "低延迟解码：融合的 DSA 解码路径":
-// a key-balanced scorer, then one exact top-k kernel that emits physical rows):
-//   BT   page addresses come straight from the block table (pool row * row stride + the
-//        layer's key-page offset), so no separate resolve launch precedes the scan;
-//   SUM  the four largest scores (as order-preserving keys) of every 32-token unit (half a
-//        page) and their slots are written beside the scores -- from them the select kernel
-//        derives a lower bound of the row's k-th score and finds the few units it must look
-//        at in full.  They are formed when a wave writes out its buffered scores, off the
-//        per-page critical path.
+// Block-table mode (BT) serves the fused score -> select path (section "低延迟解码：融合的 DSA
+// 解码路径": a key-balanced scorer, then an exact top-k that emits physical rows): page
+// addresses come straight from the block table (pool row * row stride + the layer's key-page
+// offset), so no separate resolve launch precedes the scan.
 #include <math.h>
 
 #include "dsa_device.hpp"
@@ -75,7 +70,7 @@ __device__ __forceinline__ int row_length(const ScoreArgs &a, int r, int64_t max
   return len;
 }
 
-template <int KEY_FMT, bool BT, bool SUM>
+template <int KEY_FMT, bool BT>
 __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a) {
   using KR = KeyRow<KEY_FMT>;
   __shared__ __align__(16) uint8_t s_page[kScanWaves][KR::kPageBytes];
@@ -191,7 +186,7 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
   // Score write-back.  Scores written as the keys stream in interleave small writes with the
   // read stream and cost HBM efficiency; instead each wave keeps up to kScoreBufUnits pages of
   // scores in LDS and writes them out together (at the end of its range for most workloads).
-  int nb = 0, buf_lo = 0, buf_hi = 0, buf_rem = 0, buf_row = 0, buf_pg = 0;
+  int nb = 0, buf_lo = 0, buf_hi = 0, buf_rem = 0;
   const bool vec_out = (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 && (a.ld & 3) == 0;
   auto lds_sync = [&]() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -214,50 +209,6 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
           for (int e = 0; e < 4; ++e)
             if (j + e < rq) o[e] = s4[e];
         }
-      }
-    }
-    if constexpr (SUM) {
-      // unit records from the buffered scores: lane 2q + e covers slots 32e .. 32e + 31 of page
-      // q -- unit 2p + e of the row.  It keeps the four largest of the packed keys
-      // (key & ~31) | (31 - slot), which carry their slot in the five bits they drop: one max
-      // and three medians (max of min) per score.  The record holds the four winners' exact
-      // keys (read back by slot) and their slots.  Ordering by packed key can only swap keys that share their
-      // bits above the lowest five, so a token left out has key <= (fourth key | 31), and the
-      // unit's largest key is <= (first key | 31).  Key 0 (below every finite score) with slot
-      // 255 marks a missing token.
-      const int q = lane >> 1, e = lane & 1;
-      const int rq = __shfl(buf_rem, q, 64), rowq = __shfl(buf_row, q, 64), pgq = __shfl(buf_pg, q, 64);
-      if (q < nb) {
-        uint32_t t0 = 0u, t1 = 0u, t2 = 0u, t3 = 0u;
-        const float *src = &s_sc[wid][q][32 * e];
-        // (one 16-B chunk at a time: a mid-range flush runs beside the page pipeline's registers)
-#pragma unroll 1
-        for (int c = 0; c < 8; ++c) {
-          const f32x4_t v4 = *reinterpret_cast<const f32x4_t *>(src + 4 * c);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int sl = 4 * c + i;
-            const uint32_t x = 32 * e + sl < rq ? ((score_key(v4[i]) & ~31u) | (uint32_t)(31 - sl)) : 0u;
-            // t0 >= t1 >= t2 >= t3: the middle of (t_i, t_i+1, x) is max(t_i+1, min(t_i, x))
-            const uint32_t n0 = max(t0, x), n1 = max(t1, min(t0, x));
-            const uint32_t n2 = max(t2, min(t1, x)), n3 = max(t3, min(t2, x));
-            t0 = n0;
-            t1 = n1;
-            t2 = n2;
-            t3 = n3;
-          }
-        }
-        const uint32_t tk[4] = {t0, t1, t2, t3};
-        uint32_t kx[4], slots = 0u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t sl = 31u - (tk[i] & 31u);
-          kx[i] = tk[i] ? score_key(src[sl]) : 0u;
-          slots |= (tk[i] ? sl : 255u) << (8 * i);
-        }
-        const int64_t ei = (int64_t)rowq * a.sum_ld + 2 * pgq + e;
-        *reinterpret_cast<u32x4_t *>(a.sum_key + 4 * ei) = u32x4_t{kx[0], kx[1], kx[2], kx[3]};
-        a.sum_slot[ei] = slots;
       }
     }
     lds_sync();
@@ -326,8 +277,6 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
       buf_lo = (int)(uint32_t)(uint64_t)dst;
       buf_hi = (int)(uint32_t)((uint64_t)dst >> 32);
       buf_rem = min(rem, kPage);
-      buf_row = rr;
-      buf_pg = p;
     }
     if (++nb == kScoreBufUnits) flush();
   };
@@ -392,12 +341,10 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
 
 template <int KEY_FMT>
 void launch_scan_t(const ScoreArgs &a, dim3 grid, size_t dyn, hipStream_t s) {
-  if (a.bt != nullptr && a.sum_key != nullptr)
-    hipLaunchKernelGGL((indexer_scan_kernel<KEY_FMT, true, true>), grid, dim3(256), dyn, s, a);
-  else if (a.bt != nullptr)
-    hipLaunchKernelGGL((indexer_scan_kernel<KEY_FMT, true, false>), grid, dim3(256), dyn, s, a);
+  if (a.bt != nullptr)
+    hipLaunchKernelGGL((indexer_scan_kernel<KEY_FMT, true>), grid, dim3(256), dyn, s, a);
   else
-    hipLaunchKernelGGL((indexer_scan_kernel<KEY_FMT, false, false>), grid, dim3(256), dyn, s, a);
+    hipLaunchKernelGGL((indexer_scan_kernel<KEY_FMT, false>), grid, dim3(256), dyn, s, a);
 }
 
 }  // namespace
@@ -405,7 +352,6 @@ void launch_scan_t(const ScoreArgs &a, dim3 grid, size_t dyn, hipStream_t s) {
 hipError_t launch_indexer_scan(const ScoreArgs &a, hipStream_t s) {
   if (a.n_q == 0) return hipSuccess;
   if (a.n_q > kScanMaxRows) return hipErrorInvalidValue;
-  if (a.sum_key != nullptr && a.bt == nullptr) return hipErrorInvalidValue;  // summaries come with the fused path
   const int64_t pages_ld = a.bt != nullptr ? a.bt_ld : a.off_ld;
   const int64_t max_tok = a.ld < pages_ld * kPage ? a.ld : pages_ld * kPage;
   const int64_t max_units = (int64_t)a.n_q * ((max_tok + kPage - 1) / kPage);

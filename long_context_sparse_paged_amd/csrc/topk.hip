@@ -25,7 +25,10 @@
 //            over the slices, in a second.  A slice that had more candidates than its list
 //            holds is filtered again from the scores.  An LDS radix select finds the
 //            exact k-th key tau and the number of ties at tau to keep; an ordered
-//            compaction writes the kept indices ascending.  Rows of <= 12288 scores skip
+//            compaction writes the kept indices ascending (and, for the fused decode path
+//            -- section "低延迟解码：融合的 DSA 解码路径": the top-k emits the physical KV
+//            rows attention reads -- each kept token's pool row * 64 + slot, looked up in
+//            the block table as it is written).  Rows of <= 12288 scores skip
 //            sample and collect and are loaded whole.  If the candidates are fewer than k
 //            or more than LDS holds, the row is selected from the full row instead
 //            (always correct, slower).
@@ -84,9 +87,11 @@ struct RadixLds {
 
 __device__ __forceinline__ int row_len_of(const TopkArgs &a, int r) {
   int len = a.row_len[r];
-  if (len < 0 || len > a.ld) {
+  // with physical rows the block table must cover the row too
+  const int64_t max_len = a.phys != nullptr && a.bt_ld * kPage < a.ld ? a.bt_ld * kPage : a.ld;
+  if (len < 0 || len > max_len) {
     if (threadIdx.x == 0 && blockIdx.x == 0) flag_error(a.err, DSA_DEVERR_ROW_LEN);
-    len = len < 0 ? 0 : (int)a.ld;
+    len = len < 0 ? 0 : (int)max_len;
   }
   return len;
 }
@@ -205,80 +210,7 @@ __device__ __forceinline__ uint32_t radix_select(Visit visit, int m, uint32_t km
   return kmin + prefix;
 }
 
-// Radix select with 12-bit digits over keys in [kmin, kmax], for short key sets held in
-// registers (`visit(f)` calls f(key) for each of this thread's keys): the m-th largest key
-// (1-based) and, in `gt`, the number of keys strictly larger.  Digits are taken from
-// key - kmin, from the top bit of kmax - kmin down; a 4096-bin histogram (16 KB, never
-// cleared: each thread snapshots its eight bins before and after a pass) and one block scan
-// per pass.  With max_passes below the number of digits the result is the lower edge of the
-// bin that holds the m-th largest key: at least m keys are >= it.  NT = 512.
-struct Radix12Lds {
-  uint32_t hist[4096];
-  int tmp[8];
-  int sh[2];
-};
-template <class Visit>
-__device__ __forceinline__ uint32_t radix_select12(Visit visit, int m, uint32_t kmin, uint32_t kmax, int max_passes,
-                                                   Radix12Lds &X, int &gt) {
-  constexpr int NT = kFinThreads;
-  constexpr int NW = NT / 64;
-  static_assert(NT * 8 == 4096, "eight bins per thread");
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  gt = 0;
-  const uint32_t range = kmax - kmin;
-  if (range == 0) return kmin;
-  // thread t owns bins 4095 - 8t - i (i < 8): thread order is descending bin order
-  uint32_t before[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) before[i] = X.hist[4095 - 8 * tid - i];
-  __syncthreads();  // every snapshot is taken before the first increment
-  uint32_t prefix = 0;
-  int rem = m;
-  int hi = 31 - __clz((int)range);
-  for (int p = 0; hi >= 0 && p < max_passes; ++p, hi -= 12) {
-    const int lo = hi >= 11 ? hi - 11 : 0;
-    const uint32_t above = hi >= 31 ? 0u : ~((2u << hi) - 1u);  // bits already decided
-    visit([&](uint32_t key) {
-      const uint32_t u = key - kmin;
-      if ((u & above) == prefix) atomicAdd(&X.hist[(u >> lo) & 4095u], 1u);
-    });
-    __syncthreads();
-    uint32_t c8[8];
-    int c = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t after = X.hist[4095 - 8 * tid - i];
-      c8[i] = after - before[i];
-      before[i] = after;
-      c += (int)c8[i];
-    }
-    const int incl0 = wave_scan_incl(c);
-    if (lane == 63) X.tmp[wid] = incl0;
-    __syncthreads();
-    int base = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) base += w < wid ? X.tmp[w] : 0;
-    int run = incl0 + base - c;  // keys in bins above this thread's first bin
-    if (run < rem && run + c >= rem) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (run < rem && run + (int)c8[i] >= rem) {
-          X.sh[0] = 4095 - 8 * tid - i;
-          X.sh[1] = run;
-        }
-        run += (int)c8[i];
-      }
-    }
-    __syncthreads();
-    prefix |= (uint32_t)X.sh[0] << lo;
-    rem -= X.sh[1];
-    gt += X.sh[1];
-    __syncthreads();  // X.sh and X.tmp are rewritten by the next pass
-  }
-  return kmin + prefix;
-}
-
-// Exclusive rank of `f` among the block's threads (thread order) and the block total.// Exclusive rank of `f` among the block's threads (thread order) and the block total.
+// Exclusive rank of `f` among the block's threads (thread order) and the block total.
 template <int NT>
 __device__ __forceinline__ int block_rank(bool f, int *tmp, int &total) {
   constexpr int NW = NT / 64;
@@ -590,71 +522,6 @@ __device__ __forceinline__ void select_from_regs(const uint32_t (&rk)[PER], int 
   }
 }
 
-// select_from_regs with the 12-bit radix select (no list): for key sets of at most a few
-// thousand, two or three passes instead of three or four.
-template <int PER, class IdxOf, class Emit>
-__device__ __forceinline__ void select_from_regs12(const uint32_t (&rk)[PER], int cnt, IdxOf idx_of, int keff,
-                                                   RadixLds<kFinThreads> &R, Radix12Lds &X, Emit emit) {
-  constexpr int NT = kFinThreads;
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    if (q < cnt) {
-      lo = min(lo, rk[q]);
-      hi = max(hi, rk[q]);
-    }
-  }
-  block_minmax<NT>(lo, hi, R);
-  int gt;
-  const uint32_t tau = radix_select12(
-      [&](auto f) {
-#pragma unroll
-        for (int q = 0; q < PER; ++q)
-          if (q < cnt) f(rk[q]);
-      },
-      keff, lo, hi, 3, X, gt);
-  const int need_eq = keff - gt;
-  int ce = 0, cg = 0;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    cg += (q < cnt && rk[q] > tau) ? 1 : 0;
-    ce += (q < cnt && rk[q] == tau) ? 1 : 0;
-  }
-  int tot;
-  const int eq_excl = block_scan_incl<NT>(ce, R.tmp, tot) - ce;
-  const int cs = cg + min(ce, max(0, need_eq - eq_excl));
-  int pos = block_scan_incl<NT>(cs, R.tmp, tot) - cs;
-  int eq_seen = eq_excl;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    if (q < cnt) {
-      bool sel = rk[q] > tau;
-      if (rk[q] == tau) sel = eq_seen++ < need_eq;
-      if (sel) emit(pos++, idx_of(q));
-    }
-  }
-}
-
-// Keys s_key[0, n) in index order: select_from_regs12 with thread t holding [t per, t per + cnt),
-// emitting each kept key's position.
-template <int PER, class Emit>
-__device__ __forceinline__ void select_lds12(const uint32_t *s_key, int n, int per, int keff, RadixLds<kFinThreads> &R,
-                                             Radix12Lds &X, Emit emit) {
-  const int b0 = min(n, (int)threadIdx.x * per), cnt = min(n, b0 + per) - b0;
-  uint32_t rk[PER];
-#pragma unroll
-  for (int q = 0; q < PER; ++q) rk[q] = q < cnt ? s_key[b0 + q] : 0u;
-  select_from_regs12<PER>(rk, cnt, [&](int q) { return b0 + q; }, keff, R, X, emit);
-}
-template <class Emit>
-__device__ __forceinline__ void select_lds12_any(const uint32_t *s_key, int n, int keff, RadixLds<kFinThreads> &R,
-                                                 Radix12Lds &X, Emit emit) {
-  const int per = (n + kFinThreads - 1) / kFinThreads;
-  if (per <= 4) select_lds12<4>(s_key, n, per, keff, R, X, emit);
-  else if (per <= 8) select_lds12<8>(s_key, n, per, keff, R, X, emit);
-  else select_lds12<12>(s_key, n, per, keff, R, X, emit);
-}
-
 // Exact selection and ordered output of the n candidates in s_key / s_idx (index order):
 // thread t holds candidates [t per, t per + cnt) in registers (cnt <= per <= PER).  s_key
 // doubles as the radix select's list once the registers are loaded.
@@ -672,25 +539,6 @@ __device__ __forceinline__ void select_write(uint32_t *s_key, const int32_t *s_i
     ri[q] = q < cnt ? s_idx[b0 + q] : 0;
   }
   select_from_regs<PER>(rk, cnt, [&](int q) { return ri[q]; }, keff, R, emit, s_key, list_cap);
-}
-
-// Exact selection and ordered output of the n keys in s_key (index order), emitting each kept
-// key's position in s_key: thread t holds keys [t per, t per + cnt) (cnt <= per <= PER).
-template <int PER, class Emit>
-__device__ __forceinline__ void select_positions(uint32_t *s_key, int n, int per, int keff, RadixLds<kFinThreads> &R,
-                                                 Emit emit, int list_cap) {
-  const int b0 = min(n, (int)threadIdx.x * per), cnt = min(n, b0 + per) - b0;
-  uint32_t rk[PER];
-#pragma unroll
-  for (int q = 0; q < PER; ++q) rk[q] = q < cnt ? s_key[b0 + q] : 0u;
-  select_from_regs<PER>(rk, cnt, [&](int q) { return b0 + q; }, keff, R, emit, s_key, list_cap);
-}
-template <class Emit>
-__device__ __forceinline__ void select_positions_any(uint32_t *s_key, int n, int per, int keff,
-                                                     RadixLds<kFinThreads> &R, Emit emit, int list_cap) {
-  if (per <= 5) select_positions<5>(s_key, n, per, keff, R, emit, list_cap);
-  else if (per <= 9) select_positions<9>(s_key, n, per, keff, R, emit, list_cap);
-  else select_positions<13>(s_key, n, per, keff, R, emit, list_cap);
 }
 
 // select_write with the register bound picked from a few sizes (per = candidates per thread).
@@ -738,12 +586,41 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
     c_first = tid < n_slices ? (int)cnt[tid] : 0;
   }
   const int len = row_len_of(a, r);
-  const int keff = min(a.k, len);
   int32_t *out = a.idx + (int64_t)r * a.idx_ld;
   const float *row = a.scores + (int64_t)r * a.ld;
+  // physical rows: the row's block-table row (NULL for a bad request: every entry -1)
+  int32_t *pout = nullptr;
+  const int32_t *btr = nullptr;
+  if (a.phys != nullptr) {
+    pout = a.phys + (int64_t)r * a.idx_ld;
+    const int b = a.q_req[r];
+    if (b >= 0 && b < a.n_req) btr = a.bt + (int64_t)b * a.bt_ld;
+    else if (tid == 0) flag_error(a.err, DSA_DEVERR_REQUEST);
+  }
+  const int keff = min(a.k, len);
+  auto phys_of = [&](int t) -> int32_t {
+    if (btr == nullptr) return -1;
+    const int32_t blk = btr[t >> 6];
+    if (blk < 0 || blk >= a.pool_rows) {
+      flag_error(a.err, DSA_DEVERR_BLOCK_RANGE);
+      return -1;
+    }
+    return blk * kPage + (t & (kPage - 1));
+  };
+  auto emit = [&](int pos, int32_t i) {
+    out[pos] = i;
+    if (pout) pout[pos] = phys_of(i);
+  };
 
   if (keff >= len) {  // keep everything (also len == 0)
-    for (int i = tid; i < a.k; i += NT) out[i] = i < len ? i : -1;
+    for (int i = tid; i < a.k; i += NT) {
+      if (i < len) {
+        emit(i, i);
+      } else {
+        out[i] = -1;
+        if (pout) pout[i] = -1;
+      }
+    }
     return;
   }
   int n = 0;
@@ -885,7 +762,6 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
     // strided LDS reads of a wave hit distinct banks); the loops are unrolled for a bound
     // on per picked from a few sizes
     const int per = ((n + NT - 1) / NT) | 1;
-    auto emit = [&](int pos, int32_t i) { out[pos] = i; };
     select_write_any(s_key, s_idx, n, per, keff, R, emit);
   } else {
     // exact selection over the whole row, straight from global memory
@@ -903,348 +779,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
           for (int i = tid; i < len; i += NT) f(load(i));
         },
         keff, lo, hi, 32, R, gt, s_key, kShortRow);
-    compact_rounds(load, len, tau, keff - gt, [&](int pos, int i) { out[pos] = i; }, R.tmp);
-  }
-  for (int i = keff + tid; i < a.k; i += NT) out[i] = -1;
-}
-
-// ---- fused select: exact top-k of a row from the scan's unit records ----
-// The scan recorded, for every 32-token unit of the row, four of its keys and their slots: its
-// four largest up to the lowest five key bits, so that every key of the unit is <= (first |
-// 31) and every key left out is <= (fourth | 31).  With j = min(4, ceil(2.5 k / units)) keys
-// per unit, the union of the units' first j recorded keys is a set of the row's keys, so its
-// k-th largest is <= the row's k-th largest T; est, the lower edge of the radix bin that holds
-// it, is lower still.  Every token with key >= est is then a candidate, and all of them are
-// found without reading the row:
-//   - a "live" unit ((first | 31) >= est) with (fourth | 31) < est has every key >= est among
-//     its four recorded entries;
-//   - any other live unit may hold more: its 32 scores are read.
-// Each thread owns a contiguous run of units (rows of at most kSelPre * 512 units, with their
-// records and block-table entries loaded in the first round trip), or of live units (longer
-// rows: the live units are listed in order, then their records loaded).  It counts its
-// candidates, a block scan places them, and they are written in token order with their keys
-// and physical rows.  The same exact radix select and ordered compaction as the two-kernel
-// path then keep the k best (ties to the lower index), ascending.  Rows of at most kSelCap
-// tokens are selected whole in LDS, and rows too short for k recorded keys whole in
-// registers; rows with more live units or candidates than LDS holds (long runs of equal
-// scores) are selected from the full row in global memory -- always exact, slower.
-constexpr int kSelCap = 6144;   // candidates (and whole short rows) in LDS
-constexpr int kSelLive = 4608;  // live units of a long row
-constexpr int kSelPre = 8;      // units a thread owns when the records come in the first round trip
-constexpr int kSelMaxPer = 64;  // units a thread owns (first keys) in a long row
-constexpr int kSelMidPer = 64;  // scores per thread of a row too short for the records (<= 32768)
-constexpr int kUnit = 32;       // tokens per recorded unit
-constexpr int kSelOvf = 64;     // units read in full whose keys are staged in LDS
-
-__global__ __launch_bounds__(kFinThreads) void topk_select_kernel(const SelectArgs a) {
-  constexpr int NT = kFinThreads;
-  constexpr int kEPer = (kSelLive + NT - 1) / NT;  // 9 live units per thread in a long row
-  constexpr int kOwn = kEPer > kSelPre ? kEPer : kSelPre;
-  __shared__ uint32_t s_key[kSelCap];
-  __shared__ int32_t s_tok[kSelCap];    // token of each candidate
-  __shared__ int32_t s_phy[kSelCap];    // record path: its physical row; other paths: pool row per page
-  __shared__ int32_t s_live[kSelLive];  // long rows: live units in order
-  __shared__ uint32_t s_ovk[kSelOvf][kUnit];  // keys of units read in full
-  __shared__ RadixLds<NT> R;
-  __shared__ Radix12Lds X;
-  __shared__ int s_novf;
-  const int tid = threadIdx.x, r = blockIdx.x;
-
-  int len = a.row_len[r];
-  const int b = a.q_req[r];
-  const int64_t max_tok = min(a.ld, min(a.sum_ld * (int64_t)kUnit, a.bt_ld * (int64_t)kPage));
-  uint32_t e = 0;
-  if (b < 0 || b >= a.n_req) e |= DSA_DEVERR_REQUEST;
-  if (len < 0 || len > max_tok) e |= DSA_DEVERR_ROW_LEN;
-  if (e) {
-    if (tid == 0) flag_error(a.err, e);
-    len = (b < 0 || b >= a.n_req || len < 0) ? 0 : (int)min((int64_t)len, max_tok);
-  }
-  const int keff = min(a.k, len);
-  int32_t *out = a.idx + (int64_t)r * a.idx_ld;
-  int32_t *pout = a.phys ? a.phys + (int64_t)r * a.idx_ld : nullptr;
-  const float *row = a.scores + (int64_t)r * a.ld;
-  const int32_t *btr = a.bt + (int64_t)(b < 0 || b >= a.n_req ? 0 : b) * a.bt_ld;
-  // physical row of token t from its page's pool row (-1 when the block id was bad)
-  auto phys_of = [&](int32_t prow, int t) { return prow >= 0 ? prow * kPage + (t & (kPage - 1)) : -1; };
-  auto check_blk = [&](int32_t blk) {
-    if (blk < 0 || blk >= a.pool_rows) {
-      flag_error(a.err, DSA_DEVERR_BLOCK_RANGE);
-      return -1;
-    }
-    return blk;
-  };
-  auto prow_of = [&](int page) { return check_blk(btr[page]); };
-
-  if (keff >= len) {  // keep everything (also len == 0)
-    for (int i = tid; i < a.k; i += NT) {
-      out[i] = i < len ? i : -1;
-      if (pout) pout[i] = i < len ? phys_of(prow_of(i >> 6), i) : -1;
-    }
-    return;
-  }
-  const int P = (len + kPage - 1) / kPage;
-  const int U = (len + kUnit - 1) / kUnit;
-  const int pp = (U + NT - 1) / NT;
-  const bool pre = pp <= kSelPre;
-  const int j = pre ? min(4, max(1, (5 * keff + 2 * U - 1) / (2 * U))) : 1;
-  const int64_t sb = (int64_t)r * a.sum_ld;
-  bool ok = false;
-
-  if (len <= kSelCap) {
-    // the whole row in LDS, with the row's pool rows for the physical output
-    for (int i = tid; i < len; i += NT) {
-      s_key[i] = score_key(row[i]);
-      s_tok[i] = i;
-    }
-    if (pout)
-      for (int q = tid; q < P; q += NT) s_phy[q] = prow_of(q);
-    __syncthreads();
-    select_lds12_any(s_key, len, keff, R, X, [&](int pos, int t) {
-      out[pos] = t;
-      if (pout) pout[pos] = phys_of(s_phy[t >> 6], t);
-    });
-    ok = true;
-  } else if ((int64_t)U * j < keff && len <= kSelMidPer * NT) {
-    // too short for k recorded keys: the whole row in registers, thread t holding the
-    // contiguous run [t per, t per + cnt), all loads in flight at once
-    const int per = (len + NT - 1) / NT;
-    const int b0 = min(len, tid * per), cnt = min(len, b0 + per) - b0;
-    uint32_t rk[kSelMidPer];
-    float x[kSelMidPer];
-#pragma unroll
-    for (int q = 0; q < kSelMidPer; ++q) x[q] = q < cnt ? row[b0 + q] : 0.0f;
-    if (pout)  // the row's pool rows (P <= 512 pages); select_from_regs' barriers publish them
-      for (int q = tid; q < P; q += NT) s_phy[q] = prow_of(q);
-#pragma unroll
-    for (int q = 0; q < kSelMidPer; ++q) rk[q] = score_key(x[q]);
-    select_from_regs12<kSelMidPer>(rk, cnt, [&](int q) { return b0 + q; }, keff, R, X, [&](int pos, int t) {
-      out[pos] = t;
-      if (pout) pout[pos] = phys_of(s_phy[t >> 6], t);
-    });
-    ok = true;
-  } else if ((int64_t)U * j >= keff && pp <= kSelMaxPer) {
-    // (1) thread t owns units [p0, p1).  Short enough rows (pp <= kSelPre): each unit's whole
-    // record and pool row now; else the units' first keys only (j = 1).
-    const int p0 = min(U, tid * pp), p1 = min(U, p0 + pp);
-    uint32_t k1[kSelMaxPer];
-    u32x4_t rk4[kOwn];   // records of the units (pre) or live units (long rows) this thread handles
-    uint32_t rsl[kOwn];
-    int32_t rpr[kOwn];
-    int run_u[kOwn];     // their unit indices
-    int n_own = 0;
-#pragma unroll
-    for (int q = 0; q < kSelMaxPer; ++q) k1[q] = 0u;
-    if (pre) {
-#pragma unroll
-      for (int q = 0; q < kSelPre; ++q) {
-        rk4[q] = u32x4_t{0u, 0u, 0u, 0u};
-        if (p0 + q < p1) {
-          rk4[q] = *reinterpret_cast<const u32x4_t *>(a.sum_key + 4 * (sb + p0 + q));
-          rsl[q] = a.sum_slot[sb + p0 + q];
-          rpr[q] = pout ? btr[(p0 + q) >> 1] : 0;
-        }
-        run_u[q] = p0 + q;
-      }
-      n_own = p1 - p0;
-    } else {
-#pragma unroll
-      for (int q = 0; q < kSelMaxPer; ++q)
-        if (p0 + q < p1) k1[q] = a.sum_key[4 * (sb + p0 + q)];
-    }
-    auto visit_union = [&](auto f) {  // the thread's keys of the union (0 = no token)
-      if (pre) {
-#pragma unroll
-        for (int q = 0; q < kSelPre; ++q)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (i < j && rk4[q][i] != 0u) f(rk4[q][i]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < kSelMaxPer; ++q)
-          if (k1[q] != 0u) f(k1[q]);
-      }
-    };
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    int nv = 0;
-    visit_union([&](uint32_t x) {
-      lo = min(lo, x);
-      hi = max(hi, x);
-      ++nv;
-    });
-    int nv_tot;
-    block_scan_incl<NT>(nv, R.tmp, nv_tot);
-    uint32_t est = 0u;
-    if (nv_tot >= keff) {  // (a short last unit can leave the union below k)
-      block_minmax<NT>(lo, hi, R);
-      int gt;
-      est = radix_select12(visit_union, keff, lo, hi, 1, X, gt);
-    }
-    bool fits = est != 0u;
-    if (fits && !pre) {
-      // (2) long rows: live units (first key >= est) listed in unit order, and each thread's
-      // run of them loaded
-      int nl = 0;
-#pragma unroll
-      for (int q = 0; q < kSelMaxPer; ++q) nl += (p0 + q < p1 && k1[q] != 0u && (k1[q] | 31u) >= est) ? 1 : 0;
-      int nl_tot;
-      int lpos = block_scan_incl<NT>(nl, R.tmp, nl_tot) - nl;
-      fits = nl_tot <= kSelLive;
-      if (fits) {
-#pragma unroll
-        for (int q = 0; q < kSelMaxPer; ++q)
-          if (p0 + q < p1 && k1[q] != 0u && (k1[q] | 31u) >= est) s_live[lpos++] = p0 + q;
-        __syncthreads();
-        const int ep = (nl_tot + NT - 1) / NT;
-        const int e0 = min(nl_tot, tid * ep), e1 = min(nl_tot, e0 + ep);
-        n_own = e1 - e0;
-#pragma unroll
-        for (int q = 0; q < kOwn; ++q) {
-          rk4[q] = u32x4_t{0u, 0u, 0u, 0u};
-          run_u[q] = 0;
-          if (q < n_own) {
-            const int un = s_live[e0 + q];
-            run_u[q] = un;
-            rk4[q] = *reinterpret_cast<const u32x4_t *>(a.sum_key + 4 * (sb + un));
-            rsl[q] = a.sum_slot[sb + un];
-            rpr[q] = pout ? btr[un >> 1] : 0;
-          }
-        }
-      }
-    }
-    if (fits) {
-      // (3) candidates of each handled unit: recorded keys >= est, or (fourth key >= est) the
-      // keys >= est among its 32 scores -- read now, kept as a mask and, in the first kSelOvf
-      // such units of the row, as keys in LDS (others are read again when written)
-      if (tid == 0) s_novf = 0;
-      __syncthreads();
-      uint32_t om[kOwn];
-      int ovs[kOwn];
-      int my_c = 0;
-#pragma unroll
-      for (int q = 0; q < kOwn; ++q) {
-        om[q] = 0u;
-        ovs[q] = -1;
-        if (q < n_own && (rk4[q][0] | 31u) >= est) {
-          if (pout) rpr[q] = check_blk(rpr[q]);
-          if ((rk4[q][3] | 31u) >= est) {
-            const int t0 = run_u[q] * kUnit;
-            float4 x8[8];
-#pragma unroll
-            for (int c = 0; c < 8; ++c)  // t0 + 4c < len <= ld (ld a multiple of 4): in the row
-              x8[c] = t0 + 4 * c < len ? *reinterpret_cast<const float4 *>(row + t0 + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
-            const int o = atomicAdd(&s_novf, 1);
-            ovs[q] = o < kSelOvf ? o : -1;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-              const float xv[4] = {x8[c].x, x8[c].y, x8[c].z, x8[c].w};
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const uint32_t kk = score_key(xv[i]);
-                if (t0 + 4 * c + i < len && kk >= est) om[q] |= 1u << (4 * c + i);
-                if (o < kSelOvf) s_ovk[o][4 * c + i] = kk;
-              }
-            }
-            my_c += __popc(om[q]);
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              my_c += (rk4[q][i] >= est && ((rsl[q] >> (8 * i)) & 255u) < (uint32_t)kUnit) ? 1 : 0;
-          }
-        }
-      }
-      int c_tot;
-      int pos = block_scan_incl<NT>(my_c, R.tmp, c_tot) - my_c;
-      fits = c_tot >= keff && c_tot <= kSelCap;
-      if (fits) {
-        // (4) the candidates in token order: key, token, physical row
-#pragma unroll
-        for (int q = 0; q < kOwn; ++q) {
-          if (q < n_own && (rk4[q][0] | 31u) >= est) {
-            const int t0 = run_u[q] * kUnit;
-            const int32_t prow = pout ? rpr[q] : 0;
-            if ((rk4[q][3] | 31u) >= est) {
-              uint32_t m = om[q];
-              while (m) {
-                const int sl = __ffs(m) - 1;
-                m &= m - 1u;
-                s_key[pos] = ovs[q] >= 0 ? s_ovk[ovs[q]][sl] : score_key(row[t0 + sl]);
-                s_tok[pos] = t0 + sl;
-                s_phy[pos] = phys_of(prow, t0 + sl);
-                ++pos;
-              }
-            } else {
-              // the recorded entries >= est, by slot (at most four: a small sorting network)
-              uint32_t ek[4];
-              int es[4];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const uint32_t sl = (rsl[q] >> (8 * i)) & 255u;
-                const bool in = rk4[q][i] >= est && sl < (uint32_t)kUnit;
-                ek[i] = rk4[q][i];
-                es[i] = in ? (int)sl : kUnit + i;
-              }
-              auto cswap = [&](int x, int y) {
-                if (es[y] < es[x]) {
-                  const int ts = es[x];
-                  es[x] = es[y];
-                  es[y] = ts;
-                  const uint32_t tk = ek[x];
-                  ek[x] = ek[y];
-                  ek[y] = tk;
-                }
-              };
-              cswap(0, 1);
-              cswap(2, 3);
-              cswap(0, 2);
-              cswap(1, 3);
-              cswap(1, 2);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                if (es[i] < kUnit) {
-                  s_key[pos] = ek[i];
-                  s_tok[pos] = t0 + es[i];
-                  s_phy[pos] = phys_of(prow, t0 + es[i]);
-                  ++pos;
-                }
-              }
-            }
-          }
-        }
-        __syncthreads();
-        // (5) exact selection and ordered compaction over the candidates; a kept candidate's
-        // position gives its token and physical row
-        select_lds12_any(s_key, c_tot, keff, R, X, [&](int o, int c) {
-          out[o] = s_tok[c];
-          if (pout) pout[o] = s_phy[c];
-        });
-        ok = true;
-      }
-    }
-  }
-  if (!ok) {
-    // exact selection over the whole row, straight from global memory
-    __syncthreads();
-    auto load = [&](int i) { return score_key(row[i]); };
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    for (int i = tid; i < len; i += NT) {
-      const uint32_t k = load(i);
-      lo = min(lo, k);
-      hi = max(hi, k);
-    }
-    block_minmax<NT>(lo, hi, R);
-    int gt;
-    const uint32_t tau = radix_select<NT>(
-        [&](auto f) {
-          for (int i = tid; i < len; i += NT) f(load(i));
-        },
-        keff, lo, hi, 32, R, gt, s_key, kSelCap);
-    compact_rounds(load, len, tau, keff - gt,
-                   [&](int pos, int i) {
-                     out[pos] = i;
-                     if (pout) pout[pos] = phys_of(prow_of(i >> 6), i);
-                   },
-                   R.tmp);
+    compact_rounds(load, len, tau, keff - gt, emit, R.tmp);
   }
   for (int i = keff + tid; i < a.k; i += NT) {
     out[i] = -1;
@@ -1275,19 +810,6 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
     }
   }
   hipLaunchKernelGGL(topk_finalize_kernel, dim3(a.n_rows), dim3(kFinThreads), 0, s, a, w, n_slices);
-  return hipGetLastError();
-}
-
-}  // namespace dsa
-
-namespace dsa {
-
-hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
-  if (a.n_rows == 0) return hipSuccess;
-  if (a.n_rows > 65535 || a.sum_ld > kSelectMaxUnits || a.k > kMaxTopK || (a.ld & 3) != 0 ||
-      (reinterpret_cast<uintptr_t>(a.scores) & 15) != 0)
-    return hipErrorInvalidValue;
-  hipLaunchKernelGGL(topk_select_kernel, dim3(a.n_rows), dim3(kFinThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -5,8 +5,9 @@ offsets, scores, selected indices, outputs, workspaces) and call
 dsa_resolve_pages -> dsa_indexer_score -> dsa_topk -> dsa_sparse_mla_* on one
 stream; ``VerifyStep`` does the same for speculative verification, with
 dsa_indexer_score_verify reading each key page once for all rows of a request.
-``FusedDecodeStep`` is the fused decode path: dsa_indexer_select (page resolve,
-scores, exact top-k and physical rows in two kernels) -> dsa_sparse_mla_decode_phys.
+``FusedDecodeStep`` is the fused decode path: dsa_indexer_select (scores with
+pages found through the block table, exact top-k and physical rows) ->
+dsa_sparse_mla_decode_phys.
 No arithmetic happens here.
 """
 from __future__ import annotations
@@ -163,9 +164,9 @@ class VerifyStep(_Base):
 
 
 class FusedDecodeStep:
-    """Fused decode: the scan reads pages through the block table and records each page's
-    best scores, one select kernel emits the exact top-k with physical rows, and attention
-    reads those rows directly.  The same results as DecodeStep (bit for bit)."""
+    """Fused decode: the scan reads pages through the block table (no resolve launch), the
+    top-k writes each kept token's physical row beside its index, and attention reads those
+    rows directly.  The same results as DecodeStep (bit for bit)."""
 
     def __init__(self, cache, q_idx, w, q_mla, sm_scale: float, k: int = 2048, device="cuda"):
         self.cache = cache
@@ -173,7 +174,7 @@ class FusedDecodeStep:
         self.k = k
         n_req = cache.block_table.shape[0]
         ld = int(cache.ctx_len.max().item()) if n_req else 1
-        ld = max(4, (ld + 3) // 4 * 4)  # score rows start on 16 B
+        ld = (ld + 3) // 4 * 4  # score rows start on 16 B (vector loads and stores)
         self.q_idx, self.w, self.q_mla = q_idx, w, q_mla
         self.sm_scale = sm_scale
         self.n_heads = q_mla.shape[1]
@@ -196,10 +197,10 @@ class FusedDecodeStep:
                            self.row_len, self.k, self.scores, self.idx, self.phys, self.ws_sel, self.err, stream)
 
     def score(self, stream=None):
-        """The select's first half alone (scan and page records)."""
+        """The select's first half alone (the scan)."""
         c = self.cache
         dsa_indexer_score_pages(self.layout, c.layer, c.pool, c.block_table, c.n_req, self.q_idx, self.w, self.q_req,
-                                self.row_len, self.scores, self.ws_sel, self.err, stream)
+                                self.row_len, self.scores, self.err, stream)
 
     def topk(self, stream=None):
         """The select's second half alone (needs score() first)."""

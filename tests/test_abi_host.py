@@ -252,7 +252,7 @@ def test_fused_select_errors(d):
     """dsa_indexer_select and its two halves reject bad arguments before any launch."""
     L = d.dsa_layout_make(64, 2, 0, 0, 0)
     need = d.dsa_indexer_select_workspace_size(4, 1024)
-    assert need >= 4 * 16 * 20                    # 20 B of page records per page and row
+    assert need == d.dsa_topk_workspace_size(4, 1024, 2048)  # the top-k's own workspace
     f = d.lib.dsa_indexer_select
     # layout, layer, pool, pool_bytes, bt, bt_ld, n_req, q, w, q_req, row_len, n_q, k, scores, ld,
     # idx, phys, idx_ld, ws, ws_bytes, err, stream
@@ -260,10 +260,8 @@ def test_fused_select_errors(d):
             FAKE, need, None, None]
     a = list(args); a[1] = 2
     assert f(*a) == d.DSA_ERR_BAD_SHAPE           # layer past n_layers
-    a = list(args); a[14] = 1022
-    assert f(*a) == d.DSA_ERR_BAD_SHAPE           # ld not a multiple of 4
-    a = list(args); a[14] = (1 << 20) + 4
-    assert f(*a) == d.DSA_ERR_UNSUPPORTED         # rows past 2^20 tokens
+    a = list(args); a[14] = (1 << 23) + 4
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED         # rows past 2^23 scores
     a = list(args); a[12] = 4097; a[17] = 4097
     assert f(*a) == d.DSA_ERR_UNSUPPORTED
     a = list(args); a[12] = 0
@@ -272,10 +270,12 @@ def test_fused_select_errors(d):
     assert f(*a) == d.DSA_ERR_BAD_SHAPE           # idx_ld < k
     a = list(args); a[19] = need - 1
     assert f(*a) == d.DSA_ERR_WORKSPACE_TOO_SMALL
-    a = list(args); a[13] = ODD
-    assert f(*a) == d.DSA_ERR_MISALIGNED          # scores must be 16-B aligned
+    a = list(args); a[7] = ODD
+    assert f(*a) == d.DSA_ERR_MISALIGNED          # q must be 16-B aligned
     a = list(args); a[4] = None
     assert f(*a) == d.DSA_ERR_NULL_ARG
+    a = list(args); a[18] = None
+    assert f(*a) == d.DSA_ERR_NULL_ARG            # no workspace
     a = list(args); a[11] = 0
     assert f(*a) == d.DSA_OK                      # nothing to do
     a = list(args); a[11] = 5000
@@ -284,12 +284,25 @@ def test_fused_select_errors(d):
     a = list(args); a[3] = (1 << 25) * L.row_stride
     assert f(*a) == d.DSA_ERR_UNSUPPORTED
     g = d.lib.dsa_topk_pages
+    # layout, pool_bytes, bt, bt_ld, n_req, q_req, scores, ld, row_len, n_q, k, ws, ws_bytes, idx, phys, idx_ld,
+    # err, stream
     targs = [C.byref(L), 1 << 30, FAKE, 16, 4, FAKE, FAKE, 1024, FAKE, 4, 2048, FAKE, need, FAKE, FAKE, 2048, None,
              None]
     a = list(targs); a[10] = 0
     assert g(*a) == d.DSA_ERR_BAD_SHAPE
     a = list(targs); a[12] = 0
     assert g(*a) == d.DSA_ERR_WORKSPACE_TOO_SMALL
+    a = list(targs); a[2] = None
+    assert g(*a) == d.DSA_ERR_NULL_ARG
+    h = d.lib.dsa_indexer_score_pages
+    # layout, layer, pool, pool_bytes, bt, bt_ld, n_req, q, w, q_req, row_len, n_q, scores, ld, err, stream
+    sargs = [C.byref(L), 0, FAKE, 1 << 30, FAKE, 16, 4, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1024, None, None]
+    a = list(sargs); a[1] = -1
+    assert h(*a) == d.DSA_ERR_BAD_SHAPE
+    a = list(sargs); a[5] = 0
+    assert h(*a) == d.DSA_ERR_BAD_SHAPE           # bt_ld < 1
+    a = list(sargs); a[8] = None
+    assert h(*a) == d.DSA_ERR_NULL_ARG
 
 
 def test_mla_phys_errors(d):

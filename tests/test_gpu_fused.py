@@ -4,11 +4,11 @@ The fused path must give exactly what the four-call path gives -- same scores, s
 same attention, bit for bit -- plus the physical rows of the kept tokens, and both are checked
 against the oracle (scores 1e-5 of the score + 1e-5 of the row rms; top-k within the 1e-5 tie
 window of the oracle's k-th score; attention max|dout| <= 1e-2 max|ref| per row, |dlse| <=
-1e-3).  The row lengths cover every branch of the select kernel: rows of at most k tokens,
-rows of at most 12,288 tokens (selected whole in LDS), rows too short for the page records
-to bound the k-th score (selected from the full row), and long rows that take 4, 2 or 1 of
-each page's recorded scores.  Constructed score orders (ascending, clustered, heavily tied)
-drive the overflow staging and the full-row fallback.
+1e-3).  The row lengths cover every branch of the top-k's last kernel, which writes the
+physical rows: rows of at most k tokens, rows of at most 12,288 tokens (selected whole in
+LDS), and longer rows selected from the slices' candidate lists; constructed score orders
+(ascending, clustered, heavily tied) drive slices whose lists overflow and the full-row
+fallback.
 """
 import numpy as np
 import pytest
@@ -70,9 +70,8 @@ def check_oracle(f, cache, dq, k, n_heads=12):
     check_attention(f.out, f.lse, ref_o, ref_l)
 
 
-# every branch of the select kernel at k = 2048: <= k (1, 2048), whole row in LDS (4096,
-# 12288), too short for the records (12289, 20000, 32000), records with j = 4 (40000), 3
-# (60001), 2 (131072) and 1 (300000)
+# at k = 2048: rows of <= k tokens (1, 2048), whole rows in LDS (4096, 12288), and rows of 2 to
+# 37 slices of 8192 scores
 BRANCH_CTX = [1, 2048, 4096, 12288, 12289, 20000, 32000, 40000, 60001, 131072, 300000]
 
 
@@ -98,6 +97,14 @@ def test_fused_other_k(d, k):
     assert int(f.err.item()) == 0
     check_same(f, u, cache, k)
     check_oracle(f, cache, dq, k)
+    # the two halves called one by one give the same as the one call
+    idx, phys = f.idx.clone(), f.phys.clone()
+    f.idx.fill_(-9)
+    f.phys.fill_(-9)
+    f.score()
+    f.topk()
+    torch.cuda.synchronize()
+    assert torch.equal(f.idx, idx) and torch.equal(f.phys, phys)
 
 
 def ordered_cache(ctx, pattern, seed):
