@@ -218,12 +218,20 @@ int or_latent_decode(int64_t lat_fmt, const uint8_t *row, double kv_scale, doubl
   return OR_OK;
 }
 
-/* Query element (row r, head j, dim d): bf16, or an e4m3 code times the
- * fp32 scale of its (row, head). */
+/* Query element (row r, head j, dim d): bf16, an e4m3 code times the fp32
+ * scale of its (row, head), or (q_fmt 2, indexer queries only) element d of
+ * a 68-byte MXFP4 row per (row, head) -- the MXFP4 key format ([ZH] "低延迟解码：融合的 DSA 解码路径": the indexer query
+ * is quantised to FP8 or MXFP4 before scoring; "量化：原生 MXFP4 索引器"). */
 static double q_elem(const void *q, int64_t q_fmt, const float *q_scale, int64_t heads, int64_t dim,
                      int64_t r, int64_t j, int64_t d) {
   int64_t i = (r * heads + j) * dim + d;
   if (q_fmt == 0) return or_bf16(((const uint16_t *)q)[i]);
+  if (q_fmt == 2) {  /* the MXFP4 key row layout (see or_key_decode) */
+    const uint8_t *row = (const uint8_t *)q + (r * heads + j) * 68;
+    unsigned byte = row[d / 2];
+    unsigned nib = (d % 2 == 0) ? (byte & 15u) : (byte >> 4);
+    return or_e2m1(nib) * or_e8m0(row[64 + d / 32]);
+  }
   return or_e4m3(((const uint8_t *)q)[i]) * (double)q_scale[r * heads + j];
 }
 
@@ -243,7 +251,7 @@ int or_indexer_score(const or_layout *L, int64_t layer, const uint8_t *pool, int
                      const int32_t *q_req, const int32_t *row_len, int64_t n_q, float *scores, int64_t ld,
                      int64_t *bytes_read) {
   if (!L || !pool || !bt || !n_pages || !q || !w || !q_req || !row_len || !scores) return OR_ERR_ARG;
-  if (q_fmt == 1 && !q_scale) return OR_ERR_ARG;
+  if ((q_fmt == 1 && !q_scale) || q_fmt < 0 || q_fmt > 2) return OR_ERR_ARG;
   int rc = OR_OK;
   const int64_t BLK = 512;
   if (bytes_read)
@@ -493,7 +501,7 @@ int or_sparse_mla(const or_layout *L, int64_t layer, const uint8_t *pool, int64_
                   const float *q_scale, const int32_t *q_req, int64_t n_q, int64_t H, double sm_scale,
                   double kv_scale, double *out, double *lse, int64_t *bytes_read) {
   if (!L || !pool || !bt || !n_pages || !ctx_len || !idx || !q || !q_req || !out || !lse) return OR_ERR_ARG;
-  if (q_fmt == 1 && !q_scale) return OR_ERR_ARG;
+  if ((q_fmt == 1 && !q_scale) || q_fmt < 0 || q_fmt > 1) return OR_ERR_ARG;
   int rc = OR_OK;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t r = 0; r < n_q; ++r) {

@@ -170,6 +170,7 @@ class DecodeQueries:
     w: torch.Tensor       # fp32 [B, 32]
     q_mla: torch.Tensor   # bf16 [B, H, 576]
     sm_scale: float
+    q_idx_mxfp4: torch.Tensor = None  # uint8 [B, 32, 68]: q_idx quantised to MXFP4 (OCP MX rule)
 
 
 def decode_queries(n_req: int, n_heads: int = 12, seed: int = 0, device="cpu") -> DecodeQueries:
@@ -178,8 +179,9 @@ def decode_queries(n_req: int, n_heads: int = 12, seed: int = 0, device="cpu") -
     q_idx = torch.randn(n_req, IDX_HEADS, IDX_DIM, generator=g, device=device).to(torch.bfloat16)
     w = torch.rand(n_req, IDX_HEADS, generator=g, device=device) / IDX_HEADS
     q_mla = torch.randn(n_req, n_heads, LAT_DIM, generator=g, device=device).to(torch.bfloat16)
+    q4 = F.mxfp4_key_rows(q_idx.reshape(-1, IDX_DIM)).view(n_req, IDX_HEADS, F.KEY_BYTES[1]).contiguous()
     return DecodeQueries(q_idx=q_idx, w=w.float().contiguous(), q_mla=q_mla,
-                         sm_scale=float(np.float32(1.0 / math.sqrt(LAT_DIM))))
+                         sm_scale=float(np.float32(1.0 / math.sqrt(LAT_DIM))), q_idx_mxfp4=q4)
 
 
 @dataclass

@@ -9,7 +9,8 @@ wrong head or dim index, wrong token address) would break:
   * doubling every key scale doubles every score exactly,
   * ReLU identity: score(q) - score(-q) = sum_j w_j x_j (linear part),
   * linearity in w, non-negativity for w >= 0, zero key -> +0,
-  * permuting pool rows together with the block table changes no bit.
+  * permuting pool rows together with the block table changes no bit,
+  * the FP8 and MXFP4 query modes equal feeding their decoded values.
 """
 import numpy as np
 import pytest
@@ -171,6 +172,51 @@ def test_fp8_query_mode_matches_decoded_bf16():
             want = np.float32(np.sum(p.w.numpy()[r].astype(np.float64) * np.maximum(x, 0)))
             assert abs(s8[r, t] - want) <= 1e-6 * abs(want) + 1e-30
         assert np.isnan(s8[r, 101 + r:]).all()   # causal: nothing written past the position
+
+
+def mxfp4_values(rows):
+    """[..., 68] MXFP4 rows -> [..., 128] float64 values, decoded here from the OCP MX
+    definition (e2m1 magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}, sign bit 3, E8M0 bias 127)."""
+    rows = np.asarray(rows)
+    d = np.arange(128)
+    nib = (rows[..., d // 2] >> (4 * (d % 2))) & 15
+    mags = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
+    return np.where(nib & 8, -1, 1) * mags[nib & 7] * 2.0 ** (rows[..., 64 + d // 32].astype(np.float64) - 127)
+
+
+def test_mxfp4_query_mode_matches_decoded_bf16():
+    """MXFP4 query mode: the 68-byte rows decode to e2m1 x 2^(e-127) -- values that bf16 holds
+    exactly, so feeding the decoded values as bf16 must give the same scores bit for bit."""
+    c = W.build_cache([300], key_fmt=1, lat_fmt=1, seed=21, spare_rows=2)
+    dq = W.decode_queries(2, seed=21)
+    q4 = dq.q_idx_mxfp4.numpy()
+    vals = mxfp4_values(q4)
+    assert np.array_equal(bf16_bits(vals.astype(np.float32)).view(np.uint16).astype(np.uint32) << 16,
+                          vals.astype(np.float32).view(np.uint32))  # exact in bf16
+    s4 = run_score(c, q4, dq.w.numpy(), q_fmt=2)
+    sb = run_score(c, bf16_bits(vals.astype(np.float32)), dq.w.numpy(), q_fmt=0)
+    assert np.array_equal(s4.view(np.uint32), sb.view(np.uint32))
+    # and the quantised query is close to the bf16 one it came from (MX rounding)
+    qb = dq.q_idx.float().numpy()
+    assert np.abs(vals - qb).max() <= 0.26 * np.abs(qb).max()
+
+
+def test_unit_query_mxfp4_query_mode():
+    """One nonzero MXFP4 query element (code 1.5 in block 2, scale 2^-3): x = 0.1875 k[d]."""
+    rng = np.random.default_rng(12)
+    L = 80
+    keys = F.mxfp4_key_rows(torch.from_numpy(rng.standard_normal((L, 128)).astype(np.float32))).numpy()
+    d = 71                                   # block 2, odd element: high nibble of byte 35
+    q4 = np.zeros((1, 32, 68), np.uint8)
+    q4[0, 5, 64:68] = 127                    # unit scales elsewhere
+    q4[0, 5, 64 + 2] = 124                   # 2^-3
+    q4[0, 5, d // 2] = 0x3 << 4              # e2m1 code 3 = 1.5
+    w = np.zeros((1, 32), np.float32)
+    w[0, 5] = 2.0
+    s = run_score(hand_cache(keys, None, key_fmt=1, lat_fmt=1), q4, w, q_fmt=2)
+    kd = mxfp4_values(keys)[:, d]
+    want = (2.0 * np.maximum(0.1875 * kd, 0.0)).astype(np.float32)
+    assert np.array_equal(s[0, :L], want)
 
 
 def test_bytes_counted_equal_keys_read():
