@@ -25,6 +25,10 @@ the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|mixed|long|prefill|verify]
 
+--workload mixed (64 requests, MXFP4 index keys, NVFP4 latents) scores the keys against the
+indexer query quantised to MXFP4 on native FP4 MFMA; bf16_query_us_per_step times the same
+step with the bf16 query.
+
 --workload verify is speculative verification on the same 32 x 131,072-token cache: 8 query
 rows per request (DSpark's 7 draft tokens), the indexer reading each key page once for all
 8 rows (dsa_indexer_score_verify); its roofline is the bf16 MFMA peak, because 8 rows of
@@ -111,10 +115,17 @@ def main():
                           spare_rows=wl["spare_rows"])
     kb, lb = cache.layout["key_bytes"], cache.layout["lat_bytes"]
     four_call = None
+    bf16_query = None
+    q_fmt = d.DSA_Q_BF16
     if wl["kind"] == "decode":
         dq = W.decode_queries(len(ctx), wl["heads"], seed=cfg_id, device=dev)
-        step = d.FusedDecodeStep(cache, dq.q_idx, dq.w, dq.q_mla, dq.sm_scale, k=k)
-        four_call = d.DecodeStep(cache, dq.q_idx, dq.w, dq.q_mla, dq.sm_scale, k=k)
+        # MXFP4 keys: the indexer query quantised to MXFP4 and scored on native FP4 MFMA
+        q_fmt = d.DSA_Q_MXFP4 if wl["key_fmt"] == 1 else d.DSA_Q_BF16
+        qi = dq.q_idx_mxfp4 if q_fmt == d.DSA_Q_MXFP4 else dq.q_idx
+        step = d.FusedDecodeStep(cache, qi, dq.w, dq.q_mla, dq.sm_scale, k=k, q_fmt=q_fmt)
+        four_call = d.DecodeStep(cache, qi, dq.w, dq.q_mla, dq.sm_scale, k=k, q_fmt=q_fmt)
+        if q_fmt == d.DSA_Q_MXFP4:  # for comparison: the same keys scored against the bf16 query
+            bf16_query = d.FusedDecodeStep(cache, dq.q_idx, dq.w, dq.q_mla, dq.sm_scale, k=k)
     elif wl["kind"] == "verify":
         vq = W.verify_queries(ctx, wl["rows"], wl["heads"], seed=cfg_id, device=dev)
         step = d.VerifyStep(cache, vq, k=k)
@@ -198,6 +209,18 @@ def main():
         torch.cuda.synchronize()
         four_call_ms = float(np.mean([a.elapsed_time(b) for a, b in evs_f[1:]]))
         assert torch.equal(four_call.idx, step.idx), "fused and four-call top-k differ"
+    bf16_query_ms = None
+    if bf16_query is not None:
+        evs_q = []
+        for i in range(args.steps + 1):
+            scrub()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            bf16_query.run()
+            b.record()
+            evs_q.append((a, b))
+        torch.cuda.synchronize()
+        bf16_query_ms = float(np.mean([a.elapsed_time(b) for a, b in evs_q[1:]]))
 
     out = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "scaling": "weak", "vs_baseline": None,
            "data": "synthetic (seeded; N(0,1) keys/latents/queries quantised to the cache formats)"}
@@ -224,6 +247,8 @@ def main():
             "path": "fused: dsa_indexer_select (scan via block table, top-k with physical rows)"
                     " -> dsa_sparse_mla_decode_phys",
             "four_call_us_per_step": round(four_call_ms * 1e3, 1),
+            "query_format": "mxfp4 (native FP4 MFMA scoring)" if q_fmt == d.DSA_Q_MXFP4 else "bf16",
+            "bf16_query_us_per_step": None if bf16_query_ms is None else round(bf16_query_ms * 1e3, 1),
             "dcp_merge": dcp,
             "roofline": {"kernel": "indexer_scan (dsa_indexer_score_pages: pages via the block table)",
                          "bound": "hbm",
@@ -340,7 +365,7 @@ def cpu_baseline(cache, step, wl, ctx, budget_s):
         for b in range(len(ctx)):
             L = ctx[b]
             a = time.time()
-            s = oracle.indexer_score(oc, q_idx[b:b + 1], 0, None, w[b:b + 1], np.array([b], np.int32),
+            s = oracle.indexer_score(oc, q_idx[b:b + 1], step.q_fmt, None, w[b:b + 1], np.array([b], np.int32),
                                      np.array([L], np.int32))
             t1 = time.time()
             idx = oracle.topk(s, np.array([L], np.int32), k)

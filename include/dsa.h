@@ -84,6 +84,9 @@ typedef int32_t dsa_status;
 /* Query formats. */
 #define DSA_Q_BF16 0     /* bf16 values */
 #define DSA_Q_FP8_E4M3 1 /* e4m3 codes plus one fp32 scale per (row, head): value = code * scale */
+#define DSA_Q_MXFP4 2    /* 68 B per (row, head) in the MXFP4 key format: 64 B of e2m1 pairs
+                            (element 2i in the low nibble), then four E8M0 scales, one per
+                            32 elements; value = code * 2^(scale - 127) */
 
 /* Block-packed cache layout ([ZH] "面向三种状态的 KV 缓存", figure 3): one
  * contiguous row per cache block holds, for each DSA layer in turn, the
@@ -145,14 +148,19 @@ dsa_status dsa_resolve_pages(const dsa_layout *layout, int32_t layer, const int3
  *   pool       device uint8, pool_bytes long, 16-B aligned
  *   key_off    device int64 [n_req][off_ld] from dsa_resolve_pages
  *   q          device [n_q][32][128]: bf16 (q_fmt DSA_Q_BF16) or e4m3 codes
- *              (DSA_Q_FP8_E4M3, with q_scale device fp32 [n_q][32]; else NULL)
+ *              (DSA_Q_FP8_E4M3, with q_scale device fp32 [n_q][32]; else NULL),
+ *              or device [n_q][32][68] bytes (DSA_Q_MXFP4, MXFP4 keys only)
  *   w          device fp32 [n_q][32]
  *   q_req, row_len  device int32 [n_q]
  *   scores     device fp32 [n_q][ld] (out): entries t < row_len[r] written,
  *              the rest untouched.
  *   workspace  device, >= dsa_indexer_score_workspace_size(n_q, q_fmt) bytes,
  *              256-B aligned (0 bytes, may be NULL, for bf16 queries)
- * The BF16 path streams each row's keys (decode); the FP8 path is an MFMA
+ * The BF16 and MXFP4 paths stream each row's keys (decode); MXFP4 queries on
+ * MXFP4 keys score on native FP4 MFMA with the E8M0 block scales of both
+ * ([ZH] "量化：原生 MXFP4 索引器"; the query is quantised upstream, as in
+ * "低延迟解码：融合的 DSA 解码路径"), so the result is the formula above for
+ * the decoded MXFP4 query.  The FP8 path is an MFMA
  * GEMM over tiles of consecutive rows and is fastest when consecutive rows
  * share a request (a prefill chunk).  Both accept any q_req.  The FP8 path
  * first writes the rows' sign-folded bf16 query heads and head weights into
@@ -248,8 +256,8 @@ dsa_status dsa_sparse_mla_prefill(const dsa_layout *layout, const uint8_t *pool,
  * scorer and an exact top-k selection, and it outputs the physical KV rows
  * attention reads; "面向三种状态的 KV 缓存": the pages are found through the
  * block table).  For each row r (request b = q_req[r]):
- *   scores[r][t] for t < row_len[r] exactly as dsa_indexer_score with bf16
- *   queries (same kernel, bit for bit), with each key page read through the
+ *   scores[r][t] for t < row_len[r] exactly as dsa_indexer_score with the same
+ *   q_fmt (same kernel, bit for bit), with each key page read through the
  *   block table (pool row * row_stride + layer * layer_stride + the latent
  *   page's bytes) instead of resolved offsets;
  *   idx[r][0..k)  exactly the dsa_topk result on those scores: the
@@ -265,7 +273,9 @@ dsa_status dsa_sparse_mla_prefill(const dsa_layout *layout, const uint8_t *pool,
  *   pool         device uint8, pool_bytes long, 16-B aligned
  *   block_table  device int32 [n_req][bt_ld]; row_len[r] <= 64 * bt_ld (else
  *                DSA_DEVERR_ROW_LEN and the row is cut there)
- *   q            device bf16 [n_q][32][128], 16-B aligned; w device fp32 [n_q][32]
+ *   q, q_fmt     DSA_Q_BF16: device bf16 [n_q][32][128]; DSA_Q_MXFP4 (MXFP4
+ *                keys only): device [n_q][32][68] bytes; 16-B aligned
+ *   w            device fp32 [n_q][32]
  *   q_req, row_len  device int32 [n_q]
  *   scores       device fp32 [n_q][ld] (out)
  *   idx, phys    device int32 [n_q][idx_ld] (out), idx_ld >= k
@@ -275,7 +285,7 @@ dsa_status dsa_sparse_mla_prefill(const dsa_layout *layout, const uint8_t *pool,
  * phys, pool_rows * 64 must fit int32. */
 dsa_status dsa_indexer_select_workspace_size(int32_t n_q, int64_t ld, size_t *bytes);
 dsa_status dsa_indexer_select(const dsa_layout *layout, int32_t layer, const uint8_t *pool, int64_t pool_bytes,
-                              const int32_t *block_table, int64_t bt_ld, int32_t n_req, const uint16_t *q,
+                              const int32_t *block_table, int64_t bt_ld, int32_t n_req, const void *q, int32_t q_fmt,
                               const float *w, const int32_t *q_req, const int32_t *row_len, int32_t n_q, int32_t k,
                               float *scores, int64_t ld, int32_t *idx, int32_t *phys, int64_t idx_ld,
                               void *workspace, size_t workspace_bytes, int32_t *err_flag, dsa_stream_t stream);
@@ -283,8 +293,8 @@ dsa_status dsa_indexer_select(const dsa_layout *layout, int32_t layer, const uin
  * (arguments as there): dsa_indexer_score_pages is the scan alone (no
  * workspace); dsa_topk_pages is dsa_topk with the physical-row output. */
 dsa_status dsa_indexer_score_pages(const dsa_layout *layout, int32_t layer, const uint8_t *pool, int64_t pool_bytes,
-                                   const int32_t *block_table, int64_t bt_ld, int32_t n_req, const uint16_t *q,
-                                   const float *w, const int32_t *q_req, const int32_t *row_len, int32_t n_q,
+                                   const int32_t *block_table, int64_t bt_ld, int32_t n_req, const void *q,
+                                   int32_t q_fmt, const float *w, const int32_t *q_req, const int32_t *row_len, int32_t n_q,
                                    float *scores, int64_t ld, int32_t *err_flag, dsa_stream_t stream);
 dsa_status dsa_topk_pages(const dsa_layout *layout, int64_t pool_bytes, const int32_t *block_table, int64_t bt_ld,
                           int32_t n_req, const int32_t *q_req, const float *scores, int64_t ld,

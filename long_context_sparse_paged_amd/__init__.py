@@ -30,7 +30,7 @@ DSA_DEVERR_BLOCK_RANGE, DSA_DEVERR_PAGE_COUNT, DSA_DEVERR_PAGE_OFFSET = 1, 2, 4
 DSA_DEVERR_ROW_LEN, DSA_DEVERR_INDEX, DSA_DEVERR_REQUEST = 8, 16, 32
 DSA_KEY_FP8_E4M3_SCALED, DSA_KEY_MXFP4 = 0, 1
 DSA_LAT_FP8_E4M3, DSA_LAT_NVFP4 = 0, 1
-DSA_Q_BF16, DSA_Q_FP8_E4M3 = 0, 1
+DSA_Q_BF16, DSA_Q_FP8_E4M3, DSA_Q_MXFP4 = 0, 1, 2
 
 __all__ = [
     "DsaError", "dsa_layout", "lib", "dsa_status_str", "dsa_version", "dsa_layout_make", "dsa_resolve_pages",
@@ -79,10 +79,10 @@ def _load():
         "dsa_sparse_mla_decode": ([LP, P, I64, P, I64, P, P, I64, I32, P, I32, I32, F, F, P, P, P, SZ, P, P], I32),
         "dsa_sparse_mla_decode_noalloc": ([LP, P, I64, P, I64, P, P, I64, I32, P, I32, I32, F, F, P, P, P, P], I32),
         "dsa_indexer_select_workspace_size": ([I32, I64, C.POINTER(SZ)], I32),
-        "dsa_indexer_select": ([LP, I32, P, I64, P, I64, I32, P, P, P, P, I32, I32, P, I64, P, P, I64, P, SZ, P, P],
+        "dsa_indexer_select": ([LP, I32, P, I64, P, I64, I32, P, I32, P, P, P, I32, I32, P, I64, P, P, I64, P, SZ, P, P],
                                I32),
         "dsa_sparse_mla_decode_phys": ([LP, I32, P, I64, P, I64, I32, P, I32, I32, F, F, P, P, P, SZ, P, P], I32),
-        "dsa_indexer_score_pages": ([LP, I32, P, I64, P, I64, I32, P, P, P, P, I32, P, I64, P, P], I32),
+        "dsa_indexer_score_pages": ([LP, I32, P, I64, P, I64, I32, P, I32, P, P, P, I32, P, I64, P, P], I32),
         "dsa_topk_pages": ([LP, I64, P, I64, I32, P, P, I64, P, I32, I32, P, SZ, P, P, I64, P, P], I32),
         "dsa_sparse_mla_prefill_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
         "dsa_dcp_topk_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
@@ -136,6 +136,7 @@ def _stream(stream):
 
 I32, I64, U8, F32 = (torch.int32,), (torch.int64,), (torch.uint8,), (torch.float32,)
 BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_Q_DTYPE = {DSA_Q_BF16: BF16, DSA_Q_FP8_E4M3: U8, DSA_Q_MXFP4: U8}
 
 
 def dsa_layout_make(page_size: int, n_layers: int, key_fmt: int, lat_fmt: int, extra_row_bytes: int = 0) -> dsa_layout:
@@ -204,12 +205,12 @@ def dsa_indexer_select_workspace_size(n_q: int, ld: int) -> int:
 
 
 def dsa_indexer_select(layout: dsa_layout, layer: int, pool, block_table, n_req: int, q, w, q_req, row_len, k: int,
-                       scores, idx, phys, workspace, err_flag=None, stream=None):
+                       scores, idx, phys, workspace, err_flag=None, stream=None, q_fmt: int = DSA_Q_BF16):
     """Fused decode indexer: scores, the exact top-k (ascending) and their physical rows."""
     n_q = q.shape[0]
     st = lib.dsa_indexer_select(C.byref(layout), layer, _ptr(pool, U8, "pool"), pool.numel(),
                                 _ptr(block_table, I32, "block_table"), block_table.shape[1], n_req,
-                                _ptr(q, BF16, "q"), _ptr(w, F32, "w"), _ptr(q_req, I32, "q_req"),
+                                _ptr(q, _Q_DTYPE[q_fmt], "q"), q_fmt, _ptr(w, F32, "w"), _ptr(q_req, I32, "q_req"),
                                 _ptr(row_len, I32, "row_len"), n_q, k, _ptr(scores, F32, "scores"), scores.shape[1],
                                 _ptr(idx, I32, "idx"), _ptr(phys, I32, "phys"), idx.shape[1],
                                 _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
@@ -218,11 +219,12 @@ def dsa_indexer_select(layout: dsa_layout, layer: int, pool, block_table, n_req:
 
 
 def dsa_indexer_score_pages(layout: dsa_layout, layer: int, pool, block_table, n_req: int, q, w, q_req, row_len,
-                            scores, err_flag=None, stream=None):
+                            scores, err_flag=None, stream=None, q_fmt: int = DSA_Q_BF16):
     """First half of dsa_indexer_select: the scan, pages read through the block table."""
     st = lib.dsa_indexer_score_pages(C.byref(layout), layer, _ptr(pool, U8, "pool"), pool.numel(),
                                      _ptr(block_table, I32, "block_table"), block_table.shape[1], n_req,
-                                     _ptr(q, BF16, "q"), _ptr(w, F32, "w"), _ptr(q_req, I32, "q_req"),
+                                     _ptr(q, _Q_DTYPE[q_fmt], "q"), q_fmt, _ptr(w, F32, "w"),
+                                     _ptr(q_req, I32, "q_req"),
                                      _ptr(row_len, I32, "row_len"), q.shape[0], _ptr(scores, F32, "scores"),
                                      scores.shape[1], _ptr(err_flag, I32, "err_flag"), _stream(stream))
     _check("dsa_indexer_score_pages", st)

@@ -121,7 +121,8 @@ dsa_status dsa_indexer_score(const dsa_layout *layout, const uint8_t *pool, int6
                              int32_t *err_flag, dsa_stream_t stream) {
   dsa_status st = check_layout(layout);
   if (st != DSA_OK) return st;
-  if (q_fmt != DSA_Q_BF16 && q_fmt != DSA_Q_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
+  if (q_fmt != DSA_Q_BF16 && q_fmt != DSA_Q_FP8_E4M3 && q_fmt != DSA_Q_MXFP4) return DSA_ERR_UNSUPPORTED;
+  if (q_fmt == DSA_Q_MXFP4 && layout->key_fmt != DSA_KEY_MXFP4) return DSA_ERR_UNSUPPORTED;
   if (n_q < 0 || n_req < 0 || ld < 0 || off_ld < 1 || pool_bytes < 0) return DSA_ERR_BAD_SHAPE;
   if (n_q == 0) return DSA_OK;
   if (!pool || !key_off || !q || !w || !q_req || !row_len || !scores) return DSA_ERR_NULL_ARG;
@@ -145,8 +146,9 @@ dsa_status dsa_indexer_score(const dsa_layout *layout, const uint8_t *pool, int6
   a.ld = ld;
   a.err = err_flag;
   a.key_fmt = layout->key_fmt;
+  a.q_fmt = q_fmt;
   a.ws = nullptr;
-  if (q_fmt == DSA_Q_BF16) {
+  if (q_fmt != DSA_Q_FP8_E4M3) {
     if (n_q > 4096) return DSA_ERR_UNSUPPORTED;
     return launched(launch_indexer_scan(a, stream_of(stream)));
   }
@@ -191,8 +193,8 @@ dsa_status dsa_indexer_score_verify(const dsa_layout *layout, const uint8_t *poo
 dsa_status dsa_indexer_score_workspace_size(int32_t n_q, int32_t q_fmt, size_t *bytes) {
   if (!bytes) return DSA_ERR_NULL_ARG;
   if (n_q < 0) return DSA_ERR_BAD_SHAPE;
-  if (q_fmt != DSA_Q_BF16 && q_fmt != DSA_Q_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
-  *bytes = q_fmt == DSA_Q_BF16 ? 0 : indexer_gemm_workspace_bytes(n_q);
+  if (q_fmt != DSA_Q_BF16 && q_fmt != DSA_Q_FP8_E4M3 && q_fmt != DSA_Q_MXFP4) return DSA_ERR_UNSUPPORTED;
+  *bytes = q_fmt == DSA_Q_FP8_E4M3 ? indexer_gemm_workspace_bytes(n_q) : 0;
   return DSA_OK;
 }
 
@@ -391,9 +393,11 @@ static dsa_status fused_common(const dsa_layout *layout, int64_t pool_bytes, con
   return DSA_OK;
 }
 
-static dsa_status score_pages_check(const dsa_layout *layout, int32_t layer, const uint8_t *pool, const uint16_t *q,
-                                    const float *w) {
+static dsa_status score_pages_check(const dsa_layout *layout, int32_t layer, const uint8_t *pool, const void *q,
+                                    int32_t q_fmt, const float *w) {
   if (layer < 0 || layer >= layout->n_layers) return DSA_ERR_BAD_SHAPE;
+  if (q_fmt != DSA_Q_BF16 && q_fmt != DSA_Q_MXFP4) return DSA_ERR_UNSUPPORTED;
+  if (q_fmt == DSA_Q_MXFP4 && layout->key_fmt != DSA_KEY_MXFP4) return DSA_ERR_UNSUPPORTED;
   if (!pool || !q || !w) return DSA_ERR_NULL_ARG;
   if (!aligned(pool, 16) || !aligned(q, 16) || !aligned(w, 4)) return DSA_ERR_MISALIGNED;
   return DSA_OK;
@@ -413,7 +417,7 @@ static dsa_status topk_pages_check(const dsa_layout *layout, int64_t pool_bytes,
 
 static dsa_status launch_score_pages(const dsa_layout *layout, int32_t layer, const uint8_t *pool,
                                      int64_t pool_bytes, const int32_t *block_table, int64_t bt_ld, int32_t n_req,
-                                     const uint16_t *q, const float *w, const int32_t *q_req,
+                                     const void *q, int32_t q_fmt, const float *w, const int32_t *q_req,
                                      const int32_t *row_len, int32_t n_q, float *scores, int64_t ld,
                                      int32_t *err_flag, dsa_stream_t stream) {
   ScoreArgs a{};
@@ -431,6 +435,7 @@ static dsa_status launch_score_pages(const dsa_layout *layout, int32_t layer, co
   a.ld = ld;
   a.err = err_flag;
   a.key_fmt = layout->key_fmt;
+  a.q_fmt = q_fmt;
   a.bt = block_table;
   a.bt_ld = bt_ld;
   a.pool_rows = pool_bytes / layout->row_stride;
@@ -464,16 +469,16 @@ static dsa_status launch_topk_pages(const dsa_layout *layout, int64_t pool_bytes
 }
 
 dsa_status dsa_indexer_score_pages(const dsa_layout *layout, int32_t layer, const uint8_t *pool, int64_t pool_bytes,
-                                   const int32_t *block_table, int64_t bt_ld, int32_t n_req, const uint16_t *q,
-                                   const float *w, const int32_t *q_req, const int32_t *row_len, int32_t n_q,
+                                   const int32_t *block_table, int64_t bt_ld, int32_t n_req, const void *q,
+                                   int32_t q_fmt, const float *w, const int32_t *q_req, const int32_t *row_len, int32_t n_q,
                                    float *scores, int64_t ld, int32_t *err_flag, dsa_stream_t stream) {
   dsa_status st = fused_common(layout, pool_bytes, block_table, bt_ld, n_req, q_req, row_len, n_q, scores, ld,
                                err_flag);
   if (st != DSA_OK || n_q == 0) return st;
-  st = score_pages_check(layout, layer, pool, q, w);
+  st = score_pages_check(layout, layer, pool, q, q_fmt, w);
   if (st != DSA_OK) return st;
-  return launch_score_pages(layout, layer, pool, pool_bytes, block_table, bt_ld, n_req, q, w, q_req, row_len, n_q,
-                            scores, ld, err_flag, stream);
+  return launch_score_pages(layout, layer, pool, pool_bytes, block_table, bt_ld, n_req, q, q_fmt, w, q_req, row_len,
+                            n_q, scores, ld, err_flag, stream);
 }
 
 dsa_status dsa_topk_pages(const dsa_layout *layout, int64_t pool_bytes, const int32_t *block_table, int64_t bt_ld,
@@ -492,7 +497,7 @@ dsa_status dsa_topk_pages(const dsa_layout *layout, int64_t pool_bytes, const in
 }
 
 dsa_status dsa_indexer_select(const dsa_layout *layout, int32_t layer, const uint8_t *pool, int64_t pool_bytes,
-                              const int32_t *block_table, int64_t bt_ld, int32_t n_req, const uint16_t *q,
+                              const int32_t *block_table, int64_t bt_ld, int32_t n_req, const void *q, int32_t q_fmt,
                               const float *w, const int32_t *q_req, const int32_t *row_len, int32_t n_q, int32_t k,
                               float *scores, int64_t ld, int32_t *idx, int32_t *phys, int64_t idx_ld,
                               void *workspace, size_t workspace_bytes, int32_t *err_flag, dsa_stream_t stream) {
@@ -503,11 +508,11 @@ dsa_status dsa_indexer_select(const dsa_layout *layout, int32_t layer, const uin
   if (k < 1 || idx_ld < k) return DSA_ERR_BAD_SHAPE;
   if (layer < 0 || layer >= layout->n_layers) return DSA_ERR_BAD_SHAPE;
   if (n_q == 0) return k > kMaxTopK ? DSA_ERR_UNSUPPORTED : DSA_OK;
-  st = score_pages_check(layout, layer, pool, q, w);
+  st = score_pages_check(layout, layer, pool, q, q_fmt, w);
   if (st == DSA_OK) st = topk_pages_check(layout, pool_bytes, n_q, k, ld, workspace, workspace_bytes, idx, phys, idx_ld);
   if (st != DSA_OK) return st;
-  st = launch_score_pages(layout, layer, pool, pool_bytes, block_table, bt_ld, n_req, q, w, q_req, row_len, n_q,
-                          scores, ld, err_flag, stream);
+  st = launch_score_pages(layout, layer, pool, pool_bytes, block_table, bt_ld, n_req, q, q_fmt, w, q_req, row_len,
+                          n_q, scores, ld, err_flag, stream);
   if (st != DSA_OK) return st;
   return launch_topk_pages(layout, pool_bytes, block_table, bt_ld, n_req, q_req, scores, ld, row_len, n_q, k,
                            workspace, idx, phys, idx_ld, err_flag, stream);

@@ -24,6 +24,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 
 constexpr int kPage = 64;       // tokens per cache page
 constexpr int kIdxHeads = 32;   // indexer heads

@@ -37,6 +37,7 @@ struct ScoreArgs {
   int64_t ld;
   int32_t *err;
   int32_t key_fmt;
+  int32_t q_fmt;  // DSA_Q_BF16 or DSA_Q_MXFP4 (scan); DSA_Q_FP8_E4M3 (GEMM)
   void *ws;  // e4m3 queries: indexer_gemm_workspace_bytes(n_q) bytes, 256-B aligned
   // Block-table mode (bt != NULL; the page resolve fused into the scan): the key page of
   // (request b, page p) is at bt[b * bt_ld + p] * row_stride + key_base, with bt_ld in place

@@ -27,6 +27,14 @@
 // (n, h) at K-step s takes dims [64h + 8s, 64h + 8s + 8), which makes both the
 // query fragment and the key fragment contiguous runs of bytes.
 //
+// Native FP4 scoring (QF4, MXFP4 keys with MXFP4 queries; section "量化：原生 MXFP4 索引器":
+// scoring on native FP4 matrix instructions with fp32 accumulation, and section "低延迟解码：
+// 融合的 DSA 解码路径": the indexer query is quantised to FP8 or MXFP4 upstream): no decode at
+// all -- per 32 tokens two v_mfma_scale_f32_32x32x64_f8f6f4 with both operands in e2m1 and
+// their E8M0 block scales.  Lane (n, h) at K-step s holds dims [64s + 32h, 64s + 32h + 32) --
+// exactly one 32-element MX block, i.e. 16 bytes of the row and one scale byte.  Every
+// e2m1 x e2m1 product is exact, and within a block the products share one power of two.
+//
 // Block-table mode (BT) serves the fused score -> select path (section "低延迟解码：融合的 DSA
 // 解码路径": a key-balanced scorer, then an exact top-k that emits physical rows): page
 // addresses come straight from the block table (pool row * row stride + the layer's key-page
@@ -70,7 +78,7 @@ __device__ __forceinline__ int row_length(const ScoreArgs &a, int r, int64_t max
   return len;
 }
 
-template <int KEY_FMT, bool BT>
+template <int KEY_FMT, bool BT, bool QF4>
 __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a) {
   using KR = KeyRow<KEY_FMT>;
   __shared__ __align__(16) uint8_t s_page[kScanWaves][KR::kPageBytes];
@@ -216,7 +224,10 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
   };
 
   int cur_row = -1, cur_len = 0;
+  static_assert(!QF4 || KEY_FMT == 1, "FP4 queries go with MXFP4 keys");
   bf16x8_t qf[8];
+  i32x8_t qa[2];     // QF4: the query's e2m1 block of each K-step (low four dwords)
+  uint32_t qsc[2];   // QF4: its E8M0 scale (low byte)
   float wv[16];
   const int n = lane & 31, h = lane >> 5;
   auto compute = [&](int uu, int rr) __attribute__((always_inline)) {
@@ -224,8 +235,20 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
       cur_row = rr;
       cur_len = __builtin_amdgcn_readfirstlane(row_length(a, rr, max_tok, false));
       const uint16_t *qr = reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)rr * kIdxHeads + n) * kIdxDim;
+      if constexpr (QF4) {
+        // query row of head n: 68 bytes in the key format (64 B of e2m1 pairs, 4 E8M0 scales)
+        const uint8_t *q4 = static_cast<const uint8_t *>(a.q) + ((int64_t)rr * kIdxHeads + n) * 68;
+        const uint32_t s4 = *reinterpret_cast<const uint32_t *>(q4 + 64);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8_t *>(qr + 64 * h + 8 * s);
+        for (int s = 0; s < 2; ++s) {
+          const uint32_t *qw = reinterpret_cast<const uint32_t *>(q4 + 16 * (2 * s + h));
+          qa[s] = i32x8_t{(int)qw[0], (int)qw[1], (int)qw[2], (int)qw[3], 0, 0, 0, 0};
+          qsc[s] = s4 >> (8 * (2 * s + h));
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8_t *>(qr + 64 * h + 8 * s);
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) wv[i] = a.w[(int64_t)rr * kIdxHeads + 8 * (i >> 2) + 4 * h + (i & 3)];
       // Drain here, on this rare path: loads still outstanding where it rejoins the common path
@@ -248,6 +271,16 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
           acc = mfma_32x32x16_bf16(qf[s], e4m3x8_bf16(d0, d1), acc);
         }
         scale = *reinterpret_cast<const float *>(row + 128);
+      } else if constexpr (QF4) {
+        const uint32_t sc4 = *reinterpret_cast<const uint32_t *>(row + 64);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          // 16 B of block 2s + h (68-B rows: dword reads)
+          const uint32_t *kw = reinterpret_cast<const uint32_t *>(row + 16 * (2 * s + h));
+          const i32x8_t kb = {(int)kw[0], (int)kw[1], (int)kw[2], (int)kw[3], 0, 0, 0, 0};
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[s], kb, acc, 4, 4, 0, qsc[s], 0,
+                                                                sc4 >> (8 * (2 * s + h)));
+        }
       } else {
         const uint32_t sc4 = *reinterpret_cast<const uint32_t *>(row + 64);
 #pragma unroll
@@ -339,12 +372,12 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
   if (nb > 0) flush();
 }
 
-template <int KEY_FMT>
+template <int KEY_FMT, bool QF4>
 void launch_scan_t(const ScoreArgs &a, dim3 grid, size_t dyn, hipStream_t s) {
   if (a.bt != nullptr)
-    hipLaunchKernelGGL((indexer_scan_kernel<KEY_FMT, true>), grid, dim3(256), dyn, s, a);
+    hipLaunchKernelGGL((indexer_scan_kernel<KEY_FMT, true, QF4>), grid, dim3(256), dyn, s, a);
   else
-    hipLaunchKernelGGL((indexer_scan_kernel<KEY_FMT, false>), grid, dim3(256), dyn, s, a);
+    hipLaunchKernelGGL((indexer_scan_kernel<KEY_FMT, false, QF4>), grid, dim3(256), dyn, s, a);
 }
 
 }  // namespace
@@ -359,10 +392,14 @@ hipError_t launch_indexer_scan(const ScoreArgs &a, hipStream_t s) {
   if (grid > 512) grid = 512;
   if (grid < 1) grid = 1;
   const size_t dyn = sizeof(int) * (size_t)(a.n_q + 1);
-  if (a.key_fmt == 0)
-    launch_scan_t<0>(a, dim3((unsigned)grid), dyn, s);
-  else
-    launch_scan_t<1>(a, dim3((unsigned)grid), dyn, s);
+  if (a.q_fmt == DSA_Q_MXFP4) {
+    if (a.key_fmt != 1) return hipErrorInvalidValue;
+    launch_scan_t<1, true>(a, dim3((unsigned)grid), dyn, s);
+  } else if (a.key_fmt == 0) {
+    launch_scan_t<0, false>(a, dim3((unsigned)grid), dyn, s);
+  } else {
+    launch_scan_t<1, false>(a, dim3((unsigned)grid), dyn, s);
+  }
   return hipGetLastError();
 }
 

@@ -608,7 +608,6 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (K & 15) | ((K >> 4) << 14));
 }
 
-typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 typedef __attribute__((ext_vector_type(2))) int i32x2_t;
 
 // 16 bytes from global memory straight into LDS (global_load_lds_dwordx4 with M0 = `lds`, a

@@ -524,32 +524,39 @@ __device__ __forceinline__ void select_from_regs(const uint32_t (&rk)[PER], int 
 
 // Exact selection and ordered output of the n candidates in s_key / s_idx (index order):
 // thread t holds candidates [t per, t per + cnt) in registers (cnt <= per <= PER).  s_key
-// doubles as the radix select's list once the registers are loaded.
-template <int PER, class Emit>
+// doubles as the radix select's list once the registers are loaded.  pre(index) is evaluated
+// for every candidate as soon as its index is in a register (its loads fly during the radix
+// passes); each kept candidate is emitted as emit(position, index, pre(index)).
+template <int PER, class Pre, class Emit>
 __device__ __forceinline__ void select_write(uint32_t *s_key, const int32_t *s_idx, int n, int per, int keff,
-                             RadixLds<kFinThreads> &R, Emit emit, int list_cap = kShortRow) {
+                                             RadixLds<kFinThreads> &R, Pre pre, Emit emit, int list_cap) {
   const int tid = threadIdx.x;
   const int b0 = min(n, tid * per);
   const int cnt = min(n, b0 + per) - b0;
   uint32_t rk[PER];
-  int32_t ri[PER];
+  int32_t ri[PER], pv[PER];
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
     rk[q] = q < cnt ? s_key[b0 + q] : 0u;
     ri[q] = q < cnt ? s_idx[b0 + q] : 0;
   }
-  select_from_regs<PER>(rk, cnt, [&](int q) { return ri[q]; }, keff, R, emit, s_key, list_cap);
+#pragma unroll
+  for (int q = 0; q < PER; ++q) pv[q] = q < cnt ? pre(ri[q]) : 0;
+  select_from_regs<PER>(
+      rk, cnt, [&](int q) { return q; }, keff, R, [&](int pos, int q) { emit(pos, ri[q], pv[q]); }, s_key,
+      list_cap);
 }
 
 // select_write with the register bound picked from a few sizes (per = candidates per thread).
-template <class Emit>
+template <class Pre, class Emit>
 __device__ __forceinline__ void select_write_any(uint32_t *s_key, const int32_t *s_idx, int n, int per, int keff,
-                                 RadixLds<kFinThreads> &R, Emit emit, int list_cap = kShortRow) {
-  if (per <= 5) select_write<5>(s_key, s_idx, n, per, keff, R, emit, list_cap);
-  else if (per <= 9) select_write<9>(s_key, s_idx, n, per, keff, R, emit, list_cap);
-  else if (per <= 13) select_write<13>(s_key, s_idx, n, per, keff, R, emit, list_cap);
-  else if (per <= 17) select_write<17>(s_key, s_idx, n, per, keff, R, emit, list_cap);
-  else select_write<kFinPer>(s_key, s_idx, n, per, keff, R, emit, list_cap);
+                                                 RadixLds<kFinThreads> &R, Pre pre, Emit emit,
+                                                 int list_cap = kShortRow) {
+  if (per <= 5) select_write<5>(s_key, s_idx, n, per, keff, R, pre, emit, list_cap);
+  else if (per <= 9) select_write<9>(s_key, s_idx, n, per, keff, R, pre, emit, list_cap);
+  else if (per <= 13) select_write<13>(s_key, s_idx, n, per, keff, R, pre, emit, list_cap);
+  else if (per <= 17) select_write<17>(s_key, s_idx, n, per, keff, R, pre, emit, list_cap);
+  else select_write<kFinPer>(s_key, s_idx, n, per, keff, R, pre, emit, list_cap);
 }
 
 __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkArgs a, TopkWs w, int n_slices) {
@@ -598,19 +605,21 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
     else if (tid == 0) flag_error(a.err, DSA_DEVERR_REQUEST);
   }
   const int keff = min(a.k, len);
-  auto phys_of = [&](int t) -> int32_t {
+  // physical row of token t from its block id (read from the block table beforehand)
+  auto phys_from = [&](int32_t blk, int t) -> int32_t {
     if (btr == nullptr) return -1;
-    const int32_t blk = btr[t >> 6];
     if (blk < 0 || blk >= a.pool_rows) {
       flag_error(a.err, DSA_DEVERR_BLOCK_RANGE);
       return -1;
     }
     return blk * kPage + (t & (kPage - 1));
   };
-  auto emit = [&](int pos, int32_t i) {
+  auto block_of = [&](int32_t t) -> int32_t { return btr != nullptr ? btr[t >> 6] : -1; };
+  auto emit3 = [&](int pos, int32_t i, int32_t blk) {
     out[pos] = i;
-    if (pout) pout[pos] = phys_of(i);
+    if (pout) pout[pos] = phys_from(blk, i);
   };
+  auto emit = [&](int pos, int32_t i) { emit3(pos, i, pout ? block_of(i) : -1); };
 
   if (keff >= len) {  // keep everything (also len == 0)
     for (int i = tid; i < a.k; i += NT) {
@@ -762,7 +771,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
     // strided LDS reads of a wave hit distinct banks); the loops are unrolled for a bound
     // on per picked from a few sizes
     const int per = ((n + NT - 1) / NT) | 1;
-    select_write_any(s_key, s_idx, n, per, keff, R, emit);
+    select_write_any(s_key, s_idx, n, per, keff, R, block_of, emit3);
   } else {
     // exact selection over the whole row, straight from global memory
     auto load = [&](int i) { return score_key(row[i]); };

@@ -51,13 +51,16 @@ class _Base:
 
 
 class DecodeStep(_Base):
-    """Decode: one query row per request (row_len = context length)."""
+    """Decode: one query row per request (row_len = context length).  q_fmt DSA_Q_MXFP4 takes
+    q_idx as [B, 32, 68] MXFP4 rows (MXFP4 keys: native FP4 scoring)."""
 
-    def __init__(self, cache, q_idx, w, q_mla, sm_scale: float, k: int = 2048, device="cuda"):
+    def __init__(self, cache, q_idx, w, q_mla, sm_scale: float, k: int = 2048, device="cuda",
+                 q_fmt: int = DSA_Q_BF16):
         n_req = cache.block_table.shape[0]
         ld = int(cache.ctx_len.max().item()) if n_req else 1
         super().__init__(cache, k, n_req, ld, device)
         self.q_idx, self.w, self.q_mla = q_idx, w, q_mla
+        self.q_fmt = q_fmt
         self.sm_scale = sm_scale
         self.n_heads = q_mla.shape[1]
         self.q_req = torch.arange(n_req, dtype=torch.int32, device=device)
@@ -69,8 +72,8 @@ class DecodeStep(_Base):
 
     def score(self, stream=None):
         c = self.cache
-        dsa_indexer_score(self.layout, c.pool, self.key_off, c.n_req, self.q_idx, DSA_Q_BF16, None, self.w, self.q_req,
-                          self.row_len, self.scores, None, self.err, stream)
+        dsa_indexer_score(self.layout, c.pool, self.key_off, c.n_req, self.q_idx, self.q_fmt, None, self.w,
+                          self.q_req, self.row_len, self.scores, None, self.err, stream)
 
     def attend(self, stream=None):
         c = self.cache
@@ -168,10 +171,12 @@ class FusedDecodeStep:
     top-k writes each kept token's physical row beside its index, and attention reads those
     rows directly.  The same results as DecodeStep (bit for bit)."""
 
-    def __init__(self, cache, q_idx, w, q_mla, sm_scale: float, k: int = 2048, device="cuda"):
+    def __init__(self, cache, q_idx, w, q_mla, sm_scale: float, k: int = 2048, device="cuda",
+                 q_fmt: int = DSA_Q_BF16):
         self.cache = cache
         self.layout = _layout_of(cache)
         self.k = k
+        self.q_fmt = q_fmt
         n_req = cache.block_table.shape[0]
         ld = int(cache.ctx_len.max().item()) if n_req else 1
         ld = (ld + 3) // 4 * 4  # score rows start on 16 B (vector loads and stores)
@@ -194,13 +199,14 @@ class FusedDecodeStep:
     def select(self, stream=None):
         c = self.cache
         dsa_indexer_select(self.layout, c.layer, c.pool, c.block_table, c.n_req, self.q_idx, self.w, self.q_req,
-                           self.row_len, self.k, self.scores, self.idx, self.phys, self.ws_sel, self.err, stream)
+                           self.row_len, self.k, self.scores, self.idx, self.phys, self.ws_sel, self.err, stream,
+                           q_fmt=self.q_fmt)
 
     def score(self, stream=None):
         """The select's first half alone (the scan)."""
         c = self.cache
         dsa_indexer_score_pages(self.layout, c.layer, c.pool, c.block_table, c.n_req, self.q_idx, self.w, self.q_req,
-                                self.row_len, self.scores, self.err, stream)
+                                self.row_len, self.scores, self.err, stream, q_fmt=self.q_fmt)
 
     def topk(self, stream=None):
         """The select's second half alone (needs score() first)."""

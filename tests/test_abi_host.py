@@ -101,6 +101,9 @@ def test_score_errors(d):
     Lm = d.dsa_layout_make(64, 1, 1, 1, 0)
     a = list(args); a[0] = C.byref(Lm); a[7] = 1; a[8] = FAKE   # FP8 queries need FP8 keys
     assert f(*a) == d.DSA_ERR_UNSUPPORTED
+    a = list(args); a[7] = d.DSA_Q_MXFP4                        # MXFP4 queries need MXFP4 keys
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED
+    assert d.dsa_indexer_score_workspace_size(4, d.DSA_Q_MXFP4) == 0
     a = list(args); a[12] = 0       # nothing to do
     assert f(*a) == d.DSA_OK
     # FP8 queries take a workspace: rows of bf16 query heads, and the weights
@@ -254,31 +257,35 @@ def test_fused_select_errors(d):
     need = d.dsa_indexer_select_workspace_size(4, 1024)
     assert need == d.dsa_topk_workspace_size(4, 1024, 2048)  # the top-k's own workspace
     f = d.lib.dsa_indexer_select
-    # layout, layer, pool, pool_bytes, bt, bt_ld, n_req, q, w, q_req, row_len, n_q, k, scores, ld,
+    # layout, layer, pool, pool_bytes, bt, bt_ld, n_req, q, q_fmt, w, q_req, row_len, n_q, k, scores, ld,
     # idx, phys, idx_ld, ws, ws_bytes, err, stream
-    args = [C.byref(L), 0, FAKE, 1 << 30, FAKE, 16, 4, FAKE, FAKE, FAKE, FAKE, 4, 2048, FAKE, 1024, FAKE, FAKE, 2048,
-            FAKE, need, None, None]
+    args = [C.byref(L), 0, FAKE, 1 << 30, FAKE, 16, 4, FAKE, 0, FAKE, FAKE, FAKE, 4, 2048, FAKE, 1024, FAKE, FAKE,
+            2048, FAKE, need, None, None]
     a = list(args); a[1] = 2
     assert f(*a) == d.DSA_ERR_BAD_SHAPE           # layer past n_layers
-    a = list(args); a[14] = (1 << 23) + 4
+    a = list(args); a[8] = d.DSA_Q_MXFP4
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED         # MXFP4 queries on FP8 keys
+    a = list(args); a[8] = d.DSA_Q_FP8_E4M3
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED         # the fused scan takes bf16 or MXFP4 queries
+    a = list(args); a[15] = (1 << 23) + 4
     assert f(*a) == d.DSA_ERR_UNSUPPORTED         # rows past 2^23 scores
-    a = list(args); a[12] = 4097; a[17] = 4097
+    a = list(args); a[13] = 4097; a[18] = 4097
     assert f(*a) == d.DSA_ERR_UNSUPPORTED
-    a = list(args); a[12] = 0
+    a = list(args); a[13] = 0
     assert f(*a) == d.DSA_ERR_BAD_SHAPE
-    a = list(args); a[17] = 100
+    a = list(args); a[18] = 100
     assert f(*a) == d.DSA_ERR_BAD_SHAPE           # idx_ld < k
-    a = list(args); a[19] = need - 1
+    a = list(args); a[20] = need - 1
     assert f(*a) == d.DSA_ERR_WORKSPACE_TOO_SMALL
     a = list(args); a[7] = ODD
     assert f(*a) == d.DSA_ERR_MISALIGNED          # q must be 16-B aligned
     a = list(args); a[4] = None
     assert f(*a) == d.DSA_ERR_NULL_ARG
-    a = list(args); a[18] = None
+    a = list(args); a[19] = None
     assert f(*a) == d.DSA_ERR_NULL_ARG            # no workspace
-    a = list(args); a[11] = 0
+    a = list(args); a[12] = 0
     assert f(*a) == d.DSA_OK                      # nothing to do
-    a = list(args); a[11] = 5000
+    a = list(args); a[12] = 5000
     assert f(*a) == d.DSA_ERR_UNSUPPORTED
     # phys output needs pool_row * 64 + slot to fit int32
     a = list(args); a[3] = (1 << 25) * L.row_stride
@@ -295,13 +302,13 @@ def test_fused_select_errors(d):
     a = list(targs); a[2] = None
     assert g(*a) == d.DSA_ERR_NULL_ARG
     h = d.lib.dsa_indexer_score_pages
-    # layout, layer, pool, pool_bytes, bt, bt_ld, n_req, q, w, q_req, row_len, n_q, scores, ld, err, stream
-    sargs = [C.byref(L), 0, FAKE, 1 << 30, FAKE, 16, 4, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1024, None, None]
+    # layout, layer, pool, pool_bytes, bt, bt_ld, n_req, q, q_fmt, w, q_req, row_len, n_q, scores, ld, err, stream
+    sargs = [C.byref(L), 0, FAKE, 1 << 30, FAKE, 16, 4, FAKE, 0, FAKE, FAKE, FAKE, 4, FAKE, 1024, None, None]
     a = list(sargs); a[1] = -1
     assert h(*a) == d.DSA_ERR_BAD_SHAPE
     a = list(sargs); a[5] = 0
     assert h(*a) == d.DSA_ERR_BAD_SHAPE           # bt_ld < 1
-    a = list(sargs); a[8] = None
+    a = list(sargs); a[9] = None
     assert h(*a) == d.DSA_ERR_NULL_ARG
 
 

@@ -2,7 +2,9 @@
 
 Each workload (the decode configurations at 32 x 128K, 8 x 1M and 64 mixed MXFP4/NVFP4
 requests, and the 2048-row prefill chunk on a 153,600-token prefix) is built with the same
-seeds and runs the same four calls as bench.py.  Then, for EVERY row of the decode
+seeds and runs the same calls as bench.py: the fused decode path (with MXFP4 queries on the
+MXFP4 keys of the mixed workload; that workload also once more with bf16 queries through the
+four separate calls) and the prefill step.  Then, for EVERY row of the decode
 workloads: the whole row of scores against the oracle (tolerance 1e-5 of each score + 1e-5
 of the row's rms), the top-k (bit-exact selection on the GPU's own scores, and within the
 1e-5 tie window of the oracle's k-th score), and attention on the GPU's index set (per row,
@@ -33,15 +35,22 @@ def d(gpu):
     return d
 
 
-def build_step(d, cfg):
+def build_step(d, cfg, bench_path=True):
+    """bench_path: the decode step bench.py times (the fused calls, MXFP4 queries on MXFP4
+    keys); else the four separate calls with bf16 queries."""
     wl = W.WORKLOADS[cfg]
     ctx = W.workload_ctx(cfg)
-    log(f"[case] full size {wl['name']}: {len(ctx)} cache requests, {sum(ctx)} tokens")
+    log(f"[case] full size {wl['name']}: {len(ctx)} cache requests, {sum(ctx)} tokens, bench path {bench_path}")
     cache = W.build_cache(ctx, key_fmt=wl["key_fmt"], lat_fmt=wl["lat_fmt"], seed=cfg, device="cuda",
                           spare_rows=wl["spare_rows"])
     if wl["kind"] == "decode":
         qs = W.decode_queries(len(ctx), wl["heads"], seed=cfg, device="cuda")
-        step = d.DecodeStep(cache, qs.q_idx, qs.w, qs.q_mla, qs.sm_scale, k=wl["topk"])
+        if bench_path:
+            q_fmt = d.DSA_Q_MXFP4 if wl["key_fmt"] == 1 else d.DSA_Q_BF16
+            qi = qs.q_idx_mxfp4 if q_fmt == d.DSA_Q_MXFP4 else qs.q_idx
+            step = d.FusedDecodeStep(cache, qi, qs.w, qs.q_mla, qs.sm_scale, k=wl["topk"], q_fmt=q_fmt)
+        else:
+            step = d.DecodeStep(cache, qs.q_idx, qs.w, qs.q_mla, qs.sm_scale, k=wl["topk"])
     else:
         qs = W.prefill_queries(wl["prefix"], wl["chunk"], wl["heads"], seed=cfg, device="cuda")
         step = d.PrefillStep(cache, qs, k=wl["topk"], q_fmt=d.DSA_Q_FP8_E4M3)
@@ -51,9 +60,9 @@ def build_step(d, cfg):
     return wl, ctx, cache, qs, step
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3])
-def test_full_size_decode_every_row(d, cfg):
-    wl, ctx, cache, dq, step = build_step(d, cfg)
+@pytest.mark.parametrize("cfg,bench_path", [(1, True), (2, True), (3, True), (3, False)])
+def test_full_size_decode_every_row(d, cfg, bench_path):
+    wl, ctx, cache, dq, step = build_step(d, cfg, bench_path)
     k, n = wl["topk"], len(ctx)
     oc = oracle.OracleCache(cache)
     rl = np.asarray(ctx, np.int32)
@@ -61,8 +70,12 @@ def test_full_size_decode_every_row(d, cfg):
     ld = int(step.scores.shape[1])
     got_s = step.scores.cpu().numpy()
     got_idx = step.idx.cpu().numpy()
+    if bench_path:  # physical rows: the block table's mapping of the kept tokens
+        bt = cache.block_table.cpu().numpy()
+        want = np.where(got_idx >= 0, bt[req[:, None], np.maximum(got_idx, 0) >> 6] * 64 + (got_idx & 63), -1)
+        assert np.array_equal(step.phys.cpu().numpy(), want)
     log(f"[rows] {wl['name']}: oracle scores of all {n} rows")
-    ref_s = oracle.indexer_score(oc, dq.q_idx, 0, None, dq.w, req, rl, ld=ld)
+    ref_s = oracle.indexer_score(oc, step.q_idx, step.q_fmt, None, dq.w, req, rl, ld=ld)
     check_scores(got_s, ref_s, ctx)
     log(f"[rows] {wl['name']}: top-k of all {n} rows")
     assert np.array_equal(got_idx, oracle.topk(np.nan_to_num(got_s), rl, k))
