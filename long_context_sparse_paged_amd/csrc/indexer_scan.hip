@@ -41,12 +41,27 @@
 // offset), so no separate resolve launch precedes the scan.
 #include <math.h>
 
+#include <type_traits>
+
 #include "dsa_device.hpp"
 #include "dsa_kernels.hpp"
 
 namespace dsa {
 
 namespace {
+
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled (register arrays stay statically indexed)
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_impl(F &f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F f) {
+  static_for_impl<0, N>(f);
+}
 
 constexpr int kScanWaves = 4;
 constexpr int kScanMaxRows = 4096;
@@ -169,7 +184,10 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
     while (uu >= __builtin_amdgcn_readfirstlane(s_start[rr + 1])) ++rr;
     return rr;
   };
-  u32x4_t b0[KR::kLoadsPerLane], b1[KR::kLoadsPerLane];
+  // pages in flight per wave (four in flight measured no faster for the short MXFP4 pages:
+  // their random 4352-B reads, not the bytes in flight, set the pace)
+  constexpr int NBUF = 2;
+  u32x4_t bufs[NBUF][KR::kLoadsPerLane];
   // keys are read once per step: nontemporal loads keep them from displacing cached data
   constexpr int kTail = KR::kChunks - 64 * KR::kFullLoads;  // 16-B chunks in the partial last load
   auto load = [&](u32x4_t (&buf)[KR::kLoadsPerLane], const uint8_t *src) {
@@ -314,61 +332,51 @@ __global__ __launch_bounds__(256, 2) void indexer_scan_kernel(const ScoreArgs a)
     if (++nb == kScoreBufUnits) flush();
   };
 
-  // Software pipeline: two pages in registers in flight while the third is scored from LDS.
-  // The steady-state loop handles two units per trip and always issues two pages of loads.
+  // Software pipeline: NBUF pages in registers in flight while one more is scored from LDS.
+  // The steady-state loop handles NBUF units per trip and always issues NBUF pages of loads.
   if (a.pool_bytes < KR::kPageBytes) {  // no page can be valid
     if (lane == 0) flag_error(a.err, DSA_DEVERR_PAGE_OFFSET);
     return;
   }
   int u = u_beg;
   int rl = row_of(u, r);
-  bool ok0, ok1 = false;
-  int r_0 = rl, r_1 = rl;
-  load(b0, src_of(u, ok0));
-  const uint8_t *src1 = a.pool;  // a wave with one unit still issues this load (same count on every path)
-  if (u + 1 < u_end) {
-    rl = row_of(u + 1, rl);
-    r_1 = rl;
-    src1 = src_of(u + 1, ok1);
-  }
-  load(b1, src1);
-  while (u + 3 < u_end) {
-    park(b0);
-    const bool c0 = ok0;
-    const int cr0 = r_0;
-    rl = row_of(u + 2, rl);
-    r_0 = rl;
-    load(b0, src_of(u + 2, ok0));
-    if (c0) compute(u, cr0); else __builtin_amdgcn_s_waitcnt(0x0F70);
-    ++u;
-    park(b1);
-    const bool c1 = ok1;
-    const int cr1 = r_1;
-    rl = row_of(u + 2, rl);
-    r_1 = rl;
-    load(b1, src_of(u + 2, ok1));
-    if (c1) compute(u, cr1); else __builtin_amdgcn_s_waitcnt(0x0F70);
-    ++u;
-  }
-  // the last one to three units
-  for (int t = 0; u < u_end; ++t, ++u) {
-    if ((t & 1) == 0) {
-      park(b0);
-      const bool c0 = ok0;
-      const int cr0 = r_0;
-      if (u + 2 < u_end) {
-        rl = row_of(u + 2, rl);
-        r_0 = rl;
-        load(b0, src_of(u + 2, ok0));
-      }
-      if (c0) compute(u, cr0);
-    } else {
-      park(b1);
-      const bool c1 = ok1;
-      const int cr1 = r_1;
-      if (c1) compute(u, cr1);
+  bool okb[NBUF];
+  int rowb[NBUF];
+  // units u_beg .. u_beg + NBUF - 1; a wave with fewer units still issues every load (of the
+  // pool's first page), so the number of loads in flight is the same on every path
+  static_for<NBUF>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    okb[i] = false;
+    rowb[i] = rl;
+    const uint8_t *src = a.pool;
+    if (u + i < u_end) {
+      rl = row_of(u + i, rl);
+      rowb[i] = rl;
+      src = src_of(u + i, okb[i]);
     }
-  }
+    load(bufs[i], src);
+  });
+  // unit u sits in buffer (u - u_beg) % NBUF: park it, refill the buffer with unit u + NBUF,
+  // score unit u from LDS
+  auto stage = [&](auto I, bool refill) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value;
+    park(bufs[i]);
+    const bool c = okb[i];
+    const int cr = rowb[i];
+    if (refill) {
+      rl = row_of(u + NBUF, rl);
+      rowb[i] = rl;
+      load(bufs[i], src_of(u + NBUF, okb[i]));
+    }
+    if (c) compute(u, cr); else __builtin_amdgcn_s_waitcnt(0x0F70);
+    ++u;
+  };
+  while (u + 2 * NBUF - 1 < u_end) static_for<NBUF>([&](auto I) { stage(I, true); });
+  // the last units (fewer than 2 NBUF), starting again at buffer 0
+  while (u < u_end)
+    static_for<NBUF>([&](auto I) {
+      if (u < u_end) stage(I, u + NBUF < u_end);
+    });
   if (nb > 0) flush();
 }
 
