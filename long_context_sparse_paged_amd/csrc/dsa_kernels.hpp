@@ -71,7 +71,7 @@ hipError_t launch_indexer_verify(const VerifyArgs &a, hipStream_t s);
 // Top-k: slices of kSlice scores, candidates per slice <= kSliceCap, rows of up to
 // kShortRow scores are selected wholly in LDS.
 constexpr int kSlice = 8192;
-constexpr int kSliceCap = 4096;
+constexpr int kSliceCap = 1024;  // about 6x the candidates a slice of random scores holds at k = 2048
 constexpr int kShortRow = 12288;
 constexpr int kMaxTopK = 4096;
 size_t topk_workspace_bytes(int32_t n_rows, int64_t ld);
