@@ -17,6 +17,8 @@
  *   dsa_indexer_select        scores + exact top-k + physical rows, pages found
  *                             through the block table (no separate resolve)
  *   dsa_sparse_mla_decode_phys  attention over physical rows
+ * The prefill indexer on FP8 MFMA with an exact top-k (a band of tokens rescored exactly):
+ *   dsa_prefill_select        = dsa_prefill_score_fp8 + dsa_prefill_topk_band
  * and, for decode context parallelism emulated on one GPU:
  *   dsa_dcp_topk              the exact top-k merge across token shards
  *
@@ -71,6 +73,7 @@ typedef int32_t dsa_status;
 #define DSA_DEVERR_ROW_LEN 8u      /* row_len outside [0, ld] or past the page table */
 #define DSA_DEVERR_INDEX 16u       /* selected index outside [0, ctx_len) */
 #define DSA_DEVERR_REQUEST 32u     /* q_req outside [0, n_req) */
+#define DSA_DEVERR_BOUND 64u       /* dsa_prefill_select: a score outside its error bound */
 
 /* Index-key row formats ([ZH] "K3.1 Pro 中的稀疏注意力" and "量化：原生 MXFP4 索引器"). */
 #define DSA_KEY_FP8_E4M3_SCALED 0 /* 132 B: 128 OCP e4m3 codes, then a little-endian fp32 scale */
@@ -166,6 +169,58 @@ dsa_status dsa_resolve_pages(const dsa_layout *layout, int32_t layer, const int3
  * first writes the rows' sign-folded bf16 query heads and head weights into
  * the workspace (about 8.2 KB per row). */
 dsa_status dsa_indexer_score_workspace_size(int32_t n_q, int32_t q_fmt, size_t *bytes);
+
+/* Prefill indexer and its exact top-k, scored on FP8 MFMA ([ZH] "低延迟解码：融合的 DSA
+ * 解码路径": the indexer query is FP8 with its scale folded into the head weights;
+ * "预填充：上下文并行稀疏注意力": each row keeps its top-k over the whole context).
+ * The same problem as dsa_indexer_score (q_fmt DSA_Q_FP8_E4M3, FP8 keys) followed by dsa_topk,
+ * with the same result: idx equals, bit for bit, what dsa_topk returns on dsa_indexer_score's
+ * FP8 scores.  Both operands go to the FP8 MFMA as raw e4m3 codes; every product is exact, but
+ * within each group of 8 consecutive dims the MFMA cuts the smaller products to 14 bits below
+ * the group's largest, so the scores it writes are approximations s^ with
+ *     |s^ - s| <= E_r = delta * sum_g U_rg * M_bg,   delta = 1.125 * 2^-10,
+ * s the dsa_indexer_score value, g over the 16 groups of 8 dims,
+ * U_rg = sum_j w[r][j] |q_scale[r][j]| max_{d in g} |q[r][j][d]| (code values) and
+ * M_bg = max |scale_t| max_{d in g} |k_t[d]| over the request's first ctx_len[b] tokens.  The
+ * top-k then finds the k-th largest s^, rescores exactly every token within 2 E_r of it (the
+ * bf16 MFMA arithmetic of dsa_indexer_score), and selects from those and the tokens surely
+ * above.
+ *   pool, key_off, off_ld, n_req  as dsa_indexer_score (FP8 keys)
+ *   ctx_len    device int32 [n_req]: tokens of each request; rows need row_len[r] <= ctx_len[q_req[r]]
+ *   q          device e4m3 [n_q][32][128], 16-B aligned; q_scale, w device fp32 [n_q][32]
+ *   q_req, row_len  device int32 [n_q] (prefill: row_len = position + 1)
+ *   scores     device fp32 [n_q][ld] (out), 16-B aligned: s^ for t < row_len[r] (a row whose
+ *              band holds more than 4096 tokens is rewritten with the exact s)
+ *   idx        device int32 [n_q][idx_ld] (out): as dsa_topk, idx_ld >= k
+ *   bound      device fp32 [n_q] (out, may be NULL): E_r
+ *   workspace  device, >= dsa_prefill_select_workspace_size(...) bytes, 256-B aligned
+ * 1 <= k <= 4096, ld <= 2^23, n_q and n_req <= 65535.  Errors as dsa_indexer_score and
+ * dsa_topk; a row_len past ctx_len of its request is clamped and flags DSA_DEVERR_ROW_LEN.
+ * DSA_DEVERR_BOUND would mean a score fell outside E_r (the bound rests on the measured
+ * behaviour of the instruction; this flag reports a violation instead of a silent error). */
+dsa_status dsa_prefill_select_workspace_size(int32_t n_q, int64_t ld, int32_t n_req, int64_t off_ld, int32_t k,
+                                             size_t *bytes);
+dsa_status dsa_prefill_select(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                              const int64_t *key_off, int64_t off_ld, int32_t n_req, const int32_t *ctx_len,
+                              const uint8_t *q, const float *q_scale, const float *w, const int32_t *q_req,
+                              const int32_t *row_len, int32_t n_q, int32_t k, float *scores, int64_t ld,
+                              int32_t *idx, int64_t idx_ld, float *bound, void *workspace, size_t workspace_bytes,
+                              int32_t *err_flag, dsa_stream_t stream);
+
+/* The two halves of dsa_prefill_select, for callers that time or overlap them: the FP8 MFMA
+ * scores (plus E_r and, in the workspace, the exact query rows the rescoring reads), then the
+ * band top-k.  Called in this order on the same workspace and arguments, they enqueue exactly
+ * what dsa_prefill_select does; dsa_prefill_topk_band reads only what the score half left. */
+dsa_status dsa_prefill_score_fp8(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                                 const int64_t *key_off, int64_t off_ld, int32_t n_req, const int32_t *ctx_len,
+                                 const uint8_t *q, const float *q_scale, const float *w, const int32_t *q_req,
+                                 const int32_t *row_len, int32_t n_q, float *scores, int64_t ld, float *bound,
+                                 void *workspace, size_t workspace_bytes, int32_t *err_flag, dsa_stream_t stream);
+dsa_status dsa_prefill_topk_band(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                                 const int64_t *key_off, int64_t off_ld, int32_t n_req, const int32_t *q_req,
+                                 const int32_t *row_len, int32_t n_q, int32_t k, float *scores, int64_t ld,
+                                 int32_t *idx, int64_t idx_ld, void *workspace, size_t workspace_bytes,
+                                 int32_t *err_flag, dsa_stream_t stream);
 dsa_status dsa_indexer_score(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
                              const int64_t *key_off, int64_t off_ld, int32_t n_req, const void *q, int32_t q_fmt,
                              const float *q_scale, const float *w, const int32_t *q_req, const int32_t *row_len,

@@ -28,6 +28,7 @@ DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE_TOO_SMALL, DSA_ERR_HIP, DSA_ERR_SCRATCH_L
 DSA_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 DSA_DEVERR_BLOCK_RANGE, DSA_DEVERR_PAGE_COUNT, DSA_DEVERR_PAGE_OFFSET = 1, 2, 4
 DSA_DEVERR_ROW_LEN, DSA_DEVERR_INDEX, DSA_DEVERR_REQUEST = 8, 16, 32
+DSA_DEVERR_BOUND = 64
 DSA_KEY_FP8_E4M3_SCALED, DSA_KEY_MXFP4 = 0, 1
 DSA_LAT_FP8_E4M3, DSA_LAT_NVFP4 = 0, 1
 DSA_Q_BF16, DSA_Q_FP8_E4M3, DSA_Q_MXFP4 = 0, 1, 2
@@ -38,7 +39,8 @@ __all__ = [
     "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill_workspace_size", "dsa_sparse_mla_prefill",
     "dsa_dcp_topk_workspace_size", "dsa_dcp_topk", "dsa_sparse_mla_decode_noalloc",
     "dsa_indexer_select_workspace_size", "dsa_indexer_select", "dsa_sparse_mla_decode_phys",
-    "dsa_indexer_score_pages", "dsa_topk_pages",
+    "dsa_indexer_score_pages", "dsa_topk_pages", "dsa_prefill_select_workspace_size", "dsa_prefill_select",
+    "dsa_prefill_score_fp8", "dsa_prefill_topk_band",
 ]
 
 
@@ -84,6 +86,11 @@ def _load():
         "dsa_sparse_mla_decode_phys": ([LP, I32, P, I64, P, I64, I32, P, I32, I32, F, F, P, P, P, SZ, P, P], I32),
         "dsa_indexer_score_pages": ([LP, I32, P, I64, P, I64, I32, P, I32, P, P, P, I32, P, I64, P, P], I32),
         "dsa_topk_pages": ([LP, I64, P, I64, I32, P, P, I64, P, I32, I32, P, SZ, P, P, I64, P, P], I32),
+        "dsa_prefill_select_workspace_size": ([I32, I64, I32, I64, I32, C.POINTER(SZ)], I32),
+        "dsa_prefill_select": ([LP, P, I64, P, I64, I32, P, P, P, P, P, P, I32, I32, P, I64, P, I64, P, P, SZ, P, P],
+                               I32),
+        "dsa_prefill_score_fp8": ([LP, P, I64, P, I64, I32, P, P, P, P, P, P, I32, P, I64, P, P, SZ, P, P], I32),
+        "dsa_prefill_topk_band": ([LP, P, I64, P, I64, I32, P, P, I32, I32, P, I64, P, I64, P, SZ, P, P], I32),
         "dsa_sparse_mla_prefill_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
         "dsa_dcp_topk_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
         "dsa_dcp_topk": ([P, I64, P, I32, I32, I32, P, I64, P, P, SZ, P, P], I32),
@@ -148,7 +155,9 @@ def dsa_layout_make(page_size: int, n_layers: int, key_fmt: int, lat_fmt: int, e
 def dsa_resolve_pages(layout: dsa_layout, layer: int, block_table, n_pages, pool_rows: int, lat_off, key_off,
                       err_flag=None, stream=None):
     n_req, max_pages = block_table.shape
-    st = lib.dsa_resolve_pages(C.byref(layout), layer, _ptr(block_table, I32, "block_table"), block_table.stride(0),
+    # the row stride is the leading dimension (a one-row table may carry any stride there)
+    bt_ld = block_table.stride(0) if n_req > 1 else max_pages
+    st = lib.dsa_resolve_pages(C.byref(layout), layer, _ptr(block_table, I32, "block_table"), bt_ld,
                                _ptr(n_pages, I32, "n_pages"), n_req, max_pages, pool_rows,
                                _ptr(lat_off, I64, "lat_off"), _ptr(key_off, I64, "key_off"), lat_off.shape[1],
                                _ptr(err_flag, I32, "err_flag"), _stream(stream))
@@ -216,6 +225,53 @@ def dsa_indexer_select(layout: dsa_layout, layer: int, pool, block_table, n_req:
                                 _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
                                 _ptr(err_flag, I32, "err_flag"), _stream(stream))
     _check("dsa_indexer_select", st)
+
+
+def dsa_prefill_select_workspace_size(n_q: int, ld: int, n_req: int, off_ld: int, k: int) -> int:
+    out = C.c_size_t()
+    _check("dsa_prefill_select_workspace_size",
+           lib.dsa_prefill_select_workspace_size(n_q, ld, n_req, off_ld, k, C.byref(out)))
+    return out.value
+
+
+def dsa_prefill_select(layout: dsa_layout, pool, key_off, n_req: int, ctx_len, q, q_scale, w, q_req, row_len, k: int,
+                       scores, idx, workspace, bound=None, err_flag=None, stream=None):
+    """Prefill indexer on FP8 MFMA with its exact top-k: idx as dsa_topk on dsa_indexer_score's
+    FP8 scores; scores hold the FP8 MFMA approximations, each within bound[r] of those."""
+    st = lib.dsa_prefill_select(C.byref(layout), _ptr(pool, U8, "pool"), pool.numel(), _ptr(key_off, I64, "key_off"),
+                                key_off.shape[1], n_req, _ptr(ctx_len, I32, "ctx_len"), _ptr(q, U8, "q"),
+                                _ptr(q_scale, F32, "q_scale"), _ptr(w, F32, "w"), _ptr(q_req, I32, "q_req"),
+                                _ptr(row_len, I32, "row_len"), row_len.shape[0], k, _ptr(scores, F32, "scores"),
+                                scores.shape[1], _ptr(idx, I32, "idx"), idx.shape[1], _ptr(bound, F32, "bound"),
+                                _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+                                _ptr(err_flag, I32, "err_flag"), _stream(stream))
+    _check("dsa_prefill_select", st)
+
+
+def dsa_prefill_score_fp8(layout: dsa_layout, pool, key_off, n_req: int, ctx_len, q, q_scale, w, q_req, row_len,
+                          scores, workspace, bound=None, err_flag=None, stream=None):
+    """First half of dsa_prefill_select: FP8 MFMA scores (within bound[r] of the exact ones)."""
+    st = lib.dsa_prefill_score_fp8(C.byref(layout), _ptr(pool, U8, "pool"), pool.numel(),
+                                   _ptr(key_off, I64, "key_off"), key_off.shape[1], n_req,
+                                   _ptr(ctx_len, I32, "ctx_len"), _ptr(q, U8, "q"), _ptr(q_scale, F32, "q_scale"),
+                                   _ptr(w, F32, "w"), _ptr(q_req, I32, "q_req"), _ptr(row_len, I32, "row_len"),
+                                   row_len.shape[0], _ptr(scores, F32, "scores"), scores.shape[1],
+                                   _ptr(bound, F32, "bound"), _ptr(workspace, None, "workspace"),
+                                   workspace.numel() * workspace.element_size(), _ptr(err_flag, I32, "err_flag"),
+                                   _stream(stream))
+    _check("dsa_prefill_score_fp8", st)
+
+
+def dsa_prefill_topk_band(layout: dsa_layout, pool, key_off, n_req: int, q_req, row_len, k: int, scores, idx,
+                          workspace, err_flag=None, stream=None):
+    """Second half of dsa_prefill_select: the exact top-k from the FP8 scores (same workspace)."""
+    st = lib.dsa_prefill_topk_band(C.byref(layout), _ptr(pool, U8, "pool"), pool.numel(),
+                                   _ptr(key_off, I64, "key_off"), key_off.shape[1], n_req,
+                                   _ptr(q_req, I32, "q_req"), _ptr(row_len, I32, "row_len"), row_len.shape[0], k,
+                                   _ptr(scores, F32, "scores"), scores.shape[1], _ptr(idx, I32, "idx"), idx.shape[1],
+                                   _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+                                   _ptr(err_flag, I32, "err_flag"), _stream(stream))
+    _check("dsa_prefill_topk_band", st)
 
 
 def dsa_indexer_score_pages(layout: dsa_layout, layer: int, pool, block_table, n_req: int, q, w, q_req, row_len,
@@ -330,4 +386,4 @@ def dsa_dcp_topk(scores, row_len, k: int, n_shards: int, idx, workspace, resend_
     _check("dsa_dcp_topk", st)
 
 
-from .step import DecodeStep, FusedDecodeStep, PrefillStep, VerifyStep  # noqa: E402,F401
+from .step import DecodeStep, FusedDecodeStep, PrefillSelectStep, PrefillStep, VerifyStep  # noqa: E402,F401

@@ -21,7 +21,7 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 OUT = PKG / "_build"
 LIB = OUT / "libdsa.so"
-SOURCES = ["abi.cpp", "resolve.hip", "indexer_scan.hip", "indexer_verify.hip", "indexer_gemm.hip", "topk.hip", "mla.hip", "dcp.hip"]
+SOURCES = ["abi.cpp", "resolve.hip", "indexer_scan.hip", "indexer_verify.hip", "indexer_gemm.hip", "indexer_gemm_fp8.hip", "topk.hip", "mla.hip", "dcp.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", str(ROOT / "include")]

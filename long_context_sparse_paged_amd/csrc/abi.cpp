@@ -37,6 +37,33 @@ dsa_status check_layout(const dsa_layout *L) {
 
 dsa_status launched(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
 
+// Workspace of dsa_prefill_select: 256-B aligned parts, in this order.
+struct PrefillCarve {
+  int64_t qb, qc, sw, urow, bound, mpage, mreq, topk, cnt, list, pos, total;
+};
+PrefillCarve prefill_carve(int32_t n_q, int64_t ld, int32_t n_req, int64_t off_ld) {
+  PrefillCarve c{};
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t at = o;
+    o += round_up_256(bytes);
+    return at;
+  };
+  c.qb = take((int64_t)n_q * kIdxHeads * kIdxDim * 2);
+  c.qc = take((int64_t)n_q * kIdxHeads * kIdxDim);
+  c.sw = take((int64_t)((n_q + 31) / 32) * kIdxHeads * 32 * 4);
+  c.urow = take((int64_t)n_q * 16 * 4);
+  c.bound = take((int64_t)n_q * 4);
+  c.mpage = take((int64_t)n_req * off_ld * 16 * 4);
+  c.mreq = take((int64_t)n_req * 16 * 4);
+  c.topk = take((int64_t)topk_workspace_bytes(n_q, ld));
+  c.cnt = take((int64_t)n_q * 8);
+  c.list = take((int64_t)n_q * kBandListCap * 8);
+  c.pos = take((int64_t)n_q * kBandCap * 4);
+  c.total = o;
+  return c;
+}
+
 hipStream_t stream_of(dsa_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace
@@ -196,6 +223,190 @@ dsa_status dsa_indexer_score_workspace_size(int32_t n_q, int32_t q_fmt, size_t *
   if (q_fmt != DSA_Q_BF16 && q_fmt != DSA_Q_FP8_E4M3 && q_fmt != DSA_Q_MXFP4) return DSA_ERR_UNSUPPORTED;
   *bytes = q_fmt == DSA_Q_FP8_E4M3 ? indexer_gemm_workspace_bytes(n_q) : 0;
   return DSA_OK;
+}
+
+dsa_status dsa_prefill_select_workspace_size(int32_t n_q, int64_t ld, int32_t n_req, int64_t off_ld, int32_t k,
+                                             size_t *bytes) {
+  if (!bytes) return DSA_ERR_NULL_ARG;
+  if (n_q < 0 || ld < 0 || n_req < 0 || off_ld < 1 || k < 1) return DSA_ERR_BAD_SHAPE;
+  if (k > kMaxTopK || ld > (int64_t)1024 * kSlice) return DSA_ERR_UNSUPPORTED;
+  *bytes = (size_t)prefill_carve(n_q, ld, n_req, off_ld).total;
+  return DSA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the prefill-select calls; on success *c is the workspace carve.
+dsa_status prefill_common(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes, const int64_t *key_off,
+                          int64_t off_ld, int32_t n_req, const int32_t *q_req, const int32_t *row_len, int32_t n_q,
+                          int32_t k, const float *scores, int64_t ld, void *workspace, size_t workspace_bytes,
+                          const int32_t *err_flag, PrefillCarve *c) {
+  dsa_status st = check_layout(layout);
+  if (st != DSA_OK) return st;
+  size_t need;
+  st = dsa_prefill_select_workspace_size(n_q, ld, n_req, off_ld, k, &need);
+  if (st != DSA_OK) return st;
+  if (pool_bytes < 0) return DSA_ERR_BAD_SHAPE;
+  if (layout->key_fmt != DSA_KEY_FP8_E4M3_SCALED) return DSA_ERR_UNSUPPORTED;
+  if (n_q == 0) return DSA_OK;
+  if (n_q > kMaxGridY || n_req > kMaxGridY) return DSA_ERR_UNSUPPORTED;
+  if ((int64_t)32 * ld * 4 > 0x7FFFFFFF) return DSA_ERR_UNSUPPORTED;  // the GEMM's 32-bit store offsets
+  if (!pool || !key_off || !q_req || !row_len || !scores || !workspace) return DSA_ERR_NULL_ARG;
+  if (!aligned(pool, 16) || !aligned(key_off, 8) || !aligned(q_req, 4) || !aligned(row_len, 4) ||
+      !aligned(scores, 16) || !aligned(workspace, 256) || !aligned(err_flag, 4))
+    return DSA_ERR_MISALIGNED;
+  if (workspace_bytes < need) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  *c = prefill_carve(n_q, ld, n_req, off_ld);
+  return DSA_OK;
+}
+
+PrefillWs prefill_ws(void *workspace, const PrefillCarve &c) {
+  uint8_t *base = static_cast<uint8_t *>(workspace);
+  PrefillWs pw{};
+  pw.qb = reinterpret_cast<uint16_t *>(base + c.qb);
+  pw.qc = base + c.qc;
+  pw.sw = reinterpret_cast<float *>(base + c.sw);
+  pw.urow = reinterpret_cast<float *>(base + c.urow);
+  pw.bound = reinterpret_cast<float *>(base + c.bound);
+  pw.mpage = reinterpret_cast<float *>(base + c.mpage);
+  pw.mreq = reinterpret_cast<float *>(base + c.mreq);
+  return pw;
+}
+
+hipError_t prefill_score(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes, const int64_t *key_off,
+                         int64_t off_ld, int32_t n_req, const int32_t *ctx_len, const uint8_t *q, const float *q_scale,
+                         const float *w, const int32_t *q_req, const int32_t *row_len, int32_t n_q, float *scores,
+                         int64_t ld, float *bound, void *workspace, const PrefillCarve &c, int32_t *err_flag,
+                         hipStream_t hs) {
+  ScoreArgs a{};
+  a.pool = pool;
+  a.pool_bytes = pool_bytes;
+  a.key_off = key_off;
+  a.off_ld = off_ld;
+  a.n_req = n_req;
+  a.q = q;
+  a.q_scale = q_scale;
+  a.w = w;
+  a.q_req = q_req;
+  a.row_len = row_len;
+  a.n_q = n_q;
+  a.scores = scores;
+  a.ld = ld;
+  a.err = err_flag;
+  a.key_fmt = layout->key_fmt;
+  a.q_fmt = DSA_Q_FP8_E4M3;
+  PrefillWs pw = prefill_ws(workspace, c);
+  pw.bound_out = bound;
+  const int64_t pages_ld = (ld + kPage - 1) / kPage;  // pages a row of ld tokens spans (<= 131072)
+  const int32_t max_pages = (int32_t)(off_ld < pages_ld ? off_ld : pages_ld);
+  return launch_indexer_gemm_fp8(a, pw, ctx_len, max_pages, hs);
+}
+
+hipError_t prefill_topk(const uint8_t *pool, int64_t pool_bytes, const int64_t *key_off, int64_t off_ld, int32_t n_req,
+                        const int32_t *q_req, const int32_t *row_len, int32_t n_q, int32_t k, float *scores,
+                        int64_t ld, int32_t *idx, int64_t idx_ld, void *workspace, const PrefillCarve &c,
+                        int32_t *err_flag, hipStream_t hs) {
+  uint8_t *base = static_cast<uint8_t *>(workspace);
+  const PrefillWs pw = prefill_ws(workspace, c);
+  BandWs band{};
+  band.e = pw.bound;
+  band.cnt = reinterpret_cast<int32_t *>(base + c.cnt);
+  band.list = reinterpret_cast<uint2 *>(base + c.list);
+  band.pos = reinterpret_cast<int32_t *>(base + c.pos);
+  TopkArgs t{};
+  t.scores = scores;
+  t.ld = ld;
+  t.row_len = row_len;
+  t.n_rows = n_q;
+  t.k = k;
+  t.idx = idx;
+  t.idx_ld = idx_ld;
+  t.ws = base + c.topk;
+  t.err = err_flag;
+  t.band = band;
+  hipError_t e = launch_topk(t, hs);
+  if (e != hipSuccess) return e;
+  RescoreArgs rs{};
+  rs.pool = pool;
+  rs.pool_bytes = pool_bytes;
+  rs.key_off = key_off;
+  rs.off_ld = off_ld;
+  rs.n_req = n_req;
+  rs.q_req = q_req;
+  rs.row_len = row_len;
+  rs.n_q = n_q;
+  rs.qb = pw.qb;
+  rs.sw = pw.sw;
+  rs.band = band;
+  rs.scores = scores;
+  rs.ld = ld;
+  rs.err = err_flag;
+  e = launch_band_rescore(rs, hs);
+  if (e != hipSuccess) return e;
+  return launch_topk_band_select(t, hs);
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_prefill_score_fp8(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                                 const int64_t *key_off, int64_t off_ld, int32_t n_req, const int32_t *ctx_len,
+                                 const uint8_t *q, const float *q_scale, const float *w, const int32_t *q_req,
+                                 const int32_t *row_len, int32_t n_q, float *scores, int64_t ld, float *bound,
+                                 void *workspace, size_t workspace_bytes, int32_t *err_flag, dsa_stream_t stream) {
+  PrefillCarve c{};
+  const dsa_status st = prefill_common(layout, pool, pool_bytes, key_off, off_ld, n_req, q_req, row_len, n_q, 1,
+                                       scores, ld, workspace, workspace_bytes, err_flag, &c);
+  if (st != DSA_OK || n_q == 0) return st;
+  if (!ctx_len || !q || !q_scale || !w) return DSA_ERR_NULL_ARG;
+  if (!aligned(q, 16) || !aligned(ctx_len, 4) || !aligned(q_scale, 4) || !aligned(w, 4) || !aligned(bound, 4))
+    return DSA_ERR_MISALIGNED;
+  return launched(prefill_score(layout, pool, pool_bytes, key_off, off_ld, n_req, ctx_len, q, q_scale, w, q_req,
+                                row_len, n_q, scores, ld, bound, workspace, c, err_flag, stream_of(stream)));
+}
+
+dsa_status dsa_prefill_topk_band(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                                 const int64_t *key_off, int64_t off_ld, int32_t n_req, const int32_t *q_req,
+                                 const int32_t *row_len, int32_t n_q, int32_t k, float *scores, int64_t ld,
+                                 int32_t *idx, int64_t idx_ld, void *workspace, size_t workspace_bytes,
+                                 int32_t *err_flag, dsa_stream_t stream) {
+  PrefillCarve c{};
+  const dsa_status st = prefill_common(layout, pool, pool_bytes, key_off, off_ld, n_req, q_req, row_len, n_q, k,
+                                       scores, ld, workspace, workspace_bytes, err_flag, &c);
+  if (st != DSA_OK) return st;
+  if (idx_ld < k) return DSA_ERR_BAD_SHAPE;
+  if (n_q == 0) return DSA_OK;
+  if (!idx) return DSA_ERR_NULL_ARG;
+  if (!aligned(idx, 4)) return DSA_ERR_MISALIGNED;
+  return launched(prefill_topk(pool, pool_bytes, key_off, off_ld, n_req, q_req, row_len, n_q, k, scores, ld, idx,
+                               idx_ld, workspace, c, err_flag, stream_of(stream)));
+}
+
+dsa_status dsa_prefill_select(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                              const int64_t *key_off, int64_t off_ld, int32_t n_req, const int32_t *ctx_len,
+                              const uint8_t *q, const float *q_scale, const float *w, const int32_t *q_req,
+                              const int32_t *row_len, int32_t n_q, int32_t k, float *scores, int64_t ld,
+                              int32_t *idx, int64_t idx_ld, float *bound, void *workspace, size_t workspace_bytes,
+                              int32_t *err_flag, dsa_stream_t stream) {
+  PrefillCarve c{};
+  const dsa_status st = prefill_common(layout, pool, pool_bytes, key_off, off_ld, n_req, q_req, row_len, n_q, k,
+                                       scores, ld, workspace, workspace_bytes, err_flag, &c);
+  if (st != DSA_OK) return st;
+  if (idx_ld < k) return DSA_ERR_BAD_SHAPE;
+  if (n_q == 0) return DSA_OK;
+  if (!ctx_len || !q || !q_scale || !w || !idx) return DSA_ERR_NULL_ARG;
+  if (!aligned(q, 16) || !aligned(ctx_len, 4) || !aligned(q_scale, 4) || !aligned(w, 4) || !aligned(bound, 4) ||
+      !aligned(idx, 4))
+    return DSA_ERR_MISALIGNED;
+  const hipStream_t hs = stream_of(stream);
+  if (prefill_score(layout, pool, pool_bytes, key_off, off_ld, n_req, ctx_len, q, q_scale, w, q_req, row_len, n_q,
+                    scores, ld, bound, workspace, c, err_flag, hs) != hipSuccess)
+    return DSA_ERR_HIP;
+  return launched(prefill_topk(pool, pool_bytes, key_off, off_ld, n_req, q_req, row_len, n_q, k, scores, ld, idx,
+                               idx_ld, workspace, c, err_flag, hs));
 }
 
 dsa_status dsa_topk_workspace_size(int32_t n_rows, int64_t ld, int32_t k, size_t *bytes) {

@@ -304,7 +304,103 @@ __global__ __launch_bounds__(256, 2) void indexer_gemm_kernel(const ScoreArgs a,
   if (first) __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+// ---- exact rescoring of the band tokens of the FP8 prefill path ----
+// The score of (row r, token t) exactly as indexer_gemm_kernel computes it: the same bf16
+// operands, the same MFMA chain over the same K order (lane (column n, half h) at K-step s holds
+// dims [64h + 8s, 64h + 8s + 8)), and the same fp32 epilogue, sequential over heads 0..31.  Here
+// the MFMA's 32 rows are the 32 heads of row r and its 32 columns are 32 listed tokens; an
+// element of the product depends only on its own row and column, so every x_j is the GEMM's
+// bit for bit.  One wave per workgroup; grid (n_q, kRescoreY), tiles of 32 band tokens strided
+// over y (every token of the row when the band overflowed).
+constexpr int kRescoreY = 4;
+
+__global__ __launch_bounds__(64) void band_rescore_kernel(const RescoreArgs a) {
+  const int r = blockIdx.x, lane = threadIdx.x, n = lane & 31, h = lane >> 5;
+  const int nl = a.band.cnt[2 * r], nb = a.band.cnt[2 * r + 1];
+  if (nl < 0) return;  // the whole row was kept
+  const int b = a.q_req[r];
+  if (b < 0 || b >= a.n_req) return;  // flagged by the GEMM
+  const int64_t max_tok = a.ld < a.off_ld * kPage ? a.ld : a.off_ld * kPage;
+  const int len = (int)min((int64_t)max(a.row_len[r], 0), max_tok);
+  const bool full = nb > kBandCap;
+  const int ntok = full ? len : nb;
+  const int tiles = (ntok + 31) / 32;
+  if ((int)blockIdx.y >= tiles) return;
+
+  // the row's 32 heads as the A operand: lane (head n, half h)
+  const uint16_t *qrow = a.qb + (int64_t)r * kQbRow + n * kIdxDim + 64 * h;
+  bf16x8_t af[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) af[s] = *reinterpret_cast<const bf16x8_t *>(qrow + 8 * s);
+  const float *swr = a.sw + (int64_t)(r / kGRows) * kIdxHeads * kGRows + r % kGRows;  // s_j at swr[32 j]
+  uint2 *list = a.band.list + (int64_t)r * kBandListCap;
+  const int32_t *bpos = a.band.pos + (int64_t)r * kBandCap;
+  const int64_t *koff = a.key_off + (int64_t)b * a.off_ld;
+
+  for (int q = blockIdx.y; q < tiles; q += gridDim.y) {
+    // column n: token t (list position p in band mode)
+    const int bi = 32 * q + n;
+    int t = 0, p = 0;
+    bool valid = bi < ntok;
+    if (valid) {
+      if (full) {
+        t = bi;
+      } else {
+        p = bpos[bi];
+        valid = p >= 0 && p < min(nl, kBandListCap);
+        t = valid ? (int)list[p].y : 0;
+      }
+    }
+    valid = valid && t >= 0 && t < len;
+    const int64_t off = valid ? koff[t >> 6] : -1;
+    valid = valid && off >= 0 && off + kKPB <= a.pool_bytes && (off & 15) == 0;
+    bf16x8_t bfr[8];
+    float ks = 0.0f;
+    if (valid) {
+      const uint8_t *kr = a.pool + off + (t & (kPage - 1)) * kKB;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        bfr[s] = e4m3x8_bf16(*reinterpret_cast<const uint32_t *>(kr + 64 * h + 8 * s),
+                             *reinterpret_cast<const uint32_t *>(kr + 64 * h + 8 * s + 4));
+      ks = *reinterpret_cast<const float *>(kr + 128);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) bfr[s] = bf16x8_t{};
+    }
+    f32x16_t x = f32x16_t{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) x = mfma_32x32x16_bf16(af[s], bfr[s], x);
+    // element i of lane (n, h) is head 8 (i / 4) + 4h + i % 4: lanes n < 32 take the other half's
+    float xo[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[i]), __float_as_uint(x[i]), false, false);
+      xo[i] = __uint_as_float(sw2[1]);
+    }
+    if (h == 0 && valid) {
+      const float lo = ks < 0.0f ? -INFINITY : 0.0f, hi = ks < 0.0f ? 0.0f : INFINITY;
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kIdxHeads; ++j) {
+        const int i = 4 * (j >> 3) + (j & 3);
+        const float xj = (j & 4) ? xo[i] : x[i];
+        acc = fmaf(swr[kGRows * j], __builtin_amdgcn_fmed3f(xj, lo, hi), acc);
+      }
+      const float sc = ks * acc;
+      if (full) a.scores[(int64_t)r * a.ld + t] = sc;
+      else list[p].x = score_key(sc);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_band_rescore(const RescoreArgs &a, hipStream_t s) {
+  if (a.n_q == 0) return hipSuccess;
+  if (a.band.e == nullptr) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(band_rescore_kernel, dim3(a.n_q, kRescoreY), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
 
 size_t indexer_gemm_workspace_bytes(int32_t n_q) {
   if (n_q <= 0) return 0;

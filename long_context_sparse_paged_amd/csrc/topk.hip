@@ -96,6 +96,33 @@ __device__ __forceinline__ int row_len_of(const TopkArgs &a, int r) {
   return len;
 }
 
+// Band mode helpers.  key_score inverts score_key; key_floor / key_ceil give the key of the
+// largest float <= v / smallest float >= v, so thresholds computed in fp64 round outward.
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+__device__ __forceinline__ uint32_t key_floor(double v) {
+  float f = (float)v;
+  if ((double)f > v) f = nextafterf(f, -INFINITY);
+  return score_key(f);
+}
+__device__ __forceinline__ uint32_t key_ceil(double v) {
+  float f = (float)v;
+  if ((double)f < v) f = nextafterf(f, INFINITY);
+  return score_key(f);
+}
+// E_r, or +inf when it is not a finite non-negative number (then every token is in the band)
+__device__ __forceinline__ double band_bound(const TopkArgs &a, int r) {
+  const float e = a.band.e[r];
+  return e >= 0.0f && e <= 3.402823466e38f ? (double)e : (double)INFINITY;
+}
+// In band mode the candidate threshold is lowered by 2 E_r, so the candidates hold every
+// token within 2 E_r below the k-th largest score whenever they hold the k largest.
+__device__ __forceinline__ uint32_t band_est(const TopkArgs &a, int r, uint32_t est) {
+  if (a.band.e == nullptr || est == 0u) return est;
+  return key_floor((double)key_score(est) - 2.0 * band_bound(a, r));
+}
+
 // Sample rank of the threshold: with x = k S / len sample elements expected above the
 // row's k-th score, m = 1.25 x + 6 sqrt(x) + 8 puts the k-th score below est only if a
 // Poisson(x) count exceeds its mean by > 6 standard deviations.
@@ -313,7 +340,7 @@ __global__ __launch_bounds__(256) void topk_sample_kernel(const TopkArgs a, Topk
         },
         m, lo, hi, kEstPasses, R, gt);
   }
-  if (threadIdx.x == 0) w.est[r] = est;
+  if (threadIdx.x == 0) w.est[r] = band_est(a, r, est);
 }
 
 // Slice element (chunk j, lane quad e) of thread t is beg + 1024 j + 4 t + e.
@@ -404,6 +431,7 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(const TopkArgs a, Top
           },
           m, lo, hi, kEstPasses, R, gt);
     }
+    est = band_est(a, r, est);
     if (s == 0 && tid == 0) w.est[r] = est;
   } else {
     est = w.est[r];
@@ -559,6 +587,7 @@ __device__ __forceinline__ void select_write_any(uint32_t *s_key, const int32_t 
   else select_write<kFinPer>(s_key, s_idx, n, per, keff, R, pre, emit, list_cap);
 }
 
+template <bool BAND>
 __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkArgs a, TopkWs w, int n_slices) {
   constexpr int NT = kFinThreads;
   constexpr int kBatch = 12;  // row-score loads in flight per thread (short rows)
@@ -622,6 +651,10 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
   auto emit = [&](int pos, int32_t i) { emit3(pos, i, pout ? block_of(i) : -1); };
 
   if (keff >= len) {  // keep everything (also len == 0)
+    if (BAND && tid == 0) {
+      a.band.cnt[2 * r] = -1;
+      a.band.cnt[2 * r + 1] = 0;
+    }
     for (int i = tid; i < a.k; i += NT) {
       if (i < len) {
         emit(i, i);
@@ -766,7 +799,62 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
     }
   }
   __syncthreads();
-  if (ok) {
+  if constexpr (BAND) {
+    // (1) T^: the keff-th largest key, among the candidates (which hold the keff largest when
+    // ok) or over the whole row
+    const int N = ok ? n : len;
+    auto key_at = [&](int i) { return ok ? s_key[i] : score_key(row[i]); };
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for (int i = tid; i < N; i += NT) {
+      const uint32_t k = key_at(i);
+      lo = min(lo, k);
+      hi = max(hi, k);
+    }
+    block_minmax<NT>(lo, hi, R);
+    int gt;
+    const uint32_t tau = radix_select<NT>(
+        [&](auto f) {
+          for (int i = tid; i < N; i += NT) f(key_at(i));
+        },
+        keff, lo, hi, 32, R, gt, ok ? nullptr : s_key, ok ? 0 : kShortRow);
+    // (2) the band [T^ - 2E, T^ + 2E] as keys, rounded outward
+    const double tv = (double)key_score(tau), e2 = 2.0 * band_bound(a, r);
+    const uint32_t lo_key = key_floor(tv - e2), hi_key = key_ceil(tv + e2);
+    // the candidates are the tokens with key >= est: enough unless the band reaches below it
+    const bool from_cand = ok && (len <= kShortRow || lo_key >= w.est[r]);
+    // (3) ordered compaction of the surely kept tokens (key > hi_key, listed with key all ones)
+    // and the band tokens (listed with key 0 until rescored; their list positions go to pos)
+    const int M = from_cand ? n : len;
+    uint2 *list = a.band.list + (int64_t)r * kBandListCap;
+    int32_t *bpos = a.band.pos + (int64_t)r * kBandCap;
+    int written = 0, bw = 0;
+    for (int c0 = 0; c0 < M; c0 += NT) {
+      const int i = c0 + tid;
+      uint32_t key = 0u;
+      int32_t t = i;
+      if (i < M) {
+        if (from_cand) {
+          key = s_key[i];
+          t = s_idx[i];
+        } else {
+          key = score_key(row[i]);
+        }
+      }
+      const bool sure = i < M && key > hi_key;
+      const bool band = i < M && !sure && key >= lo_key;
+      int tot, btot;
+      const int pos = written + block_rank<NT>(sure || band, R.tmp, tot);
+      const int bp = bw + block_rank<NT>(band, R.tmp, btot);
+      if ((sure || band) && pos < kBandListCap) list[pos] = make_uint2(sure ? 0xFFFFFFFFu : 0u, (uint32_t)t);
+      if (band && bp < kBandCap && pos < kBandListCap) bpos[bp] = pos;
+      written += tot;
+      bw += btot;
+    }
+    if (tid == 0) {
+      a.band.cnt[2 * r] = written;
+      a.band.cnt[2 * r + 1] = bw;
+    }
+  } else if (ok) {
     // thread t takes candidates [t per, t per + cnt) into registers (per is odd, so the
     // strided LDS reads of a wave hit distinct banks); the loops are unrolled for a bound
     // on per picked from a few sizes
@@ -790,10 +878,61 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
         keff, lo, hi, 32, R, gt, s_key, kShortRow);
     compact_rounds(load, len, tau, keff - gt, emit, R.tmp);
   }
+  if (BAND) return;  // the second pass writes the row
   for (int i = keff + tid; i < a.k; i += NT) {
     out[i] = -1;
     if (pout) pout[i] = -1;
   }
+}
+
+// Band mode, second pass (one workgroup per row): the kept tokens from the first pass's list,
+// whose band keys are now exact, or -- for a row whose band overflowed and was rescored in
+// place -- from the whole score row.
+__global__ __launch_bounds__(kFinThreads) void topk_band_select_kernel(const TopkArgs a) {
+  constexpr int NT = kFinThreads;
+  __shared__ uint32_t s_key[kShortRow];
+  __shared__ int32_t s_idx[kShortRow];
+  __shared__ RadixLds<NT> R;
+  const int tid = threadIdx.x, r = blockIdx.x;
+  const int len = row_len_of(a, r);
+  const int keff = min(a.k, len);
+  const int nl = a.band.cnt[2 * r], nb = a.band.cnt[2 * r + 1];
+  if (nl < 0) return;  // the first pass kept the whole row
+  int32_t *out = a.idx + (int64_t)r * a.idx_ld;
+  auto emit = [&](int pos, int32_t i) { out[pos] = i; };
+  if (nb <= kBandCap && nl >= keff && nl <= kBandListCap) {
+    const uint2 *list = a.band.list + (int64_t)r * kBandListCap;
+    for (int i = tid; i < nl; i += NT) {
+      const uint2 e = list[i];
+      s_key[i] = e.x;
+      s_idx[i] = (int32_t)e.y;
+    }
+    __syncthreads();
+    const int per = ((nl + NT - 1) / NT) | 1;
+    select_write_any(
+        s_key, s_idx, nl, per, keff, R, [](int32_t) { return 0; }, [&](int pos, int32_t i, int32_t) { emit(pos, i); });
+  } else {
+    // the whole row (rescored exactly when the band overflowed; a list shorter than keff
+    // means a score fell outside its bound, and the approximate row is used)
+    if (nb <= kBandCap && tid == 0) flag_error(a.err, DSA_DEVERR_BOUND);
+    const float *row = a.scores + (int64_t)r * a.ld;
+    auto load = [&](int i) { return score_key(row[i]); };
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for (int i = tid; i < len; i += NT) {
+      const uint32_t k = load(i);
+      lo = min(lo, k);
+      hi = max(hi, k);
+    }
+    block_minmax<NT>(lo, hi, R);
+    int gt;
+    const uint32_t tau = radix_select<NT>(
+        [&](auto f) {
+          for (int i = tid; i < len; i += NT) f(load(i));
+        },
+        keff, lo, hi, 32, R, gt, s_key, kShortRow);
+    compact_rounds(load, len, tau, keff - gt, emit, R.tmp);
+  }
+  for (int i = keff + tid; i < a.k; i += NT) out[i] = -1;
 }
 
 }  // namespace
@@ -818,7 +957,17 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
       hipLaunchKernelGGL(topk_collect_kernel<false>, dim3(n_slices, a.n_rows), dim3(256), 0, s, a, w, n_slices);
     }
   }
-  hipLaunchKernelGGL(topk_finalize_kernel, dim3(a.n_rows), dim3(kFinThreads), 0, s, a, w, n_slices);
+  if (a.band.e != nullptr)
+    hipLaunchKernelGGL(topk_finalize_kernel<true>, dim3(a.n_rows), dim3(kFinThreads), 0, s, a, w, n_slices);
+  else
+    hipLaunchKernelGGL(topk_finalize_kernel<false>, dim3(a.n_rows), dim3(kFinThreads), 0, s, a, w, n_slices);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_band_select(const TopkArgs &a, hipStream_t s) {
+  if (a.n_rows == 0) return hipSuccess;
+  if (a.band.e == nullptr || a.n_rows > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_band_select_kernel, dim3(a.n_rows), dim3(kFinThreads), 0, s, a);
   return hipGetLastError();
 }
 

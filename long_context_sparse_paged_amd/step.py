@@ -3,7 +3,8 @@
 ``DecodeStep`` / ``PrefillStep`` own the device buffers a step needs (page
 offsets, scores, selected indices, outputs, workspaces) and call
 dsa_resolve_pages -> dsa_indexer_score -> dsa_topk -> dsa_sparse_mla_* on one
-stream; ``VerifyStep`` does the same for speculative verification, with
+stream; ``PrefillSelectStep`` scores and selects a prefill chunk in one call,
+dsa_prefill_select (FP8 MFMA, exact top-k); ``VerifyStep`` does the same for speculative verification, with
 dsa_indexer_score_verify reading each key page once for all rows of a request.
 ``FusedDecodeStep`` is the fused decode path: dsa_indexer_select (scores with
 pages found through the block table, exact top-k and physical rows) ->
@@ -16,9 +17,11 @@ import torch
 
 from . import (DSA_Q_BF16, DSA_Q_FP8_E4M3, dsa_indexer_score, dsa_indexer_score_pages, dsa_indexer_score_verify,
                dsa_indexer_score_workspace_size, dsa_indexer_select, dsa_indexer_select_workspace_size,
-               dsa_layout_make, dsa_resolve_pages, dsa_sparse_mla_decode, dsa_sparse_mla_decode_phys,
-               dsa_sparse_mla_decode_workspace_size, dsa_sparse_mla_prefill, dsa_sparse_mla_prefill_workspace_size,
-               dsa_topk, dsa_topk_pages, dsa_topk_workspace_size)
+               dsa_layout_make, dsa_prefill_score_fp8, dsa_prefill_select, dsa_prefill_select_workspace_size,
+               dsa_prefill_topk_band, dsa_resolve_pages,
+               dsa_sparse_mla_decode, dsa_sparse_mla_decode_phys, dsa_sparse_mla_decode_workspace_size,
+               dsa_sparse_mla_prefill, dsa_sparse_mla_prefill_workspace_size, dsa_topk, dsa_topk_pages,
+               dsa_topk_workspace_size)
 
 
 def _layout_of(cache):
@@ -220,5 +223,42 @@ class FusedDecodeStep:
                                    c.kv_scale, self.out, self.lse, self.ws_mla, self.err, stream)
 
     def run(self, stream=None):
+        self.select(stream)
+        self.attend(stream)
+
+
+class PrefillSelectStep(PrefillStep):
+    """Prefill chunk with the indexer on FP8 MFMA: dsa_resolve_pages -> dsa_prefill_select
+    (approximate scores, exact top-k) -> dsa_sparse_mla_prefill.  FP8 queries only."""
+
+    def __init__(self, cache, pq, k: int = 2048, device="cuda"):
+        super().__init__(cache, pq, k=k, q_fmt=DSA_Q_FP8_E4M3, device=device)
+        self.ws_score = None
+        self.ws_topk = None
+        n_req, max_pages = cache.block_table.shape
+        nb = dsa_prefill_select_workspace_size(pq.n_q, self.scores.shape[1], n_req, max_pages, k)
+        self.ws_select = torch.empty(nb, dtype=torch.uint8, device=device)
+        self.bound = torch.empty(pq.n_q, dtype=torch.float32, device=device)
+
+    def select(self, stream=None):
+        c, pq = self.cache, self.pq
+        dsa_prefill_select(self.layout, c.pool, self.key_off, c.n_req, c.ctx_len, pq.q_idx_fp8, pq.q_idx_scale, pq.w,
+                           pq.q_req, pq.row_len, self.k, self.scores, self.idx, self.ws_select, self.bound, self.err,
+                           stream)
+
+    def score(self, stream=None):
+        """First half of select(): the FP8 MFMA scores and their bound."""
+        c, pq = self.cache, self.pq
+        dsa_prefill_score_fp8(self.layout, c.pool, self.key_off, c.n_req, c.ctx_len, pq.q_idx_fp8, pq.q_idx_scale,
+                              pq.w, pq.q_req, pq.row_len, self.scores, self.ws_select, self.bound, self.err, stream)
+
+    def topk(self, stream=None):
+        """Second half of select(): the exact top-k (band rescored)."""
+        c, pq = self.cache, self.pq
+        dsa_prefill_topk_band(self.layout, c.pool, self.key_off, c.n_req, pq.q_req, pq.row_len, self.k, self.scores,
+                              self.idx, self.ws_select, self.err, stream)
+
+    def run(self, stream=None):
+        self.resolve(stream)
         self.select(stream)
         self.attend(stream)

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(d):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 25
     for n in names:
         assert hasattr(d.lib, n), n
 
@@ -63,6 +63,69 @@ def test_layout_make_errors(d):
 
 FAKE = C.c_void_p(1 << 20)      # aligned, never dereferenced: every call below fails validation first
 ODD = C.c_void_p((1 << 20) + 2)
+
+
+def test_prefill_select_errors(d):
+    L = d.dsa_layout_make(64, 1, 0, 0, 0)
+    f = d.lib.dsa_prefill_select
+    n_q, ld, n_req, off_ld, k = 40, 5000, 2, 80, 2048
+    need = d.dsa_prefill_select_workspace_size(n_q, ld, n_req, off_ld, k)
+    # bf16 + e4m3 query rows, the band lists and the top-k's own workspace
+    assert need >= n_q * 32 * 128 * 3 + n_q * (8192 * 8 + 4096 * 4) + d.dsa_topk_workspace_size(n_q, ld, k)
+    args = [C.byref(L), FAKE, 1 << 30, FAKE, off_ld, n_req, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n_q, k, FAKE, ld,
+            FAKE, k, None, FAKE, need, None, None]
+    a = list(args); a[1] = None
+    assert f(*a) == d.DSA_ERR_NULL_ARG
+    a = list(args); a[6] = None     # ctx_len
+    assert f(*a) == d.DSA_ERR_NULL_ARG
+    a = list(args); a[8] = None     # q_scale
+    assert f(*a) == d.DSA_ERR_NULL_ARG
+    a = list(args); a[19] = None    # workspace
+    assert f(*a) == d.DSA_ERR_NULL_ARG
+    a = list(args); a[20] = need - 1
+    assert f(*a) == d.DSA_ERR_WORKSPACE_TOO_SMALL
+    a = list(args); a[19] = C.c_void_p(FAKE.value + 16)
+    assert f(*a) == d.DSA_ERR_MISALIGNED
+    a = list(args); a[14] = C.c_void_p(FAKE.value + 4)   # scores: 16-B aligned
+    assert f(*a) == d.DSA_ERR_MISALIGNED
+    a = list(args); a[17] = k - 1   # idx_ld < k
+    assert f(*a) == d.DSA_ERR_BAD_SHAPE
+    a = list(args); a[13] = 0
+    assert f(*a) == d.DSA_ERR_BAD_SHAPE
+    a = list(args); a[13] = 4097; a[17] = 4097
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED
+    Lm = d.dsa_layout_make(64, 1, 1, 1, 0)
+    a = list(args); a[0] = C.byref(Lm)   # FP8 keys only
+    assert f(*a) == d.DSA_ERR_UNSUPPORTED
+    a = list(args); a[12] = 0
+    assert f(*a) == d.DSA_OK
+    # the halves: the same checks
+    h = d.lib.dsa_prefill_score_fp8
+    hargs = [C.byref(L), FAKE, 1 << 30, FAKE, off_ld, n_req, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n_q, FAKE, ld, None,
+             FAKE, need, None, None]
+    a = list(hargs); a[6] = None
+    assert h(*a) == d.DSA_ERR_NULL_ARG
+    a = list(hargs); a[17] = need - 1
+    assert h(*a) == d.DSA_ERR_WORKSPACE_TOO_SMALL
+    a = list(hargs); a[0] = C.byref(Lm)
+    assert h(*a) == d.DSA_ERR_UNSUPPORTED
+    t = d.lib.dsa_prefill_topk_band
+    targs = [C.byref(L), FAKE, 1 << 30, FAKE, off_ld, n_req, FAKE, FAKE, n_q, k, FAKE, ld, FAKE, k, FAKE, need, None,
+             None]
+    a = list(targs); a[12] = None
+    assert t(*a) == d.DSA_ERR_NULL_ARG
+    a = list(targs); a[13] = k - 1
+    assert t(*a) == d.DSA_ERR_BAD_SHAPE
+    a = list(targs); a[14] = C.c_void_p(FAKE.value + 16)
+    assert t(*a) == d.DSA_ERR_MISALIGNED
+    a = list(targs); a[8] = 0
+    assert t(*a) == d.DSA_OK
+    out = C.c_size_t()
+    g = d.lib.dsa_prefill_select_workspace_size
+    assert g(-1, ld, n_req, off_ld, k, C.byref(out)) == d.DSA_ERR_BAD_SHAPE
+    assert g(n_q, ld, n_req, 0, k, C.byref(out)) == d.DSA_ERR_BAD_SHAPE
+    assert g(n_q, 1 << 24, n_req, off_ld, k, C.byref(out)) == d.DSA_ERR_UNSUPPORTED
+    assert g(n_q, ld, n_req, off_ld, k, None) == d.DSA_ERR_NULL_ARG
 
 
 def test_resolve_errors(d):
