@@ -39,7 +39,7 @@ dsa_status launched(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HI
 
 // Workspace of dsa_prefill_select: 256-B aligned parts, in this order.
 struct PrefillCarve {
-  int64_t qb, qc, sw, urow, bound, mpage, mreq, topk, cnt, list, pos, total;
+  int64_t qb, qc, sw, qlin, urow, bound, mpage, mreq, topk, cnt, list, pos, total;
 };
 PrefillCarve prefill_carve(int32_t n_q, int64_t ld, int32_t n_req, int64_t off_ld) {
   PrefillCarve c{};
@@ -52,6 +52,7 @@ PrefillCarve prefill_carve(int32_t n_q, int64_t ld, int32_t n_req, int64_t off_l
   c.qb = take((int64_t)n_q * kIdxHeads * kIdxDim * 2);
   c.qc = take((int64_t)n_q * kIdxHeads * kIdxDim);
   c.sw = take((int64_t)((n_q + 31) / 32) * kIdxHeads * 32 * 4);
+  c.qlin = take((int64_t)n_q * 2 * kIdxDim * 2);
   c.urow = take((int64_t)n_q * 16 * 4);
   c.bound = take((int64_t)n_q * 4);
   c.mpage = take((int64_t)n_req * off_ld * 16 * 4);
@@ -268,6 +269,7 @@ PrefillWs prefill_ws(void *workspace, const PrefillCarve &c) {
   pw.qb = reinterpret_cast<uint16_t *>(base + c.qb);
   pw.qc = base + c.qc;
   pw.sw = reinterpret_cast<float *>(base + c.sw);
+  pw.qlin = reinterpret_cast<uint16_t *>(base + c.qlin);
   pw.urow = reinterpret_cast<float *>(base + c.urow);
   pw.bound = reinterpret_cast<float *>(base + c.bound);
   pw.mpage = reinterpret_cast<float *>(base + c.mpage);

@@ -55,12 +55,14 @@ size_t indexer_gemm_workspace_bytes(int32_t n_q);
 // Every score the FP8 GEMM writes is within E_r = delta sum_g U_rg M_bg of the bf16 GEMM's
 // score for the same inputs (g over the 16 groups of 8 consecutive dims, U_rg =
 // sum_j s_j max_{d in g} |q~_jd|, M_bg = max_t |ks_t| max_{d in g} |k_td|); delta covers how the
-// FP8 MFMA truncates products inside each group of 8, plus every fp32 rounding, with a margin.
-constexpr float kFp8GroupDelta = 0x1.2p-10f;
+// FP8 MFMA truncates products inside each group of 8 (in the |x| half of the split ReLU), the
+// bf16 parts of the linear half and every fp32 rounding, with a margin.
+constexpr float kFp8GroupDelta = 0x1.6p-11f;
 struct PrefillWs {
   uint16_t *qb;  // [n_q][32][128] bf16 sign-folded queries q~ (exact)
   uint8_t *qc;   // [n_q][32][128] e4m3 codes of q~
   float *sw;     // [ceil(n_q / 32)][32][32] s_j = w_j |qs_j|, [row block][head][row]
+  uint16_t *qlin;  // [n_q][2][128] bf16: sum_j s_j q~_j as hi + lo parts
   float *urow;   // [n_q][16] U_rg
   float *mpage;  // [n_req][off_ld][16] max over each key page's tokens of |ks_t| max_{d in g} |k_td|
   float *mreq;   // [n_req][16] M_bg: the same over the request's pages

@@ -15,19 +15,27 @@
 // significant bits, so the largest product of a group is exact and each of the other seven
 // loses less than 2^(E - 13):
 //   |x^ - x| < 7 * 2^-13 * sum_g max_{d in g} |q~_d k_d|  (+ fp32 rounding)
-// for one head.  With s_j = w_j |qs_j|, the score ks sum_j s_j med3(x_j, lo, hi) (med3 is
-// 1-Lipschitz) and |q~_d k_d| <= max_{g} |q~| * max_{g} |k|:
+// for one head.
+//
+// The epilogue splits the ReLU: with s_j = w_j |qs_j| and sigma = sign(ks),
+//   score = ks sum_j s_j ReLU-part(x_j) = |ks| / 2 * (sigma L + S),
+//   L = sum_j s_j x_j = q_lin . k,   q_lin = sum_j s_j q~_j,   S = sum_j s_j |x_j|.
+// L runs on bf16 MFMA with q_lin as two bf16 parts (hi + lo, 2^-18 relative) against the keys
+// decoded from the fragments; it seeds the accumulators, and each head then costs one fma
+// with |x| (an operand modifier) per element instead of a med3 and an fma.  Only S carries the
+// FP8 truncation, so with |q~_d k_d| <= max_{g} |q~| * max_{g} |k|:
 //   |s^ - s| <= delta * sum_g U_rg * A_tg,  U_rg = sum_j s_j max_{d in g} |q~_jd|,
 //                                         A_tg = |ks_t| max_{d in g} |k_td|,
 // and for the whole row E_r = delta * sum_g U_rg M_bg with M_bg = max_t A_tg over the
-// request's tokens.  delta = 1.125 * 2^-10 covers the 7 * 2^-13 above, the fp32 rounding of
-// the group sums, of the epilogue and of the bf16 path's own sums, with a margin.  The
-// top-k kernels in band mode use E_r to find the tokens whose order it could change and
-// rescore those exactly.
+// request's tokens.  delta = 5.5 * 2^-13 covers half the 7 * 2^-13 above, the q_lin parts, the
+// fp32 rounding of the group sums, of the accumulation (which starts at |L|) and of the bf16
+// path's own sums, with a margin.  The top-k kernels in band mode use E_r to find the tokens
+// whose order it could change and rescore those exactly.  (Exact zeros are not kept: a token no
+// head scores positive comes out as a small residue, inside the bound.)
 //
 // Kernels:
 //   indexer_qprep_fp8_kernel  one workgroup per row: the bf16 q~ (for exact rescoring), the
-//                             e4m3 q~ codes, s_j as the GEMM's weight tile, and U_r;
+//                             e4m3 q~ codes, s_j as the GEMM's weight tile, q_lin and U_r;
 //   key_bound_kernel          one wave per key page: the page's group maxima of A_tg;
 //   key_bound_reduce_kernel   one workgroup per request: M_b over its pages;
 //   indexer_gemm_fp8_kernel   the GEMM: 32 query rows x 256 tokens per workgroup, as the bf16
@@ -74,6 +82,7 @@ __device__ __forceinline__ uint32_t absmax8_bits(u32x4_t v) {
 __global__ __launch_bounds__(256) void indexer_qprep_fp8_kernel(const ScoreArgs a, PrefillWs ws) {
   const int r = blockIdx.x, t = threadIdx.x, j = t >> 3, d0 = 16 * (t & 7);
   __shared__ float s_u[kIdxHeads][kGroups8 + 1];  // s_j max_{d in g} |q~_jd|, [head][group]
+  __shared__ float s_lin[kIdxHeads][kIdxDim + 4];  // s_j q~_jd
   const float qs = a.q_scale[(int64_t)r * kIdxHeads + j];
   const float s = a.w[(int64_t)r * kIdxHeads + j] * fabsf(qs);
   u32x4_t raw = *reinterpret_cast<const u32x4_t *>(static_cast<const uint8_t *>(a.q) +
@@ -92,11 +101,26 @@ __global__ __launch_bounds__(256) void indexer_qprep_fp8_kernel(const ScoreArgs 
   *reinterpret_cast<u32x4_t *>(dst + 8) = x1;
   *reinterpret_cast<u32x4_t *>(ws.qc + ((int64_t)r * kIdxHeads + j) * kIdxDim + d0) = raw;
   if ((t & 7) == 0) ws.sw[((int64_t)(r / kGRows) * kIdxHeads + j) * kGRows + r % kGRows] = s;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s_lin[j][d0 + 2 * i] = s * __uint_as_float(x0[i] << 16);
+    s_lin[j][d0 + 2 * i + 1] = s * __uint_as_float(x0[i] & 0xFFFF0000u);
+    s_lin[j][d0 + 8 + 2 * i] = s * __uint_as_float(x1[i] << 16);
+    s_lin[j][d0 + 8 + 2 * i + 1] = s * __uint_as_float(x1[i] & 0xFFFF0000u);
+  }
   __syncthreads();
   if (t < kGroups8) {
     float u = 0.0f;
     for (int i = 0; i < kIdxHeads; ++i) u += s_u[i][t];
     ws.urow[(int64_t)r * kGroups8 + t] = u;
+  }
+  if (t < kIdxDim) {  // q_lin[d] = sum_j s_j q~_jd as bf16 hi + lo
+    float q = 0.0f;
+    for (int i = 0; i < kIdxHeads; ++i) q += s_lin[i][t];
+    const __bf16 hi = (__bf16)q;
+    const __bf16 lo = (__bf16)(q - (float)hi);
+    ws.qlin[(int64_t)r * 2 * kIdxDim + t] = __builtin_bit_cast(uint16_t, hi);
+    ws.qlin[(int64_t)r * 2 * kIdxDim + kIdxDim + t] = __builtin_bit_cast(uint16_t, lo);
   }
 }
 
@@ -235,6 +259,23 @@ __global__ __launch_bounds__(256, 2) void indexer_gemm_fp8_kernel(const ScoreArg
     if (!first) stage(0);
     first = false;
 
+    // the linear part's query operand, in flight with the page: lane (row n, half h) at
+    // K-step s' holds dims 64 (s'/4) + 32h + 8 (s'%4) .. +8 of q_lin's hi and lo rows (rows past
+    // n_q read as zero)
+    bf16x8_t la[8][2];
+    {
+      const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+          ws.qlin + (int64_t)row0 * 2 * kIdxDim, 0, (int)(min(kGRows, a.n_q - row0) * 2 * kIdxDim * 2), 0x00020000);
+#pragma unroll
+      for (int sp = 0; sp < 8; ++sp) {
+#pragma unroll
+        for (int pc = 0; pc < 2; ++pc) {
+          const int voff = 2 * ((n * 2 + pc) * kIdxDim + 64 * (sp >> 2) + 32 * h + 8 * (sp & 3));
+          la[sp][pc] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(lrs, voff, 0, 0));
+        }
+      }
+    }
+
     // (1) this wave's key page -> LDS
     const int wtok0 = tile * kGTokWG + wid * kPage;
     bool page_ok = false;
@@ -260,7 +301,7 @@ __global__ __launch_bounds__(256, 2) void indexer_gemm_fp8_kernel(const ScoreArg
 
     // (2) key fragments: raw e4m3 bytes, resident for all heads
     i32x8_t kb[2][2];
-    float ks[2], lo[2], hi[2];
+    float ks[2];
     f32x16_t acc[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -272,12 +313,28 @@ __global__ __launch_bounds__(256, 2) void indexer_gemm_fp8_kernel(const ScoreArg
         for (int i = 0; i < 8; ++i) kb[c][s][i] = (int)w32[i];
       }
       ks[c] = *reinterpret_cast<const float *>(kr + 128);
-      lo[c] = ks[c] < 0.0f ? -INFINITY : 0.0f;
-      hi[c] = ks[c] < 0.0f ? 0.0f : INFINITY;
-      acc[c] = f32x16_t{};
     }
     __syncthreads();  // every wave has its key fragments: the page region becomes query buffer 1
     stage(1);
+
+    // (2b) the linear part L = q_lin . k on bf16 MFMA, the keys decoded from the fragments;
+    // acc starts at sign(ks) L, so that after the heads acc = sign(ks) L + sum_j s_j |x_j| and
+    // the score is |ks| / 2 * acc
+    if (page_ok) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        f32x16_t l = f32x16_t{};
+#pragma unroll
+        for (int sp = 0; sp < 8; ++sp) {
+          const bf16x8_t bk = e4m3x8_bf16((uint32_t)kb[c][sp >> 2][2 * (sp & 3)], (uint32_t)kb[c][sp >> 2][2 * (sp & 3) + 1]);
+          l = mfma_32x32x16_bf16(la[sp][0], bk, l);
+          l = mfma_32x32x16_bf16(la[sp][1], bk, l);
+        }
+        const float sg = ks[c] < 0.0f ? -1.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[c][i] = sg * l[i];
+      }
+    }
 
     i32x8_t qa[2][2];  // [head parity][K-step]
     auto load_qa = [&](i32x8_t(&q)[2], int buf, int hh) {
@@ -306,12 +363,12 @@ __global__ __launch_bounds__(256, 2) void indexer_gemm_fp8_kernel(const ScoreArg
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // sixteen VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // eight VALU
       }
     };
     auto accum = [&](int c, const f32x16_t &x, const float *wv) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[c][i] = fmaf(wv[i], __builtin_amdgcn_fmed3f(x[i], lo[c], hi[c]), acc[c][i]);
+      for (int i = 0; i < 16; ++i) acc[c][i] = fmaf(wv[i], fabsf(x[i]), acc[c][i]);
     };
 
     // (3) the 32 heads as one software pipeline of 64 chains (head j, column c), four heads
@@ -358,17 +415,18 @@ __global__ __launch_bounds__(256, 2) void indexer_gemm_fp8_kernel(const ScoreArg
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int t = wtok0 + 32 * c + n;
+        const float hk = 0.5f * fabsf(ks[c]);
         if (whole) {
           const int voff = 4 * (h4 * ld32 + t);
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ks[c] * acc[c][i]), ors, voff,
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hk * acc[c][i]), ors, voff,
                                                   4 * (8 * (i >> 2) + (i & 3)) * ld32, 0);
         } else {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int m = 8 * (i >> 2) + h4 + (i & 3);
-            if (((rws >> m) & 1u) && t < s_len[m]) out[m * ld + t] = ks[c] * acc[c][i];
+            if (((rws >> m) & 1u) && t < s_len[m]) out[m * ld + t] = hk * acc[c][i];
           }
         }
       }

@@ -6,8 +6,9 @@ lies within its row bound E_r = delta sum_g U_rg M_bg of that GEMM's score.  The
 rounding is measured against the per-token form of the bound, sum_g U_rg A_tg: on the
 workload's data, on inputs chosen to stress it (products over many binades, sums that cancel),
 and on a hand-built near-worst case (in every group of 8 dims one large product and seven just
-below its truncation step), which must land between 1/2 and 1 of the 7 * 2^-13 the model
-allows.  U, A and M are recomputed from the codes with torch's float8_e4m3fn decode, in fp64.
+below its truncation step), which must land between 1/2 and 1 of the 3.5 * 2^-13 the model
+allows (7 * 2^-13 on each head's dot product, halved by the split ReLU: only the |x| half is
+scored in FP8).  U, A and M are recomputed from the codes with torch's float8_e4m3fn decode, in fp64.
 """
 import numpy as np
 import pytest
@@ -21,8 +22,8 @@ from tests.test_gpu_decode import check_scores, log
 
 pytestmark = pytest.mark.gpu
 
-DELTA = 1.125 * 2.0 ** -10     # the library's delta
-MODEL = 7 * 2.0 ** -13         # the measured truncation model's worst case
+DELTA = 5.5 * 2.0 ** -13       # the library's delta
+MODEL = 3.5 * 2.0 ** -13       # the measured truncation model's worst case, halved by the split ReLU
 
 
 @pytest.fixture(scope="module")
@@ -135,7 +136,7 @@ class Case:
                 if ratio.numel():
                     worst = max(worst, float(ratio.max()))
         log(f"[measure] max |s8 - s_bf16| / sum_g U_rg A_tg = {worst:.3e} = {worst / MODEL:.3f} of the model's "
-            f"7*2^-13 (delta {DELTA:.3e})")
+            f"3.5*2^-13 (delta {DELTA:.3e})")
         assert worst <= MODEL * 1.01
         assert worst >= lo * MODEL
         return worst
@@ -240,7 +241,8 @@ def test_fp8_mfma_rounding_within_bound(d, kind):
 def test_fp8_mfma_rounding_near_worst_case(d):
     """Hand-built keys (every code 1.0, scales spread over [0.5, 1.5]) against queries whose every
     group of 8 dims holds one 256 and seven 1.875 * 2^-6, just under the 2^-5 truncation step:
-    each group loses 7 * 0.94 steps, 0.94 of the model's bound."""
+    each group loses 7 * 0.94 steps, 0.94 of the model's bound.  (All heads alike and positive,
+    so the linear half of the split ReLU is large and exact, and the |x| half carries the loss.)"""
     L = 20000
     rng = np.random.default_rng(71)
     one = torch.full((128,), 1.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
