@@ -60,7 +60,7 @@ PrefillCarve prefill_carve(int32_t n_q, int64_t ld, int32_t n_req, int64_t off_l
   c.topk = take((int64_t)topk_workspace_bytes(n_q, ld));
   c.cnt = take((int64_t)n_q * 8);
   c.list = take((int64_t)n_q * kBandListCap * 8);
-  c.pos = take((int64_t)n_q * kBandCap * 4);
+  c.pos = take((int64_t)n_q * kBandCap * 8);
   c.total = o;
   return c;
 }
@@ -316,7 +316,7 @@ hipError_t prefill_topk(const uint8_t *pool, int64_t pool_bytes, const int64_t *
   band.e = pw.bound;
   band.cnt = reinterpret_cast<int32_t *>(base + c.cnt);
   band.list = reinterpret_cast<uint2 *>(base + c.list);
-  band.pos = reinterpret_cast<int32_t *>(base + c.pos);
+  band.pos = reinterpret_cast<uint2 *>(base + c.pos);
   TopkArgs t{};
   t.scores = scores;
   t.ld = ld;

@@ -112,7 +112,7 @@ struct BandWs {
   const float *e;  // [n_rows] E_r; NULL: not band mode
   int32_t *cnt;    // [n_rows][2]: list length (-1: the first pass kept the whole row), band size
   uint2 *list;     // [n_rows][kBandListCap]: (key, token) in token order
-  int32_t *pos;    // [n_rows][kBandCap]: list position of each band token
+  uint2 *pos;      // [n_rows][kBandCap]: (list position, token) of each band token
 };
 
 struct TopkArgs {

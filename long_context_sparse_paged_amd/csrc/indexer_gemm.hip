@@ -334,61 +334,79 @@ __global__ __launch_bounds__(64) void band_rescore_kernel(const RescoreArgs a) {
   for (int s = 0; s < 8; ++s) af[s] = *reinterpret_cast<const bf16x8_t *>(qrow + 8 * s);
   const float *swr = a.sw + (int64_t)(r / kGRows) * kIdxHeads * kGRows + r % kGRows;  // s_j at swr[32 j]
   uint2 *list = a.band.list + (int64_t)r * kBandListCap;
-  const int32_t *bpos = a.band.pos + (int64_t)r * kBandCap;
+  const uint2 *bpos = a.band.pos + (int64_t)r * kBandCap;
   const int64_t *koff = a.key_off + (int64_t)b * a.off_ld;
+  const int lim = min(nl, kBandListCap);
 
-  for (int q = blockIdx.y; q < tiles; q += gridDim.y) {
-    // column n: token t (list position p in band mode)
-    const int bi = 32 * q + n;
-    int t = 0, p = 0;
-    bool valid = bi < ntok;
-    if (valid) {
-      if (full) {
-        t = bi;
+  // two tiles per round (q and q + gridDim.y), their dependent loads interleaved: column n of
+  // tile u is the token t[u] (list position p[u] in band mode)
+  for (int q0 = blockIdx.y; q0 < tiles; q0 += 2 * gridDim.y) {
+    int t[2], p[2];
+    bool valid[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int bi = 32 * (q0 + u * (int)gridDim.y) + n;
+      valid[u] = bi < ntok;
+      t[u] = 0;
+      p[u] = 0;
+      if (valid[u]) {
+        if (full) {
+          t[u] = bi;
+        } else {
+          const uint2 e = bpos[bi];
+          p[u] = (int)e.x;
+          t[u] = (int)e.y;
+          valid[u] = p[u] >= 0 && p[u] < lim;
+        }
+      }
+      valid[u] = valid[u] && t[u] >= 0 && t[u] < len;
+    }
+    int64_t off[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) off[u] = valid[u] ? koff[t[u] >> 6] : -1;
+    bf16x8_t bfr[2][8];
+    float ks[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      valid[u] = valid[u] && off[u] >= 0 && off[u] + kKPB <= a.pool_bytes && (off[u] & 15) == 0;
+      ks[u] = 0.0f;
+      if (valid[u]) {
+        const uint8_t *kr = a.pool + off[u] + (t[u] & (kPage - 1)) * kKB;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          bfr[u][s] = e4m3x8_bf16(*reinterpret_cast<const uint32_t *>(kr + 64 * h + 8 * s),
+                                  *reinterpret_cast<const uint32_t *>(kr + 64 * h + 8 * s + 4));
+        ks[u] = *reinterpret_cast<const float *>(kr + 128);
       } else {
-        p = bpos[bi];
-        valid = p >= 0 && p < min(nl, kBandListCap);
-        t = valid ? (int)list[p].y : 0;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) bfr[u][s] = bf16x8_t{};
       }
     }
-    valid = valid && t >= 0 && t < len;
-    const int64_t off = valid ? koff[t >> 6] : -1;
-    valid = valid && off >= 0 && off + kKPB <= a.pool_bytes && (off & 15) == 0;
-    bf16x8_t bfr[8];
-    float ks = 0.0f;
-    if (valid) {
-      const uint8_t *kr = a.pool + off + (t & (kPage - 1)) * kKB;
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        bfr[s] = e4m3x8_bf16(*reinterpret_cast<const uint32_t *>(kr + 64 * h + 8 * s),
-                             *reinterpret_cast<const uint32_t *>(kr + 64 * h + 8 * s + 4));
-      ks = *reinterpret_cast<const float *>(kr + 128);
-    } else {
+    for (int u = 0; u < 2; ++u) {
+      f32x16_t x = f32x16_t{};
 #pragma unroll
-      for (int s = 0; s < 8; ++s) bfr[s] = bf16x8_t{};
-    }
-    f32x16_t x = f32x16_t{};
+      for (int s = 0; s < 8; ++s) x = mfma_32x32x16_bf16(af[s], bfr[u][s], x);
+      // element i of lane (n, h) is head 8 (i / 4) + 4h + i % 4: lanes n < 32 take the other half's
+      float xo[16];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) x = mfma_32x32x16_bf16(af[s], bfr[s], x);
-    // element i of lane (n, h) is head 8 (i / 4) + 4h + i % 4: lanes n < 32 take the other half's
-    float xo[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[i]), __float_as_uint(x[i]), false, false);
-      xo[i] = __uint_as_float(sw2[1]);
-    }
-    if (h == 0 && valid) {
-      const float lo = ks < 0.0f ? -INFINITY : 0.0f, hi = ks < 0.0f ? 0.0f : INFINITY;
-      float acc = 0.0f;
-#pragma unroll
-      for (int j = 0; j < kIdxHeads; ++j) {
-        const int i = 4 * (j >> 3) + (j & 3);
-        const float xj = (j & 4) ? xo[i] : x[i];
-        acc = fmaf(swr[kGRows * j], __builtin_amdgcn_fmed3f(xj, lo, hi), acc);
+      for (int i = 0; i < 16; ++i) {
+        const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[i]), __float_as_uint(x[i]), false, false);
+        xo[i] = __uint_as_float(sw2[1]);
       }
-      const float sc = ks * acc;
-      if (full) a.scores[(int64_t)r * a.ld + t] = sc;
-      else list[p].x = score_key(sc);
+      if (h == 0 && valid[u]) {
+        const float lo = ks[u] < 0.0f ? -INFINITY : 0.0f, hi = ks[u] < 0.0f ? 0.0f : INFINITY;
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kIdxHeads; ++j) {
+          const int i = 4 * (j >> 3) + (j & 3);
+          const float xj = (j & 4) ? xo[i] : x[i];
+          acc = fmaf(swr[kGRows * j], __builtin_amdgcn_fmed3f(xj, lo, hi), acc);
+        }
+        const float sc = ks[u] * acc;
+        if (full) a.scores[(int64_t)r * a.ld + t[u]] = sc;
+        else list[p[u]].x = score_key(sc);
+      }
     }
   }
 }

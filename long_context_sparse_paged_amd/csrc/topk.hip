@@ -17,8 +17,9 @@
 //            sample key of rank m(k, len, S), set so that the row holds at least k
 //            elements >= est except with negligible probability, and a few k at most.
 //   collect  (one workgroup per 8192-score slice): the slice is loaded in one round trip
-//            and every element with key >= est is appended, in index order, to the
-//            slice's candidate list (ballot ranks; one barrier).
+//            and every element with key >= est (a float compare with est's value; NaNs
+//            too) is appended, in index order, to the slice's candidate list (ballot ranks;
+//            one barrier).
 //   finalize (one workgroup per row): the slices' candidates, concatenated in slice
 //            order, are in index order.  The first B entries of every list come in one
 //            round trip with the counts; the entries past B, numbered through a prefix
@@ -38,6 +39,8 @@
 // plain histogram would send most of a wave's atomics to one address.
 // The result is exact whatever est is, so which launches a row goes through never
 // changes its output.
+#include <type_traits>
+
 #include "dsa_device.hpp"
 #include "dsa_kernels.hpp"
 
@@ -436,24 +439,28 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(const TopkArgs a, Top
   } else {
     est = w.est[r];
   }
-  // (2) ordered append of the elements >= est
-  uint32_t key[8][4];
+  // (2) ordered append of the elements whose key is >= est.  score_key preserves order (and
+  // -0 = +0), so that is a float compare with est's value; a NaN fails "f < e" and is kept
+  // whatever its key -- extra candidates never change the selection, which works on keys.
+  // Keys are formed only for the appended elements.
+  const float ef = est == 0u ? -INFINITY : key_score(est);
   unsigned long long bal[8][4];
+  auto take = [&](auto whole) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int i = beg + 1024 * j + 4 * tid;
-    key[j][0] = score_key(v[j].x);
-    key[j][1] = score_key(v[j].y);
-    key[j][2] = score_key(v[j].z);
-    key[j][3] = score_key(v[j].w);
-    int cj = 0;
+    for (int j = 0; j < 8; ++j) {
+      const int i = beg + 1024 * j + 4 * tid;
+      const float f[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+      int cj = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      bal[j][e] = __ballot(i + e < end && key[j][e] >= est);
-      cj += __popcll(bal[j][e]);
+      for (int e = 0; e < 4; ++e) {
+        bal[j][e] = __ballot((decltype(whole)::value || i + e < end) && !(f[e] < ef));
+        cj += __popcll(bal[j][e]);
+      }
+      if (lane == 0) s_tot[j][wid] = cj;
     }
-    if (lane == 0) s_tot[j][wid] = cj;
-  }
+  };
+  if (end - beg == kSlice) take(std::true_type{});
+  else take(std::false_type{});
   __syncthreads();
   int4 tot[8];
 #pragma unroll
@@ -467,10 +474,11 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(const TopkArgs a, Top
 #pragma unroll
     for (int e = 0; e < 4; ++e) rank += __popcll(bal[j][e] & lt);
     const int i = beg + 1024 * j + 4 * tid;
+    const float f[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if ((bal[j][e] >> lane) & 1ull) {
-        if (rank < kSliceCap) out[rank] = make_uint2(key[j][e], (uint32_t)(i + e));
+        if (rank < kSliceCap) out[rank] = make_uint2(score_key(f[e]), (uint32_t)(i + e));
         ++rank;
       }
     }
@@ -778,14 +786,16 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
       }
       if (s_flag & 1) {  // slices whose list overflowed: filter them again from the scores
         const uint32_t est = w.est[r];
+        const float ef = est == 0u ? -INFINITY : key_score(est);
         for (int s = 0; s < n_slices; ++s) {
           if (s_base[s + 1] - s_base[s] <= kSliceCap) continue;  // uniform
           const int beg = s * kSlice, end = min(len, beg + kSlice);
           int written = s_base[s];
           for (int c0 = beg; c0 < end; c0 += NT) {
             const int i = c0 + tid;
-            const uint32_t key = i < end ? score_key(row[i]) : 0u;
-            const bool f = i < end && key >= est;
+            const float x = i < end ? row[i] : 0.0f;
+            const uint32_t key = score_key(x);
+            const bool f = i < end && !(x < ef);  // the same test as collect's
             int tot;
             const int pos = written + block_rank<NT>(f, R.tmp, tot);
             if (f && pos < s_base[s + 1]) {  // the same test as collect's: pos stays in the slice
@@ -823,10 +833,10 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
     // the candidates are the tokens with key >= est: enough unless the band reaches below it
     const bool from_cand = ok && (len <= kShortRow || lo_key >= w.est[r]);
     // (3) ordered compaction of the surely kept tokens (key > hi_key, listed with key all ones)
-    // and the band tokens (listed with key 0 until rescored; their list positions go to pos)
+    // and the band tokens (listed with key 0 until rescored; (list position, token) go to pos)
     const int M = from_cand ? n : len;
     uint2 *list = a.band.list + (int64_t)r * kBandListCap;
-    int32_t *bpos = a.band.pos + (int64_t)r * kBandCap;
+    uint2 *bpos = a.band.pos + (int64_t)r * kBandCap;
     int written = 0, bw = 0;
     for (int c0 = 0; c0 < M; c0 += NT) {
       const int i = c0 + tid;
@@ -846,7 +856,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
       const int pos = written + block_rank<NT>(sure || band, R.tmp, tot);
       const int bp = bw + block_rank<NT>(band, R.tmp, btot);
       if ((sure || band) && pos < kBandListCap) list[pos] = make_uint2(sure ? 0xFFFFFFFFu : 0u, (uint32_t)t);
-      if (band && bp < kBandCap && pos < kBandListCap) bpos[bp] = pos;
+      if (band && bp < kBandCap && pos < kBandListCap) bpos[bp] = make_uint2((uint32_t)pos, (uint32_t)t);
       written += tot;
       bw += btot;
     }
