@@ -523,6 +523,22 @@ def summarize_pmc(argv):
              f"scrub copy (512 MiB each way)  fetch {f_c:.1f} KiB, write {w_c:.1f} KiB",
              f"scale factors                  fetch {ff:.4f}, write {fw:.4f}",
              f"HBM bytes per launch           {traffic / 1e6:14.2f} MB", f"source sha                     {rec['source_sha']}"]
+    # every kernel of the library in the same runs, for the stages around the dominant one
+    def all_kernels(path, counter):
+        val, name = defaultdict(float), {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter and "dsa::" in r["Kernel_Name"]:
+                val[r["Dispatch_Id"]] += float(r["Counter_Value"])
+                name[r["Dispatch_Id"]] = _short_kernel(r["Kernel_Name"])
+        per = defaultdict(list)
+        for k, v in val.items():
+            per[name[k]].append(v)
+        return {n: sum(v) / len(v) for n, v in per.items()}
+    fa, wa = all_kernels(fetch_csv, "FETCH_SIZE"), all_kernels(write_csv, "WRITE_SIZE")
+    lines += ["", "# every library kernel of the run: HBM MB per launch (same scale factors)",
+              f"{'kernel':44s} {'fetch_MB':>10s} {'write_MB':>10s}"]
+    for n in sorted(set(fa) | set(wa), key=lambda n: -(fa.get(n, 0) * ff + wa.get(n, 0) * fw)):
+        lines.append(f"{n:44s} {fa.get(n, 0) * ff * 1024 / 1e6:10.2f} {wa.get(n, 0) * fw * 1024 / 1e6:10.2f}")
     open(base + ".txt", "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
