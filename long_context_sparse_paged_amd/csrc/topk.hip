@@ -595,6 +595,84 @@ __device__ __forceinline__ void select_write_any(uint32_t *s_key, const int32_t 
   else select_write<kFinPer>(s_key, s_idx, n, per, keff, R, pre, emit, list_cap);
 }
 
+// Band mode's first pass over the n candidates in s_key / s_idx (index order): thread t takes
+// [t per, t per + cnt) into registers; T^ = the keff-th largest key by radix select (s_key
+// doubles as its list); lo_key / hi_key = the band's edges.  When the band stays at or above
+// `est` (the candidates' threshold; pass 0 when the candidates are the whole row), the surely
+// kept tokens (key > hi_key) and the band are written in index order through two block scans
+// and true is returned; otherwise nothing is written and the caller classifies the whole row.
+template <int PER>
+__device__ __forceinline__ bool band_from_regs(uint32_t *s_key, const int32_t *s_idx, int n, int per, int keff,
+                                               double e2, uint32_t est, RadixLds<kFinThreads> &R, uint2 *list,
+                                               uint2 *bpos, int &written, int &bw, uint32_t &lo_key,
+                                               uint32_t &hi_key) {
+  constexpr int NT = kFinThreads;
+  const int tid = threadIdx.x;
+  const int b0 = min(n, tid * per);
+  const int cnt = min(n, b0 + per) - b0;
+  uint32_t rk[PER];
+  int32_t ri[PER];
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    rk[q] = q < cnt ? s_key[b0 + q] : 0u;
+    ri[q] = q < cnt ? s_idx[b0 + q] : 0;
+    if (q < cnt) {
+      lo = min(lo, rk[q]);
+      hi = max(hi, rk[q]);
+    }
+  }
+  block_minmax<NT>(lo, hi, R);  // its barriers also end every read of s_key
+  int gt;
+  const uint32_t tau = radix_select<NT>(
+      [&](auto f) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+          if (q < cnt) f(rk[q]);
+      },
+      keff, lo, hi, 32, R, gt, s_key, kShortRow);
+  const double tv = (double)key_score(tau);
+  lo_key = key_floor(tv - e2);
+  hi_key = key_ceil(tv + e2);
+  if (lo_key < est) return false;  // uniform
+  int cs = 0, cb = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const bool sure = q < cnt && rk[q] > hi_key;
+    const bool band = q < cnt && !sure && rk[q] >= lo_key;
+    cs += (sure || band) ? 1 : 0;
+    cb += band ? 1 : 0;
+  }
+  int tot, btot;
+  int pos = block_scan_incl<NT>(cs, R.tmp, tot) - cs;
+  int bp = block_scan_incl<NT>(cb, R.tmp, btot) - cb;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const bool sure = q < cnt && rk[q] > hi_key;
+    const bool band = q < cnt && !sure && rk[q] >= lo_key;
+    if (sure || band) {
+      if (pos < kBandListCap) list[pos] = make_uint2(sure ? 0xFFFFFFFFu : 0u, (uint32_t)ri[q]);
+      if (band) {
+        if (bp < kBandCap && pos < kBandListCap) bpos[bp] = make_uint2((uint32_t)pos, (uint32_t)ri[q]);
+        ++bp;
+      }
+      ++pos;
+    }
+  }
+  written = tot;
+  bw = btot;
+  return true;
+}
+
+template <class... Args>
+__device__ __forceinline__ bool band_from_regs_any(int per, Args &&...args) {
+  if (per <= 5) return band_from_regs<5>(args...);
+  if (per <= 9) return band_from_regs<9>(args...);
+  if (per <= 13) return band_from_regs<13>(args...);
+  if (per <= 17) return band_from_regs<17>(args...);
+  return band_from_regs<kFinPer>(args...);
+}
+
 template <bool BAND>
 __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkArgs a, TopkWs w, int n_slices) {
   constexpr int NT = kFinThreads;
@@ -810,55 +888,54 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
   }
   __syncthreads();
   if constexpr (BAND) {
-    // (1) T^: the keff-th largest key, among the candidates (which hold the keff largest when
-    // ok) or over the whole row
-    const int N = ok ? n : len;
-    auto key_at = [&](int i) { return ok ? s_key[i] : score_key(row[i]); };
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    for (int i = tid; i < N; i += NT) {
-      const uint32_t k = key_at(i);
-      lo = min(lo, k);
-      hi = max(hi, k);
-    }
-    block_minmax<NT>(lo, hi, R);
-    int gt;
-    const uint32_t tau = radix_select<NT>(
-        [&](auto f) {
-          for (int i = tid; i < N; i += NT) f(key_at(i));
-        },
-        keff, lo, hi, 32, R, gt, ok ? nullptr : s_key, ok ? 0 : kShortRow);
-    // (2) the band [T^ - 2E, T^ + 2E] as keys, rounded outward
-    const double tv = (double)key_score(tau), e2 = 2.0 * band_bound(a, r);
-    const uint32_t lo_key = key_floor(tv - e2), hi_key = key_ceil(tv + e2);
-    // the candidates are the tokens with key >= est: enough unless the band reaches below it
-    const bool from_cand = ok && (len <= kShortRow || lo_key >= w.est[r]);
-    // (3) ordered compaction of the surely kept tokens (key > hi_key, listed with key all ones)
-    // and the band tokens (listed with key 0 until rescored; (list position, token) go to pos)
-    const int M = from_cand ? n : len;
     uint2 *list = a.band.list + (int64_t)r * kBandListCap;
     uint2 *bpos = a.band.pos + (int64_t)r * kBandCap;
+    const double e2 = 2.0 * band_bound(a, r);
     int written = 0, bw = 0;
-    for (int c0 = 0; c0 < M; c0 += NT) {
-      const int i = c0 + tid;
-      uint32_t key = 0u;
-      int32_t t = i;
-      if (i < M) {
-        if (from_cand) {
-          key = s_key[i];
-          t = s_idx[i];
-        } else {
-          key = score_key(row[i]);
-        }
+    uint32_t lo_key, hi_key;
+    bool done = false;
+    if (ok) {
+      // the candidates hold the keff largest: T^ and the band from registers, unless the band
+      // reaches below the collect's threshold (then the whole row is classified below)
+      const int per = ((n + NT - 1) / NT) | 1;
+      done = band_from_regs_any(per, s_key, s_idx, n, per, keff, e2, len <= kShortRow ? 0u : w.est[r], R, list,
+                                bpos, written, bw, lo_key, hi_key);
+    } else {
+      // T^ over the whole row
+      auto load = [&](int i) { return score_key(row[i]); };
+      uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+      for (int i = tid; i < len; i += NT) {
+        const uint32_t k = load(i);
+        lo = min(lo, k);
+        hi = max(hi, k);
       }
-      const bool sure = i < M && key > hi_key;
-      const bool band = i < M && !sure && key >= lo_key;
-      int tot, btot;
-      const int pos = written + block_rank<NT>(sure || band, R.tmp, tot);
-      const int bp = bw + block_rank<NT>(band, R.tmp, btot);
-      if ((sure || band) && pos < kBandListCap) list[pos] = make_uint2(sure ? 0xFFFFFFFFu : 0u, (uint32_t)t);
-      if (band && bp < kBandCap && pos < kBandListCap) bpos[bp] = make_uint2((uint32_t)pos, (uint32_t)t);
-      written += tot;
-      bw += btot;
+      block_minmax<NT>(lo, hi, R);
+      int gt;
+      const uint32_t tau = radix_select<NT>(
+          [&](auto f) {
+            for (int i = tid; i < len; i += NT) f(load(i));
+          },
+          keff, lo, hi, 32, R, gt, s_key, kShortRow);
+      const double tv = (double)key_score(tau);
+      lo_key = key_floor(tv - e2);
+      hi_key = key_ceil(tv + e2);
+    }
+    if (!done) {
+      // ordered compaction over the whole row of the surely kept tokens (key > hi_key, listed
+      // with key all ones) and the band (listed with key 0 until rescored)
+      for (int c0 = 0; c0 < len; c0 += NT) {
+        const int i = c0 + tid;
+        const uint32_t key = i < len ? score_key(row[i]) : 0u;
+        const bool sure = i < len && key > hi_key;
+        const bool band = i < len && !sure && key >= lo_key;
+        int tot, btot;
+        const int pos = written + block_rank<NT>(sure || band, R.tmp, tot);
+        const int bp = bw + block_rank<NT>(band, R.tmp, btot);
+        if ((sure || band) && pos < kBandListCap) list[pos] = make_uint2(sure ? 0xFFFFFFFFu : 0u, (uint32_t)i);
+        if (band && bp < kBandCap && pos < kBandListCap) bpos[bp] = make_uint2((uint32_t)pos, (uint32_t)i);
+        written += tot;
+        bw += btot;
+      }
     }
     if (tid == 0) {
       a.band.cnt[2 * r] = written;
