@@ -112,6 +112,33 @@ def test_full_size_prefill_scores_and_topk(prefill, chunk):
     topk_set_ok(ref_s, oracle.topk(ref_s, rl, k), got_idx, rl, k)
 
 
+def test_full_size_prefill_select_every_row(d, prefill):
+    """The prefill step bench.py times: the indexer on FP8 MFMA with the band top-k
+    (PrefillSelectStep) on the same inputs.  For every one of the 2048 rows: the indices equal
+    the bf16-GEMM path's bit for bit (which the tests above pin to the oracle), every FP8
+    score lies within the row's reported bound of the bf16 GEMM's score, and the attention
+    output is the same."""
+    import torch
+    wl, cache, pq, step, oc, h = prefill
+    log("[case] full size prefill, FP8 select path on every row")
+    sel = d.PrefillSelectStep(cache, pq, k=wl["topk"])
+    sel.run()
+    torch.cuda.synchronize()
+    assert int(sel.err.item()) == 0
+    assert np.array_equal(sel.idx.cpu().numpy(), h["idx"])
+    rl = h["row_len"]
+    bound = sel.bound.double()
+    for r0 in range(0, len(rl), 128):
+        L = int(rl[r0 + 127])
+        a = sel.scores[r0:r0 + 128, :L].double()
+        b = step.scores[r0:r0 + 128, :L].double()
+        mask = torch.arange(L, device=a.device)[None, :] < torch.from_numpy(rl[r0:r0 + 128]).to(a.device)[:, None]
+        diff = torch.where(mask, (a - b).abs(), torch.zeros_like(a))
+        assert bool((diff <= bound[r0:r0 + 128, None]).all()), f"rows {r0}.."
+    assert torch.equal(sel.out.view(torch.int16), step.out.view(torch.int16))
+    assert torch.equal(sel.lse.view(torch.int32), step.lse.view(torch.int32))
+
+
 def test_full_size_prefill_attention_sample(prefill):
     """Attention of a seeded sample of 128 of the 2048 prefill rows (a sample: the other rows
     run the same kernel on the same launch)."""
