@@ -208,14 +208,17 @@ dsa_status dsa_prefill_select(const dsa_layout *layout, const uint8_t *pool, int
                               int32_t *err_flag, dsa_stream_t stream);
 
 /* The two halves of dsa_prefill_select, for callers that time or overlap them: the FP8 MFMA
- * scores (plus E_r and, in the workspace, the exact query rows the rescoring reads), then the
- * band top-k.  Called in this order on the same workspace and arguments, they enqueue exactly
+ * scores (plus E_r and, in the workspace, the exact query rows the rescoring reads and, when
+ * ld <= 2^18 and 64*off_ld >= ld, each long row's candidates at or above a threshold drawn from
+ * 16 sampled 256-token tiles per 32 rows, written by the GEMM itself), then the band top-k.
+ * Called in this order on the same workspace and arguments (the same k), they enqueue exactly
  * what dsa_prefill_select does; dsa_prefill_topk_band reads only what the score half left. */
 dsa_status dsa_prefill_score_fp8(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
                                  const int64_t *key_off, int64_t off_ld, int32_t n_req, const int32_t *ctx_len,
                                  const uint8_t *q, const float *q_scale, const float *w, const int32_t *q_req,
-                                 const int32_t *row_len, int32_t n_q, float *scores, int64_t ld, float *bound,
-                                 void *workspace, size_t workspace_bytes, int32_t *err_flag, dsa_stream_t stream);
+                                 const int32_t *row_len, int32_t n_q, int32_t k, float *scores, int64_t ld,
+                                 float *bound, void *workspace, size_t workspace_bytes, int32_t *err_flag,
+                                 dsa_stream_t stream);
 dsa_status dsa_prefill_topk_band(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
                                  const int64_t *key_off, int64_t off_ld, int32_t n_req, const int32_t *q_req,
                                  const int32_t *row_len, int32_t n_q, int32_t k, float *scores, int64_t ld,

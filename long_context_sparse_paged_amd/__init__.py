@@ -89,7 +89,7 @@ def _load():
         "dsa_prefill_select_workspace_size": ([I32, I64, I32, I64, I32, C.POINTER(SZ)], I32),
         "dsa_prefill_select": ([LP, P, I64, P, I64, I32, P, P, P, P, P, P, I32, I32, P, I64, P, I64, P, P, SZ, P, P],
                                I32),
-        "dsa_prefill_score_fp8": ([LP, P, I64, P, I64, I32, P, P, P, P, P, P, I32, P, I64, P, P, SZ, P, P], I32),
+        "dsa_prefill_score_fp8": ([LP, P, I64, P, I64, I32, P, P, P, P, P, P, I32, I32, P, I64, P, P, SZ, P, P], I32),
         "dsa_prefill_topk_band": ([LP, P, I64, P, I64, I32, P, P, I32, I32, P, I64, P, I64, P, SZ, P, P], I32),
         "dsa_sparse_mla_prefill_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
         "dsa_dcp_topk_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
@@ -249,13 +249,13 @@ def dsa_prefill_select(layout: dsa_layout, pool, key_off, n_req: int, ctx_len, q
 
 
 def dsa_prefill_score_fp8(layout: dsa_layout, pool, key_off, n_req: int, ctx_len, q, q_scale, w, q_req, row_len,
-                          scores, workspace, bound=None, err_flag=None, stream=None):
+                          k: int, scores, workspace, bound=None, err_flag=None, stream=None):
     """First half of dsa_prefill_select: FP8 MFMA scores (within bound[r] of the exact ones)."""
     st = lib.dsa_prefill_score_fp8(C.byref(layout), _ptr(pool, U8, "pool"), pool.numel(),
                                    _ptr(key_off, I64, "key_off"), key_off.shape[1], n_req,
                                    _ptr(ctx_len, I32, "ctx_len"), _ptr(q, U8, "q"), _ptr(q_scale, F32, "q_scale"),
                                    _ptr(w, F32, "w"), _ptr(q_req, I32, "q_req"), _ptr(row_len, I32, "row_len"),
-                                   row_len.shape[0], _ptr(scores, F32, "scores"), scores.shape[1],
+                                   row_len.shape[0], k, _ptr(scores, F32, "scores"), scores.shape[1],
                                    _ptr(bound, F32, "bound"), _ptr(workspace, None, "workspace"),
                                    workspace.numel() * workspace.element_size(), _ptr(err_flag, I32, "err_flag"),
                                    _stream(stream))

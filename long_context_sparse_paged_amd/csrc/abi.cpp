@@ -37,6 +37,10 @@ dsa_status check_layout(const dsa_layout *L) {
 
 dsa_status launched(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
 
+// The FP8 prefill GEMM writes the candidate lists itself when every row fits the tile lists
+// and the page table covers ld (else the top-k samples and collects from the scores).
+bool prefill_tile_mode(int64_t ld, int64_t off_ld) { return ld <= kTileModeMaxLd && off_ld * kPage >= ld; }
+
 // Workspace of dsa_prefill_select: 256-B aligned parts, in this order.
 struct PrefillCarve {
   int64_t qb, qc, sw, qlin, urow, bound, mpage, mreq, topk, cnt, list, pos, total;
@@ -57,7 +61,8 @@ PrefillCarve prefill_carve(int32_t n_q, int64_t ld, int32_t n_req, int64_t off_l
   c.bound = take((int64_t)n_q * 4);
   c.mpage = take((int64_t)n_req * off_ld * 16 * 4);
   c.mreq = take((int64_t)n_req * 16 * 4);
-  c.topk = take((int64_t)topk_workspace_bytes(n_q, ld));
+  c.topk = take((int64_t)(prefill_tile_mode(ld, off_ld) ? topk_tile_workspace_bytes(n_q, ld)
+                                                       : topk_workspace_bytes(n_q, ld)));
   c.cnt = take((int64_t)n_q * 8);
   c.list = take((int64_t)n_q * kBandListCap * 8);
   c.pos = take((int64_t)n_q * kBandCap * 8);
@@ -277,11 +282,34 @@ PrefillWs prefill_ws(void *workspace, const PrefillCarve &c) {
   return pw;
 }
 
+TopkArgs prefill_topk_args(const int32_t *row_len, int32_t n_q, int32_t k, float *scores, int64_t ld, int32_t *idx,
+                           int64_t idx_ld, int64_t off_ld, void *workspace, const PrefillCarve &c, int32_t *err_flag) {
+  uint8_t *base = static_cast<uint8_t *>(workspace);
+  BandWs band{};
+  band.e = reinterpret_cast<float *>(base + c.bound);
+  band.cnt = reinterpret_cast<int32_t *>(base + c.cnt);
+  band.list = reinterpret_cast<uint2 *>(base + c.list);
+  band.pos = reinterpret_cast<uint2 *>(base + c.pos);
+  TopkArgs t{};
+  t.scores = scores;
+  t.ld = ld;
+  t.row_len = row_len;
+  t.n_rows = n_q;
+  t.k = k;
+  t.idx = idx;
+  t.idx_ld = idx_ld;
+  t.ws = base + c.topk;
+  t.err = err_flag;
+  t.band = band;
+  t.tile_mode = prefill_tile_mode(ld, off_ld) ? 1 : 0;
+  return t;
+}
+
 hipError_t prefill_score(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes, const int64_t *key_off,
                          int64_t off_ld, int32_t n_req, const int32_t *ctx_len, const uint8_t *q, const float *q_scale,
-                         const float *w, const int32_t *q_req, const int32_t *row_len, int32_t n_q, float *scores,
-                         int64_t ld, float *bound, void *workspace, const PrefillCarve &c, int32_t *err_flag,
-                         hipStream_t hs) {
+                         const float *w, const int32_t *q_req, const int32_t *row_len, int32_t n_q, int32_t k,
+                         float *scores, int64_t ld, float *bound, void *workspace, const PrefillCarve &c,
+                         int32_t *err_flag, hipStream_t hs) {
   ScoreArgs a{};
   a.pool = pool;
   a.pool_bytes = pool_bytes;
@@ -303,31 +331,24 @@ hipError_t prefill_score(const dsa_layout *layout, const uint8_t *pool, int64_t 
   pw.bound_out = bound;
   const int64_t pages_ld = (ld + kPage - 1) / kPage;  // pages a row of ld tokens spans (<= 131072)
   const int32_t max_pages = (int32_t)(off_ld < pages_ld ? off_ld : pages_ld);
-  return launch_indexer_gemm_fp8(a, pw, ctx_len, max_pages, hs);
+  if (!prefill_tile_mode(ld, off_ld)) return launch_indexer_gemm_fp8(a, pw, ctx_len, max_pages, hs);
+  // tile mode: the sampled tiles, the thresholds, then every tile with the candidate lists
+  const TopkArgs t = prefill_topk_args(row_len, n_q, k, scores, ld, nullptr, k, off_ld, workspace, c, err_flag);
+  pw.tiles = tile_lists(t.ws, n_q, ld, k);
+  hipError_t e = launch_indexer_gemm_fp8_phase(a, pw, ctx_len, max_pages, true, hs);
+  if (e != hipSuccess) return e;
+  e = launch_topk_tile_est(t, hs);
+  if (e != hipSuccess) return e;
+  return launch_indexer_gemm_fp8_phase(a, pw, ctx_len, max_pages, false, hs);
 }
 
 hipError_t prefill_topk(const uint8_t *pool, int64_t pool_bytes, const int64_t *key_off, int64_t off_ld, int32_t n_req,
                         const int32_t *q_req, const int32_t *row_len, int32_t n_q, int32_t k, float *scores,
                         int64_t ld, int32_t *idx, int64_t idx_ld, void *workspace, const PrefillCarve &c,
                         int32_t *err_flag, hipStream_t hs) {
-  uint8_t *base = static_cast<uint8_t *>(workspace);
   const PrefillWs pw = prefill_ws(workspace, c);
-  BandWs band{};
-  band.e = pw.bound;
-  band.cnt = reinterpret_cast<int32_t *>(base + c.cnt);
-  band.list = reinterpret_cast<uint2 *>(base + c.list);
-  band.pos = reinterpret_cast<uint2 *>(base + c.pos);
-  TopkArgs t{};
-  t.scores = scores;
-  t.ld = ld;
-  t.row_len = row_len;
-  t.n_rows = n_q;
-  t.k = k;
-  t.idx = idx;
-  t.idx_ld = idx_ld;
-  t.ws = base + c.topk;
-  t.err = err_flag;
-  t.band = band;
+  const TopkArgs t = prefill_topk_args(row_len, n_q, k, scores, ld, idx, idx_ld, off_ld, workspace, c, err_flag);
+  const BandWs band = t.band;
   hipError_t e = launch_topk(t, hs);
   if (e != hipSuccess) return e;
   RescoreArgs rs{};
@@ -357,17 +378,18 @@ extern "C" {
 dsa_status dsa_prefill_score_fp8(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
                                  const int64_t *key_off, int64_t off_ld, int32_t n_req, const int32_t *ctx_len,
                                  const uint8_t *q, const float *q_scale, const float *w, const int32_t *q_req,
-                                 const int32_t *row_len, int32_t n_q, float *scores, int64_t ld, float *bound,
-                                 void *workspace, size_t workspace_bytes, int32_t *err_flag, dsa_stream_t stream) {
+                                 const int32_t *row_len, int32_t n_q, int32_t k, float *scores, int64_t ld,
+                                 float *bound, void *workspace, size_t workspace_bytes, int32_t *err_flag,
+                                 dsa_stream_t stream) {
   PrefillCarve c{};
-  const dsa_status st = prefill_common(layout, pool, pool_bytes, key_off, off_ld, n_req, q_req, row_len, n_q, 1,
+  const dsa_status st = prefill_common(layout, pool, pool_bytes, key_off, off_ld, n_req, q_req, row_len, n_q, k,
                                        scores, ld, workspace, workspace_bytes, err_flag, &c);
   if (st != DSA_OK || n_q == 0) return st;
   if (!ctx_len || !q || !q_scale || !w) return DSA_ERR_NULL_ARG;
   if (!aligned(q, 16) || !aligned(ctx_len, 4) || !aligned(q_scale, 4) || !aligned(w, 4) || !aligned(bound, 4))
     return DSA_ERR_MISALIGNED;
   return launched(prefill_score(layout, pool, pool_bytes, key_off, off_ld, n_req, ctx_len, q, q_scale, w, q_req,
-                                row_len, n_q, scores, ld, bound, workspace, c, err_flag, stream_of(stream)));
+                                row_len, n_q, k, scores, ld, bound, workspace, c, err_flag, stream_of(stream)));
 }
 
 dsa_status dsa_prefill_topk_band(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
@@ -404,7 +426,7 @@ dsa_status dsa_prefill_select(const dsa_layout *layout, const uint8_t *pool, int
       !aligned(idx, 4))
     return DSA_ERR_MISALIGNED;
   const hipStream_t hs = stream_of(stream);
-  if (prefill_score(layout, pool, pool_bytes, key_off, off_ld, n_req, ctx_len, q, q_scale, w, q_req, row_len, n_q,
+  if (prefill_score(layout, pool, pool_bytes, key_off, off_ld, n_req, ctx_len, q, q_scale, w, q_req, row_len, n_q, k,
                     scores, ld, bound, workspace, c, err_flag, hs) != hipSuccess)
     return DSA_ERR_HIP;
   return launched(prefill_topk(pool, pool_bytes, key_off, off_ld, n_req, q_req, row_len, n_q, k, scores, ld, idx,

@@ -104,6 +104,11 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Its inverse (the float whose key is k).
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 __device__ __forceinline__ void flag_error(int32_t *err, uint32_t bits) {
   if (err) atomicOr(err, (int32_t)bits);
 }

@@ -49,6 +49,29 @@ hipError_t launch_indexer_scan(const ScoreArgs &a, hipStream_t s);  // bf16 quer
 hipError_t launch_indexer_gemm(const ScoreArgs &a, hipStream_t s);  // e4m3 queries
 size_t indexer_gemm_workspace_bytes(int32_t n_q);
 
+// Candidates straight from the FP8 prefill GEMM (rows of at most kTileModeMaxLd tokens): the
+// GEMM appends each row's scores at or above its threshold to one list per 256-token tile, in
+// token order; the threshold comes from kSampleTiles tiles per 32-row block scored first.
+constexpr int kTileTokens = 256;
+constexpr int kTileCap = 32;
+constexpr int kTileModeMaxLd = 1024 * kTileTokens;
+constexpr int kSampleTiles = 16;
+// Sampled tile i < kSampleTiles of a row block whose longest row (row_len clamped to
+// [0, ld]) is lmax; -1 if the block has fewer tiles than that.
+__host__ __device__ inline int sample_tile(int i, int64_t lmax) {
+  const int nt = (int)((lmax + kTileTokens - 1) / kTileTokens);
+  if (nt <= kSampleTiles) return i < nt ? i : -1;
+  return (int)(((int64_t)(2 * i + 1) * nt) / (2 * kSampleTiles));
+}
+size_t topk_tile_workspace_bytes(int32_t n_rows, int64_t ld);
+struct TileLists {      // the GEMM's view of the top-k workspace in tile mode
+  uint32_t *est;        // [n_rows] threshold keys (written by the tile-est kernel)
+  uint32_t *cnt;        // [n_rows][n_tiles]
+  uint2 *cand;          // [n_rows][n_tiles][kTileCap]
+  int32_t n_tiles, k;   // n_tiles = ceil(ld / 256); k of the top-k
+};
+TileLists tile_lists(void *ws, int32_t n_rows, int64_t ld, int32_t k);
+
 // Prefill indexer on FP8 MFMA (indexer_gemm_fp8.hip): its inputs for the exact rescoring and
 // the error bound, carved from the caller's workspace.
 //
@@ -68,9 +91,15 @@ struct PrefillWs {
   float *mreq;   // [n_req][16] M_bg: the same over the request's pages
   float *bound;      // [n_q] E_r
   float *bound_out;  // [n_q] a copy of E_r for the caller (may be NULL)
+  TileLists tiles;   // tile mode: the candidate lists the GEMM appends to (tiles.cand NULL: off)
 };
 hipError_t launch_indexer_gemm_fp8(const ScoreArgs &a, const PrefillWs &ws, const int32_t *ctx_len, int32_t max_pages,
                                    hipStream_t s);
+// Tile mode, in order: the pre-pass, key bound and the GEMM over the sampled tiles only
+// (sample = true), then (after launch_topk_tile_est) the GEMM over every tile with the
+// candidate lists (sample = false).
+hipError_t launch_indexer_gemm_fp8_phase(const ScoreArgs &a, const PrefillWs &ws, const int32_t *ctx_len,
+                                         int32_t max_pages, bool sample, hipStream_t s);
 
 // Speculative-verify decode: m rows per request share each key page read.
 constexpr int kVerifyMaxRows = 8;
@@ -115,6 +144,7 @@ struct BandWs {
   uint2 *pos;      // [n_rows][kBandCap]: (list position, token) of each band token
 };
 
+
 struct TopkArgs {
   const float *scores;
   int64_t ld;
@@ -133,8 +163,10 @@ struct TopkArgs {
   const int32_t *bt;     // [n_req][bt_ld]; a row longer than 64 bt_ld flags DSA_DEVERR_ROW_LEN
   int64_t bt_ld, pool_rows;
   BandWs band;           // band mode (band.e != NULL; no physical rows)
+  int32_t tile_mode;     // band mode with the lists written by the FP8 GEMM (ld <= kTileModeMaxLd)
 };
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);            // band mode: the first pass
+hipError_t launch_topk_tile_est(const TopkArgs &a, hipStream_t s);   // tile mode: thresholds from the sampled tiles
 hipError_t launch_topk_band_select(const TopkArgs &a, hipStream_t s);  // band mode: the second pass
 
 struct RescoreArgs {

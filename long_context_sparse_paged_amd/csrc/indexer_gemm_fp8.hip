@@ -179,21 +179,44 @@ __global__ __launch_bounds__(256) void key_bound_reduce_kernel(const ScoreArgs a
 }
 
 // ---- GEMM ----
+// MODE 0: every tile.  MODE 1: only the kSampleTiles sampled tiles of each row block (the
+// scores the tile-est kernel draws thresholds from).  MODE 2: every tile, and each long row's
+// scores at or above its threshold are appended, in token order, to the row's list for the
+// tile (the lists the band top-k selects from instead of re-reading the scores).
+template <int MODE>
 __global__ __launch_bounds__(256, 2) void indexer_gemm_fp8_kernel(const ScoreArgs a, const int n_tok_tiles,
                                                                   PrefillWs ws, const int32_t *ctx_len) {
   // query tiles (e4m3 codes) are double buffered four heads at a time; buffer 1 shares its LDS
   // with the key pages, which are read only once per tile (to load the key fragments)
   __shared__ __align__(16) uint8_t s_q0[kGroup * kHeadTileB];   // [head of the group][row][128 B], swizzled
-  __shared__ __align__(16) uint8_t s_pg[kGWaves * kPageLds];    // key pages, then query buffer 1
+  __shared__ __align__(16) uint8_t s_pg[kGWaves * kPageLds];    // key pages, then query buffer 1, then scores
   __shared__ __align__(16) float s_w[kIdxHeads][kGRows];        // s_j, [head][row]
   __shared__ int s_len[kGRows];
+  __shared__ float s_ef[kGRows];   // MODE 2: each row's threshold as a float
+  __shared__ uint32_t s_emit;      // MODE 2: rows that keep lists
+  __shared__ int s_pok[kGWaves];   // MODE 2: the wave's page was read
 
-  const int tile = blockIdx.x % n_tok_tiles;
-  const int rb = blockIdx.x / n_tok_tiles, row0 = rb * kGRows;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
   const int64_t max_tok = a.ld < a.off_ld * kPage ? a.ld : a.off_ld * kPage;
-  const bool report = tile == 0;
+  int tile, rb;
+  if constexpr (MODE == 1) {
+    rb = blockIdx.x / kSampleTiles;
+    // the block's longest row, clamped to [0, ld] (the tile-est kernel computes the same)
+    uint32_t lm = 0u;
+    if (lane < kGRows && rb * kGRows + lane < a.n_q) {
+      const int64_t l = a.row_len[rb * kGRows + lane];
+      lm = (uint32_t)(l < 0 ? 0 : (l > a.ld ? a.ld : l));
+    }
+    lm = wave_max_u32(lm);
+    tile = sample_tile(blockIdx.x % kSampleTiles, lm);
+    if (tile < 0 || (int64_t)tile * kGTokWG >= max_tok) return;  // nothing in flight yet
+  } else {
+    tile = blockIdx.x % n_tok_tiles;
+    rb = blockIdx.x / n_tok_tiles;
+  }
+  const int row0 = rb * kGRows;
+  const bool report = MODE == 1 ? blockIdx.x % kSampleTiles == 0 : tile == 0;
 
   typedef void __attribute__((address_space(1))) gvoid;
   typedef void __attribute__((address_space(3))) lvoid;
@@ -244,6 +267,22 @@ __global__ __launch_bounds__(256, 2) void indexer_gemm_fp8_kernel(const ScoreArg
       }
     }
     if (wid == 0) s_len[lane] = my_len;
+  }
+  if constexpr (MODE == 2) {
+    // rows that keep lists: a valid request, longer than the top-k selects whole and than k
+    const bool emit = lane < kGRows && my_req >= 0 && my_len > kShortRow && ws.tiles.k < my_len;
+    const uint32_t em = (uint32_t)__ballot(emit);
+    if (wid == 0 && lane < kGRows) {
+      const int r = row0 + lane;
+      if (emit) {
+        const uint32_t est = ws.tiles.est[r];
+        s_ef[lane] = est == 0u ? -INFINITY : key_score(est);
+      }
+      // an emitting row's count for this tile is written below unless the tile lies past it
+      if (r < a.n_q && (!emit || (int64_t)tile * kGTokWG >= my_len))
+        ws.tiles.cnt[(int64_t)r * ws.tiles.n_tiles + tile] = 0u;
+      if (lane == 0) s_emit = em;
+    }
   }
   uint32_t todo = (uint32_t)__ballot(lane < kGRows && my_req >= 0);
   bool first = true;
@@ -431,12 +470,107 @@ __global__ __launch_bounds__(256, 2) void indexer_gemm_fp8_kernel(const ScoreArg
         }
       }
     }
+    if constexpr (MODE == 2) {
+      const uint32_t em = s_emit & rows;  // this request's rows that keep lists (uniform)
+      if (em) {
+        // (5) the tile's scores to LDS as [32 rows][256 tokens] (the page region is free once
+        // the last head group's barrier has passed)
+        float *sl = reinterpret_cast<float *>(s_pg);
+        if (lane == 0) s_pok[wid] = page_ok ? 1 : 0;
+        if (page_ok) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const float hk = 0.5f * fabsf(ks[c]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              sl[(8 * (i >> 2) + 4 * h + (i & 3)) * kGTokWG + kPage * wid + 32 * c + n] = hk * acc[c][i];
+          }
+        }
+        __syncthreads();
+        // (6) thread (row m, segment g) takes tokens 32g .. 32g + 31 of the tile: the ones at or
+        // above the row's threshold, ranked through a scan over the row's eight segments
+        const int m = tid >> 3, g = tid & 7;
+        const int t0 = tile * kGTokWG + 32 * g;
+        uint32_t mask = 0u;
+        if (((em >> m) & 1u) && s_pok[g >> 1]) {
+          const float ef = s_ef[m];
+          const int lm = s_len[m];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const f32x4_t v = *reinterpret_cast<const f32x4_t *>(&sl[m * kGTokWG + 32 * g + 4 * q]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (t0 + 4 * q + e < lm && !(v[e] < ef)) mask |= 1u << (4 * q + e);
+          }
+        }
+        const int cnt = __popc(mask);
+        int incl = cnt;
+#pragma unroll
+        for (int dd = 1; dd < 8; dd <<= 1) {
+          const int o = __shfl_up(incl, dd, 8);
+          if (g >= dd) incl += o;
+        }
+        const int total = __shfl(incl, 7, 8);
+        if ((em >> m) & 1u) {
+          const int r = row0 + m;
+          uint2 *dst = ws.tiles.cand + ((int64_t)r * ws.tiles.n_tiles + tile) * kTileCap;
+          int pos = incl - cnt;
+          while (mask) {
+            const int bpos = __ffs(mask) - 1;
+            mask &= mask - 1u;
+            if (pos < kTileCap) dst[pos] = make_uint2(score_key(sl[m * kGTokWG + 32 * g + bpos]), (uint32_t)(t0 + bpos));
+            ++pos;
+          }
+          if (g == 7) ws.tiles.cnt[(int64_t)r * ws.tiles.n_tiles + tile] = (uint32_t)total;
+        }
+      }
+    }
     __syncthreads();
   }
   if (first) __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 }  // namespace
+
+namespace {
+
+hipError_t prepass(const ScoreArgs &a, const PrefillWs &ws, const int32_t *ctx_len, int32_t max_pages, hipStream_t s) {
+  hipLaunchKernelGGL(indexer_qprep_fp8_kernel, dim3(a.n_q), dim3(256), 0, s, a, ws);
+  if (a.n_req > 0) {
+    if (max_pages > 0)
+      hipLaunchKernelGGL(key_bound_kernel, dim3((max_pages + 3) / 4, a.n_req), dim3(256), 0, s, a, ws, ctx_len,
+                         max_pages);
+    hipLaunchKernelGGL(key_bound_reduce_kernel, dim3(a.n_req), dim3(256), 0, s, a, ws, max_pages);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_indexer_gemm_fp8_phase(const ScoreArgs &a, const PrefillWs &ws, const int32_t *ctx_len,
+                                         int32_t max_pages, bool sample, hipStream_t s) {
+  if (a.n_q == 0) return hipSuccess;
+  if (a.key_fmt != 0 || ws.tiles.cand == nullptr) return hipErrorInvalidValue;
+  const int64_t max_tok = a.ld < a.off_ld * kPage ? a.ld : a.off_ld * kPage;
+  const int64_t n_tok_tiles = (max_tok + kGTokWG - 1) / kGTokWG;
+  const int64_t n_row_blocks = (a.n_q + kGRows - 1) / kGRows;
+  // the lists have one entry per 256 tokens of ld: the page table must cover ld
+  if (n_tok_tiles != ws.tiles.n_tiles || max_pages < 0 || max_pages > a.off_ld || a.n_req > 65535 ||
+      n_tok_tiles * n_row_blocks > 0x7FFFFFFF)
+    return hipErrorInvalidValue;
+  if ((int64_t)kGRows * a.ld * 4 > 0x7FFFFFFF) return hipErrorInvalidValue;  // 32-bit store offsets
+  if (sample) {
+    const hipError_t e = prepass(a, ws, ctx_len, max_pages, s);
+    if (e != hipSuccess || n_tok_tiles == 0) return e;
+    hipLaunchKernelGGL(indexer_gemm_fp8_kernel<1>, dim3((unsigned)(n_row_blocks * kSampleTiles)), dim3(256), 0, s, a,
+                       (int)n_tok_tiles, ws, ctx_len);
+  } else {
+    if (n_tok_tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(indexer_gemm_fp8_kernel<2>, dim3((unsigned)(n_row_blocks * n_tok_tiles)), dim3(256), 0, s, a,
+                       (int)n_tok_tiles, ws, ctx_len);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_indexer_gemm_fp8(const ScoreArgs &a, const PrefillWs &ws, const int32_t *ctx_len, int32_t max_pages,
                                    hipStream_t s) {
@@ -448,15 +582,9 @@ hipError_t launch_indexer_gemm_fp8(const ScoreArgs &a, const PrefillWs &ws, cons
   const int64_t grid = n_tok_tiles * n_row_blocks;
   if (grid > 0x7FFFFFFF || max_pages < 0 || max_pages > a.off_ld || a.n_req > 65535) return hipErrorInvalidValue;
   if ((int64_t)kGRows * a.ld * 4 > 0x7FFFFFFF) return hipErrorInvalidValue;  // 32-bit store offsets
-  hipLaunchKernelGGL(indexer_qprep_fp8_kernel, dim3(a.n_q), dim3(256), 0, s, a, ws);
-  if (a.n_req > 0) {
-    if (max_pages > 0)
-      hipLaunchKernelGGL(key_bound_kernel, dim3((max_pages + 3) / 4, a.n_req), dim3(256), 0, s, a, ws, ctx_len,
-                         max_pages);
-    hipLaunchKernelGGL(key_bound_reduce_kernel, dim3(a.n_req), dim3(256), 0, s, a, ws, max_pages);
-  }
-  if (grid == 0) return hipGetLastError();
-  hipLaunchKernelGGL(indexer_gemm_fp8_kernel, dim3((unsigned)grid), dim3(256), 0, s, a, (int)n_tok_tiles, ws, ctx_len);
+  const hipError_t e = prepass(a, ws, ctx_len, max_pages, s);
+  if (e != hipSuccess || grid == 0) return e;
+  hipLaunchKernelGGL(indexer_gemm_fp8_kernel<0>, dim3((unsigned)grid), dim3(256), 0, s, a, (int)n_tok_tiles, ws, ctx_len);
   return hipGetLastError();
 }
 

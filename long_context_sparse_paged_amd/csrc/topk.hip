@@ -61,13 +61,15 @@ constexpr int kFinPer = kShortRow / kFinThreads + 1;  // 25: candidates a finali
 
 struct TopkWs {
   uint32_t *est;  // [n_rows]
-  uint32_t *cnt;  // [n_rows][n_slices] candidates of the slice (may exceed kSliceCap)
-  uint2 *cand;    // [n_rows][n_slices][kSliceCap] (key, index)
+  uint32_t *cnt;  // [n_rows][n_slices] candidates of the slice (may exceed cap)
+  uint2 *cand;    // [n_rows][n_slices][cap] (key, index)
+  int slice, cap; // tokens per slice, list entries per slice: kSlice, kSliceCap (collect) or
+                  // kTileTokens, kTileCap (lists written by the FP8 prefill GEMM)
 };
 
 __host__ __device__ inline int64_t align16(int64_t x) { return (x + 15) & ~int64_t(15); }
 
-__host__ __device__ inline TopkWs carve(void *ws, int32_t n_rows, int32_t n_slices) {
+__host__ __device__ inline TopkWs carve(void *ws, int32_t n_rows, int32_t n_slices, int slice, int cap) {
   uint8_t *p = static_cast<uint8_t *>(ws);
   TopkWs w;
   w.est = reinterpret_cast<uint32_t *>(p);
@@ -75,6 +77,8 @@ __host__ __device__ inline TopkWs carve(void *ws, int32_t n_rows, int32_t n_slic
   w.cnt = reinterpret_cast<uint32_t *>(p);
   p += align16(4 * (int64_t)n_rows * n_slices);
   w.cand = reinterpret_cast<uint2 *>(p);
+  w.slice = slice;
+  w.cap = cap;
   return w;
 }
 
@@ -99,11 +103,8 @@ __device__ __forceinline__ int row_len_of(const TopkArgs &a, int r) {
   return len;
 }
 
-// Band mode helpers.  key_score inverts score_key; key_floor / key_ceil give the key of the
-// largest float <= v / smallest float >= v, so thresholds computed in fp64 round outward.
-__device__ __forceinline__ float key_score(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
+// Band mode helpers.  key_floor / key_ceil give the key of the largest float <= v / smallest
+// float >= v, so thresholds computed in fp64 round outward.
 __device__ __forceinline__ uint32_t key_floor(double v) {
   float f = (float)v;
   if ((double)f > v) f = nextafterf(f, -INFINITY);
@@ -691,19 +692,20 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
   // When rows may be long, one round trip loads the row's length, the slice counts and,
   // speculatively, the first B entries of every slice's candidate list (B: a power of two,
   // B x n_slices <= NT x kSpec).  None of these addresses depends on the length, and all
-  // are in bounds for every row: the lists are kSliceCap long, and entries past a slice's
+  // are in bounds for every row: the lists are w.cap long, and entries past a slice's
   // count (or the whole of a short row's lists) are read but not used.
   const uint32_t *cnt = w.cnt + (int64_t)r * n_slices;
-  const uint2 *cand = w.cand + (int64_t)r * n_slices * kSliceCap;
+  const int cap = w.cap;
+  const uint2 *cand = w.cand + (int64_t)r * n_slices * cap;
   int lgB = 3;  // B = 8 keeps B x n_slices <= NT x kSpec up to kMaxSlices = 1024 slices
-  while ((2 << lgB) * n_slices <= NT * kSpec && (2 << lgB) <= kSliceCap) ++lgB;
+  while ((2 << lgB) * n_slices <= NT * kSpec && (2 << lgB) <= cap) ++lgB;
   uint2 e[kSpec];
   int c_first = 0;  // count of slice tid
   if (a.ld > kShortRow) {  // uniform
 #pragma unroll
     for (int q = 0; q < kSpec; ++q) {
       const int x = tid + NT * q, s = x >> lgB, j = x & ((1 << lgB) - 1);
-      e[q] = s < n_slices ? cand[(int64_t)s * kSliceCap + j] : make_uint2(0u, 0u);
+      e[q] = s < n_slices ? cand[(int64_t)s * cap + j] : make_uint2(0u, 0u);
     }
     c_first = tid < n_slices ? (int)cnt[tid] : 0;
   }
@@ -782,7 +784,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
     for (int s0 = 0; s0 < n_slices; s0 += NT) {
       const int s = s0 + tid;
       const int c = s0 == 0 ? c_first : s < n_slices ? (int)cnt[s] : 0;
-      if (c > kSliceCap) atomicOr(&s_flag, 1);
+      if (c > cap) atomicOr(&s_flag, 1);
       else if (c > (1 << lgB)) atomicOr(&s_flag, 2);
       int total;
       const int incl = block_scan_incl<NT>(c, R.tmp, total);
@@ -806,7 +808,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
       for (int q = 0; q < kSpec; ++q) {
         const int x = tid + NT * q, s = x >> lgB, j = x & ((1 << lgB) - 1);
         const int c = sb1[q] - sb0[q];
-        if (s < n_slices && c <= kSliceCap && j < c) {
+        if (s < n_slices && c <= cap && j < c) {
           s_key[sb0[q] + j] = e[q].x;
           s_idx[sb0[q] + j] = (int32_t)e[q].y;
         }
@@ -819,7 +821,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
         for (int s0 = 0; s0 < n_slices; s0 += NT) {
           const int s = s0 + tid;
           const int c = s < n_slices ? s_base[s + 1] - s_base[s] : 0;
-          const int x = c > B && c <= kSliceCap ? c - B : 0;
+          const int x = c > B && c <= cap ? c - B : 0;
           int total;
           const int incl = block_scan_incl<NT>(x, R.tmp, total);
           if (s < n_slices) s_xbase[s] = xrun + incl - x;
@@ -851,7 +853,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
             const bool v = p < xrun;
             const int lo = v ? sl[q] : 0, j = v ? B + p - s_xbase[lo] : 0;
             dst[q] = v ? s_base[lo] + j : -1;
-            f[q] = cand[(int64_t)lo * kSliceCap + j];
+            f[q] = cand[(int64_t)lo * cap + j];
           }
 #pragma unroll
           for (int q = 0; q < kXBatch; ++q) {
@@ -866,8 +868,8 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
         const uint32_t est = w.est[r];
         const float ef = est == 0u ? -INFINITY : key_score(est);
         for (int s = 0; s < n_slices; ++s) {
-          if (s_base[s + 1] - s_base[s] <= kSliceCap) continue;  // uniform
-          const int beg = s * kSlice, end = min(len, beg + kSlice);
+          if (s_base[s + 1] - s_base[s] <= cap) continue;  // uniform
+          const int beg = s * w.slice, end = min(len, beg + w.slice);
           int written = s_base[s];
           for (int c0 = beg; c0 < end; c0 += NT) {
             const int i = c0 + tid;
@@ -1022,7 +1024,97 @@ __global__ __launch_bounds__(kFinThreads) void topk_band_select_kernel(const Top
   for (int i = keff + tid; i < a.k; i += NT) out[i] = -1;
 }
 
+// Tile mode: the threshold of each long row from its block's sampled tiles (which the GEMM
+// scored first): the m-th largest of the row's sampled keys, by the sample rank rule, lowered
+// by 2 E_r.  One workgroup per row; thread t holds 16 scores of sampled tile t / 16.
+__global__ __launch_bounds__(256) void topk_tile_est_kernel(const TopkArgs a, TopkWs w) {
+  __shared__ RadixLds<256> R;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int len = row_len_of(a, r);
+  const int keff = min(a.k, len);
+  if (len <= kShortRow || keff >= len) {  // the row's lists are not used
+    if (tid == 0) w.est[r] = 0u;
+    return;
+  }
+  // the block's longest row, as the GEMM's sample launch computes it
+  const int r0 = r & ~31;
+  uint32_t lm = 0u;
+  if (tid < 32 && r0 + tid < a.n_rows) {
+    const int64_t l = a.row_len[r0 + tid];
+    lm = (uint32_t)(l < 0 ? 0 : (l > a.ld ? a.ld : l));
+  }
+  lm = wave_max_u32(lm);  // wave 0's lanes hold the 32 rows
+  __shared__ uint32_t s_lm;
+  if (tid == 0) s_lm = lm;
+  __syncthreads();
+  const int64_t lmax = s_lm;
+  const int i = tid >> 4, part = tid & 15;
+  const int tl = sample_tile(i, lmax);
+  const float *row = a.scores + (int64_t)r * a.ld;
+  uint32_t sk[16];
+  int valid = 0;
+  const int t0 = tl * kTileTokens + 16 * part;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) sk[q] = 0u;
+  if (tl >= 0 && t0 < len) {
+    valid = min(16, len - t0);
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      if (q < valid) sk[q] = score_key(row[t0 + q]);
+  }
+  int S;
+  block_scan_incl<256>(valid, R.tmp, S);
+  uint32_t est = 0u;
+  const int m = sample_rank(keff, len, max(S, 1));
+  if (S >= 64 && m < S) {
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      if (q < valid) {
+        lo = min(lo, sk[q]);
+        hi = max(hi, sk[q]);
+      }
+    block_minmax<256>(lo, hi, R);
+    int gt;
+    est = radix_select<256>(
+        [&](auto f) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q)
+            if (q < valid) f(sk[q]);
+        },
+        m, lo, hi, kEstPasses, R, gt);
+  }
+  if (tid == 0) w.est[r] = band_est(a, r, est);
+}
+
 }  // namespace
+
+hipError_t launch_topk_tile_est(const TopkArgs &a, hipStream_t s) {
+  if (a.n_rows == 0) return hipSuccess;
+  const int n_tiles = (int)((a.ld + kTileTokens - 1) / kTileTokens);
+  if (a.band.e == nullptr || n_tiles > kMaxSlices || a.n_rows > 65535) return hipErrorInvalidValue;
+  const TopkWs w = carve(a.ws, a.n_rows, n_tiles, kTileTokens, kTileCap);
+  hipLaunchKernelGGL(topk_tile_est_kernel, dim3(a.n_rows), dim3(256), 0, s, a, w);
+  return hipGetLastError();
+}
+
+size_t topk_tile_workspace_bytes(int32_t n_rows, int64_t ld) {
+  const int64_t n_tiles = (ld + kTileTokens - 1) / kTileTokens;
+  return (size_t)(align16(4 * (int64_t)n_rows) + align16(4 * (int64_t)n_rows * n_tiles) +
+                  8 * (int64_t)n_rows * n_tiles * kTileCap);
+}
+
+TileLists tile_lists(void *ws, int32_t n_rows, int64_t ld, int32_t k) {
+  const int n_tiles = (int)((ld + kTileTokens - 1) / kTileTokens);
+  const TopkWs w = carve(ws, n_rows, n_tiles, kTileTokens, kTileCap);
+  TileLists t;
+  t.est = w.est;
+  t.cnt = w.cnt;
+  t.cand = w.cand;
+  t.n_tiles = n_tiles;
+  t.k = k;
+  return t;
+}
 
 size_t topk_workspace_bytes(int32_t n_rows, int64_t ld) {
   const int64_t n_slices = (ld + kSlice - 1) / kSlice;
@@ -1032,9 +1124,16 @@ size_t topk_workspace_bytes(int32_t n_rows, int64_t ld) {
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
   if (a.n_rows == 0) return hipSuccess;
+  if (a.tile_mode) {  // the GEMM wrote the lists and the thresholds: the band's first pass only
+    const int n_tiles = (int)((a.ld + kTileTokens - 1) / kTileTokens);
+    if (a.band.e == nullptr || n_tiles > kMaxSlices || a.n_rows > 65535) return hipErrorInvalidValue;
+    const TopkWs w = carve(a.ws, a.n_rows, n_tiles, kTileTokens, kTileCap);
+    hipLaunchKernelGGL(topk_finalize_kernel<true>, dim3(a.n_rows), dim3(kFinThreads), 0, s, a, w, n_tiles);
+    return hipGetLastError();
+  }
   const int n_slices = (int)((a.ld + kSlice - 1) / kSlice);
   if (n_slices > kMaxSlices || a.n_rows > 65535) return hipErrorInvalidValue;
-  const TopkWs w = carve(a.ws, a.n_rows, n_slices);
+  const TopkWs w = carve(a.ws, a.n_rows, n_slices, kSlice, kSliceCap);
   if (a.ld > kShortRow) {
     if (a.ld <= kOwnMaxLd && a.n_rows <= kOwnMaxRows) {
       hipLaunchKernelGGL(topk_collect_kernel<true>, dim3(n_slices, a.n_rows), dim3(256), 0, s, a, w, n_slices);

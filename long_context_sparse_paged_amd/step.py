@@ -250,7 +250,8 @@ class PrefillSelectStep(PrefillStep):
         """First half of select(): the FP8 MFMA scores and their bound."""
         c, pq = self.cache, self.pq
         dsa_prefill_score_fp8(self.layout, c.pool, self.key_off, c.n_req, c.ctx_len, pq.q_idx_fp8, pq.q_idx_scale,
-                              pq.w, pq.q_req, pq.row_len, self.scores, self.ws_select, self.bound, self.err, stream)
+                              pq.w, pq.q_req, pq.row_len, self.k, self.scores, self.ws_select, self.bound, self.err,
+                              stream)
 
     def topk(self, stream=None):
         """Second half of select(): the exact top-k (band rescored)."""

@@ -101,11 +101,13 @@ def test_prefill_select_errors(d):
     assert f(*a) == d.DSA_OK
     # the halves: the same checks
     h = d.lib.dsa_prefill_score_fp8
-    hargs = [C.byref(L), FAKE, 1 << 30, FAKE, off_ld, n_req, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n_q, FAKE, ld, None,
-             FAKE, need, None, None]
+    hargs = [C.byref(L), FAKE, 1 << 30, FAKE, off_ld, n_req, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n_q, k, FAKE, ld,
+             None, FAKE, need, None, None]
     a = list(hargs); a[6] = None
     assert h(*a) == d.DSA_ERR_NULL_ARG
-    a = list(hargs); a[17] = need - 1
+    a = list(hargs); a[13] = 0      # k
+    assert h(*a) == d.DSA_ERR_BAD_SHAPE
+    a = list(hargs); a[18] = need - 1
     assert h(*a) == d.DSA_ERR_WORKSPACE_TOO_SMALL
     a = list(hargs); a[0] = C.byref(Lm)
     assert h(*a) == d.DSA_ERR_UNSUPPORTED

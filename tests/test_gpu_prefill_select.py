@@ -155,7 +155,8 @@ def prefill_case(d, prefix, chunk, seed, k=2048, key_hook=None, q_gen=None):
 
 
 def test_select_equals_four_call_path(d):
-    """Long rows (sample + collect + band finalize), several row blocks, a ragged last block."""
+    """Long rows (candidate lists written by the GEMM from a threshold drawn from sampled tiles,
+    then the band's passes), several row blocks, a ragged last block."""
     c = prefill_case(d, 30000, 100, seed=11)
     c.check()
 
@@ -346,7 +347,7 @@ def test_halves_equal_select(d):
     ws = torch.empty_like(c.ws)
     n_req = cache.block_table.shape[0]
     d.dsa_prefill_score_fp8(c.layout, cache.pool, c.key_off, n_req, cache.ctx_len, c.codes, c.qs, c.w, c.q_req,
-                            c.row_len, s2, ws, b2, err)
+                            c.row_len, c.k, s2, ws, b2, err)
     d.dsa_prefill_topk_band(c.layout, cache.pool, c.key_off, n_req, c.q_req, c.row_len, c.k, s2, i2, ws, err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
@@ -355,3 +356,10 @@ def test_halves_equal_select(d):
     rl = c.row_len.cpu().numpy()
     for r, L in enumerate(rl):
         assert torch.equal(s2[r, :L].view(torch.int32), c.s[r, :L].view(torch.int32))
+
+
+def test_select_long_rows_sample_and_collect(d):
+    """Rows past 2^18 tokens: the GEMM does not write candidate lists and the band top-k samples
+    and collects from the score matrix instead; the same exactness."""
+    c = prefill_case(d, 290000, 40, seed=91)
+    c.check()
