@@ -363,3 +363,10 @@ def test_select_long_rows_sample_and_collect(d):
     and collects from the score matrix instead; the same exactness."""
     c = prefill_case(d, 290000, 40, seed=91)
     c.check()
+
+
+@pytest.mark.parametrize("k", [1, 7, 4096])
+def test_select_k_extremes_long_rows(d, k):
+    """k = 1, 7 and 4096 on rows long enough for the GEMM-written candidate lists."""
+    c = prefill_case(d, 24000, 35, seed=100 + k, k=k)
+    c.check()
