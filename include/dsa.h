@@ -18,7 +18,8 @@
  *                             through the block table (no separate resolve)
  *   dsa_sparse_mla_decode_phys  attention over physical rows
  * The prefill indexer on FP8 MFMA with an exact top-k (a band of tokens rescored exactly):
- *   dsa_prefill_select        = dsa_prefill_score_fp8 + dsa_prefill_topk_band
+ *   dsa_prefill_select        = dsa_prefill_score_fp8 (= dsa_prefill_prepare_fp8 +
+ *                               dsa_prefill_gemm_fp8) + dsa_prefill_topk_band
  * and, for decode context parallelism emulated on one GPU:
  *   dsa_dcp_topk              the exact top-k merge across token shards
  *
@@ -219,6 +220,21 @@ dsa_status dsa_prefill_score_fp8(const dsa_layout *layout, const uint8_t *pool, 
                                  const int32_t *row_len, int32_t n_q, int32_t k, float *scores, int64_t ld,
                                  float *bound, void *workspace, size_t workspace_bytes, int32_t *err_flag,
                                  dsa_stream_t stream);
+/* dsa_prefill_score_fp8 in its two parts, same arguments, called in this order: the pre-pass,
+ * the key bound and (candidate-list mode) the sampled tiles and thresholds; then the full
+ * GEMM.  Together they enqueue exactly what dsa_prefill_score_fp8 does. */
+dsa_status dsa_prefill_prepare_fp8(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                                   const int64_t *key_off, int64_t off_ld, int32_t n_req, const int32_t *ctx_len,
+                                   const uint8_t *q, const float *q_scale, const float *w, const int32_t *q_req,
+                                   const int32_t *row_len, int32_t n_q, int32_t k, float *scores, int64_t ld,
+                                   float *bound, void *workspace, size_t workspace_bytes, int32_t *err_flag,
+                                   dsa_stream_t stream);
+dsa_status dsa_prefill_gemm_fp8(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                                const int64_t *key_off, int64_t off_ld, int32_t n_req, const int32_t *ctx_len,
+                                const uint8_t *q, const float *q_scale, const float *w, const int32_t *q_req,
+                                const int32_t *row_len, int32_t n_q, int32_t k, float *scores, int64_t ld,
+                                float *bound, void *workspace, size_t workspace_bytes, int32_t *err_flag,
+                                dsa_stream_t stream);
 dsa_status dsa_prefill_topk_band(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
                                  const int64_t *key_off, int64_t off_ld, int32_t n_req, const int32_t *q_req,
                                  const int32_t *row_len, int32_t n_q, int32_t k, float *scores, int64_t ld,

@@ -40,7 +40,7 @@ __all__ = [
     "dsa_dcp_topk_workspace_size", "dsa_dcp_topk", "dsa_sparse_mla_decode_noalloc",
     "dsa_indexer_select_workspace_size", "dsa_indexer_select", "dsa_sparse_mla_decode_phys",
     "dsa_indexer_score_pages", "dsa_topk_pages", "dsa_prefill_select_workspace_size", "dsa_prefill_select",
-    "dsa_prefill_score_fp8", "dsa_prefill_topk_band",
+    "dsa_prefill_score_fp8", "dsa_prefill_topk_band", "dsa_prefill_prepare_fp8", "dsa_prefill_gemm_fp8",
 ]
 
 
@@ -90,6 +90,8 @@ def _load():
         "dsa_prefill_select": ([LP, P, I64, P, I64, I32, P, P, P, P, P, P, I32, I32, P, I64, P, I64, P, P, SZ, P, P],
                                I32),
         "dsa_prefill_score_fp8": ([LP, P, I64, P, I64, I32, P, P, P, P, P, P, I32, I32, P, I64, P, P, SZ, P, P], I32),
+        "dsa_prefill_prepare_fp8": ([LP, P, I64, P, I64, I32, P, P, P, P, P, P, I32, I32, P, I64, P, P, SZ, P, P], I32),
+        "dsa_prefill_gemm_fp8": ([LP, P, I64, P, I64, I32, P, P, P, P, P, P, I32, I32, P, I64, P, P, SZ, P, P], I32),
         "dsa_prefill_topk_band": ([LP, P, I64, P, I64, I32, P, P, I32, I32, P, I64, P, I64, P, SZ, P, P], I32),
         "dsa_sparse_mla_prefill_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
         "dsa_dcp_topk_workspace_size": ([I32, I32, I32, C.POINTER(SZ)], I32),
@@ -248,18 +250,33 @@ def dsa_prefill_select(layout: dsa_layout, pool, key_off, n_req: int, ctx_len, q
     _check("dsa_prefill_select", st)
 
 
-def dsa_prefill_score_fp8(layout: dsa_layout, pool, key_off, n_req: int, ctx_len, q, q_scale, w, q_req, row_len,
-                          k: int, scores, workspace, bound=None, err_flag=None, stream=None):
-    """First half of dsa_prefill_select: FP8 MFMA scores (within bound[r] of the exact ones)."""
-    st = lib.dsa_prefill_score_fp8(C.byref(layout), _ptr(pool, U8, "pool"), pool.numel(),
-                                   _ptr(key_off, I64, "key_off"), key_off.shape[1], n_req,
-                                   _ptr(ctx_len, I32, "ctx_len"), _ptr(q, U8, "q"), _ptr(q_scale, F32, "q_scale"),
-                                   _ptr(w, F32, "w"), _ptr(q_req, I32, "q_req"), _ptr(row_len, I32, "row_len"),
-                                   row_len.shape[0], k, _ptr(scores, F32, "scores"), scores.shape[1],
-                                   _ptr(bound, F32, "bound"), _ptr(workspace, None, "workspace"),
-                                   workspace.numel() * workspace.element_size(), _ptr(err_flag, I32, "err_flag"),
-                                   _stream(stream))
-    _check("dsa_prefill_score_fp8", st)
+def _prefill_score_call(name: str, layout: dsa_layout, pool, key_off, n_req: int, ctx_len, q, q_scale, w, q_req,
+                        row_len, k: int, scores, workspace, bound=None, err_flag=None, stream=None):
+    st = getattr(lib, name)(C.byref(layout), _ptr(pool, U8, "pool"), pool.numel(), _ptr(key_off, I64, "key_off"),
+                            key_off.shape[1], n_req, _ptr(ctx_len, I32, "ctx_len"), _ptr(q, U8, "q"),
+                            _ptr(q_scale, F32, "q_scale"), _ptr(w, F32, "w"), _ptr(q_req, I32, "q_req"),
+                            _ptr(row_len, I32, "row_len"), row_len.shape[0], k, _ptr(scores, F32, "scores"),
+                            scores.shape[1], _ptr(bound, F32, "bound"), _ptr(workspace, None, "workspace"),
+                            workspace.numel() * workspace.element_size(), _ptr(err_flag, I32, "err_flag"),
+                            _stream(stream))
+    _check(name, st)
+
+
+def dsa_prefill_score_fp8(*args, **kw):
+    """First half of dsa_prefill_select: FP8 MFMA scores (within bound[r] of the exact ones).
+    Arguments: layout, pool, key_off, n_req, ctx_len, q, q_scale, w, q_req, row_len, k, scores,
+    workspace, bound=None, err_flag=None, stream=None."""
+    _prefill_score_call("dsa_prefill_score_fp8", *args, **kw)
+
+
+def dsa_prefill_prepare_fp8(*args, **kw):
+    """dsa_prefill_score_fp8's first part: pre-pass, key bound, sampled tiles and thresholds."""
+    _prefill_score_call("dsa_prefill_prepare_fp8", *args, **kw)
+
+
+def dsa_prefill_gemm_fp8(*args, **kw):
+    """dsa_prefill_score_fp8's second part: the full FP8 GEMM (and its candidate lists)."""
+    _prefill_score_call("dsa_prefill_gemm_fp8", *args, **kw)
 
 
 def dsa_prefill_topk_band(layout: dsa_layout, pool, key_off, n_req: int, q_req, row_len, k: int, scores, idx,

@@ -305,12 +305,23 @@ TopkArgs prefill_topk_args(const int32_t *row_len, int32_t n_q, int32_t k, float
   return t;
 }
 
-hipError_t prefill_score(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes, const int64_t *key_off,
-                         int64_t off_ld, int32_t n_req, const int32_t *ctx_len, const uint8_t *q, const float *q_scale,
-                         const float *w, const int32_t *q_req, const int32_t *row_len, int32_t n_q, int32_t k,
-                         float *scores, int64_t ld, float *bound, void *workspace, const PrefillCarve &c,
-                         int32_t *err_flag, hipStream_t hs) {
-  ScoreArgs a{};
+// The score half in two parts: prepare (the pre-pass, the key bound and, in tile mode, the
+// sampled tiles and the thresholds) and the full GEMM.
+struct PrefillScoreCall {
+  ScoreArgs a;
+  PrefillWs pw;
+  TopkArgs t;
+  int32_t max_pages;
+  bool tile;
+};
+
+PrefillScoreCall prefill_score_call(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                                    const int64_t *key_off, int64_t off_ld, int32_t n_req, const uint8_t *q,
+                                    const float *q_scale, const float *w, const int32_t *q_req,
+                                    const int32_t *row_len, int32_t n_q, int32_t k, float *scores, int64_t ld,
+                                    float *bound, void *workspace, const PrefillCarve &c, int32_t *err_flag) {
+  PrefillScoreCall p{};
+  ScoreArgs &a = p.a;
   a.pool = pool;
   a.pool_bytes = pool_bytes;
   a.key_off = key_off;
@@ -327,19 +338,26 @@ hipError_t prefill_score(const dsa_layout *layout, const uint8_t *pool, int64_t 
   a.err = err_flag;
   a.key_fmt = layout->key_fmt;
   a.q_fmt = DSA_Q_FP8_E4M3;
-  PrefillWs pw = prefill_ws(workspace, c);
-  pw.bound_out = bound;
+  p.pw = prefill_ws(workspace, c);
+  p.pw.bound_out = bound;
   const int64_t pages_ld = (ld + kPage - 1) / kPage;  // pages a row of ld tokens spans (<= 131072)
-  const int32_t max_pages = (int32_t)(off_ld < pages_ld ? off_ld : pages_ld);
-  if (!prefill_tile_mode(ld, off_ld)) return launch_indexer_gemm_fp8(a, pw, ctx_len, max_pages, hs);
-  // tile mode: the sampled tiles, the thresholds, then every tile with the candidate lists
-  const TopkArgs t = prefill_topk_args(row_len, n_q, k, scores, ld, nullptr, k, off_ld, workspace, c, err_flag);
-  pw.tiles = tile_lists(t.ws, n_q, ld, k);
-  hipError_t e = launch_indexer_gemm_fp8_phase(a, pw, ctx_len, max_pages, true, hs);
+  p.max_pages = (int32_t)(off_ld < pages_ld ? off_ld : pages_ld);
+  p.tile = prefill_tile_mode(ld, off_ld);
+  p.t = prefill_topk_args(row_len, n_q, k, scores, ld, nullptr, k, off_ld, workspace, c, err_flag);
+  if (p.tile) p.pw.tiles = tile_lists(p.t.ws, n_q, ld, k);
+  return p;
+}
+
+hipError_t prefill_prepare(const PrefillScoreCall &p, const int32_t *ctx_len, hipStream_t hs) {
+  hipError_t e = launch_fp8_prepass(p.a, p.pw, ctx_len, p.max_pages, hs);
+  if (e != hipSuccess || !p.tile) return e;
+  e = launch_fp8_gemm(p.a, p.pw, ctx_len, 1, hs);
   if (e != hipSuccess) return e;
-  e = launch_topk_tile_est(t, hs);
-  if (e != hipSuccess) return e;
-  return launch_indexer_gemm_fp8_phase(a, pw, ctx_len, max_pages, false, hs);
+  return launch_topk_tile_est(p.t, hs);
+}
+
+hipError_t prefill_gemm(const PrefillScoreCall &p, const int32_t *ctx_len, hipStream_t hs) {
+  return launch_fp8_gemm(p.a, p.pw, ctx_len, p.tile ? 2 : 0, hs);
 }
 
 hipError_t prefill_topk(const uint8_t *pool, int64_t pool_bytes, const int64_t *key_off, int64_t off_ld, int32_t n_req,
@@ -375,12 +393,15 @@ hipError_t prefill_topk(const uint8_t *pool, int64_t pool_bytes, const int64_t *
 
 extern "C" {
 
-dsa_status dsa_prefill_score_fp8(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
-                                 const int64_t *key_off, int64_t off_ld, int32_t n_req, const int32_t *ctx_len,
-                                 const uint8_t *q, const float *q_scale, const float *w, const int32_t *q_req,
-                                 const int32_t *row_len, int32_t n_q, int32_t k, float *scores, int64_t ld,
-                                 float *bound, void *workspace, size_t workspace_bytes, int32_t *err_flag,
-                                 dsa_stream_t stream) {
+namespace {
+enum class ScorePart { kAll, kPrepare, kGemm };
+
+dsa_status prefill_score_entry(ScorePart part, const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                               const int64_t *key_off, int64_t off_ld, int32_t n_req, const int32_t *ctx_len,
+                               const uint8_t *q, const float *q_scale, const float *w, const int32_t *q_req,
+                               const int32_t *row_len, int32_t n_q, int32_t k, float *scores, int64_t ld,
+                               float *bound, void *workspace, size_t workspace_bytes, int32_t *err_flag,
+                               dsa_stream_t stream) {
   PrefillCarve c{};
   const dsa_status st = prefill_common(layout, pool, pool_bytes, key_off, off_ld, n_req, q_req, row_len, n_q, k,
                                        scores, ld, workspace, workspace_bytes, err_flag, &c);
@@ -388,8 +409,46 @@ dsa_status dsa_prefill_score_fp8(const dsa_layout *layout, const uint8_t *pool, 
   if (!ctx_len || !q || !q_scale || !w) return DSA_ERR_NULL_ARG;
   if (!aligned(q, 16) || !aligned(ctx_len, 4) || !aligned(q_scale, 4) || !aligned(w, 4) || !aligned(bound, 4))
     return DSA_ERR_MISALIGNED;
-  return launched(prefill_score(layout, pool, pool_bytes, key_off, off_ld, n_req, ctx_len, q, q_scale, w, q_req,
-                                row_len, n_q, k, scores, ld, bound, workspace, c, err_flag, stream_of(stream)));
+  const PrefillScoreCall p = prefill_score_call(layout, pool, pool_bytes, key_off, off_ld, n_req, q, q_scale, w, q_req,
+                                                row_len, n_q, k, scores, ld, bound, workspace, c, err_flag);
+  const hipStream_t hs = stream_of(stream);
+  if (part != ScorePart::kGemm && prefill_prepare(p, ctx_len, hs) != hipSuccess) return DSA_ERR_HIP;
+  if (part != ScorePart::kPrepare && prefill_gemm(p, ctx_len, hs) != hipSuccess) return DSA_ERR_HIP;
+  return DSA_OK;
+}
+}  // namespace
+
+dsa_status dsa_prefill_score_fp8(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                                 const int64_t *key_off, int64_t off_ld, int32_t n_req, const int32_t *ctx_len,
+                                 const uint8_t *q, const float *q_scale, const float *w, const int32_t *q_req,
+                                 const int32_t *row_len, int32_t n_q, int32_t k, float *scores, int64_t ld,
+                                 float *bound, void *workspace, size_t workspace_bytes, int32_t *err_flag,
+                                 dsa_stream_t stream) {
+  return prefill_score_entry(ScorePart::kAll, layout, pool, pool_bytes, key_off, off_ld, n_req, ctx_len, q, q_scale,
+                             w, q_req, row_len, n_q, k, scores, ld, bound, workspace, workspace_bytes, err_flag,
+                             stream);
+}
+
+dsa_status dsa_prefill_prepare_fp8(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                                   const int64_t *key_off, int64_t off_ld, int32_t n_req, const int32_t *ctx_len,
+                                   const uint8_t *q, const float *q_scale, const float *w, const int32_t *q_req,
+                                   const int32_t *row_len, int32_t n_q, int32_t k, float *scores, int64_t ld,
+                                   float *bound, void *workspace, size_t workspace_bytes, int32_t *err_flag,
+                                   dsa_stream_t stream) {
+  return prefill_score_entry(ScorePart::kPrepare, layout, pool, pool_bytes, key_off, off_ld, n_req, ctx_len, q,
+                             q_scale, w, q_req, row_len, n_q, k, scores, ld, bound, workspace, workspace_bytes,
+                             err_flag, stream);
+}
+
+dsa_status dsa_prefill_gemm_fp8(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
+                                const int64_t *key_off, int64_t off_ld, int32_t n_req, const int32_t *ctx_len,
+                                const uint8_t *q, const float *q_scale, const float *w, const int32_t *q_req,
+                                const int32_t *row_len, int32_t n_q, int32_t k, float *scores, int64_t ld,
+                                float *bound, void *workspace, size_t workspace_bytes, int32_t *err_flag,
+                                dsa_stream_t stream) {
+  return prefill_score_entry(ScorePart::kGemm, layout, pool, pool_bytes, key_off, off_ld, n_req, ctx_len, q, q_scale,
+                             w, q_req, row_len, n_q, k, scores, ld, bound, workspace, workspace_bytes, err_flag,
+                             stream);
 }
 
 dsa_status dsa_prefill_topk_band(const dsa_layout *layout, const uint8_t *pool, int64_t pool_bytes,
@@ -426,8 +485,9 @@ dsa_status dsa_prefill_select(const dsa_layout *layout, const uint8_t *pool, int
       !aligned(idx, 4))
     return DSA_ERR_MISALIGNED;
   const hipStream_t hs = stream_of(stream);
-  if (prefill_score(layout, pool, pool_bytes, key_off, off_ld, n_req, ctx_len, q, q_scale, w, q_req, row_len, n_q, k,
-                    scores, ld, bound, workspace, c, err_flag, hs) != hipSuccess)
+  const PrefillScoreCall p = prefill_score_call(layout, pool, pool_bytes, key_off, off_ld, n_req, q, q_scale, w, q_req,
+                                                row_len, n_q, k, scores, ld, bound, workspace, c, err_flag);
+  if (prefill_prepare(p, ctx_len, hs) != hipSuccess || prefill_gemm(p, ctx_len, hs) != hipSuccess)
     return DSA_ERR_HIP;
   return launched(prefill_topk(pool, pool_bytes, key_off, off_ld, n_req, q_req, row_len, n_q, k, scores, ld, idx,
                                idx_ld, workspace, c, err_flag, hs));

@@ -93,13 +93,12 @@ struct PrefillWs {
   float *bound_out;  // [n_q] a copy of E_r for the caller (may be NULL)
   TileLists tiles;   // tile mode: the candidate lists the GEMM appends to (tiles.cand NULL: off)
 };
-hipError_t launch_indexer_gemm_fp8(const ScoreArgs &a, const PrefillWs &ws, const int32_t *ctx_len, int32_t max_pages,
-                                   hipStream_t s);
-// Tile mode, in order: the pre-pass, key bound and the GEMM over the sampled tiles only
-// (sample = true), then (after launch_topk_tile_est) the GEMM over every tile with the
-// candidate lists (sample = false).
-hipError_t launch_indexer_gemm_fp8_phase(const ScoreArgs &a, const PrefillWs &ws, const int32_t *ctx_len,
-                                         int32_t max_pages, bool sample, hipStream_t s);
+// The FP8 prefill indexer: the pre-pass and key bound, then the GEMM -- mode 0 every tile,
+// mode 1 the sampled tiles only, mode 2 every tile with the candidate lists (tile mode:
+// mode 1, then launch_topk_tile_est, then mode 2).
+hipError_t launch_fp8_prepass(const ScoreArgs &a, const PrefillWs &ws, const int32_t *ctx_len, int32_t max_pages,
+                              hipStream_t s);
+hipError_t launch_fp8_gemm(const ScoreArgs &a, const PrefillWs &ws, const int32_t *ctx_len, int mode, hipStream_t s);
 
 // Speculative-verify decode: m rows per request share each key page read.
 constexpr int kVerifyMaxRows = 8;

@@ -532,9 +532,10 @@ __global__ __launch_bounds__(256, 2) void indexer_gemm_fp8_kernel(const ScoreArg
 
 }  // namespace
 
-namespace {
-
-hipError_t prepass(const ScoreArgs &a, const PrefillWs &ws, const int32_t *ctx_len, int32_t max_pages, hipStream_t s) {
+hipError_t launch_fp8_prepass(const ScoreArgs &a, const PrefillWs &ws, const int32_t *ctx_len, int32_t max_pages,
+                              hipStream_t s) {
+  if (a.n_q == 0) return hipSuccess;
+  if (a.key_fmt != 0 || max_pages < 0 || max_pages > a.off_ld || a.n_req > 65535) return hipErrorInvalidValue;
   hipLaunchKernelGGL(indexer_qprep_fp8_kernel, dim3(a.n_q), dim3(256), 0, s, a, ws);
   if (a.n_req > 0) {
     if (max_pages > 0)
@@ -545,46 +546,26 @@ hipError_t prepass(const ScoreArgs &a, const PrefillWs &ws, const int32_t *ctx_l
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_indexer_gemm_fp8_phase(const ScoreArgs &a, const PrefillWs &ws, const int32_t *ctx_len,
-                                         int32_t max_pages, bool sample, hipStream_t s) {
+hipError_t launch_fp8_gemm(const ScoreArgs &a, const PrefillWs &ws, const int32_t *ctx_len, int mode, hipStream_t s) {
   if (a.n_q == 0) return hipSuccess;
-  if (a.key_fmt != 0 || ws.tiles.cand == nullptr) return hipErrorInvalidValue;
+  if (a.key_fmt != 0 || mode < 0 || mode > 2) return hipErrorInvalidValue;
   const int64_t max_tok = a.ld < a.off_ld * kPage ? a.ld : a.off_ld * kPage;
   const int64_t n_tok_tiles = (max_tok + kGTokWG - 1) / kGTokWG;
   const int64_t n_row_blocks = (a.n_q + kGRows - 1) / kGRows;
-  // the lists have one entry per 256 tokens of ld: the page table must cover ld
-  if (n_tok_tiles != ws.tiles.n_tiles || max_pages < 0 || max_pages > a.off_ld || a.n_req > 65535 ||
-      n_tok_tiles * n_row_blocks > 0x7FFFFFFF)
-    return hipErrorInvalidValue;
+  if (n_tok_tiles * n_row_blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   if ((int64_t)kGRows * a.ld * 4 > 0x7FFFFFFF) return hipErrorInvalidValue;  // 32-bit store offsets
-  if (sample) {
-    const hipError_t e = prepass(a, ws, ctx_len, max_pages, s);
-    if (e != hipSuccess || n_tok_tiles == 0) return e;
+  // the lists have one entry per 256 tokens of ld: the page table must cover ld
+  if (mode != 0 && (ws.tiles.cand == nullptr || n_tok_tiles != ws.tiles.n_tiles)) return hipErrorInvalidValue;
+  if (n_tok_tiles == 0) return hipSuccess;
+  if (mode == 0)
+    hipLaunchKernelGGL(indexer_gemm_fp8_kernel<0>, dim3((unsigned)(n_row_blocks * n_tok_tiles)), dim3(256), 0, s, a,
+                       (int)n_tok_tiles, ws, ctx_len);
+  else if (mode == 1)
     hipLaunchKernelGGL(indexer_gemm_fp8_kernel<1>, dim3((unsigned)(n_row_blocks * kSampleTiles)), dim3(256), 0, s, a,
                        (int)n_tok_tiles, ws, ctx_len);
-  } else {
-    if (n_tok_tiles == 0) return hipSuccess;
+  else
     hipLaunchKernelGGL(indexer_gemm_fp8_kernel<2>, dim3((unsigned)(n_row_blocks * n_tok_tiles)), dim3(256), 0, s, a,
                        (int)n_tok_tiles, ws, ctx_len);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_indexer_gemm_fp8(const ScoreArgs &a, const PrefillWs &ws, const int32_t *ctx_len, int32_t max_pages,
-                                   hipStream_t s) {
-  if (a.n_q == 0) return hipSuccess;
-  if (a.key_fmt != 0) return hipErrorInvalidValue;
-  const int64_t max_tok = a.ld < a.off_ld * kPage ? a.ld : a.off_ld * kPage;
-  const int64_t n_tok_tiles = (max_tok + kGTokWG - 1) / kGTokWG;
-  const int64_t n_row_blocks = (a.n_q + kGRows - 1) / kGRows;
-  const int64_t grid = n_tok_tiles * n_row_blocks;
-  if (grid > 0x7FFFFFFF || max_pages < 0 || max_pages > a.off_ld || a.n_req > 65535) return hipErrorInvalidValue;
-  if ((int64_t)kGRows * a.ld * 4 > 0x7FFFFFFF) return hipErrorInvalidValue;  // 32-bit store offsets
-  const hipError_t e = prepass(a, ws, ctx_len, max_pages, s);
-  if (e != hipSuccess || grid == 0) return e;
-  hipLaunchKernelGGL(indexer_gemm_fp8_kernel<0>, dim3((unsigned)grid), dim3(256), 0, s, a, (int)n_tok_tiles, ws, ctx_len);
   return hipGetLastError();
 }
 

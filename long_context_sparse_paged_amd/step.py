@@ -17,8 +17,8 @@ import torch
 
 from . import (DSA_Q_BF16, DSA_Q_FP8_E4M3, dsa_indexer_score, dsa_indexer_score_pages, dsa_indexer_score_verify,
                dsa_indexer_score_workspace_size, dsa_indexer_select, dsa_indexer_select_workspace_size,
-               dsa_layout_make, dsa_prefill_score_fp8, dsa_prefill_select, dsa_prefill_select_workspace_size,
-               dsa_prefill_topk_band, dsa_resolve_pages,
+               dsa_layout_make, dsa_prefill_gemm_fp8, dsa_prefill_prepare_fp8, dsa_prefill_score_fp8,
+               dsa_prefill_select, dsa_prefill_select_workspace_size, dsa_prefill_topk_band, dsa_resolve_pages,
                dsa_sparse_mla_decode, dsa_sparse_mla_decode_phys, dsa_sparse_mla_decode_workspace_size,
                dsa_sparse_mla_prefill, dsa_sparse_mla_prefill_workspace_size, dsa_topk, dsa_topk_pages,
                dsa_topk_workspace_size)
@@ -246,12 +246,22 @@ class PrefillSelectStep(PrefillStep):
                            pq.q_req, pq.row_len, self.k, self.scores, self.idx, self.ws_select, self.bound, self.err,
                            stream)
 
+    def _score_args(self):
+        c, pq = self.cache, self.pq
+        return (self.layout, c.pool, self.key_off, c.n_req, c.ctx_len, pq.q_idx_fp8, pq.q_idx_scale, pq.w, pq.q_req,
+                pq.row_len, self.k, self.scores, self.ws_select, self.bound, self.err)
+
     def score(self, stream=None):
         """First half of select(): the FP8 MFMA scores and their bound."""
-        c, pq = self.cache, self.pq
-        dsa_prefill_score_fp8(self.layout, c.pool, self.key_off, c.n_req, c.ctx_len, pq.q_idx_fp8, pq.q_idx_scale,
-                              pq.w, pq.q_req, pq.row_len, self.k, self.scores, self.ws_select, self.bound, self.err,
-                              stream)
+        dsa_prefill_score_fp8(*self._score_args(), stream)
+
+    def prepare(self, stream=None):
+        """score()'s first part: pre-pass, key bound, sampled tiles and thresholds."""
+        dsa_prefill_prepare_fp8(*self._score_args(), stream)
+
+    def gemm(self, stream=None):
+        """score()'s second part: the full FP8 GEMM."""
+        dsa_prefill_gemm_fp8(*self._score_args(), stream)
 
     def topk(self, stream=None):
         """Second half of select(): the exact top-k (band rescored)."""

@@ -370,3 +370,27 @@ def test_select_k_extremes_long_rows(d, k):
     """k = 1, 7 and 4096 on rows long enough for the GEMM-written candidate lists."""
     c = prefill_case(d, 24000, 35, seed=100 + k, k=k)
     c.check()
+
+
+def test_score_parts_equal_score_half(d):
+    """dsa_prefill_prepare_fp8 then dsa_prefill_gemm_fp8 (then the band top-k): the same as the
+    one call, bit for bit."""
+    c = prefill_case(d, 27000, 36, seed=82)
+    cache = c.cache
+    s2 = torch.full_like(c.s, float("nan"))
+    i2 = torch.full_like(c.idx, -7)
+    b2 = torch.full_like(c.bound, float("nan"))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty_like(c.ws)
+    n_req = cache.block_table.shape[0]
+    args = (c.layout, cache.pool, c.key_off, n_req, cache.ctx_len, c.codes, c.qs, c.w, c.q_req, c.row_len, c.k, s2, ws,
+            b2, err)
+    d.dsa_prefill_prepare_fp8(*args)
+    d.dsa_prefill_gemm_fp8(*args)
+    d.dsa_prefill_topk_band(c.layout, cache.pool, c.key_off, n_req, c.q_req, c.row_len, c.k, s2, i2, ws, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert torch.equal(i2, c.idx)
+    assert torch.equal(b2.view(torch.int32), c.bound.view(torch.int32))
+    for r, L in enumerate(c.row_len.cpu().numpy()):
+        assert torch.equal(s2[r, :L].view(torch.int32), c.s[r, :L].view(torch.int32))
