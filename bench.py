@@ -479,7 +479,7 @@ def summarize_stats(argv):
 
 # dominant kernel of each workload and the sources its traffic figures depend on
 DOMINANT = {w: ("indexer_scan_kernel", ["indexer_scan.hip", "dsa_device.hpp"]) for w in ("decode", "long", "mixed")}
-DOMINANT["prefill"] = ("indexer_gemm_fp8_kernel", ["indexer_gemm_fp8.hip", "dsa_device.hpp"])
+DOMINANT["prefill"] = ("indexer_gemm_fp8_kernel<2>", ["indexer_gemm_fp8.hip", "dsa_device.hpp"])
 DOMINANT["verify"] = ("indexer_verify_kernel", ["indexer_verify.hip", "dsa_device.hpp"])
 
 

@@ -263,7 +263,9 @@ __global__ __launch_bounds__(256, 2) void indexer_gemm_kernel(const ScoreArgs a,
       __syncthreads();
     }
 
-    // (4) store ks * acc: element i is row 8*(i/4) + 4h + i%4, token wtok0 + 32c + n
+    // (4) store ks * acc: element i is row 8*(i/4) + 4h + i%4, token wtok0 + 32c + n.  The
+    // stores are non-temporal, so that the scores streaming out do not evict from L2 the key
+    // pages the next row blocks read again
     if (page_ok) {
       // row addresses are formed here, not hoisted out of the request loop where 16 of
       // them would hold 32 VGPRs through the head loop
@@ -287,12 +289,12 @@ __global__ __launch_bounds__(256, 2) void indexer_gemm_kernel(const ScoreArgs a,
 #pragma unroll
           for (int i = 0; i < 16; ++i)
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ks[c] * acc[c][i]), ors, voff,
-                                                  4 * (8 * (i >> 2) + (i & 3)) * ld32, 0);
+                                                  4 * (8 * (i >> 2) + (i & 3)) * ld32, 2 /* nt */);
         } else {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int m = 8 * (i >> 2) + h4 + (i & 3);
-            if (((rws >> m) & 1u) && t < s_len[m]) out[m * ld + t] = ks[c] * acc[c][i];
+            if (((rws >> m) & 1u) && t < s_len[m]) __builtin_nontemporal_store(ks[c] * acc[c][i], &out[m * ld + t]);
           }
         }
       }

@@ -54,6 +54,9 @@ namespace dsa {
 namespace {
 
 constexpr int kGRows = 32;
+// cache policy of the score stores: non-temporal (the nt bit), so that the scores streaming
+// out do not evict from L2 the key pages the next row blocks read again
+constexpr int kStoreNT = 2;
 constexpr int kGWaves = 4;
 constexpr int kGTokWG = kGWaves * kPage;   // 256
 constexpr int kKB = 132;                   // FP8 key row
@@ -460,12 +463,12 @@ __global__ __launch_bounds__(256, 2) void indexer_gemm_fp8_kernel(const ScoreArg
 #pragma unroll
           for (int i = 0; i < 16; ++i)
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hk * acc[c][i]), ors, voff,
-                                                  4 * (8 * (i >> 2) + (i & 3)) * ld32, 0);
+                                                  4 * (8 * (i >> 2) + (i & 3)) * ld32, kStoreNT);
         } else {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int m = 8 * (i >> 2) + h4 + (i & 3);
-            if (((rws >> m) & 1u) && t < s_len[m]) out[m * ld + t] = hk * acc[c][i];
+            if (((rws >> m) & 1u) && t < s_len[m]) __builtin_nontemporal_store(hk * acc[c][i], &out[m * ld + t]);
           }
         }
       }
