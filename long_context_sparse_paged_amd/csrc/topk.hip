@@ -867,22 +867,32 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
       if (s_flag & 1) {  // slices whose list overflowed: filter them again from the scores
         const uint32_t est = w.est[r];
         const float ef = est == 0u ? -INFINITY : key_score(est);
+        // thread t takes the slice's elements [per t, per t + per): all of its loads in one
+        // round trip, one block scan for the positions (index order is thread order)
+        constexpr int kRePer = kSlice / NT;  // 16: the most elements a thread takes
+        static_assert(kRePer * NT >= kSlice && kTileTokens <= kSlice, "a slice fits one pass");
+        const int per = (w.slice + NT - 1) / NT;
         for (int s = 0; s < n_slices; ++s) {
           if (s_base[s + 1] - s_base[s] <= cap) continue;  // uniform
           const int beg = s * w.slice, end = min(len, beg + w.slice);
-          int written = s_base[s];
-          for (int c0 = beg; c0 < end; c0 += NT) {
-            const int i = c0 + tid;
-            const float x = i < end ? row[i] : 0.0f;
-            const uint32_t key = score_key(x);
-            const bool f = i < end && !(x < ef);  // the same test as collect's
-            int tot;
-            const int pos = written + block_rank<NT>(f, R.tmp, tot);
-            if (f && pos < s_base[s + 1]) {  // the same test as collect's: pos stays in the slice
-              s_key[pos] = key;
-              s_idx[pos] = i;
+          const int i0 = beg + per * tid;
+          float x[kRePer];
+#pragma unroll
+          for (int q = 0; q < kRePer; ++q) x[q] = q < per && i0 + q < end ? row[i0 + q] : 0.0f;
+          int c = 0;
+#pragma unroll
+          for (int q = 0; q < kRePer; ++q) c += q < per && i0 + q < end && !(x[q] < ef) ? 1 : 0;  // collect's test
+          int tot;
+          int pos = s_base[s] + block_scan_incl<NT>(c, R.tmp, tot) - c;
+#pragma unroll
+          for (int q = 0; q < kRePer; ++q) {
+            if (q < per && i0 + q < end && !(x[q] < ef)) {
+              if (pos < s_base[s + 1]) {  // as in collect: positions stay in the slice's range
+                s_key[pos] = score_key(x[q]);
+                s_idx[pos] = i0 + q;
+              }
+              ++pos;
             }
-            written += tot;
           }
         }
       }
