@@ -58,6 +58,8 @@ constexpr int kBinLd = 20;            // ints per bin: 16 copies + 4 pad (80-B r
 constexpr int kEstPasses = 2;         // 16 leading bits of the threshold are enough
 constexpr int kFinThreads = 512;
 constexpr int kFinPer = kShortRow / kFinThreads + 1;  // 25: candidates a finalize thread holds
+constexpr int kMidPer = 64;                           // scores a finalize thread loads for a middle row
+constexpr int kMidRow = kMidPer * kFinThreads;        // 32768: rows filtered whole by the finalize
 
 struct TopkWs {
   uint32_t *est;  // [n_rows]
@@ -774,6 +776,50 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
     }
     n = len;
     ok = true;
+  } else if (len <= kMidRow) {
+    // A row of up to kMidRow scores, where k is a large share of the row and the slices'
+    // lists run long or overflow: filter the whole row against est instead, in index order.
+    // Thread t takes scores [kMidPer t, kMidPer t + kMidPer): every load in one round trip,
+    // one block scan for the positions.
+    const uint32_t est = w.est[r];
+    const float ef = est == 0u ? -INFINITY : key_score(est);
+    const int i0 = kMidPer * tid;
+    float x[kMidPer];
+    if ((reinterpret_cast<uintptr_t>(row) & 15) == 0) {  // uniform
+#pragma unroll
+      for (int q = 0; q < kMidPer; q += 4) {
+        if (i0 + q + 4 <= len) {
+          const float4 v = *reinterpret_cast<const float4 *>(row + i0 + q);
+          x[q] = v.x;
+          x[q + 1] = v.y;
+          x[q + 2] = v.z;
+          x[q + 3] = v.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[q + e] = i0 + q + e < len ? row[i0 + q + e] : 0.0f;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < kMidPer; ++q) x[q] = i0 + q < len ? row[i0 + q] : 0.0f;
+    }
+    int c = 0;
+#pragma unroll
+    for (int q = 0; q < kMidPer; ++q) c += i0 + q < len && !(x[q] < ef) ? 1 : 0;  // collect's test
+    int tot;
+    int pos = block_scan_incl<NT>(c, R.tmp, tot) - c;
+#pragma unroll
+    for (int q = 0; q < kMidPer; ++q) {
+      if (i0 + q < len && !(x[q] < ef)) {
+        if (pos < kShortRow) {
+          s_key[pos] = score_key(x[q]);
+          s_idx[pos] = i0 + q;
+        }
+        ++pos;
+      }
+    }
+    n = tot;
+    ok = n >= keff && n <= kShortRow;
   } else {
     // (len > kShortRow implies ld > kShortRow: e[] and c_first are loaded)
     if (tid == 0) s_flag = 0;
