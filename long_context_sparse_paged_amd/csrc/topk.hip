@@ -58,8 +58,7 @@ constexpr int kBinLd = 20;            // ints per bin: 16 copies + 4 pad (80-B r
 constexpr int kEstPasses = 2;         // 16 leading bits of the threshold are enough
 constexpr int kFinThreads = 512;
 constexpr int kFinPer = kShortRow / kFinThreads + 1;  // 25: candidates a finalize thread holds
-constexpr int kMidPer = 64;                           // scores a finalize thread loads for a middle row
-constexpr int kMidRow = kMidPer * kFinThreads;        // 32768: rows filtered whole by the finalize
+constexpr int kMidRow = 32768;                        // rows the finalize filters whole (64 scores a thread)
 
 struct TopkWs {
   uint32_t *est;  // [n_rows]
@@ -676,6 +675,51 @@ __device__ __forceinline__ bool band_from_regs_any(int per, Args &&...args) {
   return band_from_regs<kFinPer>(args...);
 }
 
+// Ordered filter of scores [beg, end) of `row` against ef (collect's test: kept unless x < ef,
+// so NaNs are kept) into s_key / s_idx from position `base`, keeping positions below `cap_end`;
+// returns how many passed.  Wave w takes the contiguous range beg + 64 PERW w .. + 64 PERW, its
+// lane l the scores 64 j + l of it (coalesced loads, clamped to the row so none is skipped by a
+// branch), ranks come from ballots, and every lane stores: one that does not keep its score
+// writes a pad slot past kShortRow (s_key / s_idx hold kShortRow + 64 entries).  The range must
+// hold at most NT / 64 x 64 PERW scores.
+template <int NT, int PERW>
+__device__ __forceinline__ int filter_append(const float *row, int beg, int end, float ef, uint32_t *s_key,
+                                             int32_t *s_idx, int base, int cap_end, int *tmp) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int w0 = beg + 64 * PERW * wid;
+  float x[PERW];
+#pragma unroll
+  for (int j = 0; j < PERW; ++j) x[j] = row[min(w0 + 64 * j + lane, end - 1)];
+  int cw = 0;
+#pragma unroll
+  for (int j = 0; j < PERW; ++j) cw += __popcll(__ballot(w0 + 64 * j + lane < end && !(x[j] < ef)));
+  if (lane == 0) tmp[wid] = cw;
+  __syncthreads();
+  int run = base, total = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const int t = tmp[v];
+    run += v < wid ? t : 0;
+    total += t;
+  }
+  __syncthreads();
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  const int pad = kShortRow + lane;
+#pragma unroll
+  for (int j = 0; j < PERW; ++j) {
+    const int i = w0 + 64 * j + lane;
+    const bool keep = i < end && !(x[j] < ef);
+    const unsigned long long b = __ballot(keep);
+    const int pos = run + __popcll(b & lt);
+    const int dst = keep && pos < cap_end ? pos : pad;
+    s_key[dst] = score_key(x[j]);
+    s_idx[dst] = i;
+    run += __popcll(b);
+  }
+  return total;
+}
+
 template <bool BAND>
 __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkArgs a, TopkWs w, int n_slices) {
   constexpr int NT = kFinThreads;
@@ -683,8 +727,8 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
   constexpr int kSpec = 16;   // speculative candidate loads per thread
   constexpr int kXBatch = 4;  // loads of entries past B in flight per thread
   static_assert(8 * kMaxSlices <= NT * kSpec, "a speculative share of 8 entries must cover every slice");
-  __shared__ uint32_t s_key[kShortRow];
-  __shared__ int32_t s_idx[kShortRow];
+  __shared__ uint32_t s_key[kShortRow + 64];  // + a pad slot per lane (filter_append)
+  __shared__ int32_t s_idx[kShortRow + 64];
   __shared__ int s_base[kMaxSlices + 1];
   __shared__ int s_xbase[kMaxSlices + 1];
   __shared__ RadixLds<NT> R;
@@ -758,66 +802,28 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
   int n = 0;
   bool ok;
   if (len <= kShortRow) {
+    // loads clamped to the row and stores to a pad slot past the row: no branch per element
     for (int i0 = 0; i0 < len; i0 += NT * kBatch) {
       float x[kBatch];
 #pragma unroll
-      for (int q = 0; q < kBatch; ++q) {
-        const int i = i0 + NT * q + tid;
-        x[q] = i < len ? row[i] : 0.0f;
-      }
+      for (int q = 0; q < kBatch; ++q) x[q] = row[min(i0 + NT * q + tid, len - 1)];
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
         const int i = i0 + NT * q + tid;
-        if (i < len) {
-          s_key[i] = score_key(x[q]);
-          s_idx[i] = i;
-        }
+        const int dst = i < len ? i : kShortRow + (tid & 63);
+        s_key[dst] = score_key(x[q]);
+        s_idx[dst] = i;
       }
     }
     n = len;
     ok = true;
   } else if (len <= kMidRow) {
     // A row of up to kMidRow scores, where k is a large share of the row and the slices'
-    // lists run long or overflow: filter the whole row against est instead, in index order.
-    // Thread t takes scores [kMidPer t, kMidPer t + kMidPer): every load in one round trip,
-    // one block scan for the positions.
+    // lists run long or overflow: filter the whole row against est instead, in index order,
+    // in one round trip.
     const uint32_t est = w.est[r];
     const float ef = est == 0u ? -INFINITY : key_score(est);
-    const int i0 = kMidPer * tid;
-    float x[kMidPer];
-    if ((reinterpret_cast<uintptr_t>(row) & 15) == 0) {  // uniform
-#pragma unroll
-      for (int q = 0; q < kMidPer; q += 4) {
-        if (i0 + q + 4 <= len) {
-          const float4 v = *reinterpret_cast<const float4 *>(row + i0 + q);
-          x[q] = v.x;
-          x[q + 1] = v.y;
-          x[q + 2] = v.z;
-          x[q + 3] = v.w;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[q + e] = i0 + q + e < len ? row[i0 + q + e] : 0.0f;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < kMidPer; ++q) x[q] = i0 + q < len ? row[i0 + q] : 0.0f;
-    }
-    int c = 0;
-#pragma unroll
-    for (int q = 0; q < kMidPer; ++q) c += i0 + q < len && !(x[q] < ef) ? 1 : 0;  // collect's test
-    int tot;
-    int pos = block_scan_incl<NT>(c, R.tmp, tot) - c;
-#pragma unroll
-    for (int q = 0; q < kMidPer; ++q) {
-      if (i0 + q < len && !(x[q] < ef)) {
-        if (pos < kShortRow) {
-          s_key[pos] = score_key(x[q]);
-          s_idx[pos] = i0 + q;
-        }
-        ++pos;
-      }
-    }
+    const int tot = filter_append<NT, kMidRow / NT>(row, 0, len, ef, s_key, s_idx, 0, kShortRow, R.tmp);
     n = tot;
     ok = n >= keff && n <= kShortRow;
   } else {
@@ -913,33 +919,12 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
       if (s_flag & 1) {  // slices whose list overflowed: filter them again from the scores
         const uint32_t est = w.est[r];
         const float ef = est == 0u ? -INFINITY : key_score(est);
-        // thread t takes the slice's elements [per t, per t + per): all of its loads in one
-        // round trip, one block scan for the positions (index order is thread order)
-        constexpr int kRePer = kSlice / NT;  // 16: the most elements a thread takes
-        static_assert(kRePer * NT >= kSlice && kTileTokens <= kSlice, "a slice fits one pass");
-        const int per = (w.slice + NT - 1) / NT;
+        // each overflowing slice in one round trip (filter_append)
+        static_assert(kSlice <= kFinThreads * 16 && kTileTokens <= kSlice, "a slice fits one pass");
         for (int s = 0; s < n_slices; ++s) {
           if (s_base[s + 1] - s_base[s] <= cap) continue;  // uniform
           const int beg = s * w.slice, end = min(len, beg + w.slice);
-          const int i0 = beg + per * tid;
-          float x[kRePer];
-#pragma unroll
-          for (int q = 0; q < kRePer; ++q) x[q] = q < per && i0 + q < end ? row[i0 + q] : 0.0f;
-          int c = 0;
-#pragma unroll
-          for (int q = 0; q < kRePer; ++q) c += q < per && i0 + q < end && !(x[q] < ef) ? 1 : 0;  // collect's test
-          int tot;
-          int pos = s_base[s] + block_scan_incl<NT>(c, R.tmp, tot) - c;
-#pragma unroll
-          for (int q = 0; q < kRePer; ++q) {
-            if (q < per && i0 + q < end && !(x[q] < ef)) {
-              if (pos < s_base[s + 1]) {  // as in collect: positions stay in the slice's range
-                s_key[pos] = score_key(x[q]);
-                s_idx[pos] = i0 + q;
-              }
-              ++pos;
-            }
-          }
+          filter_append<NT, kSlice / NT>(row, beg, end, ef, s_key, s_idx, s_base[s], s_base[s + 1], R.tmp);
         }
       }
     }
