@@ -173,8 +173,9 @@ __device__ __forceinline__ uint32_t bin_total(const int *h, int bin) {
 // strictly larger, using 8-bit digits of key - kmin from the top bit of kmax - kmin down.
 // With max_passes below the number of digits the result is the lower edge of the bin that
 // holds the m-th largest key: at least m keys are >= it.
-// `list` (optional, LDS, list_cap keys): after the first pass the keys of the chosen bin
-// are copied there, and later passes read only those.
+// `list` (optional, LDS, list_cap + 64 keys): after the first pass the keys of the chosen bin
+// are copied there, and later passes read only those.  visit may call f(key, valid) with
+// valid false for a slot that holds no key.
 // The histogram is never cleared: thread t reads bin 255 - t before and after each pass
 // and takes the difference (wrap-around int arithmetic), which is cheaper than clearing
 // 20 KB of LDS per pass.
@@ -195,9 +196,11 @@ __device__ __forceinline__ uint32_t radix_select(Visit visit, int m, uint32_t km
   for (int p = 0; hi >= 0 && p < max_passes; ++p, hi -= 8) {
     const int lo = hi >= 7 ? hi - 7 : 0;
     const uint32_t above = ~((2u << hi) - 1u);  // bits already decided
-    auto count = [&](uint32_t key) {
+    // every key takes an atomic (adding 0 unless it is valid and in the chosen bin so far):
+    // no branch per key
+    auto count = [&](uint32_t key, bool valid = true) {
       const uint32_t u = key - kmin;
-      if ((u & above) == prefix) atomicAdd(&my[((u >> lo) & 255u) * kBinLd], 1);
+      atomicAdd(&my[((u >> lo) & 255u) * kBinLd], valid && (u & above) == prefix ? 1 : 0);
     };
     if (nl >= 0) {
       for (int i = tid; i < nl; i += NT) count(list[i]);
@@ -231,9 +234,18 @@ __device__ __forceinline__ uint32_t radix_select(Visit visit, int m, uint32_t km
     rem -= R.sh[1];
     gt += R.sh[1];
     if (list != nullptr && nl < 0 && lo > 0 && p + 1 < max_passes && R.sh[2] <= list_cap) {
+      // the chosen bin's keys to the list, ranked by a block scan; a key outside the bin is
+      // written to its lane's pad slot past list_cap (no branch per key)
       const uint32_t mask = ~((1u << lo) - 1u);
-      visit([&](uint32_t key) {
-        if (((key - kmin) & mask) == prefix) list[atomicAdd(&R.list_n, 1)] = key;
+      int mine = 0;
+      visit([&](uint32_t key, bool valid = true) { mine += valid && ((key - kmin) & mask) == prefix ? 1 : 0; });
+      int tot;
+      int pos = block_scan_incl<NT>(mine, R.tmp, tot) - mine;
+      const int pad = list_cap + lane;
+      visit([&](uint32_t key, bool valid = true) {
+        const bool in = valid && ((key - kmin) & mask) == prefix;
+        list[in ? pos : pad] = key;
+        pos += in ? 1 : 0;
       });
       __syncthreads();
       nl = R.sh[2];
@@ -513,8 +525,9 @@ __device__ __forceinline__ void compact_rounds(Load load, int n, uint32_t tau, i
 
 // Exact selection and ordered output of keys held in registers: thread t holds cnt keys rk[]
 // whose indices idx_of(q) increase with q, and every key of thread t comes before every key of
-// thread t + 1 in index order.  Keeps the keff largest (ties to the lower index) and emits them
-// ascending as emit(position, index).  `list` (LDS, list_cap keys) is the radix select's list.
+// thread t + 1 in index order.  Keeps the keff largest (ties to the lower index): emit(pos, q,
+// sel) is called for every slot q, and the kept ones (sel) get positions 0 .. keff - 1 in index
+// order.  `list` (LDS, list_cap + 64 keys) is the radix select's list.
 template <int PER, class IdxOf, class Emit>
 __device__ __forceinline__ void select_from_regs(const uint32_t (&rk)[PER], int cnt, IdxOf idx_of, int keff,
                                                  RadixLds<kFinThreads> &R, Emit emit, uint32_t *list,
@@ -523,18 +536,15 @@ __device__ __forceinline__ void select_from_regs(const uint32_t (&rk)[PER], int 
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
-    if (q < cnt) {
-      lo = min(lo, rk[q]);
-      hi = max(hi, rk[q]);
-    }
+    lo = min(lo, q < cnt ? rk[q] : 0xFFFFFFFFu);
+    hi = max(hi, q < cnt ? rk[q] : 0u);
   }
   block_minmax<NT>(lo, hi, R);  // its barriers also end every earlier read of `list`
   int gt;
   const uint32_t tau = radix_select<NT>(
       [&](auto f) {
 #pragma unroll
-        for (int q = 0; q < PER; ++q)
-          if (q < cnt) f(rk[q]);
+        for (int q = 0; q < PER; ++q) f(rk[q], q < cnt);
       },
       keff, lo, hi, 32, R, gt, list, list_cap);
   // ordered compaction: keep key > tau, and the first need_eq keys == tau in index order
@@ -552,21 +562,23 @@ __device__ __forceinline__ void select_from_regs(const uint32_t (&rk)[PER], int 
   int eq_seen = eq_excl;
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
-    if (q < cnt) {
-      bool sel = rk[q] > tau;
-      if (rk[q] == tau) sel = eq_seen++ < need_eq;
-      if (sel) emit(pos++, idx_of(q));
-    }
+    const bool eq = q < cnt && rk[q] == tau;
+    const bool sel = q < cnt && (rk[q] > tau || (eq && eq_seen < need_eq));
+    eq_seen += eq ? 1 : 0;
+    emit(pos, q, sel);
+    pos += sel ? 1 : 0;
   }
 }
 
-// Exact selection and ordered output of the n candidates in s_key / s_idx (index order):
-// thread t holds candidates [t per, t per + cnt) in registers (cnt <= per <= PER).  s_key
-// doubles as the radix select's list once the registers are loaded.  pre(index) is evaluated
-// for every candidate as soon as its index is in a register (its loads fly during the radix
-// passes); each kept candidate is emitted as emit(position, index, pre(index)).
+// Exact selection and ordered output of the n >= 1 candidates in s_key / s_idx (index order;
+// both arrays hold list_cap + 64 entries): thread t holds candidates [t per, t per + cnt) in
+// registers (cnt <= per <= PER).  s_key doubles as the radix select's list once the registers
+// are loaded.  pre(index) is evaluated for every slot as soon as its index is in a register (its
+// loads fly during the radix passes).  The kept (index, pre(index)) pairs are staged in s_idx /
+// s_key at their output positions (a slot not kept writes its lane's pad entry), and written out
+// in order as emit(position, index, pre(index)): no branch per candidate.
 template <int PER, class Pre, class Emit>
-__device__ __forceinline__ void select_write(uint32_t *s_key, const int32_t *s_idx, int n, int per, int keff,
+__device__ __forceinline__ void select_write(uint32_t *s_key, int32_t *s_idx, int n, int per, int keff,
                                              RadixLds<kFinThreads> &R, Pre pre, Emit emit, int list_cap) {
   const int tid = threadIdx.x;
   const int b0 = min(n, tid * per);
@@ -575,19 +587,28 @@ __device__ __forceinline__ void select_write(uint32_t *s_key, const int32_t *s_i
   int32_t ri[PER], pv[PER];
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
-    rk[q] = q < cnt ? s_key[b0 + q] : 0u;
-    ri[q] = q < cnt ? s_idx[b0 + q] : 0;
+    const int j = min(b0 + q, n - 1);  // slots past cnt read a real candidate and are ignored
+    rk[q] = s_key[j];
+    ri[q] = s_idx[j];
   }
 #pragma unroll
-  for (int q = 0; q < PER; ++q) pv[q] = q < cnt ? pre(ri[q]) : 0;
+  for (int q = 0; q < PER; ++q) pv[q] = pre(ri[q]);
+  const int pad = list_cap + (tid & 63);
   select_from_regs<PER>(
-      rk, cnt, [&](int q) { return q; }, keff, R, [&](int pos, int q) { emit(pos, ri[q], pv[q]); }, s_key,
-      list_cap);
+      rk, cnt, [&](int q) { return q; }, keff, R,
+      [&](int pos, int q, bool sel) {
+        const int d = sel ? pos : pad;
+        s_idx[d] = ri[q];
+        s_key[d] = (uint32_t)pv[q];
+      },
+      s_key, list_cap);
+  __syncthreads();
+  for (int i = tid; i < keff; i += kFinThreads) emit(i, s_idx[i], (int32_t)s_key[i]);
 }
 
 // select_write with the register bound picked from a few sizes (per = candidates per thread).
 template <class Pre, class Emit>
-__device__ __forceinline__ void select_write_any(uint32_t *s_key, const int32_t *s_idx, int n, int per, int keff,
+__device__ __forceinline__ void select_write_any(uint32_t *s_key, int32_t *s_idx, int n, int per, int keff,
                                                  RadixLds<kFinThreads> &R, Pre pre, Emit emit,
                                                  int list_cap = kShortRow) {
   if (per <= 5) select_write<5>(s_key, s_idx, n, per, keff, R, pre, emit, list_cap);
@@ -629,8 +650,7 @@ __device__ __forceinline__ bool band_from_regs(uint32_t *s_key, const int32_t *s
   const uint32_t tau = radix_select<NT>(
       [&](auto f) {
 #pragma unroll
-        for (int q = 0; q < PER; ++q)
-          if (q < cnt) f(rk[q]);
+        for (int q = 0; q < PER; ++q) f(rk[q], q < cnt);
       },
       keff, lo, hi, 32, R, gt, s_key, kShortRow);
   const double tv = (double)key_score(tau);
@@ -1020,8 +1040,8 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
 // place -- from the whole score row.
 __global__ __launch_bounds__(kFinThreads) void topk_band_select_kernel(const TopkArgs a) {
   constexpr int NT = kFinThreads;
-  __shared__ uint32_t s_key[kShortRow];
-  __shared__ int32_t s_idx[kShortRow];
+  __shared__ uint32_t s_key[kShortRow + 64];  // + a pad slot per lane (select_write)
+  __shared__ int32_t s_idx[kShortRow + 64];
   __shared__ RadixLds<NT> R;
   const int tid = threadIdx.x, r = blockIdx.x;
   const int len = row_len_of(a, r);
@@ -1120,8 +1140,7 @@ __global__ __launch_bounds__(256) void topk_tile_est_kernel(const TopkArgs a, To
     est = radix_select<256>(
         [&](auto f) {
 #pragma unroll
-          for (int q = 0; q < 16; ++q)
-            if (q < valid) f(sk[q]);
+          for (int q = 0; q < 16; ++q) f(sk[q], q < valid);
         },
         m, lo, hi, kEstPasses, R, gt);
   }
