@@ -625,11 +625,12 @@ __device__ __forceinline__ void select_write_any(uint32_t *s_key, int32_t *s_idx
 // kept tokens (key > hi_key) and the band are written in index order through two block scans
 // and true is returned; otherwise nothing is written and the caller classifies the whole row.
 template <int PER>
-__device__ __forceinline__ bool band_from_regs(uint32_t *s_key, const int32_t *s_idx, int n, int per, int keff,
+__device__ __forceinline__ bool band_from_regs(uint32_t *s_key, int32_t *s_idx, int n, int per, int keff,
                                                double e2, uint32_t est, RadixLds<kFinThreads> &R, uint2 *list,
                                                uint2 *bpos, int &written, int &bw, uint32_t &lo_key,
                                                uint32_t &hi_key) {
   constexpr int NT = kFinThreads;
+  static_assert(kBandListCap + kBandCap <= kShortRow, "the list and the band positions are staged in s_key");
   const int tid = threadIdx.x;
   const int b0 = min(n, tid * per);
   const int cnt = min(n, b0 + per) - b0;
@@ -638,12 +639,11 @@ __device__ __forceinline__ bool band_from_regs(uint32_t *s_key, const int32_t *s
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
-    rk[q] = q < cnt ? s_key[b0 + q] : 0u;
-    ri[q] = q < cnt ? s_idx[b0 + q] : 0;
-    if (q < cnt) {
-      lo = min(lo, rk[q]);
-      hi = max(hi, rk[q]);
-    }
+    const int j = min(b0 + q, n - 1);  // slots past cnt read a real candidate and are ignored
+    rk[q] = s_key[j];
+    ri[q] = s_idx[j];
+    lo = min(lo, q < cnt ? rk[q] : 0xFFFFFFFFu);
+    hi = max(hi, q < cnt ? rk[q] : 0u);
   }
   block_minmax<NT>(lo, hi, R);  // its barriers also end every read of s_key
   int gt;
@@ -668,18 +668,28 @@ __device__ __forceinline__ bool band_from_regs(uint32_t *s_key, const int32_t *s
   int tot, btot;
   int pos = block_scan_incl<NT>(cs, R.tmp, tot) - cs;
   int bp = block_scan_incl<NT>(cb, R.tmp, btot) - cb;
+  // staged in LDS without a branch per candidate: list entry p as (s_key[p] = sure, s_idx[p] =
+  // index), band entry b as its list position in s_key[kBandListCap + b]; a slot that writes
+  // nothing goes to its lane's pad entry.  Then both lists are written out coalesced.
+  const int pad = kShortRow + (tid & 63);
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
     const bool sure = q < cnt && rk[q] > hi_key;
     const bool band = q < cnt && !sure && rk[q] >= lo_key;
-    if (sure || band) {
-      if (pos < kBandListCap) list[pos] = make_uint2(sure ? 0xFFFFFFFFu : 0u, (uint32_t)ri[q]);
-      if (band) {
-        if (bp < kBandCap && pos < kBandListCap) bpos[bp] = make_uint2((uint32_t)pos, (uint32_t)ri[q]);
-        ++bp;
-      }
-      ++pos;
-    }
+    const bool keep = sure || band;
+    const int d = keep && pos < kBandListCap ? pos : pad;
+    s_idx[d] = ri[q];
+    s_key[d] = sure ? 1u : 0u;
+    s_key[band && bp < kBandCap ? kBandListCap + bp : pad] = (uint32_t)pos;
+    pos += keep ? 1 : 0;
+    bp += band ? 1 : 0;
+  }
+  __syncthreads();
+  const int nlw = min(tot, kBandListCap), nbw = min(btot, kBandCap);
+  for (int i = tid; i < nlw; i += NT) list[i] = make_uint2(s_key[i] ? 0xFFFFFFFFu : 0u, (uint32_t)s_idx[i]);
+  for (int i = tid; i < nbw; i += NT) {
+    const int p = (int)s_key[kBandListCap + i];  // a band entry past the list's capacity: none
+    bpos[i] = p < kBandListCap ? make_uint2((uint32_t)p, (uint32_t)s_idx[p]) : make_uint2(0xFFFFFFFFu, 0u);
   }
   written = tot;
   bw = btot;
