@@ -365,6 +365,7 @@ template <bool OWN>
 __global__ __launch_bounds__(256) void topk_collect_kernel(const TopkArgs a, TopkWs w, int n_slices) {
   __shared__ RadixLds<256> R;
   __shared__ __align__(16) int s_tot[8][4];
+  __shared__ __align__(16) uint2 s_app[kSliceCap + 64];  // the slice's list, + a pad entry per lane
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int r = blockIdx.y, s = blockIdx.x;
   const int len = row_len_of(a, r);
@@ -481,6 +482,8 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(const TopkArgs a, Top
   for (int j = 0; j < 8; ++j) tot[j] = *reinterpret_cast<const int4 *>(s_tot[j]);
   const unsigned long long lt = (1ull << lane) - 1ull;
   uint2 *out = w.cand + ((int64_t)r * n_slices + s) * kSliceCap;
+  // the list is staged in LDS without a branch per element (an element not kept writes its
+  // lane's pad entry) and then written out with coalesced 16-B stores
   int base = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -491,12 +494,19 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(const TopkArgs a, Top
     const float f[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if ((bal[j][e] >> lane) & 1ull) {
-        if (rank < kSliceCap) out[rank] = make_uint2(score_key(f[e]), (uint32_t)(i + e));
-        ++rank;
-      }
+      const bool keep = (bal[j][e] >> lane) & 1ull;
+      s_app[keep && rank < kSliceCap ? rank : kSliceCap + lane] = make_uint2(score_key(f[e]), (uint32_t)(i + e));
+      rank += keep ? 1 : 0;
     }
     base += tot[j].x + tot[j].y + tot[j].z + tot[j].w;
+  }
+  __syncthreads();
+  const int n_out = min(base, kSliceCap);
+  for (int i = 2 * tid; i < n_out; i += 512) {
+    if (i + 1 < n_out)
+      *reinterpret_cast<uint4 *>(out + i) = *reinterpret_cast<const uint4 *>(s_app + i);
+    else
+      out[i] = s_app[i];
   }
   if (tid == 0) *my_cnt = (uint32_t)base;
 }
