@@ -1133,16 +1133,12 @@ __global__ __launch_bounds__(256) void topk_tile_est_kernel(const TopkArgs a, To
   const int tl = sample_tile(i, lmax);
   const float *row = a.scores + (int64_t)r * a.ld;
   uint32_t sk[16];
-  int valid = 0;
   const int t0 = tl * kTileTokens + 16 * part;
+  const int valid = tl >= 0 && t0 < len ? min(16, len - t0) : 0;
+  // loads clamped to the row (no branch per element); slots past `valid` are ignored
+  const int tb = tl >= 0 ? t0 : 0;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) sk[q] = 0u;
-  if (tl >= 0 && t0 < len) {
-    valid = min(16, len - t0);
-#pragma unroll
-    for (int q = 0; q < 16; ++q)
-      if (q < valid) sk[q] = score_key(row[t0 + q]);
-  }
+  for (int q = 0; q < 16; ++q) sk[q] = score_key(row[min(tb + q, len - 1)]);
   int S;
   block_scan_incl<256>(valid, R.tmp, S);
   uint32_t est = 0u;
@@ -1150,11 +1146,10 @@ __global__ __launch_bounds__(256) void topk_tile_est_kernel(const TopkArgs a, To
   if (S >= 64 && m < S) {
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
-      if (q < valid) {
-        lo = min(lo, sk[q]);
-        hi = max(hi, sk[q]);
-      }
+    for (int q = 0; q < 16; ++q) {
+      lo = min(lo, q < valid ? sk[q] : 0xFFFFFFFFu);
+      hi = max(hi, q < valid ? sk[q] : 0u);
+    }
     block_minmax<256>(lo, hi, R);
     int gt;
     est = radix_select<256>(
