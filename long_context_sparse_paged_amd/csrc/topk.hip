@@ -896,14 +896,14 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
         sb0[q] = s_base[s];
         sb1[q] = s_base[s + 1];
       }
+      const int pad = kShortRow + (tid & 63);  // where an entry not placed is written
 #pragma unroll
       for (int q = 0; q < kSpec; ++q) {
         const int x = tid + NT * q, s = x >> lgB, j = x & ((1 << lgB) - 1);
         const int c = sb1[q] - sb0[q];
-        if (s < n_slices && c <= cap && j < c) {
-          s_key[sb0[q] + j] = e[q].x;
-          s_idx[sb0[q] + j] = (int32_t)e[q].y;
-        }
+        const int d = s < n_slices && c <= cap && j < c ? sb0[q] + j : pad;
+        s_key[d] = e[q].x;
+        s_idx[d] = (int32_t)e[q].y;
       }
       if (s_flag & 2) {  // lists longer than B: only their entries past the first B
         // x(s) = entries of slice s past B (0 for short and for overflowed lists); the
@@ -949,10 +949,9 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
           }
 #pragma unroll
           for (int q = 0; q < kXBatch; ++q) {
-            if (dst[q] >= 0) {
-              s_key[dst[q]] = f[q].x;
-              s_idx[dst[q]] = (int32_t)f[q].y;
-            }
+            const int d = dst[q] >= 0 ? dst[q] : pad;
+            s_key[d] = f[q].x;
+            s_idx[d] = (int32_t)f[q].y;
           }
         }
       }
