@@ -764,9 +764,10 @@ template <bool BAND>
 __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkArgs a, TopkWs w, int n_slices) {
   constexpr int NT = kFinThreads;
   constexpr int kBatch = 12;  // row-score loads in flight per thread (short rows)
-  constexpr int kSpec = 16;   // speculative candidate loads per thread
+  constexpr int kSpec = 20;   // speculative candidate loads per thread (B = 16 up to 640 slices)
   constexpr int kXBatch = 4;  // loads of entries past B in flight per thread
   static_assert(8 * kMaxSlices <= NT * kSpec, "a speculative share of 8 entries must cover every slice");
+  static_assert(kMaxSlices <= 2 * NT, "the slice counts are loaded two per thread");
   __shared__ uint32_t s_key[kShortRow + 64];  // + a pad slot per lane (filter_append)
   __shared__ int32_t s_idx[kShortRow + 64];
   __shared__ int s_base[kMaxSlices + 1];
@@ -786,7 +787,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
   int lgB = 3;  // B = 8 keeps B x n_slices <= NT x kSpec up to kMaxSlices = 1024 slices
   while ((2 << lgB) * n_slices <= NT * kSpec && (2 << lgB) <= cap) ++lgB;
   uint2 e[kSpec];
-  int c_first = 0;  // count of slice tid
+  int c_first = 0, c_second = 0;  // counts of slices tid and tid + NT (n_slices <= 2 NT)
   if (a.ld > kShortRow) {  // uniform
 #pragma unroll
     for (int q = 0; q < kSpec; ++q) {
@@ -794,6 +795,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
       e[q] = s < n_slices ? cand[(int64_t)s * cap + j] : make_uint2(0u, 0u);
     }
     c_first = tid < n_slices ? (int)cnt[tid] : 0;
+    c_second = tid + NT < n_slices ? (int)cnt[tid + NT] : 0;
   }
   const int len = row_len_of(a, r);
   int32_t *out = a.idx + (int64_t)r * a.idx_ld;
@@ -875,9 +877,10 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
     int run = 0;
     for (int s0 = 0; s0 < n_slices; s0 += NT) {
       const int s = s0 + tid;
-      const int c = s0 == 0 ? c_first : s < n_slices ? (int)cnt[s] : 0;
-      if (c > cap) atomicOr(&s_flag, 1);
-      else if (c > (1 << lgB)) atomicOr(&s_flag, 2);
+      const int c = s0 == 0 ? c_first : s0 == NT ? c_second : s < n_slices ? (int)cnt[s] : 0;
+      // one flag update per wave (a per-thread atomic on one word serialises)
+      const bool ovf = __ballot(c > cap) != 0ull, lng = __ballot(c <= cap && c > (1 << lgB)) != 0ull;
+      if ((tid & 63) == 0 && (ovf || lng)) atomicOr(&s_flag, (ovf ? 1 : 0) | (lng ? 2 : 0));
       int total;
       const int incl = block_scan_incl<NT>(c, R.tmp, total);
       if (s < n_slices) s_base[s] = run + incl - c;
