@@ -1060,10 +1060,14 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(const TopkAr
 // Band mode, second pass (one workgroup per row): the kept tokens from the first pass's list,
 // whose band keys are now exact, or -- for a row whose band overflowed and was rescored in
 // place -- from the whole score row.
-__global__ __launch_bounds__(kFinThreads) void topk_band_select_kernel(const TopkArgs a) {
+// The list arrays are dynamic LDS of cap + 64 entries each (cap = band_select_cap(k): the list
+// is about k entries plus the band, so two workgroups fit per CU at k = 2048); a longer list
+// takes the whole-row path.
+__global__ __launch_bounds__(kFinThreads) void topk_band_select_kernel(const TopkArgs a, const int cap) {
   constexpr int NT = kFinThreads;
-  __shared__ uint32_t s_key[kShortRow + 64];  // + a pad slot per lane (select_write)
-  __shared__ int32_t s_idx[kShortRow + 64];
+  extern __shared__ __align__(16) uint32_t s_dyn[];
+  uint32_t *const s_key = s_dyn;                                              // [cap + 64]
+  int32_t *const s_idx = reinterpret_cast<int32_t *>(s_dyn + cap + 64);       // [cap + 64]
   __shared__ RadixLds<NT> R;
   const int tid = threadIdx.x, r = blockIdx.x;
   const int len = row_len_of(a, r);
@@ -1072,7 +1076,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_band_select_kernel(const Top
   if (nl < 0) return;  // the first pass kept the whole row
   int32_t *out = a.idx + (int64_t)r * a.idx_ld;
   auto emit = [&](int pos, int32_t i) { out[pos] = i; };
-  if (nb <= kBandCap && nl >= keff && nl <= kBandListCap) {
+  if (nb <= kBandCap && nl >= keff && nl <= cap) {
     const uint2 *list = a.band.list + (int64_t)r * kBandListCap;
     for (int i = tid; i < nl; i += NT) {
       const uint2 e = list[i];
@@ -1082,7 +1086,27 @@ __global__ __launch_bounds__(kFinThreads) void topk_band_select_kernel(const Top
     __syncthreads();
     const int per = ((nl + NT - 1) / NT) | 1;
     select_write_any(
-        s_key, s_idx, nl, per, keff, R, [](int32_t) { return 0; }, [&](int pos, int32_t i, int32_t) { emit(pos, i); });
+        s_key, s_idx, nl, per, keff, R, [](int32_t) { return 0; }, [&](int pos, int32_t i, int32_t) { emit(pos, i); },
+        cap);
+  } else if (nb <= kBandCap && nl >= keff) {
+    // a list longer than the LDS arrays (nl <= keff + nb <= kBandListCap): the same selection
+    // read straight from the list in global memory
+    const uint2 *list = a.band.list + (int64_t)r * kBandListCap;
+    auto lkey = [&](int i) { return list[i].x; };
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for (int i = tid; i < nl; i += NT) {
+      const uint32_t k = lkey(i);
+      lo = min(lo, k);
+      hi = max(hi, k);
+    }
+    block_minmax<NT>(lo, hi, R);
+    int gt;
+    const uint32_t tau = radix_select<NT>(
+        [&](auto f) {
+          for (int i = tid; i < nl; i += NT) f(lkey(i));
+        },
+        keff, lo, hi, 32, R, gt, s_key, cap);
+    compact_rounds(lkey, nl, tau, keff - gt, [&](int pos, int i) { emit(pos, (int32_t)list[i].y); }, R.tmp);
   } else {
     // the whole row (rescored exactly when the band overflowed; a list shorter than keff
     // means a score fell outside its bound, and the approximate row is used)
@@ -1101,7 +1125,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_band_select_kernel(const Top
         [&](auto f) {
           for (int i = tid; i < len; i += NT) f(load(i));
         },
-        keff, lo, hi, 32, R, gt, s_key, kShortRow);
+        keff, lo, hi, 32, R, gt, s_key, cap);
     compact_rounds(load, len, tau, keff - gt, emit, R.tmp);
   }
   for (int i = keff + tid; i < a.k; i += NT) out[i] = -1;
@@ -1230,7 +1254,10 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
 hipError_t launch_topk_band_select(const TopkArgs &a, hipStream_t s) {
   if (a.n_rows == 0) return hipSuccess;
   if (a.band.e == nullptr || a.n_rows > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(topk_band_select_kernel, dim3(a.n_rows), dim3(kFinThreads), 0, s, a);
+  // list capacity: k plus room for the band, in whole wave-widths (k + 512 <= kBandListCap)
+  const int cap = min(kBandListCap, (a.k + 512 + 63) / 64 * 64);
+  const size_t dyn = 2 * sizeof(uint32_t) * (size_t)(cap + 64);
+  hipLaunchKernelGGL(topk_band_select_kernel, dim3(a.n_rows), dim3(kFinThreads), dyn, s, a, cap);
   return hipGetLastError();
 }
 
