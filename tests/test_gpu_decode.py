@@ -334,6 +334,41 @@ def test_mla_flags_out_of_range_index(d):
     check_attention(step.out, step.lse, ref_o, ref_l)
 
 
+@pytest.mark.parametrize("lat_fmt", [0, 1])
+def test_mla_large_batch_matches_oracle_and_small_batches(d, lat_fmt):
+    """80 rows x 9 token splits (k = 1100 in 128-token splits, the last one short): 720
+    workgroups, more than run at once.  Every row matches the oracle, and rows run again in a
+    three-row batch give the same bits."""
+    rng = np.random.default_rng(70 + lat_fmt)
+    ctx = [int(x) for x in rng.integers(1200, 3000, size=80)]
+    k = 1100
+    cache, dq, step = make(d, ctx, key_fmt=lat_fmt, lat_fmt=lat_fmt, seed=71 + lat_fmt, k=k, spare_rows=4)
+    idx = random_sets(rng, ctx, k, drop=0.05)
+    step.resolve()
+    step.idx.copy_(torch.from_numpy(idx))
+    step.attend()
+    torch.cuda.synchronize()
+    assert int(step.err.item()) == 0
+    oc = oracle.OracleCache(cache)
+    ref_o, ref_l = oracle.sparse_mla(oc, idx, dq.q_mla, 0, None, np.arange(len(ctx), dtype=np.int32), 12,
+                                     dq.sm_scale)
+    check_attention(step.out, step.lse, ref_o, ref_l)
+    rows = [0, 41, 79]
+    sel = torch.tensor(rows, device="cuda")
+    sub = W.PagedCache(**{**cache.__dict__, "block_table": cache.block_table[sel].contiguous(),
+                          "n_pages": cache.n_pages[sel].contiguous(), "ctx_len": cache.ctx_len[sel].contiguous()})
+    s3 = d.DecodeStep(sub, dq.q_idx[sel].contiguous(), dq.w[sel].contiguous(), dq.q_mla[sel].contiguous(),
+                      dq.sm_scale, k=k)
+    s3.resolve()
+    s3.idx.copy_(torch.from_numpy(idx[rows]))
+    s3.attend()
+    torch.cuda.synchronize()
+    assert int(s3.err.item()) == 0
+    for i, r in enumerate(rows):
+        assert torch.equal(s3.out[i].view(torch.int16), step.out[r].view(torch.int16)), f"row {r}"
+        assert torch.equal(s3.lse[i], step.lse[r]), f"row {r}"
+
+
 # ------------------------------------------------------------------- the chain
 
 def run_chain_and_check(d, cache, dq, step, k=2048):
