@@ -701,7 +701,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void mla_prefill_kernel(const MlaArg
   }
   // Subtile `sub`'s rows -> ring slot sub % kPfSlots, rows kPfRow bytes apart: load kk (of
   // 20; wave w issues kk = 5w .. 5w+4) fills slot chunks 64 kk .. 64 kk + 63.  Lanes on a row's
-  // padding chunk, past the rows, or on an invalid token read the pool's first bytes instead.
+  // padding chunk, past the rows, or on an invalid token read the pool's first bytes instead
+  // (P.V clears an invalid token's value bytes; its logit is masked).
   // LDS address of this wave's first 1 KB in slot 0 (wave w fills loads 5w .. 5w+4 of a slot)
   const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(lds_addr(s_raw[0]) + 1024 * kPfPer * wid);
   auto issue = [&](int sub) {
@@ -805,6 +806,22 @@ __global__ __launch_bounds__(kPfThreads, 1) void mla_prefill_kernel(const MlaArg
       for (int st = 0; st < 8; ++st)
         xv[st] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
             (__attribute__((address_space(3))) i32x2_t *)(vb + 16 * (st >> 2) * kPfRow + 32 * (st & 3)));
+      // Byte i of xv[4 s2 + db] is token 16 s2 + 8 g + i.  A token outside the set (padding, or
+      // past the set's end) has p = 0, but its bytes are whatever its gather lane read instead
+      // (the pool's first bytes), and 0 times a NaN code is NaN: its bytes are cleared (+0).
+      const uint32_t okm = s_ok[j];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const uint32_t b8 = (okm >> (16 * s2 + 8 * g)) & 0xFFu;
+        // bit i of a nibble -> byte i (the products' terms land on distinct bits, no carries)
+        const uint32_t mlo = (((b8 & 15u) * 0x00204081u) & 0x01010101u) * 0xFFu;
+        const uint32_t mhi = (((b8 >> 4) * 0x00204081u) & 0x01010101u) * 0xFFu;
+#pragma unroll
+        for (int db = 0; db < kPfBlocks; ++db) {
+          xv[4 * s2 + db][0] &= (int)mlo;
+          xv[4 * s2 + db][1] &= (int)mhi;
+        }
+      }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         bf16x8_t pt[NHT];

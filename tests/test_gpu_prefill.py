@@ -131,6 +131,39 @@ def test_mla_prefill_all_heads_per_row(d, lat_fmt, heads, k):
     assert np.isneginf(step.lse[5].cpu().numpy()).all() and (step.out[5].float() == 0).all()
 
 
+@pytest.mark.parametrize("lat_fmt,heads,q_fmt", [(0, 96, 1), (1, 96, 1), (0, 12, 0)])
+def test_mla_prefill_padding_with_nan_at_pool_start(d, lat_fmt, heads, q_fmt):
+    """Index sets with -1 padding, and the pool's first row all 0xFF (NaN in every format, as an
+    unused or uninitialised row may be): the kernels must not let the bytes they read for a
+    padding entry reach the output, where a zero softmax weight times NaN would give NaN."""
+    seed = 90 + heads + lat_fmt
+    base = W.build_cache([3000 + 16], key_fmt=lat_fmt, lat_fmt=lat_fmt, seed=seed, device="cuda", spare_rows=2)
+    rs = base.pool.shape[1]
+    pool = torch.cat([torch.full((1, rs), 0xFF, dtype=torch.uint8, device="cuda"), base.pool])
+    bt = torch.where(base.block_table >= 0, base.block_table + 1, base.block_table)
+    cache = W.PagedCache(**{**base.__dict__, "pool": pool, "block_table": bt.contiguous()})
+    pq = W.prefill_queries(3000, 16, heads, seed=seed, device="cuda")
+    log(f"[case] poisoned pool start: lat_fmt={lat_fmt} heads={heads} q_fmt={q_fmt}")
+    step = d.PrefillStep(cache, pq, k=2048, q_fmt=q_fmt)
+    rng = np.random.default_rng(seed)
+    rl = pq.row_len.cpu().numpy()
+    idx = np.full((pq.n_q, 2048), -1, np.int32)
+    for r in range(pq.n_q):
+        sel = np.sort(rng.choice(int(rl[r]), 1500, replace=False)).astype(np.int32)
+        idx[r, :len(sel)] = sel
+        idx[r, 700:710] = -1  # padding inside the set as well as after it
+    step.resolve()
+    step.idx.copy_(torch.from_numpy(idx))
+    step.attend()
+    torch.cuda.synchronize()
+    assert int(step.err.item()) == 0
+    assert torch.isfinite(step.out.float()).all() and torch.isfinite(step.lse).all()
+    q, qs = (pq.q_mla_fp8, pq.q_mla_scale) if q_fmt == 1 else (pq.q_mla_bf16, None)
+    oc = oracle.OracleCache(cache)
+    ref_o, ref_l = oracle.sparse_mla(oc, idx, q, q_fmt, qs, pq.q_req, heads, pq.sm_scale)
+    check_attention(step.out, step.lse, ref_o, ref_l)
+
+
 def test_mla_prefill_reference_far_below_a_later_max(d):
     """The FP8-latent prefill kernel fixes each head's softmax reference at its first subtile's
     max.  Here row 2 head 0's first subtile scores far below a later token (log2 logit gap
