@@ -28,7 +28,9 @@ FLAGS=(--offload-arch=gfx950 -O1 -g -fPIC -std=c++17 -Xclang -target-feature -Xc
        -I "$ROOT/include" -Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined
        -Xarch_host -fno-sanitize-recover=undefined -Xarch_host -fno-omit-frame-pointer)
 objs=()
-for src in abi.cpp resolve.hip indexer_scan.hip indexer_verify.hip indexer_gemm.hip topk.hip mla.hip dcp.hip; do
+# the library's sources, as the in-tree build lists them
+SRCS="$(cd "$ROOT/long_context_sparse_paged_amd" && python -c 'import build; print(" ".join(build.SOURCES))')"
+for src in $SRCS; do
     "$HIPCC" -x hip "${FLAGS[@]}" -c "$ROOT/long_context_sparse_paged_amd/csrc/$src" -o "$OUT/${src%.*}.o" 2>&1 \
         | grep -v "is not a recognized feature for this target" || true
     objs+=("$OUT/${src%.*}.o")
